@@ -1,0 +1,213 @@
+/*
+ * QSA sparse main-attention prefill -- plain FP32 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, obviously correct statement of
+ * what the GPU path must compute.  Only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load it.  The product library never
+ * calls it, and the two share no code, headers, tables or helpers.
+ *
+ * Source of the definition: the page "Qwen4-Exp QSA comes to Huawei's Ascend:
+ * inside SGLang's opt-in CANN prefill PR" (orcarouter.ai blog).
+ *
+ *  - Section "What the pull request actually adds", layout-embedding
+ *    paragraph: main attention is ordinary softmax(scale * Q K^T) V; the
+ *    Ascend packing [K,V] / [Q,0] only re-expresses it, so the plain
+ *    definition below is the exact target.  The D=256 scale is kept.
+ *  - Same section, "Sizing bounds" bullet: -1 marks an unused selection entry
+ *    (tail or interior), and a row with nothing selected outputs zero.
+ *  - Section "Nine tests that passed, ...": the reference is FP32 on the CPU,
+ *    computed from the same BF16 inputs; slots are unordered physical cache
+ *    slots; widths include zero.
+ *
+ * Readings where the page is silent (each is listed in the design notes):
+ *  - query head h uses KV head floor(h / G), G = Hq / Hkv (contiguous groups);
+ *  - -1 anywhere in a row is "no slot"; any other value outside [0, S) is an
+ *    error (the oracle refuses the whole call);
+ *  - duplicates are kept: every selection entry is one softmax term;
+ *  - scores accumulate in FP32 in d order, exp is libm expf, and the output
+ *    stays FP32 (the GPU's BF16 output is compared against it).
+ *
+ * Parity pins (tests, not here): FP64 brute-force dense masked attention,
+ * torch's scaled_dot_product_attention for full and causal selections, and
+ * closed forms (single slot, uniform weights, identical V rows, empty rows).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum {
+    ORACLE_OK = 0,
+    ORACLE_BAD_SLOT = 1,  /* an entry is neither -1 nor in [0, S) */
+    ORACLE_BAD_SHAPE = 2, /* Hq % Hkv != 0, negative sizes, ... */
+    ORACLE_NO_MEMORY = 3,
+};
+
+/* BF16 is the upper half of an IEEE binary32; widening is exact. */
+static float bf16_to_float(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/*
+ * Selection-list filter (the "-1 padding" rule of the "Sizing bounds" bullet):
+ * for each token row t keep, in their original order, the entries that name a
+ * slot in [0, S).  list[t*W + i] for i < count[t] receives the kept entries;
+ * n_bad[t] counts entries that are neither -1 nor a valid slot.
+ */
+int qsa_oracle_compact(const int32_t *slot_idx, int64_t stride_t, int64_t T,
+                       int64_t W, int64_t S, int32_t *list, int64_t *count,
+                       int64_t *n_bad)
+{
+    if (T < 0 || W < 0 || S < 0)
+        return ORACLE_BAD_SHAPE;
+    for (int64_t t = 0; t < T; ++t) {
+        const int32_t *row = slot_idx + t * stride_t;
+        int64_t n = 0, bad = 0;
+        for (int64_t j = 0; j < W; ++j) {
+            int32_t s = row[j];
+            if (s >= 0 && (int64_t)s < S)
+                list[t * W + n++] = s;
+            else if (s != -1)
+                ++bad;
+        }
+        count[t] = n;
+        n_bad[t] = bad;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * One (token, query head) output row, straight from the definition:
+ *   z_j = scale * sum_d q[d] k_j[d]          (FP32, d order)
+ *   m   = max_j z_j
+ *   p_j = expf(z_j - m),  l = sum_j p_j      (j order)
+ *   o[d] = (sum_j p_j v_j[d]) / l
+ * An empty selection gives +0.0 everywhere.
+ */
+static int one_row(const uint16_t *q_row, const uint16_t *k, int64_t k_ss,
+                   const uint16_t *v, int64_t v_ss, const int32_t *sel,
+                   int64_t W, int64_t S, int32_t D, float scale, float *z,
+                   int32_t *slots, float *o)
+{
+    int64_t n = 0;
+    for (int64_t j = 0; j < W; ++j) {
+        int32_t s = sel[j];
+        if (s == -1)
+            continue;
+        if (s < 0 || (int64_t)s >= S)
+            return ORACLE_BAD_SLOT;
+        const uint16_t *k_row = k + (int64_t)s * k_ss;
+        float dot = 0.0f;
+        for (int32_t d = 0; d < D; ++d)
+            dot += bf16_to_float(q_row[d]) * bf16_to_float(k_row[d]);
+        z[n] = scale * dot;
+        slots[n] = s;
+        ++n;
+    }
+    for (int32_t d = 0; d < D; ++d)
+        o[d] = 0.0f;
+    if (n == 0)
+        return ORACLE_OK;
+
+    float m = z[0];
+    for (int64_t i = 1; i < n; ++i)
+        if (z[i] > m)
+            m = z[i];
+    float l = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        z[i] = expf(z[i] - m);
+        l += z[i];
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        const uint16_t *v_row = v + (int64_t)slots[i] * v_ss;
+        for (int32_t d = 0; d < D; ++d)
+            o[d] += z[i] * bf16_to_float(v_row[d]);
+    }
+    for (int32_t d = 0; d < D; ++d)
+        o[d] = o[d] / l;
+    return ORACLE_OK;
+}
+
+/*
+ * Sparse prefill for a chosen set of token rows.
+ *
+ * q        [T, Hq, D]  bf16 bits, element strides (q_st, q_sh, 1)
+ * k, v     [S, Hkv, D] bf16 bits, element strides (x_ss, x_sh, 1)
+ * slot_idx [T, W]      int32, element strides (s_st, 1)
+ * rows     token indices to evaluate (nrows of them); NULL means 0..nrows-1
+ * out      [nrows, Hq, D] FP32, contiguous
+ * nthreads OpenMP threads (<= 0: the runtime default)
+ *
+ * Returns ORACLE_OK, or ORACLE_BAD_SLOT if any evaluated row holds an entry
+ * outside [0, S) other than -1 (then out is unspecified).
+ */
+int qsa_oracle_prefill(const uint16_t *q, int64_t q_st, int64_t q_sh,
+                       const uint16_t *k, int64_t k_ss, int64_t k_sh,
+                       const uint16_t *v, int64_t v_ss, int64_t v_sh,
+                       const int32_t *slot_idx, int64_t s_st, int64_t S,
+                       int64_t W, int32_t Hq, int32_t Hkv, int32_t D,
+                       float scale, const int64_t *rows, int64_t nrows,
+                       float *out, int32_t nthreads)
+{
+    if (Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || W < 0 || S < 0 ||
+        nrows < 0)
+        return ORACLE_BAD_SHAPE;
+    const int32_t G = Hq / Hkv;
+    int status = ORACLE_OK;
+
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+#pragma omp parallel
+    {
+        float *z = (float *)malloc(sizeof(float) * (size_t)(W > 0 ? W : 1));
+        int32_t *slots =
+            (int32_t *)malloc(sizeof(int32_t) * (size_t)(W > 0 ? W : 1));
+        if (!z || !slots) {
+#pragma omp atomic write
+            status = ORACLE_NO_MEMORY;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t work = 0; work < nrows * (int64_t)Hq; ++work) {
+                int64_t r = work / Hq;
+                int32_t h = (int32_t)(work % Hq);
+                int64_t t = rows ? rows[r] : r;
+                int32_t g = h / G;
+                int rc = one_row(q + t * q_st + (int64_t)h * q_sh,
+                                 k + (int64_t)g * k_sh, k_ss,
+                                 v + (int64_t)g * v_sh, v_ss,
+                                 slot_idx + t * s_st, W, S, D, scale, z, slots,
+                                 out + (r * Hq + h) * (int64_t)D);
+                if (rc != ORACLE_OK) {
+#pragma omp atomic write
+                    status = rc;
+                }
+            }
+        }
+        free(z);
+        free(slots);
+    }
+    return status;
+}
+
+/* Threads the oracle will use when nthreads <= 0. */
+int qsa_oracle_default_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
