@@ -1,0 +1,208 @@
+"""Benchmark of QSA sparse main-attention prefill on one MI355X.
+
+One step = the whole hot path on one batch of resident synthetic input:
+index validation/compaction (qsa_compact_slots) followed by the gather
+attention (qsa_sparse_attend), both through the C ABI on torch's current
+stream.  The default workload is the long prefill of the page "Qwen4-Exp QSA
+comes to Huawei's Ascend: inside SGLang's opt-in CANN prefill PR" (section
+"Nine tests that passed, ..."): 7,810 query tokens, a 65,536-slot cache,
+2,051 selected slots per token, (Hq, Hkv) = (16, 2), D = 256, BF16.
+
+Prints one JSON line: selected (query-head, slot) pairs per second, the
+attention kernel's achieved bytes against the HBM roofline, and the FP32 CPU
+oracle timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_long_prefill_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "top_sparse_attention_amd", "csrc", "qsa_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_prefill",
+                    choices=["tiny", "edge_mix", "long_prefill", "two_request",
+                             "max_cache_6_1", "max_cache_3_1"])
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="token rows of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy first (for counter calibration)")
+    ap.add_argument("--seed", type=int, default=None)
+    return ap.parse_args()
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM-side bytes per attention launch from the committed counter summary,
+    or None if it is missing or was taken on another version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_sha() or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import qsa_inputs as qi
+    import top_sparse_attention_amd as qsa
+    from qsa_testutil import bf16_tensor_to_f32, empty_row_mask, gate, upload
+
+    qsa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = qi.WORKLOADS[args.workload]
+    case = gen() if args.seed is None else gen(args.seed)
+    T, S, W, Hq, Hkv = case.T, case.S, case.W, case.Hq, case.Hkv
+    q, k, v, sl = upload(case, dev)
+    out = torch.empty((T, Hq, case.D), dtype=torch.bfloat16, device=dev)
+    ws = qsa.new_workspace(T, W, dev)
+    scale = case.scale if case.scale is not None else 1.0 / np.sqrt(case.D)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step():
+        qsa.compact_slots(sl, S, ws)
+        qsa.sparse_attend(q, k, v, ws, W, scale=scale, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    a0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    a1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(K):
+        qsa.compact_slots(sl, S, ws)
+        a0[i].record()
+        qsa.sparse_attend(q, k, v, ws, W, scale=scale, out=out)
+        a1[i].record()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / K
+    attn_ms = [a0[i].elapsed_time(a1[i]) for i in range(K)]
+    attn_avg = float(np.mean(attn_ms))
+
+    # Gather ceiling: the same rows, loads and launch shape with no arithmetic.
+    sink = torch.empty(T * Hkv, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        qsa.gather_ceiling(k, v, ws, T, W, sink)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(K):
+        qsa.gather_ceiling(k, v, ws, T, W, sink)
+    c1.record()
+    torch.cuda.synchronize()
+    ceil_ms = c0.elapsed_time(c1) / K
+
+    valid = (case.slot_idx >= 0) & (case.slot_idx < S)
+    n_t = valid.sum(axis=1).astype(np.int64)
+    pairs = int(n_t.sum()) * Hq
+    # Algorithmic bytes of one attention launch: every selected K and V row of
+    # every (token, KV head) once, its slot index, Q in and O out.
+    attn_bytes = int(n_t.sum()) * Hkv * (2 * case.D * 2 + 4) + 2 * T * Hq * case.D * 2
+    gather_bytes = int(n_t.sum()) * Hkv * 2 * case.D * 2
+    flops = pairs * 4 * case.D
+    achieved = attn_bytes / (attn_avg * 1e-3) / 1e9
+
+    # Parity of this very output on a sample of rows (the oracle is the judge).
+    import oracle
+    rows = qi.sample_rows(T, 16, seed=11)
+    want = oracle.prefill(case.q, case.k_cache, case.v_cache, case.slot_idx, scale, rows=rows)
+    got = bf16_tensor_to_f32(out[torch.as_tensor(rows, device=dev)])
+    parity = gate(got, want, empty_row_mask(case.slot_idx, S, rows))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu_rows = qi.sample_rows(T, min(args.cpu_rows, T), seed=12)
+        threads = oracle.default_threads()
+        c_t0 = time.perf_counter()
+        oracle.prefill(case.q, case.k_cache, case.v_cache, case.slot_idx, scale, rows=cpu_rows,
+                       nthreads=threads)
+        c_dt = time.perf_counter() - c_t0
+        cpu_pairs = int(n_t[cpu_rows].sum()) * Hq
+        cpu = {"value": cpu_pairs / c_dt, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+               "sample": f"{cpu_rows.size} of {T} token rows (all {Hq} heads, seeded, incl. first "
+                         f"and last), {cpu_pairs} pairs in {c_dt:.2f} s"}
+
+    traffic = measured_traffic(args.workload)
+    record = {
+        "metric": "selected (query-head,slot) pairs/sec + achieved gather GB/s & % HBM roofline",
+        "value": pairs / (ms_step * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case.name, "T": T, "S": S, "W": W, "Hq": Hq, "Hkv": Hkv,
+                   "D": case.D, "scale": scale, "seed": case.info.get("seed"),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "attend_kernel_ms": attn_avg,
+        "attend_kernel_ms_min": float(np.min(attn_ms)),
+        "gather_GBps": gather_bytes / (attn_avg * 1e-3) / 1e9,
+        "gather_ceiling": {"ms": ceil_ms, "GBps": gather_bytes / (ceil_ms * 1e-3) / 1e9},
+        "mfma_frac": flops / (attn_avg * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "attend_bytes_per_launch": attn_bytes,
+        "parity": {"rows": int(rows.size), **{k_: v_ for k_, v_ in parity.items()
+                                              if k_ != "rows"}},
+        "peak_allocated_MiB": torch.cuda.max_memory_allocated(dev) / 2**20,
+    }
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * qsa.h -- C ABI of libqsa, QSA sparse main-attention prefill on MI355X (gfx950).
+ *
+ * The operation (page "Qwen4-Exp QSA comes to Huawei's Ascend: inside
+ * SGLang's opt-in CANN prefill PR", section "What the pull request actually
+ * adds"): every query token t attends only to the physical KV-cache slots its
+ * indexer selected,
+ *
+ *     out[t, h, :] = sum_j softmax_j(scale * q[t,h,:] . k[s_j, g, :]) * v[s_j, g, :]
+ *
+ * over the entries s_j of slot_idx[t, :] that are not -1, with query head h
+ * reading KV head g = h / (Hq / Hkv) (grouped query heads, contiguous groups).
+ * BF16 inputs and output, head dim 256 ("Hardware and dtype" bullet), any
+ * Hq % Hkv == 0 with no padding of the head ratio ("Head shapes" bullet).  A
+ * row with no selected slot -- all -1, or W == 0 -- outputs exactly +0.0
+ * ("Sizing bounds" bullet).  Slots may come in any order and -1 may sit
+ * anywhere in a row (section "Nine tests that passed, ...").
+ *
+ * Conventions for every entry point:
+ *  - Pointers in the views and the workspace are DEVICE pointers on the
+ *    current HIP device; the caller owns all memory.  The library allocates
+ *    nothing and keeps no pointer after the call returns.
+ *  - Strides are in elements.  The innermost stride must be 1; the other
+ *    strides of BF16 views must be multiples of 8 elements (16 bytes) and
+ *    their base pointers 16-byte aligned.  Strides may be larger than the
+ *    packed size (views of bigger buffers are fine).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work: they return before the kernels run and never synchronize,
+ *    except qsa_check_status, which synchronizes `stream`.
+ *  - Argument errors are detected on the host before anything is enqueued; the
+ *    call then returns a non-zero qsa_status, writes nothing and
+ *    qsa_last_error() describes the problem.  There is no fallback path.
+ *  - Entries of slot_idx that are neither -1 nor in [0, S) are dropped (never
+ *    dereferenced) and counted; qsa_check_status reports them.
+ *  - Calls on different streams with different workspaces may run
+ *    concurrently; calls sharing a workspace must be stream-ordered.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qsa_status {
+    QSA_OK = 0,
+    QSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    QSA_ERR_SHAPE = 2,       /* sizes disagree or are negative */
+    QSA_ERR_STRIDE = 3,      /* innermost stride != 1, misaligned base or stride */
+    QSA_ERR_SCALE = 4,       /* scale is NaN or infinite */
+    QSA_ERR_WORKSPACE = 5,   /* workspace NULL, misaligned or too small */
+    QSA_ERR_SLOT_RANGE = 6,  /* (qsa_check_status) some entry was neither -1 nor in [0, S) */
+    QSA_ERR_UNSUPPORTED = 7, /* head dim other than 256, sizes beyond 32-bit limits */
+    QSA_ERR_HIP = 8,         /* a HIP runtime call failed */
+    QSA_ERR_ALIAS = 9        /* out overlaps an input */
+} qsa_status;
+
+/* A strided 3-D BF16 tensor: q and out are [T, Hq, D]; k_cache and v_cache
+ * are [S, Hkv, D].  `data` points at element [0][0][0]. */
+typedef struct qsa_bf16_view {
+    void *data;
+    int64_t size[3];
+    int64_t stride[3];
+} qsa_bf16_view;
+
+/* A strided 2-D int32 tensor: slot_idx is [T, W]; -1 means "no slot". */
+typedef struct qsa_i32_view {
+    const int32_t *data;
+    int64_t size[2];
+    int64_t stride[2];
+} qsa_i32_view;
+
+/* Where the compaction pass leaves its results inside a workspace (byte
+ * offsets from the workspace base):
+ *   list:  int32 [T][row_stride]; row t holds its count[t] valid slots in
+ *          input order, then -1 up to the next multiple of 32;
+ *   count: int32 [T], number of valid entries of row t;
+ *   n_bad: int32 [T], entries of row t that were neither -1 nor in [0, S). */
+typedef struct qsa_workspace_map {
+    int64_t list_offset;
+    int64_t row_stride;
+    int64_t count_offset;
+    int64_t bad_offset;
+    int64_t total_bytes;
+} qsa_workspace_map;
+
+/* Library version string, e.g. "libqsa 0.1.0 gfx950". */
+const char *qsa_version(void);
+
+/* Short text for a status code. */
+const char *qsa_status_string(qsa_status status);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char *qsa_last_error(void);
+
+/* Workspace bytes needed for T tokens of W selection entries (T, W >= 0).
+ * Returns 0 for negative sizes. */
+size_t qsa_workspace_bytes(int64_t T, int64_t W);
+
+/* Fill *map with the workspace layout for T, W (see qsa_workspace_map). */
+qsa_status qsa_workspace_layout(int64_t T, int64_t W, qsa_workspace_map *map);
+
+/*
+ * Index validation and stable compaction (the -1 rules of the "Sizing
+ * bounds" bullet; unordered slots of section "Nine tests that passed, ...").
+ * For every row t of slot_idx [T, W], writes into the workspace the entries in
+ * [0, S) in their original order, their count, and the number of invalid
+ * entries (see qsa_workspace_map).  S is the number of cache slots.
+ */
+qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * Gather attention over a workspace already filled by qsa_compact_slots for
+ * the same T and W (the softmax(scale * Q K^T) V of the layout-embedding
+ * paragraph, restricted to each token's listed slots).  Rows with count 0
+ * receive +0.0.  q/out [T, Hq, 256], k_cache/v_cache [S, Hkv, 256]; W is the
+ * selection width the workspace was compacted with; scale must be finite.
+ */
+qsa_status qsa_sparse_attend(const qsa_bf16_view *q,
+                             const qsa_bf16_view *k_cache,
+                             const qsa_bf16_view *v_cache, int64_t W,
+                             float scale, const void *workspace,
+                             size_t workspace_bytes, qsa_bf16_view *out,
+                             void *stream);
+
+/*
+ * The whole sparse prefill: qsa_compact_slots followed by qsa_sparse_attend,
+ * enqueued on `stream`.  slot_idx is [T, W] with T = q->size[0].  Pass
+ * scale = 1/sqrt(256) for the default scale of the page.  The workspace must
+ * hold qsa_workspace_bytes(T, W) bytes, 256-byte aligned.
+ */
+qsa_status qsa_sparse_prefill(const qsa_bf16_view *q,
+                              const qsa_bf16_view *k_cache,
+                              const qsa_bf16_view *v_cache,
+                              const qsa_i32_view *slot_idx, float scale,
+                              qsa_bf16_view *out, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
+ * Synchronizes `stream`, then reads the invalid-entry counts that the last
+ * compaction into `workspace` (for T, W) left.  Writes their total to
+ * *n_bad (if not NULL) and returns QSA_ERR_SLOT_RANGE if it is non-zero.
+ * This is the only entry point that waits for the device.
+ */
+qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes,
+                            int64_t T, int64_t W, void *stream,
+                            int64_t *n_bad);
+
+/*
+ * Measurement aid: reads exactly the K and V rows that qsa_sparse_attend
+ * would read for this workspace (same slots, same KV heads, same load
+ * pattern) and folds them into one checksum word per (token, KV head) in
+ * sink[T * Hkv] (device memory, caller-owned), with no attention arithmetic.
+ * Its duration is the practical gather ceiling for the workload.
+ */
+qsa_status qsa_gather_ceiling(const qsa_bf16_view *k_cache,
+                              const qsa_bf16_view *v_cache, int64_t T,
+                              int64_t W, const void *workspace,
+                              size_t workspace_bytes, uint32_t *sink,
+                              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -71,6 +71,9 @@ class Case:
     def base_of(self, view: np.ndarray) -> np.ndarray:
         """The array in ``bases`` whose memory ``view`` lies in."""
         for b in self.bases.values():
+            if view is b or view.base is b:
+                return b
+        for b in self.bases.values():
             if np.shares_memory(view, b):
                 return b
         raise KeyError("view is not backed by any base array")

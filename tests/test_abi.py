@@ -1,0 +1,156 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every entry
+point its header declares, and rejects bad arguments on the host before any
+HIP call (these calls pass made-up device addresses, which the checks refuse
+before anything could read them)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_sparse_attention_amd as qsa
+
+import torch
+
+# These calls hand made-up device addresses to the library and rely on its
+# host-side checks to refuse them; never let them reach a real GPU.
+host_only = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                               reason="passes made-up device addresses: host-only")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+def _lib():
+    if not os.path.exists(qsa.library_path()):
+        from top_sparse_attention_amd import _build
+        _build.build()
+    return qsa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = _lib()
+    names = declared_functions()
+    assert "qsa_sparse_prefill" in names and len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in qsa.h but not exported"
+
+
+def test_version_and_status_strings():
+    lib = _lib()
+    assert qsa.version().startswith("libqsa")
+    for code, name in qsa.STATUS_NAMES.items():
+        assert lib.qsa_status_string(code).decode()
+        assert name.startswith("QSA_")
+
+
+def test_workspace_layout():
+    _lib()
+    m = qsa.workspace_layout(7810, 2051)
+    assert m["row_stride"] == 2080                 # next multiple of 32
+    assert m["list_offset"] == 0
+    assert m["count_offset"] >= 7810 * 2080 * 4 and m["count_offset"] % 256 == 0
+    assert m["bad_offset"] >= m["count_offset"] + 7810 * 4
+    assert m["total_bytes"] == qsa.workspace_bytes(7810, 2051)
+    assert qsa.workspace_bytes(0, 0) == 0
+    assert qsa.workspace_bytes(-1, 3) == 0
+    assert qsa.workspace_layout(5, 0)["row_stride"] == 0
+
+
+FAKE = 1 << 32        # an aligned address no test ever dereferences
+
+
+def view(size, stride, data=FAKE):
+    return qsa.BF16View(data, (ctypes.c_int64 * 3)(*size), (ctypes.c_int64 * 3)(*stride))
+
+
+def ivew(size, stride, data=FAKE):
+    return qsa.I32View(data, (ctypes.c_int64 * 2)(*size), (ctypes.c_int64 * 2)(*stride))
+
+
+def good(T=4, Hq=4, S=64, Hkv=2, W=8):
+    q = view((T, Hq, 256), (Hq * 256, 256, 1), FAKE)
+    k = view((S, Hkv, 256), (Hkv * 256, 256, 1), FAKE + (1 << 24))
+    v = view((S, Hkv, 256), (Hkv * 256, 256, 1), FAKE + (2 << 24))
+    o = view((T, Hq, 256), (Hq * 256, 256, 1), FAKE + (3 << 24))
+    s = ivew((T, W), (W, 1), FAKE + (4 << 24))
+    return q, k, v, o, s
+
+
+def prefill(q, k, v, s, o, scale=0.0625, ws=FAKE + (5 << 24), ws_bytes=1 << 30):
+    lib = _lib()
+    r = ctypes.byref
+    return lib.qsa_sparse_prefill(r(q), r(k), r(v), r(s), scale, r(o), ws, ws_bytes, None)
+
+
+BAD_CASES = {
+    "head dim 128": (lambda q, k, v, o, s: setattr(q, "size", (ctypes.c_int64 * 3)(4, 4, 128)),
+                     "QSA_ERR_UNSUPPORTED"),
+    "q stride over D": (lambda q, k, v, o, s: q.stride.__setitem__(2, 2), "QSA_ERR_STRIDE"),
+    "misaligned k base": (lambda q, k, v, o, s: setattr(k, "data", FAKE + 2), "QSA_ERR_STRIDE"),
+    "odd v token stride": (lambda q, k, v, o, s: v.stride.__setitem__(0, 516), "QSA_ERR_STRIDE"),
+    "Hq not multiple of Hkv": (lambda q, k, v, o, s: (
+        setattr(q, "size", (ctypes.c_int64 * 3)(4, 3, 256)),
+        setattr(o, "size", (ctypes.c_int64 * 3)(4, 3, 256))), "QSA_ERR_SHAPE"),
+    "out shape differs": (lambda q, k, v, o, s: o.size.__setitem__(0, 5), "QSA_ERR_SHAPE"),
+    "v shape differs": (lambda q, k, v, o, s: v.size.__setitem__(0, 63), "QSA_ERR_SHAPE"),
+    "slot rows differ": (lambda q, k, v, o, s: s.size.__setitem__(0, 3), "QSA_ERR_SHAPE"),
+    "slot stride over W": (lambda q, k, v, o, s: s.stride.__setitem__(1, 2), "QSA_ERR_STRIDE"),
+    "null q data": (lambda q, k, v, o, s: setattr(q, "data", None), "QSA_ERR_NULL"),
+    "null slot data": (lambda q, k, v, o, s: setattr(s, "data", None), "QSA_ERR_NULL"),
+    "negative size": (lambda q, k, v, o, s: k.size.__setitem__(0, -1), "QSA_ERR_SHAPE"),
+    "out aliases q": (lambda q, k, v, o, s: setattr(o, "data", q.data), "QSA_ERR_ALIAS"),
+    "out overlaps v": (lambda q, k, v, o, s: setattr(o, "data", v.data + 64), "QSA_ERR_ALIAS"),
+}
+
+
+@host_only
+@pytest.mark.parametrize("name", sorted(BAD_CASES))
+def test_bad_arguments_are_rejected_on_the_host(name):
+    q, k, v, o, s = good()
+    mutate, want = BAD_CASES[name]
+    mutate(q, k, v, o, s)
+    status = prefill(q, k, v, s, o)
+    assert qsa.STATUS_NAMES[status] == want, _lib().qsa_last_error()
+    assert _lib().qsa_last_error().decode()
+
+
+@host_only
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), -float("inf")])
+def test_non_finite_scale_is_rejected(scale):
+    q, k, v, o, s = good()
+    assert qsa.STATUS_NAMES[prefill(q, k, v, s, o, scale=scale)] == "QSA_ERR_SCALE"
+
+
+@host_only
+def test_workspace_checks():
+    q, k, v, o, s = good()
+    need = qsa.workspace_bytes(4, 8)
+    assert qsa.STATUS_NAMES[prefill(q, k, v, s, o, ws=None)] == "QSA_ERR_WORKSPACE"
+    assert qsa.STATUS_NAMES[prefill(q, k, v, s, o, ws_bytes=need - 1)] == "QSA_ERR_WORKSPACE"
+    assert qsa.STATUS_NAMES[prefill(q, k, v, s, o, ws=FAKE + 16)] == "QSA_ERR_WORKSPACE"
+
+
+@host_only
+def test_null_view_pointers():
+    lib = _lib()
+    q, k, v, o, s = good()
+    r = ctypes.byref
+    assert lib.qsa_sparse_prefill(None, r(k), r(v), r(s), 0.0625, r(o), FAKE, 1 << 30, None) == 1
+    assert lib.qsa_sparse_prefill(r(q), r(k), r(v), None, 0.0625, r(o), FAKE, 1 << 30, None) == 1
+    assert lib.qsa_compact_slots(None, 64, FAKE, 1 << 30, None) == 1
+
+
+def test_python_binding_rejects_wrong_dtypes():
+    _lib()
+    q = torch.zeros(2, 2, 256, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        qsa._bf16_view(q, "q")
+    with pytest.raises(TypeError):
+        qsa._i32_view(torch.zeros(2, 3, dtype=torch.int64), "slot_idx")

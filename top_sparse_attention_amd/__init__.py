@@ -1,0 +1,252 @@
+"""Python binding of libqsa: QSA sparse main-attention prefill on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libqsa.so`` (built in-tree by ``_build.py``); torch supplies the
+device memory and the current stream.  If the library is missing the calls
+raise instead of computing anything some other way.
+
+The operation is the one on the page "Qwen4-Exp QSA comes to Huawei's Ascend:
+inside SGLang's opt-in CANN prefill PR" (section "What the pull request
+actually adds"): ``out[t,h] = softmax(scale * q[t,h] . k[s]) . v[s]`` over the
+slots ``s`` of ``slot_idx[t]`` that are not -1, with query head ``h`` reading
+KV head ``h // (Hq // Hkv)``; rows with nothing selected are exactly zero.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "QsaError", "library_path", "load_library", "version", "workspace_bytes",
+    "workspace_layout", "new_workspace", "compact_slots", "compacted_lists",
+    "sparse_attend", "sparse_prefill", "check_status", "gather_ceiling",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqsa.so")
+HEAD_DIM = 256
+
+QSA_OK = 0
+STATUS_NAMES = {
+    0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_STRIDE",
+    4: "QSA_ERR_SCALE", 5: "QSA_ERR_WORKSPACE", 6: "QSA_ERR_SLOT_RANGE",
+    7: "QSA_ERR_UNSUPPORTED", 8: "QSA_ERR_HIP", 9: "QSA_ERR_ALIAS",
+}
+
+
+class QsaError(RuntimeError):
+    """A non-OK qsa_status; ``status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class BF16View(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("size", ctypes.c_int64 * 3),
+                ("stride", ctypes.c_int64 * 3)]
+
+
+class I32View(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("size", ctypes.c_int64 * 2),
+                ("stride", ctypes.c_int64 * 2)]
+
+
+class WorkspaceMap(ctypes.Structure):
+    _fields_ = [("list_offset", ctypes.c_int64), ("row_stride", ctypes.c_int64),
+                ("count_offset", ctypes.c_int64), ("bad_offset", ctypes.c_int64),
+                ("total_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libqsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m top_sparse_attention_amd._build` "
+            "or __graft_entry__.build(); there is no fallback implementation")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER
+    vp, i64, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.qsa_version.restype = ctypes.c_char_p
+    lib.qsa_version.argtypes = []
+    lib.qsa_status_string.restype = ctypes.c_char_p
+    lib.qsa_status_string.argtypes = [ctypes.c_int]
+    lib.qsa_last_error.restype = ctypes.c_char_p
+    lib.qsa_last_error.argtypes = []
+    lib.qsa_workspace_bytes.restype = sz
+    lib.qsa_workspace_bytes.argtypes = [i64, i64]
+    lib.qsa_workspace_layout.restype = ctypes.c_int
+    lib.qsa_workspace_layout.argtypes = [i64, i64, P(WorkspaceMap)]
+    lib.qsa_compact_slots.restype = ctypes.c_int
+    lib.qsa_compact_slots.argtypes = [P(I32View), i64, vp, sz, vp]
+    lib.qsa_sparse_attend.restype = ctypes.c_int
+    lib.qsa_sparse_attend.argtypes = [P(BF16View), P(BF16View), P(BF16View), i64, f32,
+                                      vp, sz, P(BF16View), vp]
+    lib.qsa_sparse_prefill.restype = ctypes.c_int
+    lib.qsa_sparse_prefill.argtypes = [P(BF16View), P(BF16View), P(BF16View), P(I32View),
+                                       f32, P(BF16View), vp, sz, vp]
+    lib.qsa_check_status.restype = ctypes.c_int
+    lib.qsa_check_status.argtypes = [vp, sz, i64, i64, vp, P(i64)]
+    lib.qsa_gather_ceiling.restype = ctypes.c_int
+    lib.qsa_gather_ceiling.argtypes = [P(BF16View), P(BF16View), i64, i64, vp, sz, vp, vp]
+    _lib = lib
+    return lib
+
+
+def _raise_on(status: int) -> None:
+    if status != QSA_OK:
+        raise QsaError(status, load_library().qsa_last_error().decode())
+
+
+def version() -> str:
+    return load_library().qsa_version().decode()
+
+
+def _bf16_view(t: torch.Tensor, name: str) -> BF16View:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be 3-D, got shape {tuple(t.shape)}")
+    if t.numel() and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return BF16View(t.data_ptr() if t.numel() else 0, (ctypes.c_int64 * 3)(*t.shape),
+                    (ctypes.c_int64 * 3)(*t.stride()))
+
+
+def _i32_view(t: torch.Tensor, name: str) -> I32View:
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.numel() and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return I32View(t.data_ptr() if t.numel() else 0, (ctypes.c_int64 * 2)(*t.shape),
+                   (ctypes.c_int64 * 2)(*t.stride()))
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(T: int, W: int) -> int:
+    return int(load_library().qsa_workspace_bytes(T, W))
+
+
+def workspace_layout(T: int, W: int) -> dict:
+    m = WorkspaceMap()
+    _raise_on(load_library().qsa_workspace_layout(T, W, ctypes.byref(m)))
+    return {f: getattr(m, f) for f, _ in WorkspaceMap._fields_}
+
+
+def new_workspace(T: int, W: int, device="cuda") -> torch.Tensor:
+    """A uint8 device buffer large enough for T tokens of width W."""
+    return torch.empty(max(workspace_bytes(T, W), 1), dtype=torch.uint8, device=device)
+
+
+def compact_slots(slot_idx: torch.Tensor, S: int,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Enqueue the validation/compaction pass; returns the workspace."""
+    T, W = slot_idx.shape
+    if workspace is None:
+        workspace = new_workspace(T, W, slot_idx.device)
+    sv = _i32_view(slot_idx, "slot_idx")
+    _raise_on(load_library().qsa_compact_slots(
+        ctypes.byref(sv), S, workspace.data_ptr(), workspace.numel(), _stream(workspace.device)))
+    return workspace
+
+
+def compacted_lists(workspace: torch.Tensor, T: int, W: int):
+    """Views of a compacted workspace: (list [T, row_stride], count [T], n_bad [T])."""
+    m = workspace_layout(T, W)
+    ws32 = workspace.view(torch.int32)
+    lst = ws32[m["list_offset"] // 4: m["list_offset"] // 4 + T * m["row_stride"]]
+    cnt = ws32[m["count_offset"] // 4: m["count_offset"] // 4 + T]
+    bad = ws32[m["bad_offset"] // 4: m["bad_offset"] // 4 + T]
+    return lst.view(T, m["row_stride"]), cnt, bad
+
+
+def _default_scale(scale: Optional[float], D: int) -> float:
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def sparse_attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  workspace: torch.Tensor, W: int, scale: Optional[float] = None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gather attention over an already compacted workspace."""
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    qv, kv, vv, ov = (_bf16_view(q, "q"), _bf16_view(k_cache, "k_cache"),
+                      _bf16_view(v_cache, "v_cache"), _bf16_view(out, "out"))
+    _raise_on(load_library().qsa_sparse_attend(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), W,
+        _default_scale(scale, q.shape[-1]), workspace.data_ptr(), workspace.numel(),
+        ctypes.byref(ov), _stream(q.device)))
+    return out
+
+
+def sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   slot_idx: torch.Tensor, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   check: bool = False) -> torch.Tensor:
+    """QSA sparse prefill: compaction + gather attention, on the current stream.
+
+    q [T, Hq, 256], k_cache/v_cache [S, Hkv, 256] bfloat16 (strided views are
+    fine), slot_idx [T, W] int32 with -1 for "no slot".  ``scale`` None means
+    1/sqrt(256).  ``check=True`` synchronizes and raises if any entry was
+    neither -1 nor a valid slot.
+    """
+    T, W = slot_idx.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if workspace is None:
+        workspace = new_workspace(T, W, q.device)
+    qv, kv, vv, ov = (_bf16_view(q, "q"), _bf16_view(k_cache, "k_cache"),
+                      _bf16_view(v_cache, "v_cache"), _bf16_view(out, "out"))
+    sv = _i32_view(slot_idx, "slot_idx")
+    stream = _stream(q.device)
+    _raise_on(load_library().qsa_sparse_prefill(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), ctypes.byref(sv),
+        _default_scale(scale, q.shape[-1]), ctypes.byref(ov), workspace.data_ptr(),
+        workspace.numel(), stream))
+    if check:
+        check_status(workspace, T, W)
+    return out
+
+
+def check_status(workspace: torch.Tensor, T: int, W: int) -> int:
+    """Synchronize the current stream and raise QsaError if the last
+    compaction into ``workspace`` dropped invalid entries; returns 0."""
+    n_bad = ctypes.c_int64(0)
+    status = load_library().qsa_check_status(
+        workspace.data_ptr(), workspace.numel(), T, W, _stream(workspace.device),
+        ctypes.byref(n_bad))
+    _raise_on(status)
+    return n_bad.value
+
+
+def gather_ceiling(k_cache: torch.Tensor, v_cache: torch.Tensor, workspace: torch.Tensor,
+                   T: int, W: int, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Run the gather-only measurement kernel; returns sink [T * Hkv] (int32 bits)."""
+    Hkv = k_cache.shape[1]
+    if sink is None:
+        sink = torch.empty(max(T * Hkv, 1), dtype=torch.int32, device=k_cache.device)
+    kv, vv = _bf16_view(k_cache, "k_cache"), _bf16_view(v_cache, "v_cache")
+    _raise_on(load_library().qsa_gather_ceiling(
+        ctypes.byref(kv), ctypes.byref(vv), T, W, workspace.data_ptr(), workspace.numel(),
+        sink.data_ptr(), _stream(k_cache.device)))
+    return sink

@@ -1,0 +1,325 @@
+// C ABI of libqsa (declared in include/qsa.h): host-side argument checks,
+// workspace layout and kernel launches.  Every check runs on the host before
+// any HIP call, so a rejected call enqueues nothing and touches no device.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "qsa.h"
+#include "qsa_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+qsa_status fail(qsa_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kMax32 = 0x7fffffff;
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool layout_of(int64_t T, int64_t W, qsa_workspace_map *m) {
+    if (T < 0 || W < 0) return false;
+    const int64_t row = round_up(W, qsa::kTileSlots);
+    m->list_offset = 0;
+    m->row_stride = row;
+    m->count_offset = round_up(T * row * 4, kAlign);
+    m->bad_offset = m->count_offset + round_up(T * 4, kAlign);
+    m->total_bytes = m->bad_offset + round_up(T * 4, kAlign);
+    return true;
+}
+
+// Byte span [lo, hi) covered by a strided view (all strides non-negative).
+void span_of(const qsa_bf16_view *v, uintptr_t *lo, uintptr_t *hi) {
+    int64_t last = 0;
+    for (int i = 0; i < 3; ++i) last += (v->size[i] - 1) * v->stride[i];
+    *lo = (uintptr_t)v->data;
+    *hi = (uintptr_t)v->data + (uintptr_t)(last + 1) * 2;
+}
+
+bool any_empty(const qsa_bf16_view *v) {
+    return v->size[0] == 0 || v->size[1] == 0 || v->size[2] == 0;
+}
+
+qsa_status check_bf16(const qsa_bf16_view *v, const char *name) {
+    if (!v) return fail(QSA_ERR_NULL, "%s: view pointer is NULL", name);
+    for (int i = 0; i < 3; ++i) {
+        if (v->size[i] < 0) return fail(QSA_ERR_SHAPE, "%s: negative size", name);
+        if (v->stride[i] < 0) return fail(QSA_ERR_STRIDE, "%s: negative stride", name);
+    }
+    if (v->size[2] != qsa::kHeadDim)
+        return fail(QSA_ERR_UNSUPPORTED, "%s: head dim %lld, only %d is supported", name,
+                    (long long)v->size[2], qsa::kHeadDim);
+    if (any_empty(v)) return QSA_OK;
+    if (!v->data) return fail(QSA_ERR_NULL, "%s: data is NULL", name);
+    if (v->stride[2] != 1) return fail(QSA_ERR_STRIDE, "%s: innermost stride must be 1", name);
+    if ((uintptr_t)v->data % 16)
+        return fail(QSA_ERR_STRIDE, "%s: base pointer must be 16-byte aligned", name);
+    if (v->stride[0] % 8 || v->stride[1] % 8)
+        return fail(QSA_ERR_STRIDE, "%s: strides must be multiples of 8 elements", name);
+    return QSA_OK;
+}
+
+qsa_status check_workspace(const void *ws, size_t bytes, int64_t T, int64_t W,
+                           qsa_workspace_map *m) {
+    if (!layout_of(T, W, m)) return fail(QSA_ERR_SHAPE, "negative T or W");
+    if (!ws) return fail(QSA_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)ws % kAlign) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if ((int64_t)bytes < m->total_bytes)
+        return fail(QSA_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", bytes,
+                    (long long)m->total_bytes);
+    return QSA_OK;
+}
+
+struct Problem {
+    int64_t T, S, W;
+    int32_t Hq, Hkv;
+};
+
+qsa_status check_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
+                        const qsa_bf16_view *v, const qsa_bf16_view *out, int64_t W,
+                        float scale, Problem *pr) {
+    qsa_status s;
+    if ((s = check_bf16(q, "q")) || (s = check_bf16(k, "k_cache")) ||
+        (s = check_bf16(v, "v_cache")) || (s = check_bf16(out, "out")))
+        return s;
+    for (int i = 0; i < 3; ++i) {
+        if (out->size[i] != q->size[i]) return fail(QSA_ERR_SHAPE, "out must have q's shape");
+        if (v->size[i] != k->size[i]) return fail(QSA_ERR_SHAPE, "v_cache must have k_cache's shape");
+    }
+    pr->T = q->size[0];
+    pr->S = k->size[0];
+    pr->W = W;
+    if (W < 0) return fail(QSA_ERR_SHAPE, "negative W");
+    if (q->size[1] > kMax32 || k->size[1] > kMax32)
+        return fail(QSA_ERR_UNSUPPORTED, "head counts beyond int32");
+    pr->Hq = (int32_t)q->size[1];
+    pr->Hkv = (int32_t)k->size[1];
+    if (pr->T > 0 && (pr->Hq == 0 || pr->Hkv == 0))
+        return fail(QSA_ERR_SHAPE, "Hq and Hkv must be positive");
+    if (pr->Hkv > 0 && pr->Hq % pr->Hkv)
+        return fail(QSA_ERR_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", pr->Hq, pr->Hkv);
+    if (pr->T > kMax32 || W > kMax32 || pr->S > kMax32)
+        return fail(QSA_ERR_UNSUPPORTED, "T, W and S must fit in int32");
+    if (!std::isfinite(scale)) return fail(QSA_ERR_SCALE, "scale must be finite");
+    if (!any_empty(out)) {
+        uintptr_t olo, ohi;
+        span_of(out, &olo, &ohi);
+        const qsa_bf16_view *ins[3] = {q, k, v};
+        for (const qsa_bf16_view *in : ins) {
+            if (any_empty(in)) continue;
+            uintptr_t lo, hi;
+            span_of(in, &lo, &hi);
+            if (olo < hi && lo < ohi) return fail(QSA_ERR_ALIAS, "out overlaps an input");
+        }
+    }
+    return QSA_OK;
+}
+
+qsa_status check_slots(const qsa_i32_view *sl, int64_t T, int64_t *W) {
+    if (!sl) return fail(QSA_ERR_NULL, "slot_idx: view pointer is NULL");
+    if (sl->size[0] < 0 || sl->size[1] < 0) return fail(QSA_ERR_SHAPE, "slot_idx: negative size");
+    if (sl->size[0] != T) return fail(QSA_ERR_SHAPE, "slot_idx must have one row per token");
+    *W = sl->size[1];
+    if (sl->size[0] == 0 || sl->size[1] == 0) return QSA_OK;
+    if (!sl->data) return fail(QSA_ERR_NULL, "slot_idx: data is NULL");
+    if (sl->stride[1] != 1) return fail(QSA_ERR_STRIDE, "slot_idx: innermost stride must be 1");
+    if (sl->stride[0] < 0) return fail(QSA_ERR_STRIDE, "slot_idx: negative stride");
+    if ((uintptr_t)sl->data % 4) return fail(QSA_ERR_STRIDE, "slot_idx: misaligned");
+    if (*W > kMax32 || T > kMax32) return fail(QSA_ERR_UNSUPPORTED, "T and W must fit in int32");
+    return QSA_OK;
+}
+
+qsa_status hip_fail(hipError_t e, const char *what) {
+    return fail(QSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t S, void *ws,
+                           const qsa_workspace_map &m, hipStream_t stream) {
+    qsa::CompactParams p{};
+    p.slot_idx = sl->data;
+    p.stride_t = sl->stride[0];
+    p.T = T;
+    p.W = W;
+    p.S = S;
+    p.list = (int32_t *)((char *)ws + m.list_offset);
+    p.row_stride = m.row_stride;
+    p.count = (int32_t *)((char *)ws + m.count_offset);
+    p.n_bad = (int32_t *)((char *)ws + m.bad_offset);
+    hipError_t e = qsa::launch_compact(p, stream);
+    return e == hipSuccess ? QSA_OK : hip_fail(e, "compaction launch");
+}
+
+qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
+                          const qsa_bf16_view *v, const qsa_bf16_view *out, const Problem &pr,
+                          float scale, const void *ws, const qsa_workspace_map &m,
+                          hipStream_t stream) {
+    if (pr.T == 0 || pr.Hq == 0) return QSA_OK;
+    qsa::AttendParams p{};
+    p.q = (const uint16_t *)q->data;
+    p.q_st = q->stride[0];
+    p.q_sh = q->stride[1];
+    p.k = (const uint16_t *)k->data;
+    p.k_ss = k->stride[0];
+    p.k_sh = k->stride[1];
+    p.v = (const uint16_t *)v->data;
+    p.v_ss = v->stride[0];
+    p.v_sh = v->stride[1];
+    p.list = (const int32_t *)((const char *)ws + m.list_offset);
+    p.list_stride = m.row_stride;
+    p.count = (const int32_t *)((const char *)ws + m.count_offset);
+    p.out = (uint16_t *)out->data;
+    p.o_st = out->stride[0];
+    p.o_sh = out->stride[1];
+    p.Hkv = pr.Hkv;
+    p.G = pr.Hq / pr.Hkv;
+    p.HB = (p.G + 15) / 16;
+    p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+    hipError_t e = qsa::launch_attend(p, pr.T, stream);
+    return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qsa_version(void) { return "libqsa 0.1.0 gfx950"; }
+
+const char *qsa_status_string(qsa_status s) {
+    switch (s) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_NULL: return "null pointer";
+    case QSA_ERR_SHAPE: return "bad shape";
+    case QSA_ERR_STRIDE: return "bad stride or alignment";
+    case QSA_ERR_SCALE: return "scale not finite";
+    case QSA_ERR_WORKSPACE: return "bad workspace";
+    case QSA_ERR_SLOT_RANGE: return "slot out of range";
+    case QSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case QSA_ERR_HIP: return "HIP runtime error";
+    case QSA_ERR_ALIAS: return "output aliases an input";
+    }
+    return "unknown status";
+}
+
+const char *qsa_last_error(void) { return g_last_error; }
+
+size_t qsa_workspace_bytes(int64_t T, int64_t W) {
+    qsa_workspace_map m;
+    return layout_of(T, W, &m) ? (size_t)m.total_bytes : 0;
+}
+
+qsa_status qsa_workspace_layout(int64_t T, int64_t W, qsa_workspace_map *map) {
+    if (!map) return fail(QSA_ERR_NULL, "map is NULL");
+    if (!layout_of(T, W, map)) return fail(QSA_ERR_SHAPE, "negative T or W");
+    return QSA_OK;
+}
+
+qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    if (!slot_idx) return fail(QSA_ERR_NULL, "slot_idx: view pointer is NULL");
+    const int64_t T = slot_idx->size[0];
+    int64_t W = 0;
+    qsa_status s = check_slots(slot_idx, T, &W);
+    if (s) return s;
+    if (S < 0) return fail(QSA_ERR_SHAPE, "negative S");
+    if (S > kMax32) return fail(QSA_ERR_UNSUPPORTED, "S must fit in int32");
+    qsa_workspace_map m;
+    if ((s = check_workspace(workspace, workspace_bytes, T, W, &m))) return s;
+    return enqueue_compact(slot_idx, T, W, S, workspace, m, (hipStream_t)stream);
+}
+
+qsa_status qsa_sparse_attend(const qsa_bf16_view *q, const qsa_bf16_view *k_cache,
+                             const qsa_bf16_view *v_cache, int64_t W, float scale,
+                             const void *workspace, size_t workspace_bytes,
+                             qsa_bf16_view *out, void *stream) {
+    Problem pr;
+    qsa_status s = check_attend(q, k_cache, v_cache, out, W, scale, &pr);
+    if (s) return s;
+    qsa_workspace_map m;
+    if ((s = check_workspace(workspace, workspace_bytes, pr.T, W, &m))) return s;
+    return enqueue_attend(q, k_cache, v_cache, out, pr, scale, workspace, m, (hipStream_t)stream);
+}
+
+qsa_status qsa_sparse_prefill(const qsa_bf16_view *q, const qsa_bf16_view *k_cache,
+                              const qsa_bf16_view *v_cache, const qsa_i32_view *slot_idx,
+                              float scale, qsa_bf16_view *out, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    if (!slot_idx) return fail(QSA_ERR_NULL, "slot_idx: view pointer is NULL");
+    Problem pr;
+    qsa_status s = check_attend(q, k_cache, v_cache, out, slot_idx->size[1], scale, &pr);
+    if (s) return s;
+    int64_t W = 0;
+    if ((s = check_slots(slot_idx, pr.T, &W))) return s;
+    qsa_workspace_map m;
+    if ((s = check_workspace(workspace, workspace_bytes, pr.T, W, &m))) return s;
+    if (pr.T == 0) return QSA_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, workspace, m, st))) return s;
+    return enqueue_attend(q, k_cache, v_cache, out, pr, scale, workspace, m, st);
+}
+
+qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes, int64_t T,
+                            int64_t W, void *stream, int64_t *n_bad) {
+    qsa_workspace_map m;
+    qsa_status s = check_workspace(workspace, workspace_bytes, T, W, &m);
+    if (s) return s;
+    if (n_bad) *n_bad = 0;
+    if (T == 0) return QSA_OK;
+    std::vector<int32_t> bad((size_t)T);
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    e = hipMemcpy(bad.data(), (const char *)workspace + m.bad_offset, (size_t)T * 4,
+                  hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "status copy");
+    int64_t total = 0;
+    for (int32_t b : bad) total += b;
+    if (n_bad) *n_bad = total;
+    if (total) return fail(QSA_ERR_SLOT_RANGE, "%lld selection entries were neither -1 nor in [0, S)",
+                           (long long)total);
+    return QSA_OK;
+}
+
+qsa_status qsa_gather_ceiling(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_cache,
+                              int64_t T, int64_t W, const void *workspace,
+                              size_t workspace_bytes, uint32_t *sink, void *stream) {
+    qsa_status s;
+    if ((s = check_bf16(k_cache, "k_cache")) || (s = check_bf16(v_cache, "v_cache"))) return s;
+    for (int i = 0; i < 3; ++i)
+        if (v_cache->size[i] != k_cache->size[i])
+            return fail(QSA_ERR_SHAPE, "v_cache must have k_cache's shape");
+    if (T < 0 || W < 0) return fail(QSA_ERR_SHAPE, "negative T or W");
+    if (T > kMax32 || k_cache->size[1] > kMax32)
+        return fail(QSA_ERR_UNSUPPORTED, "sizes beyond int32");
+    qsa_workspace_map m;
+    if ((s = check_workspace(workspace, workspace_bytes, T, W, &m))) return s;
+    if (T == 0 || k_cache->size[1] == 0) return QSA_OK;
+    if (!sink) return fail(QSA_ERR_NULL, "sink is NULL");
+    qsa::CeilingParams p{};
+    p.k = (const uint16_t *)k_cache->data;
+    p.k_ss = k_cache->stride[0];
+    p.k_sh = k_cache->stride[1];
+    p.v = (const uint16_t *)v_cache->data;
+    p.v_ss = v_cache->stride[0];
+    p.v_sh = v_cache->stride[1];
+    p.list = (const int32_t *)((const char *)workspace + m.list_offset);
+    p.list_stride = m.row_stride;
+    p.count = (const int32_t *)((const char *)workspace + m.count_offset);
+    p.sink = sink;
+    p.Hkv = (int32_t)k_cache->size[1];
+    hipError_t e = qsa::launch_ceiling(p, T, (hipStream_t)stream);
+    return e == hipSuccess ? QSA_OK : hip_fail(e, "gather-ceiling launch");
+}
+
+}  // extern "C"
