@@ -75,8 +75,12 @@ typedef struct qsa_i32_view {
 
 /* Where the compaction pass leaves its results inside a workspace (byte
  * offsets from the workspace base):
- *   list:  int32 [T][row_stride]; row t holds its count[t] valid slots in
- *          input order, then -1 up to the next multiple of 32;
+ *   list:  int32 [T][row_stride]; row t holds its count[t] valid slots,
+ *          then -1 up to the next multiple of 32.  Order: the row is cut into
+ *          runs of 2304 consecutive input entries, kept in input order; inside
+ *          a run the valid entries are stably sorted by slot >> r, where
+ *          b = max(1, ceil(log2 S)) and r = max(0, b - 7) (at most 128 slot
+ *          ranges, ascending; input order within a range);
  *   count: int32 [T], number of valid entries of row t;
  *   n_bad: int32 [T], entries of row t that were neither -1 nor in [0, S). */
 typedef struct qsa_workspace_map {
@@ -104,11 +108,14 @@ size_t qsa_workspace_bytes(int64_t T, int64_t W);
 qsa_status qsa_workspace_layout(int64_t T, int64_t W, qsa_workspace_map *map);
 
 /*
- * Index validation and stable compaction (the -1 rules of the "Sizing
- * bounds" bullet; unordered slots of section "Nine tests that passed, ...").
- * For every row t of slot_idx [T, W], writes into the workspace the entries in
- * [0, S) in their original order, their count, and the number of invalid
- * entries (see qsa_workspace_map).  S is the number of cache slots.
+ * Index validation and compaction (the -1 rules of the "Sizing bounds"
+ * bullet; unordered slots of section "Nine tests that passed, ...").  For
+ * every row t of slot_idx [T, W], writes into the workspace the entries in
+ * [0, S) grouped into ascending slot ranges (see qsa_workspace_map for the
+ * exact order), their count, and the number of invalid entries.  S is the
+ * number of cache slots.  Duplicates are kept.  The attention result does
+ * not depend on the order of a row; the grouping only makes the gathers of
+ * one tile fall close together in memory.
  */
 qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S,
                              void *workspace, size_t workspace_bytes,

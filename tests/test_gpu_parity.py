@@ -22,6 +22,7 @@ from qsa_testutil import (bf16_tensor_bits, bf16_tensor_to_f32, empty_row_mask, 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
+SORT_RUN = 2304      # entries the compaction pass sorts together
 
 
 def run_case(case, rows=None, out=None):
@@ -47,19 +48,37 @@ def check_against_oracle(case, rows=None, out=None):
 
 # ------------------------------------------------------------------ compaction
 
+def group_shift(S):
+    """r of the header: valid entries are grouped by slot >> r."""
+    b = 1
+    while b < 31 and (1 << b) < S:
+        b += 1
+    return max(0, b - 7)
+
+
 def check_compaction(case):
     _, _, _, sl = upload(case, DEV)
     ws = qsa.compact_slots(sl, case.S)
     torch.cuda.synchronize()
     lst, cnt, bad = (x.cpu().numpy() for x in qsa.compacted_lists(ws, case.T, case.W))
-    want_list, want_cnt, want_bad = oracle.compact(case.slot_idx, case.S)
+    want_cnt = np.zeros(case.T, dtype=np.int64)
+    want_bad = np.zeros(case.T, dtype=np.int64)
+    r = group_shift(case.S)
+    for t in range(case.T):
+        # The oracle filter keeps input order; the library then stably groups
+        # each run of SORT_RUN input entries by slot >> r.
+        want = []
+        for r0 in range(0, case.W, SORT_RUN):
+            part = case.slot_idx[t:t + 1, r0:r0 + SORT_RUN]
+            kept, k_cnt, k_bad = oracle.compact(np.ascontiguousarray(part), case.S)
+            want.extend(sorted(kept[0, :k_cnt[0]].tolist(), key=lambda s_: s_ >> r))
+            want_bad[t] += k_bad[0]
+        want_cnt[t] = len(want)
+        np.testing.assert_array_equal(lst[t, :len(want)], np.array(want, dtype=np.int32))
+        pad_end = (len(want) + 31) // 32 * 32
+        assert np.all(lst[t, len(want):pad_end] == -1)
     np.testing.assert_array_equal(cnt, want_cnt)
     np.testing.assert_array_equal(bad, want_bad)
-    for t in range(case.T):
-        n = int(want_cnt[t])
-        np.testing.assert_array_equal(lst[t, :n], want_list[t, :n])
-        pad_end = (n + 31) // 32 * 32
-        assert np.all(lst[t, n:pad_end] == -1)
     return ws
 
 
@@ -69,6 +88,22 @@ def test_compaction_tiny_bit_exact():
 
 def test_compaction_edge_mix_bit_exact():
     check_compaction(qi.edge_mix())
+
+
+def test_compaction_of_rows_longer_than_one_sort_run():
+    case = qi.random_case(43, T=6, S=100000, Hq=2, Hkv=1, W=5000, pad_frac=0.1, interior=True)
+    check_compaction(case)
+    check_against_oracle(case)
+
+
+def test_compaction_with_duplicates_and_tiny_caches():
+    for S in (1, 2, 3, 17):
+        rng = np.random.Generator(np.random.PCG64(44 + S))
+        case = qi.random_case(45, T=9, S=S, Hq=3, Hkv=1, W=1)
+        case.slot_idx = rng.integers(-1, S, size=(9, 70)).astype(np.int32)
+        case.bases["slot_idx"] = case.slot_idx
+        check_compaction(case)
+        check_against_oracle(case)
 
 
 def test_compaction_counts_invalid_entries_and_drops_them():
@@ -176,24 +211,31 @@ def test_padding_position_is_bitwise_irrelevant():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_physical_relocation_is_bitwise_irrelevant():
-    case = qi.random_case(703, T=25, S=1500, Hq=24, Hkv=2, W=333)
+def _relocate(case, new_of_old, S_new):
+    """Move cache row s to row new_of_old[s] of a bigger cache and remap the
+    selection accordingly; rows not used by the map get fresh values."""
+    rng = np.random.Generator(np.random.PCG64(S_new))
+    k2 = qi.normal_bf16(rng, (S_new,) + case.k_cache.shape[1:])
+    v2 = qi.normal_bf16(rng, (S_new,) + case.v_cache.shape[1:])
+    k2[new_of_old] = case.k_cache
+    v2[new_of_old] = case.v_cache
+    sel = np.where(case.slot_idx >= 0, new_of_old[np.maximum(case.slot_idx, 0)], -1)
+    case.k_cache, case.v_cache = k2, v2
+    case.slot_idx = sel.astype(np.int32)
+    case.bases.update(k=k2, v=v2, slot_idx=case.slot_idx)
+
+
+def test_any_relocation_stays_within_the_gate():
+    case = qi.random_case(705, T=25, S=1500, Hq=24, Hkv=2, W=333)
     a, _ = run_case(case)
-    rng = np.random.Generator(np.random.PCG64(704))
-    perm = rng.permutation(case.S)          # new row of old slot s is perm[s]
-    k2 = np.empty_like(case.k_cache)
-    v2 = np.empty_like(case.v_cache)
-    k2[perm] = case.k_cache
-    v2[perm] = case.v_cache
-    case.k_cache[:] = k2
-    case.v_cache[:] = v2
-    case.slot_idx[:] = perm[case.slot_idx]
-    b, _ = run_case(case)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    rng = np.random.Generator(np.random.PCG64(706))
+    _relocate(case, rng.permutation(case.S), case.S)
+    b, _ = check_against_oracle(case)[:2]
+    gate(bf16_tensor_to_f32(b), bf16_tensor_to_f32(a), np.zeros(case.T, dtype=bool))
 
 
 def test_heads_with_identical_queries_give_identical_outputs():
-    case = qi.random_case(705, T=17, S=800, Hq=12, Hkv=1, W=100)
+    case = qi.random_case(709, T=17, S=800, Hq=12, Hkv=1, W=100)
     case.q[:] = case.q[:, :1, :]
     o, _ = run_case(case)
     bits = bf16_tensor_bits(o)
@@ -212,16 +254,36 @@ def test_repeated_runs_are_bitwise_deterministic():
 
 
 def test_slot_order_changes_output_only_within_the_gate():
-    case = qi.random_case(707, T=20, S=5000, Hq=8, Hkv=1, W=777)
+    case = qi.random_case(707, T=20, S=5000, Hq=8, Hkv=1, W=777, pad_frac=0.2, interior=True)
     a, _ = run_case(case)
     rng = np.random.Generator(np.random.PCG64(708))
     case.slot_idx[:] = rng.permuted(case.slot_idx, axis=1)
-    b, _ = run_case(case)
+    b, _ = check_against_oracle(case)[:2]
     gate(bf16_tensor_to_f32(b), bf16_tensor_to_f32(a), np.zeros(case.T, dtype=bool))
 
 
+def test_order_of_slot_range_groups_is_bitwise_irrelevant():
+    """Rows that differ only in the order of their groups (slot >> r) give
+    bitwise identical outputs: the compaction pass orders the groups itself."""
+    case = qi.random_case(712, T=12, S=4096, Hq=6, Hkv=1, W=600)
+    r = group_shift(case.S)
+    a, _ = run_case(case)
+    rng = np.random.Generator(np.random.PCG64(713))
+    rows = []
+    for t in range(case.T):
+        groups = {}
+        for s_ in case.slot_idx[t].tolist():
+            groups.setdefault(s_ >> r, []).append(s_)
+        keys = list(groups)
+        rng.shuffle(keys)
+        rows.append([s_ for k_ in keys for s_ in groups[k_]])
+    case.slot_idx[:] = np.array(rows, dtype=np.int32)
+    b, _ = run_case(case)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_large_scale_is_finite_and_matches_oracle():
-    case = qi.random_case(709, T=16, S=2000, Hq=6, Hkv=1, W=500, scale=3.0)
+    case = qi.random_case(711, T=16, S=2000, Hq=6, Hkv=1, W=500, scale=3.0)
     o, _, _ = check_against_oracle(case)
     assert torch.isfinite(o.float()).all()
 

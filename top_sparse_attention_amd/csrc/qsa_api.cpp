@@ -32,7 +32,7 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 bool layout_of(int64_t T, int64_t W, qsa_workspace_map *m) {
     if (T < 0 || W < 0) return false;
-    const int64_t row = round_up(W, qsa::kTileSlots);
+    const int64_t row = round_up(W, qsa::kListPad);
     m->list_offset = 0;
     m->row_stride = row;
     m->count_offset = round_up(T * row * 4, kAlign);
@@ -154,6 +154,9 @@ qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t
     p.T = T;
     p.W = W;
     p.S = S;
+    int bits = 1;   // width of S - 1, at least one bit
+    while (bits < 31 && ((int64_t)1 << bits) < S) ++bits;
+    p.key_bits = bits + 1;   // one more bit for the key that marks invalid entries
     p.list = (int32_t *)((char *)ws + m.list_offset);
     p.row_stride = m.row_stride;
     p.count = (int32_t *)((char *)ws + m.count_offset);

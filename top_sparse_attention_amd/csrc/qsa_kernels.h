@@ -9,15 +9,27 @@ namespace qsa {
 
 // Head dim the kernels are written for (the only one the method uses).
 constexpr int kHeadDim = 256;
-// Slots per gather tile, and the granularity the compacted lists are padded to.
-constexpr int kTileSlots = 32;
+// Slots per gather tile: one 16-row MFMA block of K and V rows (16 KiB).
+constexpr int kTileSlots = 16;
+// Compacted lists are padded with -1 to a multiple of this.
+constexpr int kListPad = 32;
 // Waves that share one (token, KV head, head block) work item.
 constexpr int kWavesPerItem = 4;
+// Work items resident per CU (sizes the LDS and register budget).
+constexpr int kItemsPerCU = 2;
+// Entries of a selection row sorted together by the compaction pass.
+constexpr int kSortThreads = 256;
+constexpr int kSortItemsPerThread = 9;
+constexpr int kSortChunk = kSortThreads * kSortItemsPerThread;   // 2304
+// Key bits the compaction pass sorts on: the padding bit and the top 7 bits
+// of the slot range (128 groups).
+constexpr int kSortKeyBits = 8;
 
 struct CompactParams {
     const int32_t *slot_idx;
     int64_t stride_t;
     int64_t T, W, S;
+    int32_t key_bits;    // radix-sort key width: S - 1 < 2^key_bits, plus one bit for padding
     int32_t *list;
     int64_t row_stride;
     int32_t *count;

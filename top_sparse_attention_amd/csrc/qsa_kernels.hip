@@ -9,26 +9,34 @@
 // two, and needs no host synchronisation.
 //
 // Two passes:
-//  1. compact_kernel: per token row, a stable filter of the selection list
-//     (keeps entries in [0, S) in input order, counts the rest as invalid),
-//     padded with -1 to a multiple of the tile size.
+//  1. compact_kernel: per token row, keep the entries in [0, S) (counting
+//     the others as invalid), group them into ascending slot ranges (a
+//     partial radix sort), and pad the list with -1 to a multiple of
+//     kListPad.  The order does not change the result (the softmax sum is
+//     order-free) but makes each wave's consecutive gathers land in few
+//     large pages of the cache, which the memory system serves markedly
+//     faster than uniformly scattered rows.
 //  2. attend_kernel: one work item = (token t, KV head g, block of up to 16
-//     query heads of that group).  kWavesPerItem waves split the item's
-//     32-slot tiles round-robin; each wave gathers its tile's K and V rows
-//     (512 B each, 16-byte coalesced loads, double-buffered through
-//     registers), stages them in LDS, computes the 32x16 score tile with
-//     bf16 MFMA (K rows x query heads), runs an online softmax in FP32,
-//     and accumulates P.V with bf16 MFMA reading V through LDS transpose
-//     loads.  The waves' partial (max, sum, O) are merged through LDS at
-//     the end and the row is written in BF16.
+//     query heads of that group), kItemsPerCU items resident per CU.  The
+//     item's kWavesPerItem waves split its 16-slot tiles round-robin; each
+//     wave gathers a tile's K and V rows (512 B each, 16-byte coalesced
+//     loads, prefetched one tile ahead through registers), stages them in
+//     LDS, computes the 16x16 score tile with bf16 MFMA (K rows x query
+//     heads), runs an online softmax in FP32 and accumulates P.V with bf16
+//     MFMA fed by LDS transpose loads.  The waves' partial (max, sum, O) are
+//     merged through LDS at the end and the row is written in BF16.
 //
 // MFMA orientation: scores are computed transposed, S^T = K_tile . Q^T, so
 // that one lane owns one query head (column) of the MFMA output: the row
 // maximum needs only two cross-lane steps and the O rescale is one scalar per
-// lane.  The output O^T = V^T . P^T uses the same lane-to-head map.
+// lane.  The output O^T = V^T . P^T uses the same lane-to-head map, and the
+// 16x16 score tile in MFMA output layout is directly the P^T operand of the
+// 16x16x16 MFMA.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <hipcub/block/block_radix_sort.hpp>
 
 #include "qsa_kernels.h"
 
@@ -45,18 +53,27 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 #define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T *)(p))
 
-constexpr int kRowBytes = kHeadDim * 2;          // one K or V row: 512 B
-constexpr int kChunksPerRow = kRowBytes / 16;    // 32 sixteen-byte chunks
-constexpr int kTileBytes = kTileSlots * kRowBytes;  // 16 KiB of K (or V)
-constexpr int kWaveLds = 2 * kTileBytes;         // K tile + V tile per wave
+constexpr int kRowBytes = kHeadDim * 2;             // one K or V row: 512 B
+constexpr int kChunksPerRow = kRowBytes / 16;       // 32 sixteen-byte chunks
+constexpr int kTileBytes = kTileSlots * kRowBytes;  // 8 KiB of K (or V)
+constexpr int kWaveLds = 2 * kTileBytes;            // K tile + V tile per wave
 constexpr int kThreads = 64 * kWavesPerItem;
-constexpr int kLoadsPerTile = kTileBytes / (64 * 16);  // 16 dwordx4 per lane
+constexpr int kLoadsPerTile = kTileBytes / (64 * 16);  // 8 dwordx4 per lane
+constexpr int kHeadBlock = 16;                      // query heads per MFMA column block
+constexpr int kDimBlocks = kHeadDim / 16;           // 16 output blocks of 16 dims
 constexpr float kNegInf = -__builtin_huge_valf();
 // A new running maximum is adopted only when it exceeds the current one by
 // more than this (log2 units); otherwise probabilities may reach 2^8, which
 // FP32 sums and BF16 probabilities hold exactly as well.  This skips most
 // rescales of the O accumulators.
 constexpr float kRescaleSlack = 8.0f;
+
+// Partial results of the waves of one item, merged at the end (reuses the
+// tile area): O [wave][db][lane] as f32x4, then max and sum [wave][head].
+constexpr int kMergeOBytes = kWavesPerItem * kDimBlocks * 64 * 16;
+constexpr int kAttendLds = kWavesPerItem * kWaveLds + 2 * kWavesPerItem * kHeadBlock * 4;
+static_assert(kMergeOBytes <= kWavesPerItem * kWaveLds, "merge area must fit in the tiles");
+static_assert(kItemsPerCU * kAttendLds <= 160 * 1024, "LDS budget of a gfx950 CU");
 
 // A row of zeros: masked tile rows and absent query heads load from here, so
 // every load is unconditional and no select waits on loaded data.
@@ -82,33 +99,53 @@ __device__ __forceinline__ int lds_off(int r, int chunk) {
 
 // ---------------------------------------------------------------- compaction
 
-__global__ __launch_bounds__(256) void compact_kernel(const CompactParams p) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= p.T) return;
+// One workgroup per token row.  The row is processed in chunks of
+// kSortChunk entries; each chunk's valid slots are radix-sorted on the top
+// kSortKeyBits bits of a key_bits-wide key (invalid entries carry the key
+// 2^(key_bits-1), so they sort last), i.e. grouped into at most 128 ascending
+// slot ranges, stable inside a range, and appended to the compacted list.
+// Two radix passes; a full sort would cost more and buys no locality.
+__global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactParams p) {
+    using Sort = hipcub::BlockRadixSort<uint32_t, kSortThreads, kSortItemsPerThread>;
+    __shared__ typename Sort::TempStorage sort_tmp;
+    __shared__ int chunk_valid, chunk_bad;
+
+    const int64_t t = blockIdx.x;
     const int32_t *src = p.slot_idx + t * p.stride_t;
     int32_t *dst = p.list + t * p.row_stride;
-    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const uint32_t pad_key = 1u << (p.key_bits - 1);
     int n = 0, bad = 0;
-    for (int64_t base = 0; base < p.W; base += 256) {
-        int32_t e[4];
+    for (int64_t base = 0; base < p.W; base += kSortChunk) {
+        if (threadIdx.x == 0) chunk_valid = chunk_bad = 0;
+        __syncthreads();
+        uint32_t key[kSortItemsPerThread];
+        int my_valid = 0, my_bad = 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t i = base + u * 64 + lane;
-            e[u] = i < p.W ? src[i] : -1;
+        for (int u = 0; u < kSortItemsPerThread; ++u) {
+            const int64_t i = base + threadIdx.x * kSortItemsPerThread + u;
+            const int32_t e = i < p.W ? src[i] : -1;
+            const bool ok = e >= 0 && (int64_t)e < p.S;
+            my_valid += ok;
+            my_bad += !ok && e != -1;
+            key[u] = ok ? (uint32_t)e : pad_key;
         }
+        atomicAdd(&chunk_valid, my_valid);
+        atomicAdd(&chunk_bad, my_bad);
+        Sort(sort_tmp).Sort(key, max(p.key_bits - kSortKeyBits, 0), p.key_bits);
+        __syncthreads();   // the counters above are complete
+        const int nv = chunk_valid;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bool ok = e[u] >= 0 && (int64_t)e[u] < p.S;
-            const uint64_t keep = __ballot(ok);
-            if (ok) dst[n + __popcll(keep & below)] = e[u];
-            n += __popcll(keep);
-            bad += __popcll(__ballot(!ok && e[u] != -1));
+        for (int u = 0; u < kSortItemsPerThread; ++u) {
+            const int pos = threadIdx.x * kSortItemsPerThread + u;
+            if (pos < nv) dst[n + pos] = (int32_t)key[u];
         }
+        n += nv;
+        bad += chunk_bad;
+        __syncthreads();   // counters are reset by the next chunk
     }
-    const int padded = (n + kTileSlots - 1) & ~(kTileSlots - 1);
-    for (int i = n + lane; i < padded; i += 64) dst[i] = -1;
-    if (lane == 0) {
+    const int padded = (n + kListPad - 1) / kListPad * kListPad;
+    for (int i = n + threadIdx.x; i < padded; i += kSortThreads) dst[i] = -1;
+    if (threadIdx.x == 0) {
         p.count[t] = n;
         p.n_bad[t] = bad;
     }
@@ -116,10 +153,10 @@ __global__ __launch_bounds__(256) void compact_kernel(const CompactParams p) {
 
 // ---------------------------------------------------------------- gathers
 
-// Issue the 2 x 16 dwordx4 loads of one tile.  `slot` holds, in lane r (and
-// r + 32), the slot of tile row r (-1: none).  Load q covers rows 2q (lanes
-// 0-31) and 2q+1 (lanes 32-63), one 16-byte chunk per lane, so each row is
-// one fully coalesced 512-byte read.
+// Issue the 2 x 8 dwordx4 loads of one tile.  `slot` holds, in lane r (and
+// every lane congruent to r mod 16), the slot of tile row r (-1: none).  Load
+// q covers rows 2q (lanes 0-31) and 2q+1 (lanes 32-63), one 16-byte chunk per
+// lane, so each row is one fully coalesced 512-byte read.
 __device__ __forceinline__ void gather_tile(u32x4_t (&rk)[kLoadsPerTile],
                                             u32x4_t (&rv)[kLoadsPerTile], int slot,
                                             const uint16_t *kb, int64_t k_ss,
@@ -151,10 +188,21 @@ __device__ __forceinline__ void stage_tile(const u32x4_t (&rk)[kLoadsPerTile],
     }
 }
 
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Slot of tile row (lane & 15) for tile `tile`, or -1 past the list.
+__device__ __forceinline__ int tile_slot(const int32_t *list, int tile, int ntiles, int lane) {
+    return tile < ntiles ? list[tile * kTileSlots + (lane & 15)] : -1;
+}
+
 // ---------------------------------------------------------------- attention
 
-__global__ __launch_bounds__(kThreads, 1) void attend_kernel(const AttendParams p) {
-    __shared__ __attribute__((aligned(16))) char smem[kWavesPerItem * kWaveLds];
+__global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const AttendParams p) {
+    __shared__ __attribute__((aligned(16))) char smem[kAttendLds];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -167,8 +215,8 @@ __global__ __launch_bounds__(kThreads, 1) void attend_kernel(const AttendParams 
     const int rem = (int)(item - t * per_t);
     const int g = rem / p.HB;
     const int hb = rem - g * p.HB;
-    const int h0 = g * p.G + hb * 16;
-    const int nh = min(16, p.G - hb * 16);
+    const int h0 = g * p.G + hb * kHeadBlock;
+    const int nh = min(kHeadBlock, p.G - hb * kHeadBlock);
     const int n = p.count[t];
 
     uint16_t *out_t = p.out + t * p.o_st + (int64_t)h0 * p.o_sh;
@@ -199,64 +247,45 @@ __global__ __launch_bounds__(kThreads, 1) void attend_kernel(const AttendParams 
 
     float m = kNegInf;   // running max (log2 domain) for head c
     float lsum = 0.0f;   // this lane's share of the softmax denominator
-    f32x4_t o[16];
+    f32x4_t o[kDimBlocks];
 #pragma unroll
-    for (int db = 0; db < 16; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     u32x4_t rk[kLoadsPerTile], rv[kLoadsPerTile];
     int tile = wave;
-    int slot_next = -1;
-    if (tile < ntiles) {
-        const int slot_cur = list[tile * kTileSlots + (lane & 31)];
-        if (tile + kWavesPerItem < ntiles)
-            slot_next = list[(tile + kWavesPerItem) * kTileSlots + (lane & 31)];
-        gather_tile(rk, rv, slot_cur, kb, p.k_ss, vb, p.v_ss, lane);
-    }
+    int slot_next = tile_slot(list, tile + kWavesPerItem, ntiles, lane);
+    if (tile < ntiles)
+        gather_tile(rk, rv, tile_slot(list, tile, ntiles, lane), kb, p.k_ss, vb, p.v_ss, lane);
+
+    const int tr_row = 4 * j + (c >> 2);    // V row this lane addresses in a transpose load
+    const int tr_sub = c & 3;               // which 4 of the 16 dims of a block
 
     for (; tile < ntiles; tile += kWavesPerItem) {
-        // The previous tile's LDS reads must be done before it is overwritten.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_fence();   // the previous tile's LDS reads are done
         stage_tile(rk, rv, ks_lds, vs_lds, lane);
         const int nt = tile + kWavesPerItem;
         if (nt < ntiles) {
             gather_tile(rk, rv, slot_next, kb, p.k_ss, vb, p.v_ss, lane);
-            slot_next = nt + kWavesPerItem < ntiles
-                            ? list[(nt + kWavesPerItem) * kTileSlots + (lane & 31)]
-                            : -1;
+            slot_next = tile_slot(list, nt + kWavesPerItem, ntiles, lane);
         }
-        // Other lanes of this wave wrote the rows read below.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_fence();   // other lanes of this wave wrote the rows read below
 
-        // S^T for the two 16-slot blocks: s0[i] / s1[i] = score of tile slot
-        // 4j+i / 16+4j+i against head c.
-        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-        bf16x8_t ka[2][8];
+        // S^T for the tile: s[i] = score of tile slot 4j+i against head c.
+        bf16x8_t ka[8];
 #pragma unroll
-        for (int kstep = 0; kstep < 8; ++kstep) {
-            ka[0][kstep] = *LDS_PTR(bf16x8_t, ks_lds + lds_off(c, 4 * kstep + j));
-            ka[1][kstep] = *LDS_PTR(bf16x8_t, ks_lds + lds_off(16 + c, 4 * kstep + j));
-        }
+        for (int kstep = 0; kstep < 8; ++kstep)
+            ka[kstep] = *LDS_PTR(bf16x8_t, ks_lds + lds_off(c, 4 * kstep + j));
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kstep = 0; kstep < 8; ++kstep) {
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kstep], qb[kstep], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kstep], qb[kstep], s1, 0, 0, 0);
-        }
+        for (int kstep = 0; kstep < 8; ++kstep)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kstep], qb[kstep], s, 0, 0, 0);
 
         // Online softmax in the log2 domain; slots at or past n are masked.
         const int first = tile * kTileSlots + 4 * j;
-        float x[8];
+        float x[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = first + i < n ? s0[i] * p.scale_log2e : kNegInf;
-            x[4 + i] = first + 16 + i < n ? s1[i] * p.scale_log2e : kNegInf;
-        }
-        float mt = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
+        for (int i = 0; i < 4; ++i) x[i] = first + i < n ? s[i] * p.scale_log2e : kNegInf;
+        float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const bool raise = mt > m + kRescaleSlack;
@@ -265,39 +294,32 @@ __global__ __launch_bounds__(kThreads, 1) void attend_kernel(const AttendParams 
             const float alpha = __builtin_amdgcn_exp2f(m - m_new);
             lsum *= alpha;
 #pragma unroll
-            for (int db = 0; db < 16; ++db) o[db] *= alpha;
+            for (int db = 0; db < kDimBlocks; ++db) o[db] *= alpha;
         }
         m = m_new;
-        bf16x8_t pb;
+        bf16x4_t pb;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
             const __bf16 pr = (__bf16)__builtin_amdgcn_exp2f(x[i] - m);
             pb[i] = pr;
             lsum += (float)pr;
         }
 
-        // O^T += V^T . P^T.  The k index (slot) runs over tile slots 4j..4j+3
-        // then 16+4j..16+4j+3 for lane group j, matching pb.  Each half comes
-        // from one ds_read_b64_tr_b16: lane i of a 16-lane group addresses
-        // row R0 + i/4, dims 16 db + 4 (i%4); lane c then receives
-        // V[R0 + e][16 db + c] for e = 0..3.
-        const int tr_row0 = 4 * j + (c >> 2);
-        const int tr_sub = (c & 3);
-        bf16x8_t va[16];
+        // O^T += V^T . P^T over the tile's 16 slots.  The k index of lane
+        // group j is slots 4j..4j+3, matching pb.  ds_read_b64_tr_b16: lane i
+        // of a 16-lane group addresses row 4j + i/4, dims 16 db + 4 (i%4);
+        // lane c then receives V[4j + e][16 db + c] for e = 0..3.
+        bf16x4_t va[kDimBlocks];
 #pragma unroll
-        for (int db = 0; db < 16; ++db) {
+        for (int db = 0; db < kDimBlocks; ++db) {
             const int chunk = 2 * db + (tr_sub >> 1);
-            const int byte_in = 8 * (tr_sub & 1);
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                LDS_PTR(i16x4_t, vs_lds + lds_off(tr_row0, chunk) + byte_in));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                LDS_PTR(i16x4_t, vs_lds + lds_off(16 + tr_row0, chunk) + byte_in));
             va[db] = __builtin_bit_cast(
-                bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(
+                              i16x4_t, vs_lds + lds_off(tr_row, chunk) + 8 * (tr_sub & 1))));
         }
 #pragma unroll
-        for (int db = 0; db < 16; ++db)
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb, o[db], 0, 0, 0);
+        for (int db = 0; db < kDimBlocks; ++db)
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[db], pb, o[db], 0, 0, 0);
     }
 
     // Whole-head denominator of this wave: add the four lane groups.
@@ -306,14 +328,14 @@ __global__ __launch_bounds__(kThreads, 1) void attend_kernel(const AttendParams 
 
     // Merge the waves' partial states through LDS (reusing the tile area).
     __syncthreads();
-    f32x4_t *part_o = (f32x4_t *)smem;                        // [wave][db][lane]
-    float *part_m = (float *)(smem + kWavesPerItem * 16 * 64 * 16);  // [wave][16]
-    float *part_l = part_m + kWavesPerItem * 16;                      // [wave][16]
+    f32x4_t *part_o = (f32x4_t *)smem;                                     // [wave][db][lane]
+    float *part_m = (float *)(smem + kWavesPerItem * kWaveLds);            // [wave][head]
+    float *part_l = part_m + kWavesPerItem * kHeadBlock;                   // [wave][head]
 #pragma unroll
-    for (int db = 0; db < 16; ++db) part_o[(wave * 16 + db) * 64 + lane] = o[db];
+    for (int db = 0; db < kDimBlocks; ++db) part_o[(wave * kDimBlocks + db) * 64 + lane] = o[db];
     if (j == 0) {
-        part_m[wave * 16 + c] = m;
-        part_l[wave * 16 + c] = lsum;
+        part_m[wave * kHeadBlock + c] = m;
+        part_l[wave * kHeadBlock + c] = lsum;
     }
     __syncthreads();
 
@@ -321,16 +343,16 @@ __global__ __launch_bounds__(kThreads, 1) void attend_kernel(const AttendParams 
     float mmax = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWavesPerItem; ++w) {
-        mw[w] = part_m[w * 16 + c];
+        mw[w] = part_m[w * kHeadBlock + c];
         mmax = fmaxf(mmax, mw[w]);
     }
     float l_tot = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWavesPerItem; ++w) {
         fw[w] = __builtin_amdgcn_exp2f(mw[w] - mmax);   // 0 for waves without tiles
-        l_tot += fw[w] * part_l[w * 16 + c];
+        l_tot += fw[w] * part_l[w * kHeadBlock + c];
     }
-    constexpr int kDbPerWave = 16 / kWavesPerItem;
+    constexpr int kDbPerWave = kDimBlocks / kWavesPerItem;
     if (c < nh) {
         uint16_t *orow = out_t + (int64_t)c * p.o_sh;
 #pragma unroll
@@ -338,7 +360,8 @@ __global__ __launch_bounds__(kThreads, 1) void attend_kernel(const AttendParams 
             const int db = wave * kDbPerWave + d;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int w = 0; w < kWavesPerItem; ++w) acc += fw[w] * part_o[(w * 16 + db) * 64 + lane];
+            for (int w = 0; w < kWavesPerItem; ++w)
+                acc += fw[w] * part_o[(w * kDimBlocks + db) * 64 + lane];
             bf16x4_t ob;
 #pragma unroll
             for (int i = 0; i < 4; ++i) ob[i] = (__bf16)(acc[i] / l_tot);
@@ -349,10 +372,12 @@ __global__ __launch_bounds__(kThreads, 1) void attend_kernel(const AttendParams 
 
 // ---------------------------------------------------------------- gather ceiling
 
-// Reads the same rows with the same tiles, waves and load pattern as
-// attend_kernel, folds them with XOR and writes one word per (t, g).
-__global__ __launch_bounds__(kThreads, 1) void ceiling_kernel(const CeilingParams p) {
-    __shared__ uint32_t fold[kWavesPerItem];
+// Reads the same rows with the same tiles, waves, prefetch distance and
+// residency as attend_kernel, folds them with XOR and writes one word per
+// (t, g): the cost of the gathers alone.
+__global__ __launch_bounds__(kThreads, kItemsPerCU) void ceiling_kernel(const CeilingParams p) {
+    // Same LDS footprint as attend_kernel, so the same number of items fit a CU.
+    __shared__ __attribute__((aligned(16))) char smem[kAttendLds];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t item = blockIdx.x;
@@ -367,27 +392,22 @@ __global__ __launch_bounds__(kThreads, 1) void ceiling_kernel(const CeilingParam
     u32x4_t acc = {0, 0, 0, 0};
     u32x4_t rk[kLoadsPerTile], rv[kLoadsPerTile];
     int tile = wave;
-    int slot_next = -1;
-    if (tile < ntiles) {
-        const int slot_cur = list[tile * kTileSlots + (lane & 31)];
-        if (tile + kWavesPerItem < ntiles)
-            slot_next = list[(tile + kWavesPerItem) * kTileSlots + (lane & 31)];
-        gather_tile(rk, rv, slot_cur, kb, p.k_ss, vb, p.v_ss, lane);
-    }
+    int slot_next = tile_slot(list, tile + kWavesPerItem, ntiles, lane);
+    if (tile < ntiles)
+        gather_tile(rk, rv, tile_slot(list, tile, ntiles, lane), kb, p.k_ss, vb, p.v_ss, lane);
     for (; tile < ntiles; tile += kWavesPerItem) {
 #pragma unroll
         for (int q = 0; q < kLoadsPerTile; ++q) acc ^= rk[q] ^ rv[q];
         const int nt = tile + kWavesPerItem;
         if (nt < ntiles) {
             gather_tile(rk, rv, slot_next, kb, p.k_ss, vb, p.v_ss, lane);
-            slot_next = nt + kWavesPerItem < ntiles
-                            ? list[(nt + kWavesPerItem) * kTileSlots + (lane & 31)]
-                            : -1;
+            slot_next = tile_slot(list, nt + kWavesPerItem, ntiles, lane);
         }
     }
     uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off);
+    uint32_t *fold = (uint32_t *)smem;
     if (lane == 0) fold[wave] = x;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -401,8 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void ceiling_kernel(const CeilingParam
 
 hipError_t launch_compact(const CompactParams &p, hipStream_t stream) {
     if (p.T == 0) return hipSuccess;
-    const int64_t blocks = (p.T + 3) / 4;
-    hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(compact_kernel, dim3((unsigned)p.T), dim3(kSortThreads), 0, stream, p);
     return hipGetLastError();
 }
 
