@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_prefill",
                     choices=["tiny", "edge_mix", "long_prefill", "two_request",
-                             "max_cache_6_1", "max_cache_3_1"])
+                             "max_cache_6_1", "max_cache_3_1", "decode_batch"])
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="token rows of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,9 +100,26 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # Few-token workloads run the split path (qsa_sparse_decode's steps):
+    # compaction, split attention into FP32 partials, merge.
+    split = args.workload == "decode_batch"
+    splits = qsa.decode_splits(T, W, Hq, Hkv) if split else 1
+    parts = qsa.new_partials(splits, T, Hq, dev) if split else None
+
+    def attend():
+        if split:
+            qsa.sparse_attend_partial(q, k, v, ws, W, splits, 0, splits, parts, scale=scale)
+        else:
+            qsa.sparse_attend(q, k, v, ws, W, scale=scale, out=out)
+
+    def finish():
+        if split:
+            qsa.merge_partials(parts, splits, T, Hq, out=out)
+
     def step():
         qsa.compact_slots(sl, S, ws)
-        qsa.sparse_attend(q, k, v, ws, W, scale=scale, out=out)
+        attend()
+        finish()
 
     for _ in range(args.warmup):
         step()
@@ -118,8 +135,9 @@ def main():
     for i in range(K):
         qsa.compact_slots(sl, S, ws)
         a0[i].record()
-        qsa.sparse_attend(q, k, v, ws, W, scale=scale, out=out)
+        attend()
         a1[i].record()
+        finish()
     t1.record()
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
@@ -186,7 +204,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": case.name, "T": T, "S": S, "W": W, "Hq": Hq, "Hkv": Hkv,
                    "D": case.D, "scale": scale, "seed": case.info.get("seed"),
-                   "parallelism": "none (1 GPU)"},
+                   "splits": splits, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic},

@@ -122,6 +122,19 @@ qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S,
                              void *stream);
 
 /*
+ * qsa_compact_slots for one shard of a cache split by slot ranges: entries in
+ * [lo, hi) are kept and stored as slot - lo (the shard's own numbering, so
+ * the shard's K/V views start at slot lo).  Entries that are neither -1 nor
+ * in [0, S) are counted as invalid exactly as in qsa_compact_slots; valid
+ * entries outside [lo, hi) belong to other shards and are skipped silently.
+ * Requires 0 <= lo <= hi <= S.  qsa_compact_slots(s, S, ...) is
+ * qsa_compact_slot_range(s, S, 0, S, ...).
+ */
+qsa_status qsa_compact_slot_range(const qsa_i32_view *slot_idx, int64_t S,
+                                  int64_t lo, int64_t hi, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
  * Gather attention over a workspace already filled by qsa_compact_slots for
  * the same T and W (the softmax(scale * Q K^T) V of the layout-embedding
  * paragraph, restricted to each token's listed slots).  Rows with count 0
@@ -147,6 +160,66 @@ qsa_status qsa_sparse_prefill(const qsa_bf16_view *q,
                               const qsa_i32_view *slot_idx, float scale,
                               qsa_bf16_view *out, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/*
+ * Split attention and its merge.  The softmax over a token's selected slots
+ * can be evaluated over disjoint shares of the slots and combined exactly
+ * with a log-sum-exp rescale; this serves decode and other small-T batches
+ * (too few (token, KV head) items to fill the GPU, so each item's slots are
+ * dealt to several workgroups) and a cache sharded by slot ranges (each
+ * shard produces its share, as in the decode context parallelism the page
+ * names in section "Where this sits in the Qwen4Exp serving build-out").
+ *
+ * A partials buffer holds n_parts shares for [T, Hq] rows: FP32 O [n_parts]
+ * [T][Hq][256] (not divided by the sum), then FP32 (m, l) [n_parts][T][Hq][2]
+ * at the next 256-byte boundary, where m is the running maximum of
+ * scale * q.k * log2(e) and l the sum of 2^(score - m).  An empty share has
+ * m = -inf, l = 0, O = 0.  qsa_partials_bytes gives the size (256-byte
+ * aligned buffer required).
+ */
+size_t qsa_partials_bytes(int64_t n_parts, int64_t T, int64_t Hq);
+
+/* Deal each item's tiles of a compacted workspace (from qsa_compact_slots or
+ * qsa_compact_slot_range, for the same T, W) to `splits` workgroups and write
+ * their shares into parts [part_base, part_base + splits) of a partials
+ * buffer holding n_parts parts. */
+qsa_status qsa_sparse_attend_partial(const qsa_bf16_view *q,
+                                     const qsa_bf16_view *k_cache,
+                                     const qsa_bf16_view *v_cache, int64_t W,
+                                     float scale, const void *workspace,
+                                     size_t workspace_bytes, int32_t splits,
+                                     int64_t part_base, int64_t n_parts,
+                                     void *partials, size_t partials_bytes,
+                                     void *stream);
+
+/* out[t,h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the n_parts
+ * shares (M = max_s m_s), rounded to BF16; exactly +0.0 when every share is
+ * empty.  out is [T, Hq, 256] and must not overlap the partials. */
+qsa_status qsa_merge_partials(const void *partials, size_t partials_bytes,
+                              int64_t n_parts, int64_t T, int64_t Hq,
+                              qsa_bf16_view *out, void *stream);
+
+/* Splits per item that qsa_sparse_decode uses for these sizes (a pure
+ * function of the sizes: enough workgroups to cover the GPU, at least one
+ * tile per wave per split, at most 64). */
+int32_t qsa_decode_splits(int64_t T, int64_t W, int32_t Hq, int32_t Hkv);
+
+/* Workspace bytes for qsa_sparse_decode: the compaction area followed by the
+ * partials of qsa_decode_splits(T, W, Hq, Hkv) shares. */
+size_t qsa_decode_workspace_bytes(int64_t T, int64_t W, int32_t Hq, int32_t Hkv);
+
+/*
+ * The same operation as qsa_sparse_prefill, organised for few tokens
+ * (decode steps, short batches): compaction, split attention over
+ * qsa_decode_splits shares per item, merge.  Same arguments and conventions
+ * as qsa_sparse_prefill; the workspace must hold qsa_decode_workspace_bytes.
+ */
+qsa_status qsa_sparse_decode(const qsa_bf16_view *q,
+                             const qsa_bf16_view *k_cache,
+                             const qsa_bf16_view *v_cache,
+                             const qsa_i32_view *slot_idx, float scale,
+                             qsa_bf16_view *out, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /*
  * Synchronizes `stream`, then reads the invalid-entry counts that the last

@@ -259,6 +259,38 @@ def max_cache(seed: int = 105, heads=(6, 1)) -> Case:
                             {"seed": seed})
 
 
+DECODE_REQUESTS = 16
+
+
+def decode_batch(seed: int = 106) -> Case:
+    """A decode step for 16 requests in one 262,144-slot paged cache.
+
+    Request i holds a context of 8,192 + 1,024 i tokens whose logical
+    positions map, in order, onto its own range of a seeded permutation of
+    the cache slots.  Its one new token sits at the last position p and
+    selects, by the causal-tail rule of `two_request`, its last
+    r = (p + 1) % 4 positions plus 2,048 - r distinct earlier ones.
+    (Hq,Hkv)=(24,2), W=2,048, default scale.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    S, Hq, Hkv, W = 262144, 24, 2, CAUSAL_BUDGET
+    T = DECODE_REQUESTS
+    lengths = 8192 + 1024 * np.arange(T)
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+    perm = rng.permutation(S)
+    pos = lengths - 1
+    r = (pos + 1) % COMPRESSION
+    logical = shuffle_rows(rng, distinct_draws(rng, pos - r + 1, T, W))
+    col = np.arange(W)[None, :]
+    tail = col >= (W - r)[:, None]
+    logical = np.where(tail, pos[:, None] - (W - 1 - col), logical)
+    phys = perm[starts[:, None] + logical]
+    sel = shuffle_rows(rng, phys)
+    return _contiguous_case("decode_batch", rng, T, S, Hq, Hkv, sel, None,
+                            {"seed": seed, "perm": perm, "lengths": lengths,
+                             "starts": starts, "positions": pos})
+
+
 WORKLOADS = {
     "tiny": tiny,
     "edge_mix": edge_mix,
@@ -266,6 +298,7 @@ WORKLOADS = {
     "two_request": two_request,
     "max_cache_6_1": lambda seed=105: max_cache(seed, (6, 1)),
     "max_cache_3_1": lambda seed=105: max_cache(seed, (3, 1)),
+    "decode_batch": decode_batch,
 }
 
 

@@ -154,3 +154,56 @@ def test_python_binding_rejects_wrong_dtypes():
         qsa._bf16_view(q, "q")
     with pytest.raises(TypeError):
         qsa._i32_view(torch.zeros(2, 3, dtype=torch.int64), "slot_idx")
+
+
+def test_partials_and_decode_sizes():
+    _lib()
+    rows = 3 * 5 * 7
+    o_bytes = (rows * 256 * 4 + 255) // 256 * 256
+    assert qsa.partials_bytes(3, 5, 7) == o_bytes + (rows * 8 + 255) // 256 * 256
+    assert qsa.partials_bytes(-1, 5, 7) == 0
+    # enough workgroups to cover the GPU, >= 4 tiles per split, <= 64 splits
+    assert qsa.decode_splits(16, 2048, 24, 2) == 32
+    assert qsa.decode_splits(1, 2048, 16, 2) == 32
+    assert qsa.decode_splits(1, 100000, 16, 2) == 64
+    assert qsa.decode_splits(7810, 2051, 16, 2) == 1
+    assert qsa.decode_splits(4, 64, 8, 1) == 1
+    assert qsa.decode_splits(0, 64, 8, 1) == 1
+    ws = qsa.workspace_bytes(16, 2048)
+    assert qsa.decode_workspace_bytes(16, 2048, 24, 2) == \
+        (ws + 255) // 256 * 256 + qsa.partials_bytes(32, 16, 24)
+
+
+@host_only
+def test_split_entry_points_reject_bad_arguments():
+    lib = _lib()
+    r = ctypes.byref
+    q, k, v, o, s = good()
+    ws, part = FAKE + (5 << 24), FAKE + (6 << 24)
+    big = 1 << 30
+
+    def partial(splits=2, base=0, n_parts=2, part_bytes=big, parts=part):
+        return qsa.STATUS_NAMES[lib.qsa_sparse_attend_partial(
+            r(q), r(k), r(v), 8, 0.0625, ws, big, splits, base, n_parts, parts, part_bytes,
+            None)]
+
+    assert partial(splits=0) == "QSA_ERR_SHAPE"
+    assert partial(base=1) == "QSA_ERR_SHAPE"            # parts [1, 3) beyond n_parts = 2
+    assert partial(base=-1) == "QSA_ERR_SHAPE"
+    assert partial(part_bytes=qsa.partials_bytes(2, 4, 4) - 1) == "QSA_ERR_WORKSPACE"
+    assert partial(parts=None) == "QSA_ERR_WORKSPACE"
+    assert partial(parts=FAKE + 8) == "QSA_ERR_WORKSPACE"
+    assert partial(parts=q.data) == "QSA_ERR_ALIAS"       # partials on top of q
+    assert qsa.STATUS_NAMES[lib.qsa_merge_partials(part, big, 0, 4, 4, r(o), None)] == \
+        "QSA_ERR_SHAPE"
+    bad_o = view((5, 4, 256), (1024, 256, 1), FAKE + (3 << 24))
+    assert qsa.STATUS_NAMES[lib.qsa_merge_partials(part, big, 2, 4, 4, r(bad_o), None)] == \
+        "QSA_ERR_SHAPE"
+    over = view((4, 4, 256), (1024, 256, 1), part + 256)
+    assert qsa.STATUS_NAMES[lib.qsa_merge_partials(part, big, 2, 4, 4, r(over), None)] == \
+        "QSA_ERR_ALIAS"
+    for lo, hi in ((-1, 10), (10, 5), (0, 65)):
+        assert qsa.STATUS_NAMES[lib.qsa_compact_slot_range(r(s), 64, lo, hi, ws, big, None)] == \
+            "QSA_ERR_SHAPE"
+    assert qsa.STATUS_NAMES[lib.qsa_sparse_decode(
+        r(q), r(k), r(v), r(s), 0.0625, r(o), ws, 16, None)] == "QSA_ERR_WORKSPACE"

@@ -1,0 +1,161 @@
+"""GPU parity of split attention: qsa_sparse_attend_partial + qsa_merge_partials,
+qsa_sparse_decode, and a cache sharded by slot ranges (the context-parallel
+layout of the decode work named in section "Where this sits in the Qwen4Exp
+serving build-out" of the page "Qwen4-Exp QSA comes to Huawei's Ascend",
+rehearsed on one GPU).  Same gate as every floating-point test.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_inputs as qi
+import top_sparse_attention_amd as qsa
+from qsa_testutil import bf16_tensor_bits, bf16_tensor_to_f32, empty_row_mask, gate, upload
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def oracle_rows(case, rows=None):
+    scale = case.scale if case.scale is not None else 1.0 / 16.0
+    return oracle.prefill(case.q, case.k_cache, case.v_cache, case.slot_idx, scale, rows=rows)
+
+
+def check(case, got, rows=None):
+    want = oracle_rows(case, rows)
+    g = bf16_tensor_to_f32(got if rows is None else got[torch.as_tensor(rows, device=DEV)])
+    m = gate(g, want, empty_row_mask(case.slot_idx, case.S, rows))
+    print(f"{case.name}: {m}", flush=True)
+    return m
+
+
+def test_decode_batch_workload():
+    case = qi.decode_batch()
+    q, k, v, sl = upload(case, DEV)
+    assert qsa.decode_splits(case.T, case.W, case.Hq, case.Hkv) == 32
+    out = qsa.sparse_decode(q, k, v, sl)
+    torch.cuda.synchronize()
+    check(case, out)
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,W,pad", [(1, 16, 2, 2048, 0.0), (2, 24, 2, 300, 0.3),
+                                           (5, 12, 1, 2051, 0.5), (3, 40, 2, 100, 0.0),
+                                           (7, 3, 1, 17, 0.2), (1, 6, 1, 1, 0.0)])
+def test_decode_small_batches(T, Hq, Hkv, W, pad):
+    case = qi.random_case(800 + T * 7 + W, T=T, S=20000, Hq=Hq, Hkv=Hkv, W=W, pad_frac=pad,
+                          interior=True)
+    q, k, v, sl = upload(case, DEV)
+    out = qsa.sparse_decode(q, k, v, sl, scale=case.scale)
+    torch.cuda.synchronize()
+    check(case, out)
+
+
+def test_decode_empty_rows_and_zero_width_are_exact_zero():
+    case = qi.random_case(820, T=6, S=999, Hq=8, Hkv=1, W=50)
+    case.slot_idx[[1, 4]] = -1
+    q, k, v, sl = upload(case, DEV)
+    out = qsa.sparse_decode(q, k, v, sl)
+    torch.cuda.synchronize()
+    check(case, out)
+    assert torch.all(out[[1, 4]].view(torch.int16) == 0)
+    case0 = qi.random_case(821, T=3, S=64, Hq=4, Hkv=2, W=0)
+    q, k, v, sl = upload(case0, DEV)
+    out = qsa.sparse_decode(q, k, v, sl)
+    torch.cuda.synchronize()
+    assert torch.all(out.view(torch.int16) == 0)
+
+
+def test_decode_single_slot_is_bit_exact():
+    case = qi.random_case(822, T=4, S=3000, Hq=24, Hkv=2, W=300, pad_frac=299 / 300,
+                          interior=True)
+    q, k, v, sl = upload(case, DEV)
+    out = qsa.sparse_decode(q, k, v, sl)
+    torch.cuda.synchronize()
+    bits = bf16_tensor_bits(out)
+    for t in range(case.T):
+        (s,) = case.slot_idx[t][case.slot_idx[t] != -1]
+        for h in range(case.Hq):
+            np.testing.assert_array_equal(bits[t, h], case.v_cache[s, h // 12])
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64, 200])
+def test_any_split_count_merges_to_the_same_attention(splits):
+    """splits beyond the tile count leave some shares empty."""
+    case = qi.random_case(830 + splits, T=9, S=5000, Hq=16, Hkv=2, W=700, pad_frac=0.2,
+                          interior=True)
+    q, k, v, sl = upload(case, DEV)
+    ws = qsa.compact_slots(sl, case.S)
+    parts = qsa.new_partials(splits, case.T, case.Hq, DEV)
+    qsa.sparse_attend_partial(q, k, v, ws, case.W, splits, 0, splits, parts, scale=case.scale)
+    out = qsa.merge_partials(parts, splits, case.T, case.Hq)
+    torch.cuda.synchronize()
+    check(case, out)
+
+
+def test_merge_of_all_empty_parts_is_exact_zero():
+    T, Hq, n = 5, 6, 3
+    parts = qsa.new_partials(n, T, Hq, DEV)
+    nbytes = T * Hq * n * 256 * 4
+    ml_off = (nbytes + 255) // 256 * 256
+    f = parts.view(torch.float32)
+    f[: nbytes // 4] = 123.0
+    ml = f[ml_off // 4: ml_off // 4 + n * T * Hq * 2].view(n, T, Hq, 2)
+    ml[..., 0] = -float("inf")
+    ml[..., 1] = 0.0
+    out = qsa.merge_partials(parts, n, T, Hq)
+    torch.cuda.synchronize()
+    assert torch.all(out.view(torch.int16) == 0)
+
+
+@pytest.mark.parametrize("bounds", [(0.5,), (0.25, 0.3, 0.9), (0.0, 0.999)])
+def test_cache_sharded_by_slot_ranges(bounds):
+    """Each shard sees only its slot range through a view of the cache that
+    starts at its first slot; the merged shares equal the unsharded attention."""
+    case = qi.random_case(840 + len(bounds), T=33, S=12000, Hq=16, Hkv=2, W=900,
+                          pad_frac=0.1, interior=True)
+    q, k, v, sl = upload(case, DEV)
+    cuts = [0] + [int(b * case.S) for b in bounds] + [case.S]
+    n = len(cuts) - 1
+    parts = qsa.new_partials(n, case.T, case.Hq, DEV)
+    for i in range(n):
+        lo, hi = cuts[i], cuts[i + 1]
+        ws = qsa.compact_slot_range(sl, case.S, lo, hi)
+        qsa.sparse_attend_partial(q, k[lo:hi], v[lo:hi], ws, case.W, 1, i, n, parts,
+                                  scale=case.scale)
+    out = qsa.merge_partials(parts, n, case.T, case.Hq)
+    torch.cuda.synchronize()
+    check(case, out)
+    whole = qsa.sparse_prefill(q, k, v, sl, scale=case.scale)
+    torch.cuda.synchronize()
+    gate(bf16_tensor_to_f32(out), bf16_tensor_to_f32(whole), np.zeros(case.T, dtype=bool))
+
+
+def test_shard_compaction_keeps_local_numbering():
+    case = qi.random_case(850, T=20, S=3000, Hq=2, Hkv=1, W=200, pad_frac=0.1, interior=True)
+    case.slot_idx[3, 5] = 3000          # invalid everywhere
+    _, _, _, sl = upload(case, DEV)
+    lo, hi = 1000, 2200
+    ws = qsa.compact_slot_range(sl, case.S, lo, hi)
+    torch.cuda.synchronize()
+    lst, cnt, bad = (x.cpu().numpy() for x in qsa.compacted_lists(ws, case.T, case.W))
+    for t in range(case.T):
+        row = case.slot_idx[t]
+        mine = sorted(int(s) - lo for s in row if lo <= s < hi)
+        assert cnt[t] == len(mine)
+        assert sorted(lst[t, :cnt[t]].tolist()) == mine
+        assert bad[t] == (1 if t == 3 else 0)
+
+
+def test_split_path_on_the_long_prefill_sampled_rows():
+    case = qi.long_prefill()
+    q, k, v, sl = upload(case, DEV)
+    ws = qsa.compact_slots(sl, case.S)
+    parts = qsa.new_partials(3, case.T, case.Hq, DEV)
+    qsa.sparse_attend_partial(q, k, v, ws, case.W, 3, 0, 3, parts)
+    out = qsa.merge_partials(parts, 3, case.T, case.Hq)
+    torch.cuda.synchronize()
+    rows = qi.sample_rows(case.T, 32)
+    check(case, out, rows)
+    assert torch.isfinite(out.float()).all()

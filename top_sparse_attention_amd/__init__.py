@@ -24,6 +24,8 @@ __all__ = [
     "QsaError", "library_path", "load_library", "version", "workspace_bytes",
     "workspace_layout", "new_workspace", "compact_slots", "compacted_lists",
     "sparse_attend", "sparse_prefill", "check_status", "gather_ceiling",
+    "compact_slot_range", "partials_bytes", "new_partials", "sparse_attend_partial",
+    "merge_partials", "decode_splits", "decode_workspace_bytes", "sparse_decode",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -103,6 +105,22 @@ def load_library():
     lib.qsa_check_status.argtypes = [vp, sz, i64, i64, vp, P(i64)]
     lib.qsa_gather_ceiling.restype = ctypes.c_int
     lib.qsa_gather_ceiling.argtypes = [P(BF16View), P(BF16View), i64, i64, vp, sz, vp, vp]
+    lib.qsa_compact_slot_range.restype = ctypes.c_int
+    lib.qsa_compact_slot_range.argtypes = [P(I32View), i64, i64, i64, vp, sz, vp]
+    lib.qsa_partials_bytes.restype = sz
+    lib.qsa_partials_bytes.argtypes = [i64, i64, i64]
+    lib.qsa_sparse_attend_partial.restype = ctypes.c_int
+    lib.qsa_sparse_attend_partial.argtypes = [P(BF16View), P(BF16View), P(BF16View), i64, f32,
+                                              vp, sz, ctypes.c_int32, i64, i64, vp, sz, vp]
+    lib.qsa_merge_partials.restype = ctypes.c_int
+    lib.qsa_merge_partials.argtypes = [vp, sz, i64, i64, i64, P(BF16View), vp]
+    lib.qsa_decode_splits.restype = ctypes.c_int32
+    lib.qsa_decode_splits.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32]
+    lib.qsa_decode_workspace_bytes.restype = sz
+    lib.qsa_decode_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32]
+    lib.qsa_sparse_decode.restype = ctypes.c_int
+    lib.qsa_sparse_decode.argtypes = [P(BF16View), P(BF16View), P(BF16View), P(I32View), f32,
+                                      P(BF16View), vp, sz, vp]
     _lib = lib
     return lib
 
@@ -250,3 +268,79 @@ def gather_ceiling(k_cache: torch.Tensor, v_cache: torch.Tensor, workspace: torc
         ctypes.byref(kv), ctypes.byref(vv), T, W, workspace.data_ptr(), workspace.numel(),
         sink.data_ptr(), _stream(k_cache.device)))
     return sink
+
+
+# ---------------------------------------------------------------- split attention
+
+def compact_slot_range(slot_idx: torch.Tensor, S: int, lo: int, hi: int,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Compaction for the cache shard [lo, hi): kept slots are stored as slot - lo."""
+    T, W = slot_idx.shape
+    if workspace is None:
+        workspace = new_workspace(T, W, slot_idx.device)
+    sv = _i32_view(slot_idx, "slot_idx")
+    _raise_on(load_library().qsa_compact_slot_range(
+        ctypes.byref(sv), S, lo, hi, workspace.data_ptr(), workspace.numel(),
+        _stream(workspace.device)))
+    return workspace
+
+
+def partials_bytes(n_parts: int, T: int, Hq: int) -> int:
+    return int(load_library().qsa_partials_bytes(n_parts, T, Hq))
+
+
+def new_partials(n_parts: int, T: int, Hq: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(partials_bytes(n_parts, T, Hq), 1), dtype=torch.uint8, device=device)
+
+
+def sparse_attend_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          workspace: torch.Tensor, W: int, splits: int, part_base: int,
+                          n_parts: int, partials: torch.Tensor,
+                          scale: Optional[float] = None) -> torch.Tensor:
+    """Write `splits` shares of each item into parts [part_base, part_base + splits)."""
+    qv, kv, vv = _bf16_view(q, "q"), _bf16_view(k_cache, "k_cache"), _bf16_view(v_cache, "v_cache")
+    _raise_on(load_library().qsa_sparse_attend_partial(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), W,
+        _default_scale(scale, q.shape[-1]), workspace.data_ptr(), workspace.numel(),
+        splits, part_base, n_parts, partials.data_ptr(), partials.numel(), _stream(q.device)))
+    return partials
+
+
+def merge_partials(partials: torch.Tensor, n_parts: int, T: int, Hq: int,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((T, Hq, HEAD_DIM), dtype=torch.bfloat16, device=partials.device)
+    ov = _bf16_view(out, "out")
+    _raise_on(load_library().qsa_merge_partials(
+        partials.data_ptr(), partials.numel(), n_parts, T, Hq, ctypes.byref(ov),
+        _stream(partials.device)))
+    return out
+
+
+def decode_splits(T: int, W: int, Hq: int, Hkv: int) -> int:
+    return int(load_library().qsa_decode_splits(T, W, Hq, Hkv))
+
+
+def decode_workspace_bytes(T: int, W: int, Hq: int, Hkv: int) -> int:
+    return int(load_library().qsa_decode_workspace_bytes(T, W, Hq, Hkv))
+
+
+def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  slot_idx: torch.Tensor, scale: Optional[float] = None,
+                  out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sparse attention for few tokens: compaction, split attention, merge."""
+    T, W = slot_idx.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if workspace is None:
+        nbytes = decode_workspace_bytes(T, W, q.shape[1], k_cache.shape[1])
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    qv, kv, vv, ov = (_bf16_view(q, "q"), _bf16_view(k_cache, "k_cache"),
+                      _bf16_view(v_cache, "v_cache"), _bf16_view(out, "out"))
+    sv = _i32_view(slot_idx, "slot_idx")
+    _raise_on(load_library().qsa_sparse_decode(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), ctypes.byref(sv),
+        _default_scale(scale, q.shape[-1]), ctypes.byref(ov), workspace.data_ptr(),
+        workspace.numel(), _stream(q.device)))
+    return out

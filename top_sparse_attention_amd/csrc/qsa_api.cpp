@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -88,17 +89,15 @@ struct Problem {
     int32_t Hq, Hkv;
 };
 
-qsa_status check_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
-                        const qsa_bf16_view *v, const qsa_bf16_view *out, int64_t W,
-                        float scale, Problem *pr) {
+// Checks of q, k_cache, v_cache, W and scale shared by every attention entry point.
+qsa_status check_inputs(const qsa_bf16_view *q, const qsa_bf16_view *k, const qsa_bf16_view *v,
+                        int64_t W, float scale, Problem *pr) {
     qsa_status s;
     if ((s = check_bf16(q, "q")) || (s = check_bf16(k, "k_cache")) ||
-        (s = check_bf16(v, "v_cache")) || (s = check_bf16(out, "out")))
+        (s = check_bf16(v, "v_cache")))
         return s;
-    for (int i = 0; i < 3; ++i) {
-        if (out->size[i] != q->size[i]) return fail(QSA_ERR_SHAPE, "out must have q's shape");
+    for (int i = 0; i < 3; ++i)
         if (v->size[i] != k->size[i]) return fail(QSA_ERR_SHAPE, "v_cache must have k_cache's shape");
-    }
     pr->T = q->size[0];
     pr->S = k->size[0];
     pr->W = W;
@@ -114,16 +113,36 @@ qsa_status check_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
     if (pr->T > kMax32 || W > kMax32 || pr->S > kMax32)
         return fail(QSA_ERR_UNSUPPORTED, "T, W and S must fit in int32");
     if (!std::isfinite(scale)) return fail(QSA_ERR_SCALE, "scale must be finite");
+    return QSA_OK;
+}
+
+// A written byte range [lo, hi) must not overlap any of q, k_cache, v_cache.
+qsa_status check_no_overlap(uintptr_t lo, uintptr_t hi, const qsa_bf16_view *q,
+                            const qsa_bf16_view *k, const qsa_bf16_view *v, const char *what) {
+    const qsa_bf16_view *ins[3] = {q, k, v};
+    for (const qsa_bf16_view *in : ins) {
+        if (any_empty(in)) continue;
+        uintptr_t ilo, ihi;
+        span_of(in, &ilo, &ihi);
+        if (lo < ihi && ilo < hi) return fail(QSA_ERR_ALIAS, "%s overlaps an input", what);
+    }
+    return QSA_OK;
+}
+
+qsa_status check_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
+                        const qsa_bf16_view *v, const qsa_bf16_view *out, int64_t W,
+                        float scale, Problem *pr) {
+    qsa_status s;
+    if ((s = check_bf16(q, "q")) || (s = check_bf16(k, "k_cache")) ||
+        (s = check_bf16(v, "v_cache")) || (s = check_bf16(out, "out")))
+        return s;
+    for (int i = 0; i < 3; ++i)
+        if (out->size[i] != q->size[i]) return fail(QSA_ERR_SHAPE, "out must have q's shape");
+    if ((s = check_inputs(q, k, v, W, scale, pr))) return s;
     if (!any_empty(out)) {
         uintptr_t olo, ohi;
         span_of(out, &olo, &ohi);
-        const qsa_bf16_view *ins[3] = {q, k, v};
-        for (const qsa_bf16_view *in : ins) {
-            if (any_empty(in)) continue;
-            uintptr_t lo, hi;
-            span_of(in, &lo, &hi);
-            if (olo < hi && lo < ohi) return fail(QSA_ERR_ALIAS, "out overlaps an input");
-        }
+        if ((s = check_no_overlap(olo, ohi, q, k, v, "out"))) return s;
     }
     return QSA_OK;
 }
@@ -146,16 +165,18 @@ qsa_status hip_fail(hipError_t e, const char *what) {
     return fail(QSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t S, void *ws,
-                           const qsa_workspace_map &m, hipStream_t stream) {
+qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t S, int64_t lo,
+                           int64_t hi, void *ws, const qsa_workspace_map &m, hipStream_t stream) {
     qsa::CompactParams p{};
     p.slot_idx = sl->data;
     p.stride_t = sl->stride[0];
     p.T = T;
     p.W = W;
     p.S = S;
-    int bits = 1;   // width of S - 1, at least one bit
-    while (bits < 31 && ((int64_t)1 << bits) < S) ++bits;
+    p.lo = lo;
+    p.hi = hi;
+    int bits = 1;   // width of hi - lo - 1, at least one bit
+    while (bits < 31 && ((int64_t)1 << bits) < hi - lo) ++bits;
     p.key_bits = bits + 1;   // one more bit for the key that marks invalid entries
     p.list = (int32_t *)((char *)ws + m.list_offset);
     p.row_stride = m.row_stride;
@@ -165,12 +186,98 @@ qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t
     return e == hipSuccess ? QSA_OK : hip_fail(e, "compaction launch");
 }
 
+void fill_attend(qsa::AttendParams &p, const qsa_bf16_view *q, const qsa_bf16_view *k,
+                 const qsa_bf16_view *v, const Problem &pr, float scale, const void *ws,
+                 const qsa_workspace_map &m);
+
 qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
                           const qsa_bf16_view *v, const qsa_bf16_view *out, const Problem &pr,
                           float scale, const void *ws, const qsa_workspace_map &m,
                           hipStream_t stream) {
     if (pr.T == 0 || pr.Hq == 0) return QSA_OK;
     qsa::AttendParams p{};
+    fill_attend(p, q, k, v, pr, scale, ws, m);
+    p.out = (uint16_t *)out->data;
+    p.o_st = out->stride[0];
+    p.o_sh = out->stride[1];
+    hipError_t e = qsa::launch_attend(p, pr.T, stream);
+    return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
+}
+
+// Partials buffer: O [n_parts][T][Hq][256] FP32, then (m, l) [n_parts][T][Hq][2] FP32.
+struct PartialsMap {
+    int64_t ml_offset, total_bytes;
+};
+
+bool partials_of(int64_t n_parts, int64_t T, int64_t Hq, PartialsMap *pm) {
+    if (n_parts < 0 || T < 0 || Hq < 0) return false;
+    const int64_t rows = n_parts * T * Hq;
+    pm->ml_offset = round_up(rows * qsa::kHeadDim * 4, kAlign);
+    pm->total_bytes = pm->ml_offset + round_up(rows * 8, kAlign);
+    return true;
+}
+
+qsa_status check_partials(const void *buf, size_t bytes, int64_t n_parts, int64_t T, int64_t Hq,
+                          PartialsMap *pm) {
+    if (!partials_of(n_parts, T, Hq, pm)) return fail(QSA_ERR_SHAPE, "negative partials size");
+    if (!buf) return fail(QSA_ERR_WORKSPACE, "partials buffer is NULL");
+    if ((uintptr_t)buf % kAlign) return fail(QSA_ERR_WORKSPACE, "partials must be 256-byte aligned");
+    if ((int64_t)bytes < pm->total_bytes)
+        return fail(QSA_ERR_WORKSPACE, "partials buffer holds %zu bytes, %lld needed", bytes,
+                    (long long)pm->total_bytes);
+    return QSA_OK;
+}
+
+qsa_status enqueue_partial(const qsa_bf16_view *q, const qsa_bf16_view *k,
+                           const qsa_bf16_view *v, const Problem &pr, float scale, const void *ws,
+                           const qsa_workspace_map &m, int32_t splits, int64_t part_base,
+                           void *partials, const PartialsMap &pm, hipStream_t stream) {
+    if (pr.T == 0 || pr.Hq == 0) return QSA_OK;
+    qsa::AttendParams p{};
+    fill_attend(p, q, k, v, pr, scale, ws, m);
+    p.splits = splits;
+    p.part_base = part_base;
+    p.T = pr.T;
+    p.Hq = pr.Hq;
+    p.part_o = (float *)partials;
+    p.part_ml = (float *)((char *)partials + pm.ml_offset);
+    hipError_t e = qsa::launch_attend_partial(p, pr.T, stream);
+    return e == hipSuccess ? QSA_OK : hip_fail(e, "partial attention launch");
+}
+
+qsa_status enqueue_merge(const void *partials, const PartialsMap &pm, int64_t n_parts, int64_t T,
+                         int32_t Hq, const qsa_bf16_view *out, hipStream_t stream) {
+    qsa::MergeParams p{};
+    p.part_o = (const float *)partials;
+    p.part_ml = (const float *)((const char *)partials + pm.ml_offset);
+    p.n_parts = n_parts;
+    p.T = T;
+    p.Hq = Hq;
+    p.out = (uint16_t *)out->data;
+    p.o_st = out->stride[0];
+    p.o_sh = out->stride[1];
+    hipError_t e = qsa::launch_merge(p, stream);
+    return e == hipSuccess ? QSA_OK : hip_fail(e, "merge launch");
+}
+
+// Splits per item for qsa_sparse_decode: enough workgroups to cover every
+// CU a few times over, at least 4 tiles (one per wave) per split, at most 64.
+// A pure function of the sizes, so results are reproducible.
+int32_t decode_splits(int64_t T, int64_t W, int32_t Hq, int32_t Hkv) {
+    if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0) return 1;
+    const int64_t G = Hq / Hkv;
+    const int64_t items = T * Hkv * ((G + 15) / 16);
+    const int64_t tiles = (W + qsa::kTileSlots - 1) / qsa::kTileSlots;
+    const int64_t target_blocks = 2048;
+    int64_t s = (target_blocks + items - 1) / items;
+    s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / qsa::kWavesPerItem));
+    s = std::min<int64_t>(s, 64);
+    return (int32_t)std::max<int64_t>(s, 1);
+}
+
+void fill_attend(qsa::AttendParams &p, const qsa_bf16_view *q, const qsa_bf16_view *k,
+                 const qsa_bf16_view *v, const Problem &pr, float scale, const void *ws,
+                 const qsa_workspace_map &m) {
     p.q = (const uint16_t *)q->data;
     p.q_st = q->stride[0];
     p.q_sh = q->stride[1];
@@ -183,15 +290,11 @@ qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
     p.list = (const int32_t *)((const char *)ws + m.list_offset);
     p.list_stride = m.row_stride;
     p.count = (const int32_t *)((const char *)ws + m.count_offset);
-    p.out = (uint16_t *)out->data;
-    p.o_st = out->stride[0];
-    p.o_sh = out->stride[1];
     p.Hkv = pr.Hkv;
     p.G = pr.Hq / pr.Hkv;
     p.HB = (p.G + 15) / 16;
     p.scale_log2e = (float)((double)scale * 1.4426950408889634);
-    hipError_t e = qsa::launch_attend(p, pr.T, stream);
-    return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
+    p.splits = 1;
 }
 
 }  // namespace
@@ -229,8 +332,8 @@ qsa_status qsa_workspace_layout(int64_t T, int64_t W, qsa_workspace_map *map) {
     return QSA_OK;
 }
 
-qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+qsa_status qsa_compact_slot_range(const qsa_i32_view *slot_idx, int64_t S, int64_t lo, int64_t hi,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
     if (!slot_idx) return fail(QSA_ERR_NULL, "slot_idx: view pointer is NULL");
     const int64_t T = slot_idx->size[0];
     int64_t W = 0;
@@ -238,9 +341,16 @@ qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S, void *work
     if (s) return s;
     if (S < 0) return fail(QSA_ERR_SHAPE, "negative S");
     if (S > kMax32) return fail(QSA_ERR_UNSUPPORTED, "S must fit in int32");
+    if (lo < 0 || hi < lo || hi > S) return fail(QSA_ERR_SHAPE, "need 0 <= lo <= hi <= S");
     qsa_workspace_map m;
     if ((s = check_workspace(workspace, workspace_bytes, T, W, &m))) return s;
-    return enqueue_compact(slot_idx, T, W, S, workspace, m, (hipStream_t)stream);
+    return enqueue_compact(slot_idx, T, W, S, lo, hi, workspace, m, (hipStream_t)stream);
+}
+
+qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    return qsa_compact_slot_range(slot_idx, S, 0, S < 0 ? 0 : S, workspace, workspace_bytes,
+                                  stream);
 }
 
 qsa_status qsa_sparse_attend(const qsa_bf16_view *q, const qsa_bf16_view *k_cache,
@@ -269,8 +379,97 @@ qsa_status qsa_sparse_prefill(const qsa_bf16_view *q, const qsa_bf16_view *k_cac
     if ((s = check_workspace(workspace, workspace_bytes, pr.T, W, &m))) return s;
     if (pr.T == 0) return QSA_OK;
     hipStream_t st = (hipStream_t)stream;
-    if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, workspace, m, st))) return s;
+    if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, 0, pr.S, workspace, m, st))) return s;
     return enqueue_attend(q, k_cache, v_cache, out, pr, scale, workspace, m, st);
+}
+
+size_t qsa_partials_bytes(int64_t n_parts, int64_t T, int64_t Hq) {
+    PartialsMap pm;
+    return partials_of(n_parts, T, Hq, &pm) ? (size_t)pm.total_bytes : 0;
+}
+
+qsa_status qsa_sparse_attend_partial(const qsa_bf16_view *q, const qsa_bf16_view *k_cache,
+                                     const qsa_bf16_view *v_cache, int64_t W, float scale,
+                                     const void *workspace, size_t workspace_bytes,
+                                     int32_t splits, int64_t part_base, int64_t n_parts,
+                                     void *partials, size_t partials_bytes, void *stream) {
+    Problem pr;
+    qsa_status s = check_inputs(q, k_cache, v_cache, W, scale, &pr);
+    if (s) return s;
+    if (splits < 1 || splits > 4096) return fail(QSA_ERR_SHAPE, "splits must be in [1, 4096]");
+    if (part_base < 0 || part_base + splits > n_parts)
+        return fail(QSA_ERR_SHAPE, "parts [part_base, part_base + splits) must lie in [0, n_parts)");
+    qsa_workspace_map m;
+    if ((s = check_workspace(workspace, workspace_bytes, pr.T, W, &m))) return s;
+    PartialsMap pm;
+    if ((s = check_partials(partials, partials_bytes, n_parts, pr.T, pr.Hq, &pm))) return s;
+    if ((s = check_no_overlap((uintptr_t)partials, (uintptr_t)partials + (uintptr_t)pm.total_bytes,
+                              q, k_cache, v_cache, "partials")))
+        return s;
+    return enqueue_partial(q, k_cache, v_cache, pr, scale, workspace, m, splits, part_base,
+                           partials, pm, (hipStream_t)stream);
+}
+
+qsa_status qsa_merge_partials(const void *partials, size_t partials_bytes, int64_t n_parts,
+                              int64_t T, int64_t Hq, qsa_bf16_view *out, void *stream) {
+    qsa_status s = check_bf16(out, "out");
+    if (s) return s;
+    if (out->size[0] != T || out->size[1] != Hq)
+        return fail(QSA_ERR_SHAPE, "out must be [T, Hq, 256]");
+    if (n_parts < 1) return fail(QSA_ERR_SHAPE, "n_parts must be positive");
+    if (T > kMax32 || Hq > kMax32) return fail(QSA_ERR_UNSUPPORTED, "sizes beyond int32");
+    PartialsMap pm;
+    if ((s = check_partials(partials, partials_bytes, n_parts, T, Hq, &pm))) return s;
+    uintptr_t olo, ohi;
+    if (!any_empty(out)) {
+        span_of(out, &olo, &ohi);
+        const uintptr_t plo = (uintptr_t)partials, phi = plo + (uintptr_t)pm.total_bytes;
+        if (olo < phi && plo < ohi) return fail(QSA_ERR_ALIAS, "out overlaps the partials");
+    }
+    if (T == 0 || Hq == 0) return QSA_OK;
+    return enqueue_merge(partials, pm, n_parts, T, (int32_t)Hq, out, (hipStream_t)stream);
+}
+
+int32_t qsa_decode_splits(int64_t T, int64_t W, int32_t Hq, int32_t Hkv) {
+    return decode_splits(T, W, Hq, Hkv);
+}
+
+size_t qsa_decode_workspace_bytes(int64_t T, int64_t W, int32_t Hq, int32_t Hkv) {
+    qsa_workspace_map m;
+    PartialsMap pm;
+    if (!layout_of(T, W, &m) || Hq < 0) return 0;
+    if (!partials_of(decode_splits(T, W, Hq, Hkv), T, Hq, &pm)) return 0;
+    return (size_t)(round_up(m.total_bytes, kAlign) + pm.total_bytes);
+}
+
+qsa_status qsa_sparse_decode(const qsa_bf16_view *q, const qsa_bf16_view *k_cache,
+                             const qsa_bf16_view *v_cache, const qsa_i32_view *slot_idx,
+                             float scale, qsa_bf16_view *out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    if (!slot_idx) return fail(QSA_ERR_NULL, "slot_idx: view pointer is NULL");
+    Problem pr;
+    qsa_status s = check_attend(q, k_cache, v_cache, out, slot_idx->size[1], scale, &pr);
+    if (s) return s;
+    int64_t W = 0;
+    if ((s = check_slots(slot_idx, pr.T, &W))) return s;
+    const size_t need = qsa_decode_workspace_bytes(pr.T, W, pr.Hq, pr.Hkv);
+    if (!workspace) return fail(QSA_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)workspace % kAlign) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(QSA_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+    if (pr.T == 0) return QSA_OK;
+    qsa_workspace_map m;
+    layout_of(pr.T, W, &m);
+    const int32_t splits = decode_splits(pr.T, W, pr.Hq, pr.Hkv);
+    void *partials = (char *)workspace + round_up(m.total_bytes, kAlign);
+    PartialsMap pm;
+    partials_of(splits, pr.T, pr.Hq, &pm);
+    hipStream_t st = (hipStream_t)stream;
+    if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, 0, pr.S, workspace, m, st))) return s;
+    if ((s = enqueue_partial(q, k_cache, v_cache, pr, scale, workspace, m, splits, 0, partials, pm,
+                             st)))
+        return s;
+    return enqueue_merge(partials, pm, splits, pr.T, pr.Hq, out, st);
 }
 
 qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes, int64_t T,

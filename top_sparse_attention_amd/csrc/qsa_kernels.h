@@ -29,7 +29,8 @@ struct CompactParams {
     const int32_t *slot_idx;
     int64_t stride_t;
     int64_t T, W, S;
-    int32_t key_bits;    // radix-sort key width: S - 1 < 2^key_bits, plus one bit for padding
+    int64_t lo, hi;      // entries in [lo, hi) are kept, stored as slot - lo
+    int32_t key_bits;    // radix-sort key width: hi - lo - 1 < 2^(key_bits-1), plus one bit for padding
     int32_t *list;
     int64_t row_stride;
     int32_t *count;
@@ -52,6 +53,23 @@ struct AttendParams {
     int32_t G;           // query heads per KV head
     int32_t HB;          // 16-head blocks per KV head: ceil(G / 16)
     float scale_log2e;   // scale * log2(e)
+    // Split mode only: each item's tiles are dealt to `splits` workgroups, and
+    // workgroup s writes partial (O, m, l) to part (part_base + s).
+    int32_t splits;
+    int64_t part_base;
+    int64_t T;
+    int32_t Hq;
+    float *part_o;       // [n_parts][T][Hq][256], O not yet divided by l
+    float *part_ml;      // [n_parts][T][Hq][2]: running max (log2 units) and sum
+};
+
+struct MergeParams {
+    const float *part_o;
+    const float *part_ml;
+    int64_t n_parts, T;
+    int32_t Hq;
+    uint16_t *out;
+    int64_t o_st, o_sh;
 };
 
 struct CeilingParams {
@@ -68,6 +86,8 @@ struct CeilingParams {
 
 hipError_t launch_compact(const CompactParams &p, hipStream_t stream);
 hipError_t launch_attend(const AttendParams &p, int64_t T, hipStream_t stream);
+hipError_t launch_attend_partial(const AttendParams &p, int64_t T, hipStream_t stream);
+hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
 hipError_t launch_ceiling(const CeilingParams &p, int64_t T, hipStream_t stream);
 
 }  // namespace qsa

@@ -99,7 +99,10 @@ __device__ __forceinline__ int lds_off(int r, int chunk) {
 
 // ---------------------------------------------------------------- compaction
 
-// One workgroup per token row.  The row is processed in chunks of
+// One workgroup per token row.  Entries in [lo, hi) are kept and stored as
+// slot - lo (a cache shard's local numbering; lo = 0, hi = S keeps them
+// all); entries that are neither -1 nor in [0, S) are counted as invalid.
+// The row is processed in chunks of
 // kSortChunk entries; each chunk's valid slots are radix-sorted on the top
 // kSortKeyBits bits of a key_bits-wide key (invalid entries carry the key
 // 2^(key_bits-1), so they sort last), i.e. grouped into at most 128 ascending
@@ -124,10 +127,11 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
         for (int u = 0; u < kSortItemsPerThread; ++u) {
             const int64_t i = base + threadIdx.x * kSortItemsPerThread + u;
             const int32_t e = i < p.W ? src[i] : -1;
-            const bool ok = e >= 0 && (int64_t)e < p.S;
-            my_valid += ok;
-            my_bad += !ok && e != -1;
-            key[u] = ok ? (uint32_t)e : pad_key;
+            const bool in_cache = e >= 0 && (int64_t)e < p.S;
+            const bool keep = in_cache && (int64_t)e >= p.lo && (int64_t)e < p.hi;
+            my_valid += keep;
+            my_bad += !in_cache && e != -1;
+            key[u] = keep ? (uint32_t)((int64_t)e - p.lo) : pad_key;
         }
         atomicAdd(&chunk_valid, my_valid);
         atomicAdd(&chunk_bad, my_bad);
@@ -201,6 +205,12 @@ __device__ __forceinline__ int tile_slot(const int32_t *list, int tile, int ntil
 
 // ---------------------------------------------------------------- attention
 
+// kSplit = false: workgroup = one item, all its tiles, BF16 output.
+// kSplit = true: workgroup = (item, split s); it takes tiles s, s + splits,
+// s + 2 splits, ... and writes FP32 (O, m, l) of that share to part
+// part_base + s, for qsa_merge_partials (or another shard's partials) to
+// combine.
+template <bool kSplit>
 __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const AttendParams p) {
     __shared__ __attribute__((aligned(16))) char smem[kAttendLds];
 
@@ -209,7 +219,9 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
     const int c = lane & 15;   // MFMA column: query head within the block / A-operand row
     const int j = lane >> 4;   // MFMA lane group
 
-    const int64_t item = blockIdx.x;
+    const int splits = kSplit ? p.splits : 1;
+    const int64_t item = kSplit ? blockIdx.x / splits : blockIdx.x;
+    const int split = kSplit ? (int)(blockIdx.x - item * splits) : 0;
     const int64_t per_t = (int64_t)p.Hkv * p.HB;
     const int64_t t = item / per_t;
     const int rem = (int)(item - t * per_t);
@@ -219,8 +231,23 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
     const int nh = min(kHeadBlock, p.G - hb * kHeadBlock);
     const int n = p.count[t];
 
-    uint16_t *out_t = p.out + t * p.o_st + (int64_t)h0 * p.o_sh;
-    if (n == 0) {
+    const int ntiles = (n + kTileSlots - 1) / kTileSlots;
+    const int64_t part_row = kSplit ? ((p.part_base + split) * p.T + t) * p.Hq + h0 : 0;
+    if (kSplit && split >= ntiles) {
+        // This share is empty: max -inf, sum 0, O 0.
+        for (int idx = threadIdx.x; idx < nh * (kHeadDim / 4); idx += kThreads) {
+            const int hh = idx / (kHeadDim / 4), q4 = idx % (kHeadDim / 4);
+            *(f32x4_t *)(p.part_o + (part_row + hh) * kHeadDim + 4 * q4) =
+                f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if (threadIdx.x < nh) {
+            p.part_ml[(part_row + threadIdx.x) * 2] = kNegInf;
+            p.part_ml[(part_row + threadIdx.x) * 2 + 1] = 0.0f;
+        }
+        return;
+    }
+    uint16_t *out_t = kSplit ? nullptr : p.out + t * p.o_st + (int64_t)h0 * p.o_sh;
+    if (!kSplit && n == 0) {
         // Nothing selected: the output row is exactly +0.0.
         for (int idx = threadIdx.x; idx < nh * kChunksPerRow; idx += kThreads) {
             const int hh = idx / kChunksPerRow, ch = idx % kChunksPerRow;
@@ -238,7 +265,6 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
         for (int ks = 0; ks < 8; ++ks) qb[ks] = ldg16<bf16x8_t>(qrow + 32 * ks + 8 * j);
     }
 
-    const int ntiles = (n + kTileSlots - 1) / kTileSlots;
     const int32_t *list = p.list + t * p.list_stride;
     const uint16_t *kb = p.k + (int64_t)g * p.k_sh;
     const uint16_t *vb = p.v + (int64_t)g * p.v_sh;
@@ -251,22 +277,24 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
 #pragma unroll
     for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // This wave's tiles: split + splits * (wave + kWavesPerItem * i).
+    const int step = splits * kWavesPerItem;
     u32x4_t rk[kLoadsPerTile], rv[kLoadsPerTile];
-    int tile = wave;
-    int slot_next = tile_slot(list, tile + kWavesPerItem, ntiles, lane);
+    int tile = split + splits * wave;
+    int slot_next = tile_slot(list, tile + step, ntiles, lane);
     if (tile < ntiles)
         gather_tile(rk, rv, tile_slot(list, tile, ntiles, lane), kb, p.k_ss, vb, p.v_ss, lane);
 
     const int tr_row = 4 * j + (c >> 2);    // V row this lane addresses in a transpose load
     const int tr_sub = c & 3;               // which 4 of the 16 dims of a block
 
-    for (; tile < ntiles; tile += kWavesPerItem) {
+    for (; tile < ntiles; tile += step) {
         wave_lds_fence();   // the previous tile's LDS reads are done
         stage_tile(rk, rv, ks_lds, vs_lds, lane);
-        const int nt = tile + kWavesPerItem;
+        const int nt = tile + step;
         if (nt < ntiles) {
             gather_tile(rk, rv, slot_next, kb, p.k_ss, vb, p.v_ss, lane);
-            slot_next = tile_slot(list, nt + kWavesPerItem, ntiles, lane);
+            slot_next = tile_slot(list, nt + step, ntiles, lane);
         }
         wave_lds_fence();   // other lanes of this wave wrote the rows read below
 
@@ -354,7 +382,10 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
     }
     constexpr int kDbPerWave = kDimBlocks / kWavesPerItem;
     if (c < nh) {
-        uint16_t *orow = out_t + (int64_t)c * p.o_sh;
+        if (kSplit && wave == 0 && j == 0) {
+            p.part_ml[(part_row + c) * 2] = mmax;
+            p.part_ml[(part_row + c) * 2 + 1] = l_tot;
+        }
 #pragma unroll
         for (int d = 0; d < kDbPerWave; ++d) {
             const int db = wave * kDbPerWave + d;
@@ -362,12 +393,47 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
 #pragma unroll
             for (int w = 0; w < kWavesPerItem; ++w)
                 acc += fw[w] * part_o[(w * kDimBlocks + db) * 64 + lane];
-            bf16x4_t ob;
+            if (kSplit) {
+                *(f32x4_t *)(p.part_o + (part_row + c) * kHeadDim + 16 * db + 4 * j) = acc;
+            } else {
+                bf16x4_t ob;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ob[i] = (__bf16)(acc[i] / l_tot);
-            *(u32x2_t *)(orow + 16 * db + 4 * j) = __builtin_bit_cast(u32x2_t, ob);
+                for (int i = 0; i < 4; ++i) ob[i] = (__bf16)(acc[i] / l_tot);
+                *(u32x2_t *)(out_t + (int64_t)c * p.o_sh + 16 * db + 4 * j) =
+                    __builtin_bit_cast(u32x2_t, ob);
+            }
         }
     }
+}
+
+// ---------------------------------------------------------------- merge
+
+// out[t, h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the parts s,
+// M = max_s m_s; exactly +0.0 when no part saw a slot.  One wave per (t, h)
+// row, 4 dims per lane.
+__global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t rows = p.T * p.Hq;
+    if (row >= rows) return;
+    const int64_t t = row / p.Hq;
+    const int h = (int)(row - t * p.Hq);
+    float mmax = kNegInf;
+    for (int64_t s = 0; s < p.n_parts; ++s) mmax = fmaxf(mmax, p.part_ml[(s * rows + row) * 2]);
+    bf16x4_t ob = {(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+    if (mmax != kNegInf) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float l_tot = 0.0f;
+        for (int64_t s = 0; s < p.n_parts; ++s) {
+            const float w = __builtin_amdgcn_exp2f(p.part_ml[(s * rows + row) * 2] - mmax);
+            l_tot += w * p.part_ml[(s * rows + row) * 2 + 1];
+            acc += w * *(const f32x4_t *)(p.part_o + (s * rows + row) * kHeadDim + 4 * lane);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ob[i] = (__bf16)(acc[i] / l_tot);
+    }
+    *(u32x2_t *)(p.out + t * p.o_st + (int64_t)h * p.o_sh + 4 * lane) =
+        __builtin_bit_cast(u32x2_t, ob);
 }
 
 // ---------------------------------------------------------------- gather ceiling
@@ -428,7 +494,21 @@ hipError_t launch_compact(const CompactParams &p, hipStream_t stream) {
 hipError_t launch_attend(const AttendParams &p, int64_t T, hipStream_t stream) {
     const int64_t items = T * (int64_t)p.Hkv * p.HB;
     if (items == 0) return hipSuccess;
-    hipLaunchKernelGGL(attend_kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(attend_kernel<false>, dim3((unsigned)items), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend_partial(const AttendParams &p, int64_t T, hipStream_t stream) {
+    const int64_t blocks = T * (int64_t)p.Hkv * p.HB * p.splits;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(attend_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeParams &p, hipStream_t stream) {
+    const int64_t rows = p.T * p.Hq;
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
