@@ -3,7 +3,9 @@
 One step = the whole hot path on one batch of resident synthetic input:
 index validation/compaction (qsa_compact_slots) followed by the gather
 attention (qsa_sparse_attend), both through the C ABI on torch's current
-stream.  The default workload is the long prefill of the page "Qwen4-Exp QSA
+stream.  Other workloads: `decode_batch` runs the split path (compaction,
+qsa_sparse_attend_partial, qsa_merge_partials) and `long_prefill_fp8kv` the
+FP8 E4M3 KV-cache variant (qsa_sparse_attend_fp8kv).  The default workload is the long prefill of the page "Qwen4-Exp QSA
 comes to Huawei's Ascend: inside SGLang's opt-in CANN prefill PR" (section
 "Nine tests that passed, ..."): 7,810 query tokens, a 65,536-slot cache,
 2,051 selected slots per token, (Hq, Hkv) = (16, 2), D = 256, BF16.
@@ -38,7 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_prefill",
                     choices=["tiny", "edge_mix", "long_prefill", "two_request",
-                             "max_cache_6_1", "max_cache_3_1", "decode_batch"])
+                             "max_cache_6_1", "max_cache_3_1", "decode_batch",
+                             "long_prefill_fp8kv"])
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="token rows of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -78,7 +81,7 @@ def main():
 
     import qsa_inputs as qi
     import top_sparse_attention_amd as qsa
-    from qsa_testutil import bf16_tensor_to_f32, empty_row_mask, gate, upload
+    from qsa_testutil import bf16_tensor_to_f32, empty_row_mask, gate, upload, upload_fp8
 
     qsa.load_library()
     dev = torch.device("cuda:0")
@@ -87,6 +90,10 @@ def main():
     case = gen() if args.seed is None else gen(args.seed)
     T, S, W, Hq, Hkv = case.T, case.S, case.W, case.Hq, case.Hkv
     q, k, v, sl = upload(case, dev)
+    fp8 = "k8" in case.info
+    if fp8:
+        # The cache in FP8 E4M3 (one scale per tensor); the BF16 copies are freed.
+        k, v, k_scale, v_scale = upload_fp8(case, dev)
     out = torch.empty((T, Hq, case.D), dtype=torch.bfloat16, device=dev)
     ws = qsa.new_workspace(T, W, dev)
     scale = case.scale if case.scale is not None else 1.0 / np.sqrt(case.D)
@@ -109,6 +116,8 @@ def main():
     def attend():
         if split:
             qsa.sparse_attend_partial(q, k, v, ws, W, splits, 0, splits, parts, scale=scale)
+        elif fp8:
+            qsa.sparse_attend_fp8kv(q, k, v, k_scale, v_scale, ws, W, scale=scale, out=out)
         else:
             qsa.sparse_attend(q, k, v, ws, W, scale=scale, out=out)
 
@@ -147,13 +156,14 @@ def main():
 
     # Gather ceiling: the same rows, loads and launch shape with no arithmetic.
     sink = torch.empty(T * Hkv, dtype=torch.int32, device=dev)
+    ceiling = qsa.gather_ceiling_fp8kv if fp8 else qsa.gather_ceiling
     for _ in range(2):
-        qsa.gather_ceiling(k, v, ws, T, W, sink)
+        ceiling(k, v, ws, T, W, sink)
     c0 = torch.cuda.Event(enable_timing=True)
     c1 = torch.cuda.Event(enable_timing=True)
     c0.record()
     for _ in range(K):
-        qsa.gather_ceiling(k, v, ws, T, W, sink)
+        ceiling(k, v, ws, T, W, sink)
     c1.record()
     torch.cuda.synchronize()
     ceil_ms = c0.elapsed_time(c1) / K
@@ -163,15 +173,25 @@ def main():
     pairs = int(n_t.sum()) * Hq
     # Algorithmic bytes of one attention launch: every selected K and V row of
     # every (token, KV head) once, its slot index, Q in and O out.
-    attn_bytes = int(n_t.sum()) * Hkv * (2 * case.D * 2 + 4) + 2 * T * Hq * case.D * 2
-    gather_bytes = int(n_t.sum()) * Hkv * 2 * case.D * 2
+    kv_bytes = 1 if fp8 else 2
+    attn_bytes = int(n_t.sum()) * Hkv * (2 * case.D * kv_bytes + 4) + 2 * T * Hq * case.D * 2
+    gather_bytes = int(n_t.sum()) * Hkv * 2 * case.D * kv_bytes
     flops = pairs * 4 * case.D
     achieved = attn_bytes / (attn_avg * 1e-3) / 1e9
 
     # Parity of this very output on a sample of rows (the oracle is the judge).
     import oracle
+
+    def run_oracle(rows_, nthreads=0):
+        if fp8:
+            return oracle.prefill_fp8kv(case.q, case.info["k8"], case.info["v8"], k_scale,
+                                        v_scale, case.slot_idx, scale, rows=rows_,
+                                        nthreads=nthreads)
+        return oracle.prefill(case.q, case.k_cache, case.v_cache, case.slot_idx, scale,
+                              rows=rows_, nthreads=nthreads)
+
     rows = qi.sample_rows(T, 16, seed=11)
-    want = oracle.prefill(case.q, case.k_cache, case.v_cache, case.slot_idx, scale, rows=rows)
+    want = run_oracle(rows)
     got = bf16_tensor_to_f32(out[torch.as_tensor(rows, device=dev)])
     parity = gate(got, want, empty_row_mask(case.slot_idx, S, rows))
 
@@ -180,8 +200,7 @@ def main():
         cpu_rows = qi.sample_rows(T, min(args.cpu_rows, T), seed=12)
         threads = oracle.default_threads()
         c_t0 = time.perf_counter()
-        oracle.prefill(case.q, case.k_cache, case.v_cache, case.slot_idx, scale, rows=cpu_rows,
-                       nthreads=threads)
+        run_oracle(cpu_rows, threads)
         c_dt = time.perf_counter() - c_t0
         cpu_pairs = int(n_t[cpu_rows].sum()) * Hq
         cpu = {"value": cpu_pairs / c_dt, "unit": "pairs/s", "cores": threads, "kind": "oracle",
@@ -200,7 +219,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+fp8kv" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": case.name, "T": T, "S": S, "W": W, "Hq": Hq, "Hkv": Hkv,
                    "D": case.D, "scale": scale, "seed": case.info.get("seed"),

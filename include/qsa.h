@@ -66,6 +66,15 @@ typedef struct qsa_bf16_view {
     int64_t stride[3];
 } qsa_bf16_view;
 
+/* A strided 3-D tensor of FP8 E4M3 codes (one byte per element; OCP "fn"
+ * encoding: bias 7, no infinities) for an FP8 KV cache [S, Hkv, D]; strides
+ * in elements (= bytes), multiples of 16 apart from the unit innermost one. */
+typedef struct qsa_fp8_view {
+    void *data;
+    int64_t size[3];
+    int64_t stride[3];
+} qsa_fp8_view;
+
 /* A strided 2-D int32 tensor: slot_idx is [T, W]; -1 means "no slot". */
 typedef struct qsa_i32_view {
     const int32_t *data;
@@ -243,6 +252,38 @@ qsa_status qsa_gather_ceiling(const qsa_bf16_view *k_cache,
                               int64_t W, const void *workspace,
                               size_t workspace_bytes, uint32_t *sink,
                               void *stream);
+
+/*
+ * FP8 KV-cache variant.  The page's section "Where this sits in the Qwen4Exp
+ * serving build-out" reports decode measured with an fp8_e4m3 KV cache; the
+ * page defines no scaling, so the reading here is one scale per tensor: each
+ * K element is decode(code) * k_scale and each V element decode(code) *
+ * v_scale.  The computation is otherwise the one of qsa_sparse_attend /
+ * qsa_sparse_prefill (q and out stay BF16), with half the gathered bytes.
+ * k_scale and v_scale must be finite.
+ */
+qsa_status qsa_sparse_attend_fp8kv(const qsa_bf16_view *q,
+                                   const qsa_fp8_view *k_cache,
+                                   const qsa_fp8_view *v_cache, float k_scale,
+                                   float v_scale, int64_t W, float scale,
+                                   const void *workspace, size_t workspace_bytes,
+                                   qsa_bf16_view *out, void *stream);
+
+qsa_status qsa_sparse_prefill_fp8kv(const qsa_bf16_view *q,
+                                    const qsa_fp8_view *k_cache,
+                                    const qsa_fp8_view *v_cache, float k_scale,
+                                    float v_scale, const qsa_i32_view *slot_idx,
+                                    float scale, qsa_bf16_view *out,
+                                    void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/* qsa_gather_ceiling for an FP8 KV cache (same tiles, waves and loads as
+ * qsa_sparse_attend_fp8kv; XOR of the 32-bit words of every read row). */
+qsa_status qsa_gather_ceiling_fp8kv(const qsa_fp8_view *k_cache,
+                                    const qsa_fp8_view *v_cache, int64_t T,
+                                    int64_t W, const void *workspace,
+                                    size_t workspace_bytes, uint32_t *sink,
+                                    void *stream);
 
 #ifdef __cplusplus
 }

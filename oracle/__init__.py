@@ -54,6 +54,12 @@ def _load():
             vp, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64,
             i32, i32, i32, ctypes.c_float, vp, i64, vp, i32]
         lib.qsa_oracle_prefill.restype = ctypes.c_int
+        lib.qsa_oracle_prefill_fp8kv.argtypes = [
+            vp, i64, i64, vp, i64, i64, vp, i64, i64, ctypes.c_float, ctypes.c_float,
+            vp, i64, i64, i64, i32, i32, i32, ctypes.c_float, vp, i64, vp, i32]
+        lib.qsa_oracle_prefill_fp8kv.restype = ctypes.c_int
+        lib.qsa_oracle_e4m3_to_float.argtypes = [ctypes.c_uint8]
+        lib.qsa_oracle_e4m3_to_float.restype = ctypes.c_float
         lib.qsa_oracle_default_threads.argtypes = []
         lib.qsa_oracle_default_threads.restype = ctypes.c_int
         _lib = lib
@@ -98,6 +104,11 @@ def compact(slot_idx: np.ndarray, S: int):
     return lists[:, :W], counts, n_bad
 
 
+def e4m3_to_float(code: int) -> float:
+    """The oracle's decoding of one FP8 E4M3 byte."""
+    return float(_load().qsa_oracle_e4m3_to_float(int(code)))
+
+
 def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
             slot_idx: np.ndarray, scale: float, rows=None,
             nthreads: int = 0) -> np.ndarray:
@@ -108,9 +119,23 @@ def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     slot_idx is [T, W] int32 with -1 meaning "no slot".  ``scale`` must be
     given explicitly.  Returns float32 [len(rows), Hq, D].
     """
-    for name, a in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
-        if a.dtype != np.uint16 or a.ndim != 3:
-            raise TypeError(f"{name} must be a 3-D uint16 (bf16 bits) array")
+    return _prefill(q, k_cache, v_cache, slot_idx, scale, rows, nthreads, None)
+
+
+def prefill_fp8kv(q: np.ndarray, k8: np.ndarray, v8: np.ndarray, k_scale: float,
+                  v_scale: float, slot_idx: np.ndarray, scale: float, rows=None,
+                  nthreads: int = 0) -> np.ndarray:
+    """FP32 sparse prefill with an FP8 E4M3 KV cache: k8/v8 are [S, Hkv, D]
+    uint8 codes meaning decode(code) * k_scale (resp. v_scale)."""
+    return _prefill(q, k8, v8, slot_idx, scale, rows, nthreads, (k_scale, v_scale))
+
+
+def _prefill(q, k_cache, v_cache, slot_idx, scale, rows, nthreads, fp8_scales):
+    kv_dtype = np.uint16 if fp8_scales is None else np.uint8
+    for name, a, dt in (("q", q, np.uint16), ("k_cache", k_cache, kv_dtype),
+                        ("v_cache", v_cache, kv_dtype)):
+        if a.dtype != dt or a.ndim != 3:
+            raise TypeError(f"{name} must be a 3-D {np.dtype(dt).name} array")
         if a.shape[2] > 1 and a.strides[2] != a.itemsize:
             raise ValueError(f"{name} must have unit stride over D")
     if slot_idx.dtype != np.int32 or slot_idx.ndim != 2:
@@ -132,11 +157,18 @@ def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
             raise IndexError("row index out of range")
     out = np.empty((rows_arr.size, Hq, D), dtype=np.float32)
     qs, ks, vs, ss = (_elem_strides(a) for a in (q, k_cache, v_cache, slot_idx))
-    rc = _load().qsa_oracle_prefill(
-        _ptr(q), qs[0], qs[1], _ptr(k_cache), ks[0], ks[1],
-        _ptr(v_cache), vs[0], vs[1], _ptr(slot_idx), ss[0], S, W,
-        Hq, Hkv, D, float(scale), _ptr(rows_arr), rows_arr.size, _ptr(out),
-        int(nthreads))
+    if fp8_scales is None:
+        rc = _load().qsa_oracle_prefill(
+            _ptr(q), qs[0], qs[1], _ptr(k_cache), ks[0], ks[1],
+            _ptr(v_cache), vs[0], vs[1], _ptr(slot_idx), ss[0], S, W,
+            Hq, Hkv, D, float(scale), _ptr(rows_arr), rows_arr.size, _ptr(out),
+            int(nthreads))
+    else:
+        rc = _load().qsa_oracle_prefill_fp8kv(
+            _ptr(q), qs[0], qs[1], _ptr(k_cache), ks[0], ks[1],
+            _ptr(v_cache), vs[0], vs[1], float(fp8_scales[0]), float(fp8_scales[1]),
+            _ptr(slot_idx), ss[0], S, W, Hq, Hkv, D, float(scale), _ptr(rows_arr),
+            rows_arr.size, _ptr(out), int(nthreads))
     if rc == BAD_SLOT:
         raise ValueError("slot_idx holds an entry that is neither -1 nor in [0, S)")
     if rc != OK:

@@ -27,6 +27,10 @@
  *  - scores accumulate in FP32 in d order, exp is libm expf, and the output
  *    stays FP32 (the GPU's BF16 output is compared against it).
  *
+ * FP8 KV-cache variant (qsa_oracle_prefill_fp8kv): K and V bytes are FP8
+ * E4M3 codes, decoded from the format's definition and multiplied by one
+ * scale per tensor; everything after that is the same FP32 computation.
+ *
  * Parity pins (tests, not here): FP64 brute-force dense masked attention,
  * torch's scaled_dot_product_attention for full and causal selections, and
  * closed forms (single slot, uniform weights, identical V rows, empty rows).
@@ -54,6 +58,36 @@ static float bf16_to_float(uint16_t bits)
     float f;
     memcpy(&f, &u, sizeof f);
     return f;
+}
+
+/*
+ * FP8 E4M3 ("fn" variant of the OCP 8-bit floating point formats): 1 sign
+ * bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 encodes
+ * subnormals m/8 * 2^-6; no infinities; exponent 15 with mantissa 7 is NaN.
+ * Used for the FP8 KV-cache variant (the page's section "Where this sits in
+ * the Qwen4Exp serving build-out" mentions an fp8_e4m3 KV cache).
+ */
+float qsa_oracle_e4m3_to_float(uint8_t b)
+{
+    const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    float v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexpf((float)m / 8.0f, -6);
+    else
+        v = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return sign ? -v : v;
+}
+
+/* One K or V element as a real number: BF16 as is, FP8 decoded and scaled by
+ * the tensor's scale (reading: real = decode(byte) * scale, one scale per
+ * tensor). */
+static float kv_elem(const void *row, int32_t d, int fp8, float kv_scale)
+{
+    if (fp8)
+        return qsa_oracle_e4m3_to_float(((const uint8_t *)row)[d]) * kv_scale;
+    return bf16_to_float(((const uint16_t *)row)[d]);
 }
 
 /*
@@ -92,11 +126,12 @@ int qsa_oracle_compact(const int32_t *slot_idx, int64_t stride_t, int64_t T,
  *   o[d] = (sum_j p_j v_j[d]) / l
  * An empty selection gives +0.0 everywhere.
  */
-static int one_row(const uint16_t *q_row, const uint16_t *k, int64_t k_ss,
-                   const uint16_t *v, int64_t v_ss, const int32_t *sel,
-                   int64_t W, int64_t S, int32_t D, float scale, float *z,
-                   int32_t *slots, float *o)
+static int one_row(const uint16_t *q_row, const void *k, int64_t k_ss,
+                   const void *v, int64_t v_ss, int fp8, float k_scale,
+                   float v_scale, const int32_t *sel, int64_t W, int64_t S,
+                   int32_t D, float scale, float *z, int32_t *slots, float *o)
 {
+    const size_t esz = fp8 ? 1 : 2;   /* bytes per K/V element */
     int64_t n = 0;
     for (int64_t j = 0; j < W; ++j) {
         int32_t s = sel[j];
@@ -104,10 +139,10 @@ static int one_row(const uint16_t *q_row, const uint16_t *k, int64_t k_ss,
             continue;
         if (s < 0 || (int64_t)s >= S)
             return ORACLE_BAD_SLOT;
-        const uint16_t *k_row = k + (int64_t)s * k_ss;
+        const char *k_row = (const char *)k + (size_t)((int64_t)s * k_ss) * esz;
         float dot = 0.0f;
         for (int32_t d = 0; d < D; ++d)
-            dot += bf16_to_float(q_row[d]) * bf16_to_float(k_row[d]);
+            dot += bf16_to_float(q_row[d]) * kv_elem(k_row, d, fp8, k_scale);
         z[n] = scale * dot;
         slots[n] = s;
         ++n;
@@ -127,9 +162,9 @@ static int one_row(const uint16_t *q_row, const uint16_t *k, int64_t k_ss,
         l += z[i];
     }
     for (int64_t i = 0; i < n; ++i) {
-        const uint16_t *v_row = v + (int64_t)slots[i] * v_ss;
+        const char *v_row = (const char *)v + (size_t)((int64_t)slots[i] * v_ss) * esz;
         for (int32_t d = 0; d < D; ++d)
-            o[d] += z[i] * bf16_to_float(v_row[d]);
+            o[d] += z[i] * kv_elem(v_row, d, fp8, v_scale);
     }
     for (int32_t d = 0; d < D; ++d)
         o[d] = o[d] / l;
@@ -149,14 +184,16 @@ static int one_row(const uint16_t *q_row, const uint16_t *k, int64_t k_ss,
  * Returns ORACLE_OK, or ORACLE_BAD_SLOT if any evaluated row holds an entry
  * outside [0, S) other than -1 (then out is unspecified).
  */
-int qsa_oracle_prefill(const uint16_t *q, int64_t q_st, int64_t q_sh,
-                       const uint16_t *k, int64_t k_ss, int64_t k_sh,
-                       const uint16_t *v, int64_t v_ss, int64_t v_sh,
+static int prefill_any(const uint16_t *q, int64_t q_st, int64_t q_sh,
+                       const void *k, int64_t k_ss, int64_t k_sh,
+                       const void *v, int64_t v_ss, int64_t v_sh, int fp8,
+                       float k_scale, float v_scale,
                        const int32_t *slot_idx, int64_t s_st, int64_t S,
                        int64_t W, int32_t Hq, int32_t Hkv, int32_t D,
                        float scale, const int64_t *rows, int64_t nrows,
                        float *out, int32_t nthreads)
 {
+    const size_t esz = fp8 ? 1 : 2;
     if (Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || W < 0 || S < 0 ||
         nrows < 0)
         return ORACLE_BAD_SHAPE;
@@ -186,10 +223,10 @@ int qsa_oracle_prefill(const uint16_t *q, int64_t q_st, int64_t q_sh,
                 int64_t t = rows ? rows[r] : r;
                 int32_t g = h / G;
                 int rc = one_row(q + t * q_st + (int64_t)h * q_sh,
-                                 k + (int64_t)g * k_sh, k_ss,
-                                 v + (int64_t)g * v_sh, v_ss,
-                                 slot_idx + t * s_st, W, S, D, scale, z, slots,
-                                 out + (r * Hq + h) * (int64_t)D);
+                                 (const char *)k + (size_t)((int64_t)g * k_sh) * esz, k_ss,
+                                 (const char *)v + (size_t)((int64_t)g * v_sh) * esz, v_ss,
+                                 fp8, k_scale, v_scale, slot_idx + t * s_st, W, S, D,
+                                 scale, z, slots, out + (r * Hq + h) * (int64_t)D);
                 if (rc != ORACLE_OK) {
 #pragma omp atomic write
                     status = rc;
@@ -200,6 +237,38 @@ int qsa_oracle_prefill(const uint16_t *q, int64_t q_st, int64_t q_sh,
         free(slots);
     }
     return status;
+}
+
+int qsa_oracle_prefill(const uint16_t *q, int64_t q_st, int64_t q_sh,
+                       const uint16_t *k, int64_t k_ss, int64_t k_sh,
+                       const uint16_t *v, int64_t v_ss, int64_t v_sh,
+                       const int32_t *slot_idx, int64_t s_st, int64_t S,
+                       int64_t W, int32_t Hq, int32_t Hkv, int32_t D,
+                       float scale, const int64_t *rows, int64_t nrows,
+                       float *out, int32_t nthreads)
+{
+    return prefill_any(q, q_st, q_sh, k, k_ss, k_sh, v, v_ss, v_sh, 0, 1.0f,
+                       1.0f, slot_idx, s_st, S, W, Hq, Hkv, D, scale, rows,
+                       nrows, out, nthreads);
+}
+
+/*
+ * The same sparse prefill with an FP8 E4M3 KV cache: k8, v8 hold one byte
+ * per element (strides in elements = bytes) and every element means
+ * decode(byte) * k_scale (resp. v_scale).
+ */
+int qsa_oracle_prefill_fp8kv(const uint16_t *q, int64_t q_st, int64_t q_sh,
+                             const uint8_t *k8, int64_t k_ss, int64_t k_sh,
+                             const uint8_t *v8, int64_t v_ss, int64_t v_sh,
+                             float k_scale, float v_scale,
+                             const int32_t *slot_idx, int64_t s_st, int64_t S,
+                             int64_t W, int32_t Hq, int32_t Hkv, int32_t D,
+                             float scale, const int64_t *rows, int64_t nrows,
+                             float *out, int32_t nthreads)
+{
+    return prefill_any(q, q_st, q_sh, k8, k_ss, k_sh, v8, v_ss, v_sh, 1,
+                       k_scale, v_scale, slot_idx, s_st, S, W, Hq, Hkv, D,
+                       scale, rows, nrows, out, nthreads);
 }
 
 /* Threads the oracle will use when nthreads <= 0. */

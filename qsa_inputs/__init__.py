@@ -259,6 +259,37 @@ def max_cache(seed: int = 105, heads=(6, 1)) -> Case:
                             {"seed": seed})
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3_codes(x: np.ndarray, scale: float) -> np.ndarray:
+    """FP8 E4M3 (fn) codes of x / scale, rounded to nearest even by torch's
+    float8_e4m3fn conversion; |x / scale| must not exceed 448."""
+    import torch
+    y = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32) / np.float32(scale))
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def with_fp8_kv(case: Case) -> Case:
+    """The same problem with K and V quantized to FP8 E4M3, one scale per
+    tensor (amax / 448).  Adds k8, v8, k_scale, v_scale to the case; k8/v8
+    keep k_cache/v_cache's layout (strides in bytes = elements)."""
+    out = {}
+    for name, view in (("k", case.k_cache), ("v", case.v_cache)):
+        real = bf16_to_f32(view)
+        amax = float(np.abs(real).max()) if real.size else 1.0
+        scale = amax / E4M3_MAX if amax > 0 else 1.0
+        base = case.base_of(view)
+        codes = e4m3_codes(bf16_to_f32(base), scale)
+        off = (view.__array_interface__["data"][0] - base.__array_interface__["data"][0]) // 2
+        v8 = np.lib.stride_tricks.as_strided(codes.reshape(-1)[off:], shape=view.shape,
+                                             strides=[s_ // 2 for s_ in view.strides])
+        out[name] = (codes, v8, scale)
+    case.info.update(k8=out["k"][1], v8=out["v"][1], k_scale=out["k"][2],
+                     v_scale=out["v"][2], k8_base=out["k"][0], v8_base=out["v"][0])
+    return case
+
+
 DECODE_REQUESTS = 16
 
 
@@ -299,6 +330,7 @@ WORKLOADS = {
     "max_cache_6_1": lambda seed=105: max_cache(seed, (6, 1)),
     "max_cache_3_1": lambda seed=105: max_cache(seed, (3, 1)),
     "decode_batch": decode_batch,
+    "long_prefill_fp8kv": lambda seed=103: with_fp8_kv(long_prefill(seed)),
 }
 
 

@@ -38,6 +38,20 @@ def upload(case, device="cuda"):
     return view_of(case.q), view_of(case.k_cache), view_of(case.v_cache), view_of(case.slot_idx)
 
 
+def upload_fp8(case, device="cuda"):
+    """The FP8 K/V codes of a case made by qsa_inputs.with_fp8_kv, as uint8
+    device views with the same strides.  Returns (k8, v8, k_scale, v_scale)."""
+    import torch
+
+    out = []
+    for name in ("k", "v"):
+        base, view = case.info[f"{name}8_base"], case.info[f"{name}8"]
+        dev = torch.from_numpy(np.ascontiguousarray(base)).to(device)
+        off = view.__array_interface__["data"][0] - base.__array_interface__["data"][0]
+        out.append(torch.as_strided(dev, view.shape, list(view.strides), off))
+    return out[0], out[1], case.info["k_scale"], case.info["v_scale"]
+
+
 def bf16_tensor_to_f32(t) -> np.ndarray:
     """A (CPU or GPU) torch bfloat16 tensor as float32 numpy."""
     return t.detach().float().cpu().numpy()

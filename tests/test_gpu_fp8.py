@@ -1,0 +1,117 @@
+"""GPU parity of the FP8 E4M3 KV-cache variant against the FP32 oracle.
+
+Reading (the page names an fp8_e4m3 KV cache in section "Where this sits in
+the Qwen4Exp serving build-out" but defines no scaling): one scale per
+tensor, element = decode(code) * scale.  Same gate as the BF16 path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_inputs as qi
+import top_sparse_attention_amd as qsa
+from qsa_testutil import (bf16_tensor_bits, bf16_tensor_to_f32, empty_row_mask, gate, upload,
+                          upload_fp8)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def run_fp8(case, out=None):
+    q, _, _, sl = upload(case, DEV)
+    k8, v8, ks, vs = upload_fp8(case, DEV)
+    o = qsa.sparse_prefill_fp8kv(q, k8, v8, ks, vs, sl, scale=case.scale, out=out)
+    torch.cuda.synchronize()
+    return o
+
+
+def oracle_fp8(case, rows=None):
+    scale = case.scale if case.scale is not None else 1.0 / 16.0
+    return oracle.prefill_fp8kv(case.q, case.info["k8"], case.info["v8"], case.info["k_scale"],
+                                case.info["v_scale"], case.slot_idx, scale, rows=rows)
+
+
+def check_fp8(case, rows=None):
+    o = run_fp8(case)
+    got = bf16_tensor_to_f32(o if rows is None else o[torch.as_tensor(rows, device=DEV)])
+    m = gate(got, oracle_fp8(case, rows), empty_row_mask(case.slot_idx, case.S, rows))
+    print(f"{case.name} fp8: {m}", flush=True)
+    return o
+
+
+def test_fp8_tiny():
+    check_fp8(qi.with_fp8_kv(qi.tiny()))
+
+
+def test_fp8_edge_mix_strided_views():
+    case = qi.with_fp8_kv(qi.edge_mix())
+    assert case.info["k8"].strides[0] == 512          # K and V interleaved per slot
+    check_fp8(case)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (24, 2), (12, 1), (6, 1), (3, 1), (20, 1)])
+def test_fp8_head_shapes(Hq, Hkv):
+    case = qi.with_fp8_kv(qi.random_case(900 + Hq + Hkv, T=37, S=5000, Hq=Hq, Hkv=Hkv, W=333,
+                                         pad_frac=0.15, interior=True))
+    check_fp8(case)
+
+
+@pytest.mark.parametrize("W", [1, 15, 16, 17, 2051])
+def test_fp8_widths(W):
+    check_fp8(qi.with_fp8_kv(qi.random_case(920 + W, T=11, S=6000, Hq=8, Hkv=1, W=W,
+                                            scale=0.09)))
+
+
+def test_fp8_single_slot_rows_are_bit_exact():
+    case = qi.with_fp8_kv(qi.random_case(930, T=20, S=700, Hq=6, Hkv=2, W=5, pad_frac=0.8,
+                                         interior=True))
+    o = run_fp8(case)
+    want = oracle_fp8(case)
+    want_bits = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy()
+    np.testing.assert_array_equal(bf16_tensor_bits(o).view(np.int16), want_bits)
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (2.0**-7, 4.0)])
+def test_fp8_equals_bf16_path_for_power_of_two_scales(k_scale, v_scale):
+    """decode(code) * 2^k is exact in BF16, and folding a power of two into
+    the softmax scale or the output commutes with rounding: both GPU paths
+    must agree bit for bit."""
+    case = qi.random_case(940, T=29, S=4000, Hq=16, Hkv=2, W=700, pad_frac=0.1)
+    rng = np.random.Generator(np.random.PCG64(941))
+    k8 = qi.e4m3_codes(rng.standard_normal(case.k_cache.shape).astype(np.float32) * 40, 1.0)
+    v8 = qi.e4m3_codes(rng.standard_normal(case.v_cache.shape).astype(np.float32) * 40, 1.0)
+    q, _, _, sl = upload(case, DEV)
+    k8_t, v8_t = torch.from_numpy(k8).to(DEV), torch.from_numpy(v8).to(DEV)
+    a = qsa.sparse_prefill_fp8kv(q, k8_t, v8_t, k_scale, v_scale, sl)
+    kb = (k8_t.view(torch.float8_e4m3fn).float() * k_scale).to(torch.bfloat16)
+    vb = (v8_t.view(torch.float8_e4m3fn).float() * v_scale).to(torch.bfloat16)
+    b = qsa.sparse_prefill(q, kb, vb, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_fp8_gather_ceiling_reads_exactly_the_selected_rows():
+    case = qi.with_fp8_kv(qi.random_case(950, T=21, S=2500, Hq=4, Hkv=2, W=150, pad_frac=0.3,
+                                         interior=True))
+    _, _, _, sl = upload(case, DEV)
+    k8, v8, _, _ = upload_fp8(case, DEV)
+    ws = qsa.compact_slots(sl, case.S)
+    sink = qsa.gather_ceiling_fp8kv(k8, v8, ws, case.T, case.W)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    kw = np.ascontiguousarray(case.info["k8"]).view(np.uint32)
+    vw = np.ascontiguousarray(case.info["v8"]).view(np.uint32)
+    for t in range(case.T):
+        sel = case.slot_idx[t][case.slot_idx[t] != -1]
+        for g in range(case.Hkv):
+            want = np.bitwise_xor.reduce(np.concatenate([kw[sel, g].ravel(), vw[sel, g].ravel()]))
+            assert got[t * case.Hkv + g] == (want if sel.size else 0)
+
+
+def test_fp8_long_prefill_sampled_rows():
+    case = qi.with_fp8_kv(qi.long_prefill())
+    rows = qi.sample_rows(case.T, 64)
+    o = check_fp8(case, rows)
+    assert torch.isfinite(o.float()).all()

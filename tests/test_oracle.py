@@ -263,3 +263,59 @@ def test_large_scale_with_the_argmax_at_either_end(oracle_mod, where):
         logits = np.sort(k[sel[t], 0] @ q[t, 0].astype(np.float64))
         if 80.0 * (logits[-1] - logits[-2]) > 30:
             np.testing.assert_allclose(got[t, 0], v[best, 0], rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------- FP8 KV cache
+
+def test_e4m3_decoding_matches_torch_float8_e4m3fn(oracle_mod):
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    got = np.array([oracle_mod.e4m3_to_float(c) for c in codes], dtype=np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    assert oracle_mod.e4m3_to_float(0x7E) == 448.0 and oracle_mod.e4m3_to_float(0x01) == 2.0**-9
+
+
+def _fp8_as_bf16(codes, kv_scale):
+    """Exact BF16 bits of decode(code) * kv_scale for power-of-two scales."""
+    real = torch.from_numpy(codes).view(torch.float8_e4m3fn).float() * kv_scale
+    bits = real.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(qi.bf16_to_f32(bits), real.numpy())     # exact
+    return bits
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.0078125, 4.0), (2.0**-10, 2.0**-6)])
+def test_fp8_oracle_equals_bf16_oracle_on_exactly_representable_values(oracle_mod, k_scale,
+                                                                        v_scale):
+    case = qi.random_case(60, T=7, S=90, Hq=6, Hkv=2, W=25, pad_frac=0.2, interior=True)
+    rng = np.random.Generator(np.random.PCG64(61))
+    k8 = qi.e4m3_codes(rng.standard_normal(case.k_cache.shape).astype(np.float32) * 30, 1.0)
+    v8 = qi.e4m3_codes(rng.standard_normal(case.v_cache.shape).astype(np.float32) * 30, 1.0)
+    a = oracle_mod.prefill_fp8kv(case.q, k8, v8, k_scale, v_scale, case.slot_idx, 0.07)
+    b = oracle_mod.prefill(case.q, _fp8_as_bf16(k8, k_scale), _fp8_as_bf16(v8, v_scale),
+                           case.slot_idx, 0.07)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_fp8_oracle_matches_dense_bruteforce_with_arbitrary_scales(oracle_mod):
+    case = qi.with_fp8_kv(qi.random_case(62, T=6, S=48, Hq=4, Hkv=2, W=20, pad_frac=0.25,
+                                         interior=True))
+    k8, v8, ks, vs = (case.info[n] for n in ("k8", "v8", "k_scale", "v_scale"))
+    got = oracle_mod.prefill_fp8kv(case.q, k8, v8, ks, vs, case.slot_idx, 0.0625)
+    kr = torch.from_numpy(np.ascontiguousarray(k8)).view(torch.float8_e4m3fn).double() * ks
+    vr = torch.from_numpy(np.ascontiguousarray(v8)).view(torch.float8_e4m3fn).double() * vs
+    # brute force on the dequantized values (float64 throughout)
+    q = qi.bf16_to_f32(case.q).astype(np.float64)
+    k, v = kr.numpy(), vr.numpy()
+    T, Hq, _ = q.shape
+    G = Hq // case.Hkv
+    want = np.zeros((T, Hq, 256))
+    for t in range(T):
+        sel = case.slot_idx[t][case.slot_idx[t] != -1]
+        for h in range(Hq):
+            z = 0.0625 * (k[sel, h // G] @ q[t, h])
+            w = np.exp(z - z.max())
+            want[t, h] = (w / w.sum()) @ v[sel, h // G]
+    assert rel_l2(got, want) < 1e-5

@@ -26,6 +26,7 @@ __all__ = [
     "sparse_attend", "sparse_prefill", "check_status", "gather_ceiling",
     "compact_slot_range", "partials_bytes", "new_partials", "sparse_attend_partial",
     "merge_partials", "decode_splits", "decode_workspace_bytes", "sparse_decode",
+    "sparse_attend_fp8kv", "sparse_prefill_fp8kv", "gather_ceiling_fp8kv",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -121,6 +122,14 @@ def load_library():
     lib.qsa_sparse_decode.restype = ctypes.c_int
     lib.qsa_sparse_decode.argtypes = [P(BF16View), P(BF16View), P(BF16View), P(I32View), f32,
                                       P(BF16View), vp, sz, vp]
+    lib.qsa_sparse_attend_fp8kv.restype = ctypes.c_int
+    lib.qsa_sparse_attend_fp8kv.argtypes = [P(BF16View), P(BF16View), P(BF16View), f32, f32,
+                                            i64, f32, vp, sz, P(BF16View), vp]
+    lib.qsa_sparse_prefill_fp8kv.restype = ctypes.c_int
+    lib.qsa_sparse_prefill_fp8kv.argtypes = [P(BF16View), P(BF16View), P(BF16View), f32, f32,
+                                             P(I32View), f32, P(BF16View), vp, sz, vp]
+    lib.qsa_gather_ceiling_fp8kv.restype = ctypes.c_int
+    lib.qsa_gather_ceiling_fp8kv.argtypes = [P(BF16View), P(BF16View), i64, i64, vp, sz, vp, vp]
     _lib = lib
     return lib
 
@@ -344,3 +353,65 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _default_scale(scale, q.shape[-1]), ctypes.byref(ov), workspace.data_ptr(),
         workspace.numel(), _stream(q.device)))
     return out
+
+
+# ---------------------------------------------------------------- FP8 KV cache
+
+def _fp8_view(t: torch.Tensor, name: str) -> BF16View:
+    """An FP8 E4M3 cache tensor (uint8 codes or torch.float8_e4m3fn), 3-D.
+    qsa_fp8_view has the layout of qsa_bf16_view, so the same struct is used."""
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name} must hold FP8 E4M3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be 3-D, got shape {tuple(t.shape)}")
+    if t.numel() and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return BF16View(t.data_ptr() if t.numel() else 0, (ctypes.c_int64 * 3)(*t.shape),
+                    (ctypes.c_int64 * 3)(*t.stride()))
+
+
+def sparse_attend_fp8kv(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, k_scale: float,
+                        v_scale: float, workspace: torch.Tensor, W: int,
+                        scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    qv, kv, vv, ov = (_bf16_view(q, "q"), _fp8_view(k8, "k_cache"), _fp8_view(v8, "v_cache"),
+                      _bf16_view(out, "out"))
+    _raise_on(load_library().qsa_sparse_attend_fp8kv(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), float(k_scale), float(v_scale), W,
+        _default_scale(scale, q.shape[-1]), workspace.data_ptr(), workspace.numel(),
+        ctypes.byref(ov), _stream(q.device)))
+    return out
+
+
+def sparse_prefill_fp8kv(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, k_scale: float,
+                         v_scale: float, slot_idx: torch.Tensor, scale: Optional[float] = None,
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sparse prefill over an FP8 E4M3 KV cache (element = decode(code) * scale)."""
+    T, W = slot_idx.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if workspace is None:
+        workspace = new_workspace(T, W, q.device)
+    qv, kv, vv, ov = (_bf16_view(q, "q"), _fp8_view(k8, "k_cache"), _fp8_view(v8, "v_cache"),
+                      _bf16_view(out, "out"))
+    sv = _i32_view(slot_idx, "slot_idx")
+    _raise_on(load_library().qsa_sparse_prefill_fp8kv(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), float(k_scale), float(v_scale),
+        ctypes.byref(sv), _default_scale(scale, q.shape[-1]), ctypes.byref(ov),
+        workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+    return out
+
+
+def gather_ceiling_fp8kv(k8: torch.Tensor, v8: torch.Tensor, workspace: torch.Tensor, T: int,
+                         W: int, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    Hkv = k8.shape[1]
+    if sink is None:
+        sink = torch.empty(max(T * Hkv, 1), dtype=torch.int32, device=k8.device)
+    kv, vv = _fp8_view(k8, "k_cache"), _fp8_view(v8, "v_cache")
+    _raise_on(load_library().qsa_gather_ceiling_fp8kv(
+        ctypes.byref(kv), ctypes.byref(vv), T, W, workspace.data_ptr(), workspace.numel(),
+        sink.data_ptr(), _stream(k8.device)))
+    return sink

@@ -42,19 +42,33 @@ bool layout_of(int64_t T, int64_t W, qsa_workspace_map *m) {
     return true;
 }
 
+// A K/V cache of either element type, seen through the same fields.
+struct KvView {
+    const qsa_bf16_view *view;   // for FP8, the qsa_fp8_view reinterpreted (same layout)
+    int elem_bytes;
+};
+
+static_assert(sizeof(qsa_fp8_view) == sizeof(qsa_bf16_view), "view layouts must agree");
+
+const qsa_bf16_view *as_view(const qsa_fp8_view *v) {
+    return reinterpret_cast<const qsa_bf16_view *>(v);
+}
+
 // Byte span [lo, hi) covered by a strided view (all strides non-negative).
-void span_of(const qsa_bf16_view *v, uintptr_t *lo, uintptr_t *hi) {
+void span_of(const qsa_bf16_view *v, uintptr_t *lo, uintptr_t *hi, int elem_bytes = 2) {
     int64_t last = 0;
     for (int i = 0; i < 3; ++i) last += (v->size[i] - 1) * v->stride[i];
     *lo = (uintptr_t)v->data;
-    *hi = (uintptr_t)v->data + (uintptr_t)(last + 1) * 2;
+    *hi = (uintptr_t)v->data + (uintptr_t)(last + 1) * elem_bytes;
 }
 
 bool any_empty(const qsa_bf16_view *v) {
     return v->size[0] == 0 || v->size[1] == 0 || v->size[2] == 0;
 }
 
-qsa_status check_bf16(const qsa_bf16_view *v, const char *name) {
+// Rows must start on 16-byte boundaries: base aligned, strides a multiple of
+// 16 bytes (8 BF16 or 16 FP8 elements), unit innermost stride.
+qsa_status check_view(const qsa_bf16_view *v, const char *name, int elem_bytes) {
     if (!v) return fail(QSA_ERR_NULL, "%s: view pointer is NULL", name);
     for (int i = 0; i < 3; ++i) {
         if (v->size[i] < 0) return fail(QSA_ERR_SHAPE, "%s: negative size", name);
@@ -68,9 +82,15 @@ qsa_status check_bf16(const qsa_bf16_view *v, const char *name) {
     if (v->stride[2] != 1) return fail(QSA_ERR_STRIDE, "%s: innermost stride must be 1", name);
     if ((uintptr_t)v->data % 16)
         return fail(QSA_ERR_STRIDE, "%s: base pointer must be 16-byte aligned", name);
-    if (v->stride[0] % 8 || v->stride[1] % 8)
-        return fail(QSA_ERR_STRIDE, "%s: strides must be multiples of 8 elements", name);
+    const int64_t per16 = 16 / elem_bytes;
+    if (v->stride[0] % per16 || v->stride[1] % per16)
+        return fail(QSA_ERR_STRIDE, "%s: strides must be multiples of %lld elements", name,
+                    (long long)per16);
     return QSA_OK;
+}
+
+qsa_status check_bf16(const qsa_bf16_view *v, const char *name) {
+    return check_view(v, name, 2);
 }
 
 qsa_status check_workspace(const void *ws, size_t bytes, int64_t T, int64_t W,
@@ -91,10 +111,10 @@ struct Problem {
 
 // Checks of q, k_cache, v_cache, W and scale shared by every attention entry point.
 qsa_status check_inputs(const qsa_bf16_view *q, const qsa_bf16_view *k, const qsa_bf16_view *v,
-                        int64_t W, float scale, Problem *pr) {
+                        int64_t W, float scale, Problem *pr, int kv_bytes = 2) {
     qsa_status s;
-    if ((s = check_bf16(q, "q")) || (s = check_bf16(k, "k_cache")) ||
-        (s = check_bf16(v, "v_cache")))
+    if ((s = check_bf16(q, "q")) || (s = check_view(k, "k_cache", kv_bytes)) ||
+        (s = check_view(v, "v_cache", kv_bytes)))
         return s;
     for (int i = 0; i < 3; ++i)
         if (v->size[i] != k->size[i]) return fail(QSA_ERR_SHAPE, "v_cache must have k_cache's shape");
@@ -118,12 +138,13 @@ qsa_status check_inputs(const qsa_bf16_view *q, const qsa_bf16_view *k, const qs
 
 // A written byte range [lo, hi) must not overlap any of q, k_cache, v_cache.
 qsa_status check_no_overlap(uintptr_t lo, uintptr_t hi, const qsa_bf16_view *q,
-                            const qsa_bf16_view *k, const qsa_bf16_view *v, const char *what) {
+                            const qsa_bf16_view *k, const qsa_bf16_view *v, const char *what,
+                            int kv_bytes = 2) {
     const qsa_bf16_view *ins[3] = {q, k, v};
-    for (const qsa_bf16_view *in : ins) {
-        if (any_empty(in)) continue;
+    for (int i = 0; i < 3; ++i) {
+        if (any_empty(ins[i])) continue;
         uintptr_t ilo, ihi;
-        span_of(in, &ilo, &ihi);
+        span_of(ins[i], &ilo, &ihi, i == 0 ? 2 : kv_bytes);
         if (lo < ihi && ilo < hi) return fail(QSA_ERR_ALIAS, "%s overlaps an input", what);
     }
     return QSA_OK;
@@ -131,19 +152,25 @@ qsa_status check_no_overlap(uintptr_t lo, uintptr_t hi, const qsa_bf16_view *q,
 
 qsa_status check_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
                         const qsa_bf16_view *v, const qsa_bf16_view *out, int64_t W,
-                        float scale, Problem *pr) {
+                        float scale, Problem *pr, int kv_bytes = 2) {
     qsa_status s;
-    if ((s = check_bf16(q, "q")) || (s = check_bf16(k, "k_cache")) ||
-        (s = check_bf16(v, "v_cache")) || (s = check_bf16(out, "out")))
+    if ((s = check_bf16(q, "q")) || (s = check_view(k, "k_cache", kv_bytes)) ||
+        (s = check_view(v, "v_cache", kv_bytes)) || (s = check_bf16(out, "out")))
         return s;
     for (int i = 0; i < 3; ++i)
         if (out->size[i] != q->size[i]) return fail(QSA_ERR_SHAPE, "out must have q's shape");
-    if ((s = check_inputs(q, k, v, W, scale, pr))) return s;
+    if ((s = check_inputs(q, k, v, W, scale, pr, kv_bytes))) return s;
     if (!any_empty(out)) {
         uintptr_t olo, ohi;
         span_of(out, &olo, &ohi);
-        if ((s = check_no_overlap(olo, ohi, q, k, v, "out"))) return s;
+        if ((s = check_no_overlap(olo, ohi, q, k, v, "out", kv_bytes))) return s;
     }
+    return QSA_OK;
+}
+
+qsa_status check_fp8_scales(float k_scale, float v_scale) {
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
+        return fail(QSA_ERR_SCALE, "k_scale and v_scale must be finite");
     return QSA_OK;
 }
 
@@ -190,17 +217,24 @@ void fill_attend(qsa::AttendParams &p, const qsa_bf16_view *q, const qsa_bf16_vi
                  const qsa_bf16_view *v, const Problem &pr, float scale, const void *ws,
                  const qsa_workspace_map &m);
 
+// KV element type and scales of one call (BF16: scales are 1 and unused).
+struct KvKind {
+    qsa::KvType type = qsa::KvType::kBf16;
+    float k_scale = 1.0f, v_scale = 1.0f;
+};
+
 qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
                           const qsa_bf16_view *v, const qsa_bf16_view *out, const Problem &pr,
                           float scale, const void *ws, const qsa_workspace_map &m,
-                          hipStream_t stream) {
+                          hipStream_t stream, KvKind kv = KvKind()) {
     if (pr.T == 0 || pr.Hq == 0) return QSA_OK;
     qsa::AttendParams p{};
-    fill_attend(p, q, k, v, pr, scale, ws, m);
+    fill_attend(p, q, k, v, pr, scale * kv.k_scale, ws, m);
+    p.v_scale = kv.v_scale;
     p.out = (uint16_t *)out->data;
     p.o_st = out->stride[0];
     p.o_sh = out->stride[1];
-    hipError_t e = qsa::launch_attend(p, pr.T, stream);
+    hipError_t e = qsa::launch_attend(p, kv.type, pr.T, stream);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
 }
 
@@ -235,13 +269,14 @@ qsa_status enqueue_partial(const qsa_bf16_view *q, const qsa_bf16_view *k,
     if (pr.T == 0 || pr.Hq == 0) return QSA_OK;
     qsa::AttendParams p{};
     fill_attend(p, q, k, v, pr, scale, ws, m);
+    p.v_scale = 1.0f;
     p.splits = splits;
     p.part_base = part_base;
     p.T = pr.T;
     p.Hq = pr.Hq;
     p.part_o = (float *)partials;
     p.part_ml = (float *)((char *)partials + pm.ml_offset);
-    hipError_t e = qsa::launch_attend_partial(p, pr.T, stream);
+    hipError_t e = qsa::launch_attend_partial(p, qsa::KvType::kBf16, pr.T, stream);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "partial attention launch");
 }
 
@@ -493,11 +528,18 @@ qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes, int64
     return QSA_OK;
 }
 
-qsa_status qsa_gather_ceiling(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_cache,
-                              int64_t T, int64_t W, const void *workspace,
-                              size_t workspace_bytes, uint32_t *sink, void *stream) {
+}  // extern "C"
+
+namespace {
+
+qsa_status gather_ceiling_any(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_cache,
+                              int kv_bytes, qsa::KvType kv, int64_t T, int64_t W,
+                              const void *workspace, size_t workspace_bytes, uint32_t *sink,
+                              void *stream) {
     qsa_status s;
-    if ((s = check_bf16(k_cache, "k_cache")) || (s = check_bf16(v_cache, "v_cache"))) return s;
+    if ((s = check_view(k_cache, "k_cache", kv_bytes)) ||
+        (s = check_view(v_cache, "v_cache", kv_bytes)))
+        return s;
     for (int i = 0; i < 3; ++i)
         if (v_cache->size[i] != k_cache->size[i])
             return fail(QSA_ERR_SHAPE, "v_cache must have k_cache's shape");
@@ -509,10 +551,10 @@ qsa_status qsa_gather_ceiling(const qsa_bf16_view *k_cache, const qsa_bf16_view 
     if (T == 0 || k_cache->size[1] == 0) return QSA_OK;
     if (!sink) return fail(QSA_ERR_NULL, "sink is NULL");
     qsa::CeilingParams p{};
-    p.k = (const uint16_t *)k_cache->data;
+    p.k = k_cache->data;
     p.k_ss = k_cache->stride[0];
     p.k_sh = k_cache->stride[1];
-    p.v = (const uint16_t *)v_cache->data;
+    p.v = v_cache->data;
     p.v_ss = v_cache->stride[0];
     p.v_sh = v_cache->stride[1];
     p.list = (const int32_t *)((const char *)workspace + m.list_offset);
@@ -520,8 +562,62 @@ qsa_status qsa_gather_ceiling(const qsa_bf16_view *k_cache, const qsa_bf16_view 
     p.count = (const int32_t *)((const char *)workspace + m.count_offset);
     p.sink = sink;
     p.Hkv = (int32_t)k_cache->size[1];
-    hipError_t e = qsa::launch_ceiling(p, T, (hipStream_t)stream);
+    hipError_t e = qsa::launch_ceiling(p, kv, T, (hipStream_t)stream);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "gather-ceiling launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+qsa_status qsa_gather_ceiling(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_cache,
+                              int64_t T, int64_t W, const void *workspace,
+                              size_t workspace_bytes, uint32_t *sink, void *stream) {
+    return gather_ceiling_any(k_cache, v_cache, 2, qsa::KvType::kBf16, T, W, workspace,
+                              workspace_bytes, sink, stream);
+}
+
+qsa_status qsa_gather_ceiling_fp8kv(const qsa_fp8_view *k8, const qsa_fp8_view *v8, int64_t T,
+                                    int64_t W, const void *workspace, size_t workspace_bytes,
+                                    uint32_t *sink, void *stream) {
+    return gather_ceiling_any(as_view(k8), as_view(v8), 1, qsa::KvType::kFp8, T, W, workspace,
+                              workspace_bytes, sink, stream);
+}
+
+qsa_status qsa_sparse_attend_fp8kv(const qsa_bf16_view *q, const qsa_fp8_view *k8,
+                                   const qsa_fp8_view *v8, float k_scale, float v_scale,
+                                   int64_t W, float scale, const void *workspace,
+                                   size_t workspace_bytes, qsa_bf16_view *out, void *stream) {
+    Problem pr;
+    qsa_status s = check_attend(q, as_view(k8), as_view(v8), out, W, scale, &pr, 1);
+    if (s) return s;
+    if ((s = check_fp8_scales(k_scale, v_scale))) return s;
+    qsa_workspace_map m;
+    if ((s = check_workspace(workspace, workspace_bytes, pr.T, W, &m))) return s;
+    KvKind kv{qsa::KvType::kFp8, k_scale, v_scale};
+    return enqueue_attend(q, as_view(k8), as_view(v8), out, pr, scale, workspace, m,
+                          (hipStream_t)stream, kv);
+}
+
+qsa_status qsa_sparse_prefill_fp8kv(const qsa_bf16_view *q, const qsa_fp8_view *k8,
+                                    const qsa_fp8_view *v8, float k_scale, float v_scale,
+                                    const qsa_i32_view *slot_idx, float scale,
+                                    qsa_bf16_view *out, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    if (!slot_idx) return fail(QSA_ERR_NULL, "slot_idx: view pointer is NULL");
+    Problem pr;
+    qsa_status s = check_attend(q, as_view(k8), as_view(v8), out, slot_idx->size[1], scale, &pr, 1);
+    if (s) return s;
+    if ((s = check_fp8_scales(k_scale, v_scale))) return s;
+    int64_t W = 0;
+    if ((s = check_slots(slot_idx, pr.T, &W))) return s;
+    qsa_workspace_map m;
+    if ((s = check_workspace(workspace, workspace_bytes, pr.T, W, &m))) return s;
+    if (pr.T == 0) return QSA_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, 0, pr.S, workspace, m, st))) return s;
+    KvKind kv{qsa::KvType::kFp8, k_scale, v_scale};
+    return enqueue_attend(q, as_view(k8), as_view(v8), out, pr, scale, workspace, m, st, kv);
 }
 
 }  // extern "C"

@@ -37,13 +37,18 @@ struct CompactParams {
     int32_t *n_bad;
 };
 
+// Element type of the K/V cache: BF16, or FP8 E4M3 codes with one scale per
+// tensor (the softmax scale absorbs k_scale; v_scale multiplies the output).
+enum class KvType { kBf16, kFp8 };
+
 struct AttendParams {
     const uint16_t *q;
     int64_t q_st, q_sh;
-    const uint16_t *k;
+    const void *k;       // [S, Hkv, 256] of the KV type; strides in elements
     int64_t k_ss, k_sh;
-    const uint16_t *v;
+    const void *v;
     int64_t v_ss, v_sh;
+    float v_scale;       // FP8 only
     const int32_t *list;
     int64_t list_stride;
     const int32_t *count;
@@ -73,9 +78,9 @@ struct MergeParams {
 };
 
 struct CeilingParams {
-    const uint16_t *k;
+    const void *k;
     int64_t k_ss, k_sh;
-    const uint16_t *v;
+    const void *v;
     int64_t v_ss, v_sh;
     const int32_t *list;
     int64_t list_stride;
@@ -85,9 +90,10 @@ struct CeilingParams {
 };
 
 hipError_t launch_compact(const CompactParams &p, hipStream_t stream);
-hipError_t launch_attend(const AttendParams &p, int64_t T, hipStream_t stream);
-hipError_t launch_attend_partial(const AttendParams &p, int64_t T, hipStream_t stream);
+hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_t stream);
+hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
+                                 hipStream_t stream);
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
-hipError_t launch_ceiling(const CeilingParams &p, int64_t T, hipStream_t stream);
+hipError_t launch_ceiling(const CeilingParams &p, KvType kv, int64_t T, hipStream_t stream);
 
 }  // namespace qsa

@@ -49,16 +49,29 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 #define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T *)(p))
 
-constexpr int kRowBytes = kHeadDim * 2;             // one K or V row: 512 B
+constexpr int kRowBytes = kHeadDim * 2;             // one BF16 K or V row in LDS: 512 B
 constexpr int kChunksPerRow = kRowBytes / 16;       // 32 sixteen-byte chunks
 constexpr int kTileBytes = kTileSlots * kRowBytes;  // 8 KiB of K (or V)
 constexpr int kWaveLds = 2 * kTileBytes;            // K tile + V tile per wave
 constexpr int kThreads = 64 * kWavesPerItem;
-constexpr int kLoadsPerTile = kTileBytes / (64 * 16);  // 8 dwordx4 per lane
+constexpr int kMaxLoadsPerTile = kTileBytes / (64 * 16);  // 8 dwordx4 per lane (BF16)
+
+// How one tile of a cache with this element type is gathered: a row of 256
+// elements is split into 16-byte chunks, one per lane, and one dwordx4 load
+// instruction covers kRowsPerLoad whole rows.
+template <KvType KV>
+struct KvGather {
+    static constexpr int kElemBytes = KV == KvType::kFp8 ? 1 : 2;
+    static constexpr int kRowBytesHbm = kHeadDim * kElemBytes;  // 512 or 256
+    static constexpr int kLanesPerRow = kRowBytesHbm / 16;        // 32 or 16
+    static constexpr int kRowsPerLoad = 64 / kLanesPerRow;        // 2 or 4
+    static constexpr int kLoads = kTileSlots / kRowsPerLoad;      // 8 or 4
+};
 constexpr int kHeadBlock = 16;                      // query heads per MFMA column block
 constexpr int kDimBlocks = kHeadDim / 16;           // 16 output blocks of 16 dims
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -157,38 +170,75 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
 
 // ---------------------------------------------------------------- gathers
 
-// Issue the 2 x 8 dwordx4 loads of one tile.  `slot` holds, in lane r (and
-// every lane congruent to r mod 16), the slot of tile row r (-1: none).  Load
-// q covers rows 2q (lanes 0-31) and 2q+1 (lanes 32-63), one 16-byte chunk per
-// lane, so each row is one fully coalesced 512-byte read.
-__device__ __forceinline__ void gather_tile(u32x4_t (&rk)[kLoadsPerTile],
-                                            u32x4_t (&rv)[kLoadsPerTile], int slot,
-                                            const uint16_t *kb, int64_t k_ss,
-                                            const uint16_t *vb, int64_t v_ss, int lane) {
-    const int ch8 = (lane & 31) * 8;
-    const bool upper = lane >= 32;
+// Issue the dwordx4 loads of one tile of K and of V.  `slot` holds, in lane
+// r (and every lane congruent to r mod 16), the slot of tile row r (-1:
+// none).  Load q covers kRowsPerLoad consecutive tile rows, each one whole
+// row read by kLanesPerRow consecutive lanes, 16 bytes per lane, so every
+// row is one fully coalesced read.  kb/vb are byte pointers to head g of
+// slot 0; k_ss/v_ss are slot strides in bytes.
+template <KvType KV>
+__device__ __forceinline__ void gather_tile(u32x4_t (&rk)[kMaxLoadsPerTile],
+                                            u32x4_t (&rv)[kMaxLoadsPerTile], int slot,
+                                            const char *kb, int64_t k_ss, const char *vb,
+                                            int64_t v_ss, int lane) {
+    using G = KvGather<KV>;
+    const int byte_in_row = (lane % G::kLanesPerRow) * 16;
+    const int sub = lane / G::kLanesPerRow;   // which row of the load this lane reads
 #pragma unroll
-    for (int q = 0; q < kLoadsPerTile; ++q) {
-        const int s_lo = __builtin_amdgcn_readlane(slot, 2 * q);
-        const int s_hi = __builtin_amdgcn_readlane(slot, 2 * q + 1);
-        const int s = upper ? s_hi : s_lo;
-        const uint16_t *kp = s >= 0 ? kb + (int64_t)s * k_ss + ch8 : kZeroRow + ch8;
-        const uint16_t *vp = s >= 0 ? vb + (int64_t)s * v_ss + ch8 : kZeroRow + ch8;
+    for (int q = 0; q < G::kLoads; ++q) {
+        int s = __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q);
+#pragma unroll
+        for (int r = 1; r < G::kRowsPerLoad; ++r) {
+            const int sr = __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q + r);
+            s = sub == r ? sr : s;
+        }
+        const char *zero = (const char *)kZeroRow + byte_in_row;
+        const char *kp = s >= 0 ? kb + (int64_t)s * k_ss + byte_in_row : zero;
+        const char *vp = s >= 0 ? vb + (int64_t)s * v_ss + byte_in_row : zero;
         rk[q] = ldg16<u32x4_t>(kp);
         rv[q] = ldg16<u32x4_t>(vp);
     }
 }
 
-__device__ __forceinline__ void stage_tile(const u32x4_t (&rk)[kLoadsPerTile],
-                                           const u32x4_t (&rv)[kLoadsPerTile],
-                                           char *ks, char *vs, int lane) {
-    const int ch = lane & 31;
-    const int half = lane >> 5;
+// 16 FP8 E4M3 codes -> 16 BF16 values (exact: every E4M3 value is a BF16
+// value), as two 16-byte chunks.
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t w, u32x4_t &lo, u32x4_t &hi) {
+    u32x2_t pk[8];
 #pragma unroll
-    for (int q = 0; q < kLoadsPerTile; ++q) {
-        const int off = lds_off(2 * q + half, ch);
-        *LDS_PTR(u32x4_t, ks + off) = rk[q];
-        *LDS_PTR(u32x4_t, vs + off) = rv[q];
+    for (int i = 0; i < 4; ++i) {
+        const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+        const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+        const bf16x4_t x = {(__bf16)a[0], (__bf16)a[1], (__bf16)b[0], (__bf16)b[1]};
+        pk[i] = __builtin_bit_cast(u32x2_t, x);
+    }
+    lo = u32x4_t{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+    hi = u32x4_t{pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
+}
+
+// Write a gathered tile into the wave's LDS tiles as BF16 rows (swizzled).
+template <KvType KV>
+__device__ __forceinline__ void stage_tile(const u32x4_t (&rk)[kMaxLoadsPerTile],
+                                           const u32x4_t (&rv)[kMaxLoadsPerTile],
+                                           char *ks, char *vs, int lane) {
+    using G = KvGather<KV>;
+    const int chunk = lane % G::kLanesPerRow;
+    const int sub = lane / G::kLanesPerRow;
+#pragma unroll
+    for (int q = 0; q < G::kLoads; ++q) {
+        const int r = G::kRowsPerLoad * q + sub;
+        if constexpr (KV == KvType::kBf16) {
+            const int off = lds_off(r, chunk);
+            *LDS_PTR(u32x4_t, ks + off) = rk[q];
+            *LDS_PTR(u32x4_t, vs + off) = rv[q];
+        } else {
+            u32x4_t k0, k1, v0, v1;
+            fp8x16_to_bf16(rk[q], k0, k1);
+            fp8x16_to_bf16(rv[q], v0, v1);
+            *LDS_PTR(u32x4_t, ks + lds_off(r, 2 * chunk)) = k0;
+            *LDS_PTR(u32x4_t, ks + lds_off(r, 2 * chunk + 1)) = k1;
+            *LDS_PTR(u32x4_t, vs + lds_off(r, 2 * chunk)) = v0;
+            *LDS_PTR(u32x4_t, vs + lds_off(r, 2 * chunk + 1)) = v1;
+        }
     }
 }
 
@@ -210,8 +260,9 @@ __device__ __forceinline__ int tile_slot(const int32_t *list, int tile, int ntil
 // s + 2 splits, ... and writes FP32 (O, m, l) of that share to part
 // part_base + s, for qsa_merge_partials (or another shard's partials) to
 // combine.
-template <bool kSplit>
+template <bool kSplit, KvType KV>
 __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const AttendParams p) {
+    using Gth = KvGather<KV>;
     __shared__ __attribute__((aligned(16))) char smem[kAttendLds];
 
     const int lane = threadIdx.x & 63;
@@ -266,8 +317,9 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
     }
 
     const int32_t *list = p.list + t * p.list_stride;
-    const uint16_t *kb = p.k + (int64_t)g * p.k_sh;
-    const uint16_t *vb = p.v + (int64_t)g * p.v_sh;
+    const char *kb = (const char *)p.k + (int64_t)g * p.k_sh * Gth::kElemBytes;
+    const char *vb = (const char *)p.v + (int64_t)g * p.v_sh * Gth::kElemBytes;
+    const int64_t k_ss = p.k_ss * Gth::kElemBytes, v_ss = p.v_ss * Gth::kElemBytes;
     char *ks_lds = smem + wave * kWaveLds;
     char *vs_lds = ks_lds + kTileBytes;
 
@@ -279,21 +331,21 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
 
     // This wave's tiles: split + splits * (wave + kWavesPerItem * i).
     const int step = splits * kWavesPerItem;
-    u32x4_t rk[kLoadsPerTile], rv[kLoadsPerTile];
+    u32x4_t rk[kMaxLoadsPerTile], rv[kMaxLoadsPerTile];
     int tile = split + splits * wave;
     int slot_next = tile_slot(list, tile + step, ntiles, lane);
     if (tile < ntiles)
-        gather_tile(rk, rv, tile_slot(list, tile, ntiles, lane), kb, p.k_ss, vb, p.v_ss, lane);
+        gather_tile<KV>(rk, rv, tile_slot(list, tile, ntiles, lane), kb, k_ss, vb, v_ss, lane);
 
     const int tr_row = 4 * j + (c >> 2);    // V row this lane addresses in a transpose load
     const int tr_sub = c & 3;               // which 4 of the 16 dims of a block
 
     for (; tile < ntiles; tile += step) {
         wave_lds_fence();   // the previous tile's LDS reads are done
-        stage_tile(rk, rv, ks_lds, vs_lds, lane);
+        stage_tile<KV>(rk, rv, ks_lds, vs_lds, lane);
         const int nt = tile + step;
         if (nt < ntiles) {
-            gather_tile(rk, rv, slot_next, kb, p.k_ss, vb, p.v_ss, lane);
+            gather_tile<KV>(rk, rv, slot_next, kb, k_ss, vb, v_ss, lane);
             slot_next = tile_slot(list, nt + step, ntiles, lane);
         }
         wave_lds_fence();   // other lanes of this wave wrote the rows read below
@@ -393,6 +445,7 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
 #pragma unroll
             for (int w = 0; w < kWavesPerItem; ++w)
                 acc += fw[w] * part_o[(w * kDimBlocks + db) * 64 + lane];
+            if constexpr (KV == KvType::kFp8) acc *= p.v_scale;
             if (kSplit) {
                 *(f32x4_t *)(p.part_o + (part_row + c) * kHeadDim + 16 * db + 4 * j) = acc;
             } else {
@@ -441,7 +494,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 // Reads the same rows with the same tiles, waves, prefetch distance and
 // residency as attend_kernel, folds them with XOR and writes one word per
 // (t, g): the cost of the gathers alone.
+template <KvType KV>
 __global__ __launch_bounds__(kThreads, kItemsPerCU) void ceiling_kernel(const CeilingParams p) {
+    using Gth = KvGather<KV>;
     // Same LDS footprint as attend_kernel, so the same number of items fit a CU.
     __shared__ __attribute__((aligned(16))) char smem[kAttendLds];
     const int lane = threadIdx.x & 63;
@@ -452,21 +507,22 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void ceiling_kernel(const Ce
     const int n = p.count[t];
     const int ntiles = (n + kTileSlots - 1) / kTileSlots;
     const int32_t *list = p.list + t * p.list_stride;
-    const uint16_t *kb = p.k + (int64_t)g * p.k_sh;
-    const uint16_t *vb = p.v + (int64_t)g * p.v_sh;
+    const char *kb = (const char *)p.k + (int64_t)g * p.k_sh * Gth::kElemBytes;
+    const char *vb = (const char *)p.v + (int64_t)g * p.v_sh * Gth::kElemBytes;
+    const int64_t k_ss = p.k_ss * Gth::kElemBytes, v_ss = p.v_ss * Gth::kElemBytes;
 
     u32x4_t acc = {0, 0, 0, 0};
-    u32x4_t rk[kLoadsPerTile], rv[kLoadsPerTile];
+    u32x4_t rk[kMaxLoadsPerTile], rv[kMaxLoadsPerTile];
     int tile = wave;
     int slot_next = tile_slot(list, tile + kWavesPerItem, ntiles, lane);
     if (tile < ntiles)
-        gather_tile(rk, rv, tile_slot(list, tile, ntiles, lane), kb, p.k_ss, vb, p.v_ss, lane);
+        gather_tile<KV>(rk, rv, tile_slot(list, tile, ntiles, lane), kb, k_ss, vb, v_ss, lane);
     for (; tile < ntiles; tile += kWavesPerItem) {
 #pragma unroll
-        for (int q = 0; q < kLoadsPerTile; ++q) acc ^= rk[q] ^ rv[q];
+        for (int q = 0; q < Gth::kLoads; ++q) acc ^= rk[q] ^ rv[q];
         const int nt = tile + kWavesPerItem;
         if (nt < ntiles) {
-            gather_tile(rk, rv, slot_next, kb, p.k_ss, vb, p.v_ss, lane);
+            gather_tile<KV>(rk, rv, slot_next, kb, k_ss, vb, v_ss, lane);
             slot_next = tile_slot(list, nt + kWavesPerItem, ntiles, lane);
         }
     }
@@ -491,17 +547,28 @@ hipError_t launch_compact(const CompactParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_attend(const AttendParams &p, int64_t T, hipStream_t stream) {
+hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_t stream) {
     const int64_t items = T * (int64_t)p.Hkv * p.HB;
     if (items == 0) return hipSuccess;
-    hipLaunchKernelGGL(attend_kernel<false>, dim3((unsigned)items), dim3(kThreads), 0, stream, p);
+    if (kv == KvType::kFp8)
+        hipLaunchKernelGGL((attend_kernel<false, KvType::kFp8>), dim3((unsigned)items),
+                           dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attend_kernel<false, KvType::kBf16>), dim3((unsigned)items),
+                           dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_attend_partial(const AttendParams &p, int64_t T, hipStream_t stream) {
+hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
+                                 hipStream_t stream) {
     const int64_t blocks = T * (int64_t)p.Hkv * p.HB * p.splits;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(attend_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    if (kv == KvType::kFp8)
+        hipLaunchKernelGGL((attend_kernel<true, KvType::kFp8>), dim3((unsigned)blocks),
+                           dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attend_kernel<true, KvType::kBf16>), dim3((unsigned)blocks),
+                           dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -512,10 +579,15 @@ hipError_t launch_merge(const MergeParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_ceiling(const CeilingParams &p, int64_t T, hipStream_t stream) {
+hipError_t launch_ceiling(const CeilingParams &p, KvType kv, int64_t T, hipStream_t stream) {
     const int64_t items = T * (int64_t)p.Hkv;
     if (items == 0) return hipSuccess;
-    hipLaunchKernelGGL(ceiling_kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, p);
+    if (kv == KvType::kFp8)
+        hipLaunchKernelGGL(ceiling_kernel<KvType::kFp8>, dim3((unsigned)items), dim3(kThreads), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL(ceiling_kernel<KvType::kBf16>, dim3((unsigned)items), dim3(kThreads), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
