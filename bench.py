@@ -4,8 +4,9 @@ One step = the whole hot path on one batch of resident synthetic input:
 index validation/compaction (qsa_compact_slots) followed by the gather
 attention (qsa_sparse_attend), both through the C ABI on torch's current
 stream.  Other workloads: `decode_batch` runs the split path (compaction,
-qsa_sparse_attend_partial, qsa_merge_partials) and `long_prefill_fp8kv` the
-FP8 E4M3 KV-cache variant (qsa_sparse_attend_fp8kv).  The default workload is the long prefill of the page "Qwen4-Exp QSA
+qsa_sparse_attend_partial, qsa_merge_partials), `long_prefill_fp8kv` the
+FP8 E4M3 KV-cache variant (qsa_sparse_attend_fp8kv) and `long_prefill_block4`
+micro-block selections (qsa_compact_blocks, then qsa_sparse_attend).  The default workload is the long prefill of the page "Qwen4-Exp QSA
 comes to Huawei's Ascend: inside SGLang's opt-in CANN prefill PR" (section
 "Nine tests that passed, ..."): 7,810 query tokens, a 65,536-slot cache,
 2,051 selected slots per token, (Hq, Hkv) = (16, 2), D = 256, BF16.
@@ -41,7 +42,7 @@ def parse():
     ap.add_argument("--workload", default="long_prefill",
                     choices=["tiny", "edge_mix", "long_prefill", "two_request",
                              "max_cache_6_1", "max_cache_3_1", "decode_batch",
-                             "long_prefill_fp8kv"])
+                             "long_prefill_fp8kv", "long_prefill_block4"])
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="token rows of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -95,7 +96,11 @@ def main():
         # The cache in FP8 E4M3 (one scale per tensor); the BF16 copies are freed.
         k, v, k_scale, v_scale = upload_fp8(case, dev)
     out = torch.empty((T, Hq, case.D), dtype=torch.bfloat16, device=dev)
-    ws = qsa.new_workspace(T, W, dev)
+    # Micro-block selections: each entry names `bs` consecutive slots, and the
+    # compacted list (the attention's input) is bs times wider.
+    bs = int(case.info.get("block_size", 1))
+    Wl = W * bs
+    ws = qsa.new_workspace(T, Wl, dev)
     scale = case.scale if case.scale is not None else 1.0 / np.sqrt(case.D)
     torch.cuda.synchronize()
 
@@ -113,20 +118,26 @@ def main():
     splits = qsa.decode_splits(T, W, Hq, Hkv) if split else 1
     parts = qsa.new_partials(splits, T, Hq, dev) if split else None
 
+    def compact():
+        if bs > 1:
+            qsa.compact_blocks(sl, S, bs, ws)
+        else:
+            qsa.compact_slots(sl, S, ws)
+
     def attend():
         if split:
             qsa.sparse_attend_partial(q, k, v, ws, W, splits, 0, splits, parts, scale=scale)
         elif fp8:
             qsa.sparse_attend_fp8kv(q, k, v, k_scale, v_scale, ws, W, scale=scale, out=out)
         else:
-            qsa.sparse_attend(q, k, v, ws, W, scale=scale, out=out)
+            qsa.sparse_attend(q, k, v, ws, Wl, scale=scale, out=out)
 
     def finish():
         if split:
             qsa.merge_partials(parts, splits, T, Hq, out=out)
 
     def step():
-        qsa.compact_slots(sl, S, ws)
+        compact()
         attend()
         finish()
 
@@ -142,7 +153,7 @@ def main():
     torch.cuda.synchronize()
     t0.record()
     for i in range(K):
-        qsa.compact_slots(sl, S, ws)
+        compact()
         a0[i].record()
         attend()
         a1[i].record()
@@ -158,18 +169,18 @@ def main():
     sink = torch.empty(T * Hkv, dtype=torch.int32, device=dev)
     ceiling = qsa.gather_ceiling_fp8kv if fp8 else qsa.gather_ceiling
     for _ in range(2):
-        ceiling(k, v, ws, T, W, sink)
+        ceiling(k, v, ws, T, Wl, sink)
     c0 = torch.cuda.Event(enable_timing=True)
     c1 = torch.cuda.Event(enable_timing=True)
     c0.record()
     for _ in range(K):
-        ceiling(k, v, ws, T, W, sink)
+        ceiling(k, v, ws, T, Wl, sink)
     c1.record()
     torch.cuda.synchronize()
     ceil_ms = c0.elapsed_time(c1) / K
 
-    valid = (case.slot_idx >= 0) & (case.slot_idx < S)
-    n_t = valid.sum(axis=1).astype(np.int64)
+    valid = (case.slot_idx >= 0) & (case.slot_idx < S // bs)
+    n_t = valid.sum(axis=1).astype(np.int64) * bs      # selected slots per token
     pairs = int(n_t.sum()) * Hq
     # Algorithmic bytes of one attention launch: every selected K and V row of
     # every (token, KV head) once, its slot index, Q in and O out.
@@ -183,6 +194,9 @@ def main():
     import oracle
 
     def run_oracle(rows_, nthreads=0):
+        if bs > 1:
+            return oracle.prefill_blocks(case.q, case.k_cache, case.v_cache, case.slot_idx, bs,
+                                         scale, rows=rows_, nthreads=nthreads)
         if fp8:
             return oracle.prefill_fp8kv(case.q, case.info["k8"], case.info["v8"], k_scale,
                                         v_scale, case.slot_idx, scale, rows=rows_,
@@ -193,7 +207,7 @@ def main():
     rows = qi.sample_rows(T, 16, seed=11)
     want = run_oracle(rows)
     got = bf16_tensor_to_f32(out[torch.as_tensor(rows, device=dev)])
-    parity = gate(got, want, empty_row_mask(case.slot_idx, S, rows))
+    parity = gate(got, want, n_t[rows] == 0)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -223,7 +237,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": case.name, "T": T, "S": S, "W": W, "Hq": Hq, "Hkv": Hkv,
                    "D": case.D, "scale": scale, "seed": case.info.get("seed"),
-                   "splits": splits, "parallelism": "none (1 GPU)"},
+                   "splits": splits, "block_size": bs, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic},

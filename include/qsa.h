@@ -144,6 +144,34 @@ qsa_status qsa_compact_slot_range(const qsa_i32_view *slot_idx, int64_t S,
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * Micro-block selections.  QSA selects micro-blocks of consecutive tokens
+ * rather than single tokens (page, section "Why QSA is the awkward part, in
+ * numbers"; a block size of 4 is the later "block4" work of section "Nine
+ * tests that passed, ...").  Reading: block b of the physical cache is slots
+ * b * block_size .. b * block_size + block_size - 1, and S must be a multiple
+ * of block_size (1..64).  block_idx is [T, W] with -1 for "no block"; an
+ * entry that is neither -1 nor in [0, S / block_size) is invalid (dropped,
+ * counted).  qsa_compact_blocks fills a workspace for T rows of width
+ * W * block_size (size it with qsa_workspace_bytes(T, W * block_size)): the
+ * valid blocks, grouped as in qsa_compact_slots by block id, each expanded
+ * into its block_size slots in ascending order; count[t] counts slots.
+ * qsa_sparse_attend with that width then runs the attention unchanged.
+ */
+qsa_status qsa_compact_blocks(const qsa_i32_view *block_idx, int64_t S,
+                              int32_t block_size, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* qsa_compact_blocks followed by qsa_sparse_attend (the whole prefill for
+ * micro-block selections). */
+qsa_status qsa_sparse_prefill_blocks(const qsa_bf16_view *q,
+                                     const qsa_bf16_view *k_cache,
+                                     const qsa_bf16_view *v_cache,
+                                     const qsa_i32_view *block_idx,
+                                     int32_t block_size, float scale,
+                                     qsa_bf16_view *out, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
  * Gather attention over a workspace already filled by qsa_compact_slots for
  * the same T and W (the softmax(scale * Q K^T) V of the layout-embedding
  * paragraph, restricted to each token's listed slots).  Rows with count 0

@@ -104,6 +104,26 @@ def compact(slot_idx: np.ndarray, S: int):
     return lists[:, :W], counts, n_bad
 
 
+def expand_blocks(block_idx: np.ndarray, block_size: int) -> np.ndarray:
+    """Micro-block selections as slot selections: entry b becomes the slots
+    b*block_size .. b*block_size + block_size - 1, in that order; -1 stays
+    -1 (block_size copies); other negative entries stay invalid."""
+    b = np.asarray(block_idx, dtype=np.int64)
+    offs = np.arange(block_size, dtype=np.int64)
+    slots = np.where(b[..., None] >= 0, b[..., None] * block_size + offs, b[..., None])
+    # an invalid negative entry other than -1 must remain invalid after expansion
+    slots = np.where((b[..., None] < -1), -2, slots)
+    return slots.reshape(b.shape[0], -1).astype(np.int32)
+
+
+def prefill_blocks(q, k_cache, v_cache, block_idx, block_size, scale, rows=None, nthreads=0):
+    """FP32 sparse prefill where each selection entry names a micro-block of
+    block_size consecutive cache slots (reading: block b = slots
+    b*block_size .. b*block_size + block_size - 1)."""
+    return prefill(q, k_cache, v_cache, expand_blocks(block_idx, block_size), scale, rows=rows,
+                   nthreads=nthreads)
+
+
 def e4m3_to_float(code: int) -> float:
     """The oracle's decoding of one FP8 E4M3 byte."""
     return float(_load().qsa_oracle_e4m3_to_float(int(code)))

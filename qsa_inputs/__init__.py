@@ -290,6 +290,19 @@ def with_fp8_kv(case: Case) -> Case:
     return case
 
 
+def long_prefill_blocks(seed: int = 107, block_size: int = 4) -> Case:
+    """The long prefill with micro-block selections: T=7,810, S=65,536,
+    (16,2); every token selects 513 distinct random blocks of 4 consecutive
+    slots (2,052 slots) in random order.  ``slot_idx`` holds block ids;
+    info["block_size"] says how many slots each covers."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, S = 7810, 65536
+    Wb = -(-2051 // block_size)
+    sel = shuffle_rows(rng, distinct_draws(rng, S // block_size, T, Wb))
+    return _contiguous_case(f"long_prefill_block{block_size}", rng, T, S, 16, 2, sel, None,
+                            {"seed": seed, "block_size": block_size})
+
+
 DECODE_REQUESTS = 16
 
 
@@ -331,6 +344,7 @@ WORKLOADS = {
     "max_cache_3_1": lambda seed=105: max_cache(seed, (3, 1)),
     "decode_batch": decode_batch,
     "long_prefill_fp8kv": lambda seed=103: with_fp8_kv(long_prefill(seed)),
+    "long_prefill_block4": long_prefill_blocks,
 }
 
 

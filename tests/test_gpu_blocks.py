@@ -1,0 +1,105 @@
+"""GPU parity of micro-block selections (each entry names block_size
+consecutive cache slots; page "Qwen4-Exp QSA comes to Huawei's Ascend",
+sections "Why QSA is the awkward part, in numbers" and "Nine tests that
+passed, ..." for the block4 work).  Same gate as the slot path."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_inputs as qi
+import top_sparse_attention_amd as qsa
+from qsa_testutil import bf16_tensor_to_f32, gate, upload
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def block_case(seed, T, S, Hq, Hkv, nblocks, bs, pad_frac=0.0, interior=False):
+    case = qi.random_case(seed, T=T, S=S // bs, Hq=Hq, Hkv=Hkv, W=nblocks, pad_frac=pad_frac,
+                          interior=interior)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    k = qi.normal_bf16(rng, (S, Hkv, 256))
+    v = qi.normal_bf16(rng, (S, Hkv, 256))
+    case.k_cache, case.v_cache = k, v
+    case.bases.update(k=k, v=v)
+    case.info["block_size"] = bs
+    return case
+
+
+def empty_blocks(case):
+    return ~np.any(case.slot_idx >= 0, axis=1)
+
+
+def check_blocks(case, rows=None):
+    bs = case.info["block_size"]
+    q, k, v, sl = upload(case, DEV)
+    out = qsa.sparse_prefill_blocks(q, k, v, sl, bs, scale=case.scale)
+    torch.cuda.synchronize()
+    scale = case.scale if case.scale is not None else 1.0 / 16.0
+    want = oracle.prefill_blocks(case.q, case.k_cache, case.v_cache, case.slot_idx, bs, scale,
+                                 rows=rows)
+    got = bf16_tensor_to_f32(out if rows is None else out[torch.as_tensor(rows, device=DEV)])
+    empty = empty_blocks(case) if rows is None else empty_blocks(case)[rows]
+    m = gate(got, want, empty)
+    print(f"{case.name} block{bs}: {m}", flush=True)
+    return out, (q, k, v, sl)
+
+
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 16])
+def test_block_sizes(bs):
+    check_blocks(block_case(1000 + bs, T=29, S=8192, Hq=16, Hkv=2, nblocks=400 // bs + 3, bs=bs,
+                            pad_frac=0.2, interior=True))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(24, 2), (12, 1), (3, 1)])
+def test_block4_head_shapes(Hq, Hkv):
+    check_blocks(block_case(1020 + Hq, T=17, S=4096, Hq=Hq, Hkv=Hkv, nblocks=129, bs=4))
+
+
+def test_block_path_equals_slot_path_on_the_expanded_selection():
+    """Blocks are grouped by block id exactly as their slots would be grouped
+    by slot id, so both paths sum in the same order: bit-identical outputs."""
+    case = block_case(1030, T=23, S=8192, Hq=16, Hkv=2, nblocks=200, bs=4, pad_frac=0.1,
+                      interior=True)
+    out, (q, k, v, sl) = check_blocks(case)
+    slots = torch.from_numpy(oracle.expand_blocks(case.slot_idx, 4)).to(DEV)
+    ref = qsa.sparse_prefill(q, k, v, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_block_compaction_counts_slots_and_invalid_blocks():
+    case = block_case(1040, T=12, S=2048, Hq=2, Hkv=1, nblocks=60, bs=4, pad_frac=0.3,
+                      interior=True)
+    case.slot_idx[2, 0] = 512           # one past the last block
+    case.slot_idx[5, 1] = -9
+    _, _, _, sl = upload(case, DEV)
+    ws = qsa.compact_blocks(sl, 2048, 4)
+    torch.cuda.synchronize()
+    lst, cnt, bad = (x.cpu().numpy() for x in qsa.compacted_lists(ws, case.T, case.W * 4))
+    for t in range(case.T):
+        row = case.slot_idx[t]
+        good = row[(row >= 0) & (row < 512)]
+        assert cnt[t] == 4 * good.size
+        assert sorted(lst[t, :cnt[t]].tolist()) == sorted((good[:, None] * 4 + np.arange(4))
+                                                          .ravel().tolist())
+        assert bad[t] == (1 if t in (2, 5) else 0)
+    with pytest.raises(qsa.QsaError):
+        qsa.check_status(ws, case.T, case.W * 4)
+
+
+def test_block_size_must_divide_the_cache():
+    case = block_case(1050, T=3, S=64, Hq=2, Hkv=1, nblocks=4, bs=4)
+    q, k, v, sl = upload(case, DEV)
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.sparse_prefill_blocks(q, k[:63], v[:63], sl, 4)
+    assert e.value.status == 2
+
+
+def test_long_prefill_block4_sampled_rows():
+    case = qi.long_prefill_blocks()
+    rows = qi.sample_rows(case.T, 64)
+    out, _ = check_blocks(case, rows)
+    assert torch.isfinite(out.float()).all()

@@ -319,3 +319,39 @@ def test_fp8_oracle_matches_dense_bruteforce_with_arbitrary_scales(oracle_mod):
             w = np.exp(z - z.max())
             want[t, h] = (w / w.sum()) @ v[sel, h // G]
     assert rel_l2(got, want) < 1e-5
+
+
+# ---------------------------------------------------------------- micro-blocks
+
+def test_block_expansion_hand_cases(oracle_mod):
+    # block b covers slots b*bs .. b*bs + bs - 1; -1 stays "no slot"
+    got = oracle_mod.expand_blocks(np.array([[3, -1, 0]], dtype=np.int32), 4)
+    assert got.tolist() == [[12, 13, 14, 15, -1, -1, -1, -1, 0, 1, 2, 3]]
+    got = oracle_mod.expand_blocks(np.array([[1], [-1], [2]], dtype=np.int32), 2)
+    assert got.tolist() == [[2, 3], [-1, -1], [4, 5]]
+    same = np.array([[5, 2, -1, 7]], dtype=np.int32)
+    assert np.array_equal(oracle_mod.expand_blocks(same, 1), same)
+    bad = oracle_mod.expand_blocks(np.array([[-3]], dtype=np.int32), 3)
+    assert np.all(bad < -1)                 # stays invalid, not "no slot"
+
+
+@pytest.mark.parametrize("bs", [2, 4, 8])
+def test_block_oracle_matches_dense_bruteforce(oracle_mod, bs):
+    S, T = 64, 5
+    case = qi.random_case(70 + bs, T=T, S=S, Hq=4, Hkv=2, W=1)
+    rng = np.random.Generator(np.random.PCG64(71 + bs))
+    blocks = np.full((T, 6), -1, dtype=np.int32)
+    for t in range(T):
+        k = int(rng.integers(1, 6))
+        blocks[t, :k] = rng.choice(S // bs, size=k, replace=False)
+        blocks[t] = rng.permutation(blocks[t])
+    got = oracle_mod.prefill_blocks(case.q, case.k_cache, case.v_cache, blocks, bs, 0.0625)
+    member = np.zeros((T, S), dtype=bool)
+    for t in range(T):
+        for b in blocks[t][blocks[t] >= 0]:
+            member[t, b * bs:(b + 1) * bs] = True
+    dense = qi.Case("dense", case.q, case.k_cache, case.v_cache,
+                    np.where(member, np.arange(S)[None, :], -1).astype(np.int32), None,
+                    case.bases)
+    want = dense_masked_attention_fp64(dense, 0.0625)
+    assert rel_l2(got, want) < 1e-5

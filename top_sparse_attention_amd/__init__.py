@@ -27,6 +27,7 @@ __all__ = [
     "compact_slot_range", "partials_bytes", "new_partials", "sparse_attend_partial",
     "merge_partials", "decode_splits", "decode_workspace_bytes", "sparse_decode",
     "sparse_attend_fp8kv", "sparse_prefill_fp8kv", "gather_ceiling_fp8kv",
+    "compact_blocks", "sparse_prefill_blocks",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -128,6 +129,11 @@ def load_library():
     lib.qsa_sparse_prefill_fp8kv.restype = ctypes.c_int
     lib.qsa_sparse_prefill_fp8kv.argtypes = [P(BF16View), P(BF16View), P(BF16View), f32, f32,
                                              P(I32View), f32, P(BF16View), vp, sz, vp]
+    lib.qsa_compact_blocks.restype = ctypes.c_int
+    lib.qsa_compact_blocks.argtypes = [P(I32View), i64, ctypes.c_int32, vp, sz, vp]
+    lib.qsa_sparse_prefill_blocks.restype = ctypes.c_int
+    lib.qsa_sparse_prefill_blocks.argtypes = [P(BF16View), P(BF16View), P(BF16View), P(I32View),
+                                              ctypes.c_int32, f32, P(BF16View), vp, sz, vp]
     lib.qsa_gather_ceiling_fp8kv.restype = ctypes.c_int
     lib.qsa_gather_ceiling_fp8kv.argtypes = [P(BF16View), P(BF16View), i64, i64, vp, sz, vp, vp]
     _lib = lib
@@ -415,3 +421,38 @@ def gather_ceiling_fp8kv(k8: torch.Tensor, v8: torch.Tensor, workspace: torch.Te
         ctypes.byref(kv), ctypes.byref(vv), T, W, workspace.data_ptr(), workspace.numel(),
         sink.data_ptr(), _stream(k8.device)))
     return sink
+
+
+# ---------------------------------------------------------------- micro-blocks
+
+def compact_blocks(block_idx: torch.Tensor, S: int, block_size: int,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Compaction of micro-block selections into a workspace of width
+    W * block_size (block b = slots b*block_size .. +block_size-1)."""
+    T, W = block_idx.shape
+    if workspace is None:
+        workspace = new_workspace(T, W * block_size, block_idx.device)
+    bv = _i32_view(block_idx, "block_idx")
+    _raise_on(load_library().qsa_compact_blocks(
+        ctypes.byref(bv), S, block_size, workspace.data_ptr(), workspace.numel(),
+        _stream(workspace.device)))
+    return workspace
+
+
+def sparse_prefill_blocks(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_idx: torch.Tensor, block_size: int,
+                          scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    T, W = block_idx.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if workspace is None:
+        workspace = new_workspace(T, W * block_size, q.device)
+    qv, kv, vv, ov = (_bf16_view(q, "q"), _bf16_view(k_cache, "k_cache"),
+                      _bf16_view(v_cache, "v_cache"), _bf16_view(out, "out"))
+    bv = _i32_view(block_idx, "block_idx")
+    _raise_on(load_library().qsa_sparse_prefill_blocks(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), ctypes.byref(bv), block_size,
+        _default_scale(scale, q.shape[-1]), ctypes.byref(ov), workspace.data_ptr(),
+        workspace.numel(), _stream(q.device)))
+    return out

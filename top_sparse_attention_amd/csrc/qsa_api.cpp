@@ -193,8 +193,10 @@ qsa_status hip_fail(hipError_t e, const char *what) {
 }
 
 qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t S, int64_t lo,
-                           int64_t hi, void *ws, const qsa_workspace_map &m, hipStream_t stream) {
+                           int64_t hi, void *ws, const qsa_workspace_map &m, hipStream_t stream,
+                           int32_t block = 1) {
     qsa::CompactParams p{};
+    p.block = block;
     p.slot_idx = sl->data;
     p.stride_t = sl->stride[0];
     p.T = T;
@@ -380,6 +382,55 @@ qsa_status qsa_compact_slot_range(const qsa_i32_view *slot_idx, int64_t S, int64
     qsa_workspace_map m;
     if ((s = check_workspace(workspace, workspace_bytes, T, W, &m))) return s;
     return enqueue_compact(slot_idx, T, W, S, lo, hi, workspace, m, (hipStream_t)stream);
+}
+
+// Micro-block selections: check block_size and S, and give the list width.
+qsa_status check_blocks(int32_t block_size, int64_t S, int64_t W, int64_t *slots_wide) {
+    if (block_size < 1 || block_size > 64)
+        return fail(QSA_ERR_SHAPE, "block_size must be in [1, 64]");
+    if (S % block_size)
+        return fail(QSA_ERR_SHAPE, "S (%lld) must be a multiple of block_size (%d)", (long long)S,
+                    block_size);
+    if (W * block_size > kMax32) return fail(QSA_ERR_UNSUPPORTED, "W * block_size beyond int32");
+    *slots_wide = W * block_size;
+    return QSA_OK;
+}
+
+qsa_status qsa_compact_blocks(const qsa_i32_view *block_idx, int64_t S, int32_t block_size,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    if (!block_idx) return fail(QSA_ERR_NULL, "block_idx: view pointer is NULL");
+    const int64_t T = block_idx->size[0];
+    int64_t W = 0, Ws = 0;
+    qsa_status s = check_slots(block_idx, T, &W);
+    if (s) return s;
+    if (S < 0) return fail(QSA_ERR_SHAPE, "negative S");
+    if (S > kMax32) return fail(QSA_ERR_UNSUPPORTED, "S must fit in int32");
+    if ((s = check_blocks(block_size, S, W, &Ws))) return s;
+    qsa_workspace_map m;
+    if ((s = check_workspace(workspace, workspace_bytes, T, Ws, &m))) return s;
+    const int64_t nb = S / block_size;
+    return enqueue_compact(block_idx, T, W, nb, 0, nb, workspace, m, (hipStream_t)stream,
+                           block_size);
+}
+
+qsa_status qsa_sparse_prefill_blocks(const qsa_bf16_view *q, const qsa_bf16_view *k_cache,
+                                     const qsa_bf16_view *v_cache, const qsa_i32_view *block_idx,
+                                     int32_t block_size, float scale, qsa_bf16_view *out,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+    if (!block_idx) return fail(QSA_ERR_NULL, "block_idx: view pointer is NULL");
+    Problem pr;
+    qsa_status s = check_attend(q, k_cache, v_cache, out, block_idx->size[1], scale, &pr);
+    if (s) return s;
+    int64_t W = 0, Ws = 0;
+    if ((s = check_slots(block_idx, pr.T, &W))) return s;
+    if ((s = check_blocks(block_size, pr.S, W, &Ws))) return s;
+    qsa_workspace_map m;
+    if ((s = check_workspace(workspace, workspace_bytes, pr.T, Ws, &m))) return s;
+    if (pr.T == 0) return QSA_OK;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t nb = pr.S / block_size;
+    if ((s = enqueue_compact(block_idx, pr.T, W, nb, 0, nb, workspace, m, st, block_size))) return s;
+    return enqueue_attend(q, k_cache, v_cache, out, pr, scale, workspace, m, st);
 }
 
 qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S, void *workspace,

@@ -30,6 +30,8 @@ struct CompactParams {
     int64_t stride_t;
     int64_t T, W, S;
     int64_t lo, hi;      // entries in [lo, hi) are kept, stored as slot - lo
+    int32_t block;       // slots per entry: entry e selects slots e*block .. e*block+block-1
+                         // (S, lo, hi counted in entries of this size)
     int32_t key_bits;    // radix-sort key width: hi - lo - 1 < 2^(key_bits-1), plus one bit for padding
     int32_t *list;
     int64_t row_stride;

@@ -115,6 +115,8 @@ __device__ __forceinline__ int lds_off(int r, int chunk) {
 // One workgroup per token row.  Entries in [lo, hi) are kept and stored as
 // slot - lo (a cache shard's local numbering; lo = 0, hi = S keeps them
 // all); entries that are neither -1 nor in [0, S) are counted as invalid.
+// With block > 1 an entry names a micro-block of `block` consecutive slots
+// (S, lo, hi then count blocks) and expands to those slots in order.
 // The row is processed in chunks of
 // kSortChunk entries; each chunk's valid slots are radix-sorted on the top
 // kSortKeyBits bits of a key_bits-wide key (invalid entries carry the key
@@ -154,16 +156,19 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
 #pragma unroll
         for (int u = 0; u < kSortItemsPerThread; ++u) {
             const int pos = threadIdx.x * kSortItemsPerThread + u;
-            if (pos < nv) dst[n + pos] = (int32_t)key[u];
+            if (pos < nv)
+                for (int i = 0; i < p.block; ++i)
+                    dst[(int64_t)(n + pos) * p.block + i] = (int32_t)key[u] * p.block + i;
         }
         n += nv;
         bad += chunk_bad;
         __syncthreads();   // counters are reset by the next chunk
     }
-    const int padded = (n + kListPad - 1) / kListPad * kListPad;
-    for (int i = n + threadIdx.x; i < padded; i += kSortThreads) dst[i] = -1;
+    const int slots = n * p.block;
+    const int padded = (slots + kListPad - 1) / kListPad * kListPad;
+    for (int i = slots + threadIdx.x; i < padded; i += kSortThreads) dst[i] = -1;
     if (threadIdx.x == 0) {
-        p.count[t] = n;
+        p.count[t] = slots;
         p.n_bad[t] = bad;
     }
 }
