@@ -60,6 +60,11 @@ def _load():
         lib.qsa_oracle_prefill_fp8kv.restype = ctypes.c_int
         lib.qsa_oracle_e4m3_to_float.argtypes = [ctypes.c_uint8]
         lib.qsa_oracle_e4m3_to_float.restype = ctypes.c_float
+        lib.qsa_oracle_indexer_scores.argtypes = [vp, i64, i64, vp, i64, i64, i64, i32, i32,
+                                                  vp, i32]
+        lib.qsa_oracle_indexer_scores.restype = ctypes.c_int
+        lib.qsa_oracle_indexer_select.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp]
+        lib.qsa_oracle_indexer_select.restype = ctypes.c_int
         lib.qsa_oracle_default_threads.argtypes = []
         lib.qsa_oracle_default_threads.restype = ctypes.c_int
         _lib = lib
@@ -193,4 +198,43 @@ def _prefill(q, k_cache, v_cache, slot_idx, scale, rows, nthreads, fp8_scales):
         raise ValueError("slot_idx holds an entry that is neither -1 nor in [0, S)")
     if rc != OK:
         raise ValueError(f"oracle prefill failed with status {rc}")
+    return out
+
+
+def indexer_scores(iq: np.ndarray, ik: np.ndarray, nthreads: int = 0) -> np.ndarray:
+    """score[t, c] = sum_h max(0, iq[t,h] . ik[c]) in FP32.  iq is [T, H, D] and
+    ik [C, D] (or [C, 1, D]), both uint16 BF16 bits with unit inner stride."""
+    if ik.ndim == 3:
+        ik = ik[:, 0, :]
+    if iq.dtype != np.uint16 or ik.dtype != np.uint16 or iq.ndim != 3 or ik.ndim != 2:
+        raise TypeError("iq must be [T, H, D] and ik [C, D] uint16 (bf16 bits)")
+    T, H, D = iq.shape
+    C = ik.shape[0]
+    if ik.shape[1] != D:
+        raise ValueError("head dims disagree")
+    out = np.empty((T, C), dtype=np.float32)
+    qs, ks = _elem_strides(iq), _elem_strides(ik)
+    if (D > 1 and (qs[2] != 1 or ks[1] != 1)):
+        raise ValueError("unit inner stride required")
+    rc = _load().qsa_oracle_indexer_scores(_ptr(iq), qs[0], qs[1], _ptr(ik), ks[0], T, C, H, D,
+                                           _ptr(out), int(nthreads))
+    if rc != OK:
+        raise ValueError(f"oracle indexer scores failed with status {rc}")
+    return out
+
+
+def indexer_select(scores: np.ndarray, positions: np.ndarray, slot_of_pos: np.ndarray,
+                   budget: int) -> np.ndarray:
+    """Top-`budget` complete causal blocks per query (ties to the lower block),
+    expanded to slots with the causal tail; returns int32 [T, 4*budget + 3]."""
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    slot_of_pos = np.ascontiguousarray(slot_of_pos, dtype=np.int32)
+    T, C = scores.shape
+    out = np.empty((T, 4 * budget + 3), dtype=np.int32)
+    rc = _load().qsa_oracle_indexer_select(_ptr(scores), T, C, _ptr(positions),
+                                           _ptr(slot_of_pos), slot_of_pos.size, int(budget),
+                                           _ptr(out))
+    if rc != OK:
+        raise ValueError(f"oracle indexer select failed with status {rc}")
     return out

@@ -280,3 +280,117 @@ int qsa_oracle_default_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * QSA indexer and Top-K selection (the step before main attention; page
+ * section "Why QSA is the awkward part, in numbers": a multi-query indexer
+ * with 4 query heads sharing 1 key head, head dim 128, compression ratio 4,
+ * a fixed budget; section "Nine tests that passed, ...": causal tails of 0-3
+ * tokens).  Readings (the page gives the structure, not the formulas):
+ *  - one index key per compressed block of 4 consecutive positions;
+ *  - score(t, c) = sum_h max(0, iq[t,h] . ik[c]), FP32, d order then h order;
+ *  - a query at position p ranks the complete blocks before it
+ *    (4c + 3 <= p) and keeps the `budget` best, ties to the lower c;
+ *  - its selection is the positions of the kept blocks (ascending c, each
+ *    block's 4 positions in order) followed by its r = (p+1) % 4 tail
+ *    positions p-r+1..p, mapped to physical slots by slot_of_pos, then -1 up
+ *    to the row width 4*budget + 3.
+ */
+int qsa_oracle_indexer_scores(const uint16_t *iq, int64_t q_st, int64_t q_sh,
+                              const uint16_t *ik, int64_t k_st, int64_t T,
+                              int64_t C, int32_t H, int32_t D, float *scores,
+                              int32_t nthreads)
+{
+    if (T < 0 || C < 0 || H <= 0 || D <= 0)
+        return ORACLE_BAD_SHAPE;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t c = 0; c < C; ++c) {
+            float total = 0.0f;
+            for (int32_t h = 0; h < H; ++h) {
+                const uint16_t *qr = iq + t * q_st + (int64_t)h * q_sh;
+                const uint16_t *kr = ik + c * k_st;
+                float dot = 0.0f;
+                for (int32_t d = 0; d < D; ++d)
+                    dot += bf16_to_float(qr[d]) * bf16_to_float(kr[d]);
+                total += dot > 0.0f ? dot : 0.0f;
+            }
+            scores[t * C + c] = total;
+        }
+    }
+    return ORACLE_OK;
+}
+
+typedef struct {
+    float score;
+    int32_t block;
+} ranked;
+
+/* Better first: higher score, then lower block index. */
+static int rank_order(const void *a, const void *b)
+{
+    const ranked *x = (const ranked *)a, *y = (const ranked *)b;
+    if (x->score != y->score)
+        return x->score > y->score ? -1 : 1;
+    return (x->block > y->block) - (x->block < y->block);
+}
+
+static int int_order(const void *a, const void *b)
+{
+    const int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+int qsa_oracle_indexer_select(const float *scores, int64_t T, int64_t C,
+                              const int32_t *positions,
+                              const int32_t *slot_of_pos, int64_t L,
+                              int32_t budget, int32_t *slot_idx)
+{
+    if (T < 0 || C < 0 || budget < 0)
+        return ORACLE_BAD_SHAPE;
+    const int64_t width = 4 * (int64_t)budget + 3;
+    ranked *cand = (ranked *)malloc(sizeof(ranked) * (size_t)(C > 0 ? C : 1));
+    int32_t *kept = (int32_t *)malloc(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
+    if (!cand || !kept) {
+        free(cand);
+        free(kept);
+        return ORACLE_NO_MEMORY;
+    }
+    int status = ORACLE_OK;
+    for (int64_t t = 0; t < T && status == ORACLE_OK; ++t) {
+        const int64_t p = positions[t];
+        const int64_t eligible = (p + 1) / 4 < C ? (p + 1) / 4 : C;
+        if (p < 0 || p >= L) {
+            status = ORACLE_BAD_SHAPE;
+            break;
+        }
+        for (int64_t c = 0; c < eligible; ++c) {
+            cand[c].score = scores[t * C + c];
+            cand[c].block = (int32_t)c;
+        }
+        qsort(cand, (size_t)eligible, sizeof(ranked), rank_order);
+        const int64_t n = eligible < budget ? eligible : budget;
+        for (int64_t i = 0; i < n; ++i)
+            kept[i] = cand[i].block;
+        qsort(kept, (size_t)n, sizeof(int32_t), int_order);
+        int32_t *row = slot_idx + t * width;
+        int64_t w = 0;
+        for (int64_t i = 0; i < n; ++i)
+            for (int j = 0; j < 4; ++j)
+                row[w++] = slot_of_pos[4 * (int64_t)kept[i] + j];
+        const int64_t r = (p + 1) % 4;
+        for (int64_t pos = p - r + 1; pos <= p; ++pos)
+            row[w++] = slot_of_pos[pos];
+        while (w < width)
+            row[w++] = -1;
+    }
+    free(cand);
+    free(kept);
+    return status;
+}

@@ -355,3 +355,63 @@ def test_block_oracle_matches_dense_bruteforce(oracle_mod, bs):
                     case.bases)
     want = dense_masked_attention_fp64(dense, 0.0625)
     assert rel_l2(got, want) < 1e-5
+
+
+# ---------------------------------------------------------------- indexer + Top-K
+
+def _slot_map(spec):
+    kind, *args = spec.split(":")
+    n = int(args[0])
+    if kind == "identity":
+        return np.arange(n, dtype=np.int32)
+    a, b = int(args[1]), int(args[2])
+    return (a * np.arange(n) + b).astype(np.int32)
+
+
+def test_indexer_select_golden_cases(oracle_mod):
+    with open(os.path.join(GOLDEN, "indexer_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        scores = np.array([c["scores"]], dtype=np.float32)
+        row = oracle_mod.indexer_select(scores, np.array([c["p"]]), _slot_map(c["slot_of_pos"]),
+                                        c["budget"])
+        assert row[0].tolist() == c["row"], c["why"]
+
+
+def test_indexer_scores_match_float64_einsum(oracle_mod):
+    rng = np.random.Generator(np.random.PCG64(80))
+    iq = qi.normal_bf16(rng, (9, 4, 128))
+    ik = qi.normal_bf16(rng, (37, 128))
+    got = oracle_mod.indexer_scores(iq, ik)
+    dots = np.einsum("thd,cd->thc", f32(iq).astype(np.float64), f32(ik).astype(np.float64))
+    want = np.maximum(dots, 0).sum(axis=1)
+    np.testing.assert_allclose(got, want, rtol=2e-5, atol=1e-4)
+    # ReLU matters: the plain sum of the dot products differs
+    assert not np.allclose(got, dots.sum(axis=1), rtol=1e-3)
+
+
+def test_indexer_select_properties(oracle_mod):
+    rng = np.random.Generator(np.random.PCG64(81))
+    T, C, budget = 40, 64, 9
+    scores = rng.integers(0, 6, size=(T, C)).astype(np.float32)      # many ties
+    positions = rng.integers(0, 4 * C, size=T).astype(np.int32)
+    slot_of_pos = rng.permutation(4 * C).astype(np.int32)
+    inv = np.argsort(slot_of_pos)
+    rows = oracle_mod.indexer_select(scores, positions, slot_of_pos, budget)
+    for t in range(T):
+        p = int(positions[t])
+        eligible = min((p + 1) // 4, C)
+        r = (p + 1) % 4
+        n = min(eligible, budget)
+        row = rows[t]
+        assert np.all(row[4 * n + r:] == -1) and np.all(row[:4 * n + r] >= 0)
+        pos = inv[row[:4 * n + r]]
+        blocks = pos[:4 * n].reshape(n, 4) // 4
+        assert np.all(blocks == blocks[:, :1]) and np.all(np.diff(blocks[:, 0]) > 0)
+        assert np.all(blocks[:, 0] * 4 + 3 <= p)
+        assert pos[4 * n:].tolist() == list(range(p - r + 1, p + 1))
+        chosen = set(blocks[:, 0].tolist())
+        worst = min(((scores[t, c], -c) for c in chosen), default=None)
+        for c in range(eligible):
+            if c not in chosen:
+                assert (scores[t, c], -c) < worst
