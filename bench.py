@@ -6,7 +6,9 @@ attention (qsa_sparse_attend), both through the C ABI on torch's current
 stream.  Other workloads: `decode_batch` runs the split path (compaction,
 qsa_sparse_attend_partial, qsa_merge_partials), `long_prefill_fp8kv` the
 FP8 E4M3 KV-cache variant (qsa_sparse_attend_fp8kv) and `long_prefill_block4`
-micro-block selections (qsa_compact_blocks, then qsa_sparse_attend).  The default workload is the long prefill of the page "Qwen4-Exp QSA
+micro-block selections (qsa_compact_blocks, then qsa_sparse_attend);
+`indexed_long_prefill` makes the selection inside the step with the QSA
+indexer and Top-K (qsa_indexer_topk) before the same two passes.  The default workload is the long prefill of the page "Qwen4-Exp QSA
 comes to Huawei's Ascend: inside SGLang's opt-in CANN prefill PR" (section
 "Nine tests that passed, ..."): 7,810 query tokens, a 65,536-slot cache,
 2,051 selected slots per token, (Hq, Hkv) = (16, 2), D = 256, BF16.
@@ -42,7 +44,8 @@ def parse():
     ap.add_argument("--workload", default="long_prefill",
                     choices=["tiny", "edge_mix", "long_prefill", "two_request",
                              "max_cache_6_1", "max_cache_3_1", "decode_batch",
-                             "long_prefill_fp8kv", "long_prefill_block4"])
+                             "long_prefill_fp8kv", "long_prefill_block4",
+                             "indexed_long_prefill"])
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="token rows of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -112,6 +115,21 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # Indexed workloads make their selection on the GPU first (QSA indexer
+    # scores + Top-K), inside the step.
+    indexed = "iq" in case.info
+    if indexed:
+        to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        iq = to_dev(case.info["iq"].view(np.int16)).view(torch.bfloat16)
+        ik = to_dev(case.info["ik"].view(np.int16)).view(torch.bfloat16)
+        ipos, isop = to_dev(case.info["positions"]), to_dev(case.info["slot_of_pos"])
+        iscores = torch.empty((T, ik.shape[0]), dtype=torch.float32, device=dev)
+        budget = case.info["budget"]
+
+    def select():
+        if indexed:
+            qsa.indexer_topk(iq, ik, ipos, isop, budget, scores=iscores, out=sl)
+
     # Few-token workloads run the split path (qsa_sparse_decode's steps):
     # compaction, split attention into FP32 partials, merge.
     split = args.workload == "decode_batch"
@@ -137,6 +155,7 @@ def main():
             qsa.merge_partials(parts, splits, T, Hq, out=out)
 
     def step():
+        select()
         compact()
         attend()
         finish()
@@ -150,9 +169,12 @@ def main():
     t1 = torch.cuda.Event(enable_timing=True)
     a0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     a1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    s1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     torch.cuda.synchronize()
     t0.record()
     for i in range(K):
+        select()
+        s1[i].record()
         compact()
         a0[i].record()
         attend()
@@ -164,6 +186,8 @@ def main():
     ms_step = ms_total / K
     attn_ms = [a0[i].elapsed_time(a1[i]) for i in range(K)]
     attn_avg = float(np.mean(attn_ms))
+    select_ms = float(np.mean([(t0 if i == 0 else a1[i - 1]).elapsed_time(s1[i])
+                               for i in range(K)])) if indexed else None
 
     # Gather ceiling: the same rows, loads and launch shape with no arithmetic.
     sink = torch.empty(T * Hkv, dtype=torch.int32, device=dev)
@@ -179,8 +203,15 @@ def main():
     torch.cuda.synchronize()
     ceil_ms = c0.elapsed_time(c1) / K
 
-    valid = (case.slot_idx >= 0) & (case.slot_idx < S // bs)
-    n_t = valid.sum(axis=1).astype(np.int64) * bs      # selected slots per token
+    if indexed:
+        # 4 positions per kept block (at most `budget` complete causal blocks)
+        # plus the causal tail; fixed by the positions alone.
+        p_ = case.info["positions"].astype(np.int64)
+        n_t = 4 * np.minimum(np.minimum((p_ + 1) // 4, case.info["ik"].shape[0]), budget) \
+            + (p_ + 1) % 4
+    else:
+        valid = (case.slot_idx >= 0) & (case.slot_idx < S // bs)
+        n_t = valid.sum(axis=1).astype(np.int64) * bs      # selected slots per token
     pairs = int(n_t.sum()) * Hq
     # Algorithmic bytes of one attention launch: every selected K and V row of
     # every (token, KV head) once, its slot index, Q in and O out.
@@ -205,12 +236,28 @@ def main():
                               rows=rows_, nthreads=nthreads)
 
     rows = qi.sample_rows(T, 16, seed=11)
-    want = run_oracle(rows)
-    got = bf16_tensor_to_f32(out[torch.as_tensor(rows, device=dev)])
-    parity = gate(got, want, n_t[rows] == 0)
+    if indexed:
+        # The oracle makes its own selection for the sampled rows; rows whose
+        # GPU selection is identical are checked against the oracle's
+        # attention over that selection (near-tie cuts may differ).
+        o_sel = oracle.indexer_select(oracle.indexer_scores(case.info["iq"][rows],
+                                                            case.info["ik"]),
+                                      case.info["positions"][rows], case.info["slot_of_pos"],
+                                      budget)
+        same = np.all(sl[torch.as_tensor(rows, device=dev)].cpu().numpy() == o_sel, axis=1)
+        rows_same = rows[same]
+        want = oracle.prefill(np.ascontiguousarray(case.q[rows_same]), case.k_cache,
+                              case.v_cache, np.ascontiguousarray(o_sel[same]), scale)
+        got = bf16_tensor_to_f32(out[torch.as_tensor(rows_same, device=dev)])
+        parity = gate(got, want, n_t[rows_same] == 0)
+        parity["selection_rows_identical"] = f"{int(same.sum())}/{rows.size}"
+    else:
+        want = run_oracle(rows)
+        got = bf16_tensor_to_f32(out[torch.as_tensor(rows, device=dev)])
+        parity = gate(got, want, n_t[rows] == 0)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not indexed:
         cpu_rows = qi.sample_rows(T, min(args.cpu_rows, T), seed=12)
         threads = oracle.default_threads()
         c_t0 = time.perf_counter()
@@ -243,6 +290,7 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": cpu,
         "attend_kernel_ms": attn_avg,
+        "indexer_topk_ms": select_ms,
         "attend_kernel_ms_min": float(np.min(attn_ms)),
         "gather_GBps": gather_bytes / (attn_avg * 1e-3) / 1e9,
         "gather_ceiling": {"ms": ceil_ms, "GBps": gather_bytes / (ceil_ms * 1e-3) / 1e9},

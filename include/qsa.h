@@ -313,6 +313,48 @@ qsa_status qsa_gather_ceiling_fp8kv(const qsa_fp8_view *k_cache,
                                     size_t workspace_bytes, uint32_t *sink,
                                     void *stream);
 
+/*
+ * QSA indexer and Top-K selection: the step that produces slot_idx (page,
+ * section "Why QSA is the awkward part, in numbers": a multi-query indexer,
+ * 4 query heads sharing 1 key head, head dim 128, compression ratio 4, a fixed
+ * budget; section "Nine tests that passed, ...": causal tails of 0-3
+ * positions).  The page gives the structure, not the formulas; readings:
+ *  - ik holds one key per block of 4 consecutive positions of the request,
+ *    block c = positions 4c .. 4c+3, so C = L / 4 (rounded either way);
+ *  - score(t, c) = sum over the 4 heads of max(0, iq[t,h] . ik[c]) (FP32
+ *    accumulation of BF16 products);
+ *  - a query at position p = positions[t] ranks the complete blocks before it
+ *    (4c + 3 <= p) and keeps the `budget` best, ties to the lower c;
+ *  - its row of slot_idx [T, 4*budget + 3] lists the positions of the kept
+ *    blocks (ascending c, 4 each), then its r = (p+1) % 4 tail positions
+ *    p-r+1 .. p, each mapped through slot_of_pos [L] (the request's
+ *    position -> physical slot table), then -1.  budget = 512 gives the
+ *    2,051-wide rows of the long prefill.
+ * Positions outside [0, L) give an all -1 row.  iq is [T, 4, 128], ik
+ * [C, 1, 128] (BF16, rows 16-byte aligned); positions, slot_of_pos, scores
+ * and slot_idx are device memory.  scores is caller-owned FP32 [T, C]
+ * scratch (qsa_indexer_scores_bytes); entries past a query's causal limit are
+ * left unspecified.
+ */
+size_t qsa_indexer_scores_bytes(int64_t T, int64_t C);
+
+qsa_status qsa_indexer_scores(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
+                              const int32_t *positions, float *scores,
+                              size_t scores_bytes, void *stream);
+
+qsa_status qsa_indexer_select(const float *scores, size_t scores_bytes,
+                              int64_t T, int64_t C, const int32_t *positions,
+                              const int32_t *slot_of_pos, int64_t L,
+                              int32_t budget, qsa_i32_view *slot_idx,
+                              void *stream);
+
+/* qsa_indexer_scores followed by qsa_indexer_select. */
+qsa_status qsa_indexer_topk(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
+                            const int32_t *positions,
+                            const int32_t *slot_of_pos, int64_t L,
+                            int32_t budget, float *scores, size_t scores_bytes,
+                            qsa_i32_view *slot_idx, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

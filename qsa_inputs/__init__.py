@@ -303,6 +303,43 @@ def long_prefill_blocks(seed: int = 107, block_size: int = 4) -> Case:
                             {"seed": seed, "block_size": block_size})
 
 
+INDEX_HEADS = 4
+INDEX_DIM = 128
+
+
+def indexed_case(seed: int, L: int, T: int, Hq: int, Hkv: int, budget: int,
+                 integer_keys: bool = False, name: str = "indexed") -> Case:
+    """A request of L positions whose last T are being prefilled, with QSA
+    indexer inputs: iq [T, 4, 128] and ik [C = ceil(L/4), 1, 128] (one key
+    per block of 4 positions), positions [T] = L-T .. L-1, and a seeded
+    position -> slot table (page size 1) into an S = L slot cache.  With
+    integer_keys the indexer values are small integers, so every score is
+    exact in FP32.  slot_idx is left empty (W = 4*budget + 3, all -1): it is
+    what the indexer produces."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    C = -(-L // 4)
+    if integer_keys:
+        iq = bf16_bits(rng.integers(-2, 3, size=(T, INDEX_HEADS, INDEX_DIM)).astype(np.float32))
+        ik = bf16_bits(rng.integers(-2, 3, size=(C, 1, INDEX_DIM)).astype(np.float32))
+    else:
+        iq = normal_bf16(rng, (T, INDEX_HEADS, INDEX_DIM))
+        ik = normal_bf16(rng, (C, 1, INDEX_DIM))
+    positions = (L - T + np.arange(T)).astype(np.int32)
+    slot_of_pos = rng.permutation(L).astype(np.int32)
+    sel = np.full((T, 4 * budget + 3), -1, dtype=np.int32)
+    case = _contiguous_case(name, rng, T, L, Hq, Hkv, sel, None,
+                            {"seed": seed, "budget": budget})
+    case.info.update(iq=iq, ik=ik, positions=positions, slot_of_pos=slot_of_pos)
+    return case
+
+
+def indexed_long_prefill(seed: int = 108) -> Case:
+    """The long prefill with its selection made by the indexer: a 65,536-token
+    request whose last 7,810 tokens are prefilled, (16,2), budget 512 blocks
+    (2,048 positions + a causal tail of up to 3 = 2,051-wide rows)."""
+    return indexed_case(seed, 65536, 7810, 16, 2, 512, name="indexed_long_prefill")
+
+
 DECODE_REQUESTS = 16
 
 
@@ -345,6 +382,7 @@ WORKLOADS = {
     "decode_batch": decode_batch,
     "long_prefill_fp8kv": lambda seed=103: with_fp8_kv(long_prefill(seed)),
     "long_prefill_block4": long_prefill_blocks,
+    "indexed_long_prefill": indexed_long_prefill,
 }
 
 

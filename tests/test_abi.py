@@ -207,3 +207,26 @@ def test_split_entry_points_reject_bad_arguments():
             "QSA_ERR_SHAPE"
     assert qsa.STATUS_NAMES[lib.qsa_sparse_decode(
         r(q), r(k), r(v), r(s), 0.0625, r(o), ws, 16, None)] == "QSA_ERR_WORKSPACE"
+
+
+@host_only
+def test_indexer_entry_points_reject_bad_arguments():
+    lib = _lib()
+    r = ctypes.byref
+    iq = view((8, 4, 128), (512, 128, 1), FAKE)
+    ik = view((16, 1, 128), (128, 128, 1), FAKE + (1 << 24))
+    out = ivew((8, 4 * 5 + 3), (23, 1), FAKE + (2 << 24))
+    pos, sop, sc = FAKE + (3 << 24), FAKE + (4 << 24), FAKE + (5 << 24)
+    big = 1 << 30
+
+    def topk(iq_=iq, ik_=ik, L=64, budget=5, out_=out, sc_bytes=big):
+        return qsa.STATUS_NAMES[lib.qsa_indexer_topk(r(iq_), r(ik_), pos, sop, L, budget, sc,
+                                                     sc_bytes, r(out_), None)]
+
+    assert topk(iq_=view((8, 2, 128), (256, 128, 1), FAKE)) == "QSA_ERR_UNSUPPORTED"
+    assert topk(ik_=view((16, 1, 64), (64, 64, 1), FAKE)) == "QSA_ERR_UNSUPPORTED"
+    assert topk(L=100) == "QSA_ERR_SHAPE"                    # 16 keys cannot cover 100 positions
+    assert topk(budget=0) == "QSA_ERR_SHAPE"
+    assert topk(out_=ivew((8, 22), (22, 1), FAKE + (2 << 24))) == "QSA_ERR_SHAPE"
+    assert topk(sc_bytes=8 * 16 * 4 - 1) == "QSA_ERR_WORKSPACE"
+    assert qsa.indexer_scores.__doc__ and lib.qsa_indexer_scores_bytes(8, 16) == 512

@@ -1,0 +1,154 @@
+"""GPU parity of the QSA indexer and Top-K selection against the oracle.
+
+Readings (page "Qwen4-Exp QSA comes to Huawei's Ascend", section "Why QSA is
+the awkward part, in numbers", and the causal tails of section "Nine tests
+that passed, ..."): score(t, c) = sum over 4 heads of max(0, iq . ik[c]);
+the top `budget` complete causal blocks, ties to the lower block; positions
+of those blocks, then the tail, mapped to slots.
+
+The selection is an integer result decided by floating point.  With integer
+index values every score is exact in FP32 on both sides, so the selections
+must be identical, ties included.  With random values the scores agree to
+rounding and the selections may differ only among blocks whose scores lie
+within that rounding of the cut.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_inputs as qi
+import top_sparse_attention_amd as qsa
+from qsa_testutil import bf16_tensor_to_f32, empty_row_mask, gate, upload
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def dev_inputs(case):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    iq = t(case.info["iq"].view(np.int16)).view(torch.bfloat16)
+    ik = t(case.info["ik"].view(np.int16)).view(torch.bfloat16)
+    return iq, ik, t(case.info["positions"]), t(case.info["slot_of_pos"])
+
+
+def run_indexer(case):
+    iq, ik, pos, sop = dev_inputs(case)
+    scores = torch.full((case.T, ik.shape[0]), float("nan"), dtype=torch.float32, device=DEV)
+    sel = qsa.indexer_topk(iq, ik, pos, sop, case.info["budget"], scores=scores)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy(), sel.cpu().numpy()
+
+
+def limits(case):
+    C = case.info["ik"].shape[0]
+    return np.minimum((case.info["positions"].astype(np.int64) + 1) // 4, C)
+
+
+@pytest.mark.parametrize("L,T,budget", [(8192, 100, 64), (4099, 37, 300), (777, 50, 8)])
+def test_integer_scores_and_selection_are_exact(L, T, budget):
+    case = qi.indexed_case(1100 + L, L=L, T=T, Hq=8, Hkv=1, budget=budget, integer_keys=True)
+    # spread the queries over the whole request, including the first positions
+    case.info["positions"][:] = np.sort(np.random.Generator(np.random.PCG64(1101))
+                                        .choice(L, size=T, replace=False)).astype(np.int32)
+    scores, sel = run_indexer(case)
+    want = oracle.indexer_scores(case.info["iq"], case.info["ik"])
+    lim = limits(case)
+    for t in range(T):
+        np.testing.assert_array_equal(scores[t, :lim[t]], want[t, :lim[t]])
+    want_sel = oracle.indexer_select(want, case.info["positions"], case.info["slot_of_pos"],
+                                     budget)
+    np.testing.assert_array_equal(sel, want_sel)
+
+
+def test_random_scores_match_and_selection_differs_only_at_the_cut():
+    case = qi.indexed_case(1110, L=16384, T=64, Hq=8, Hkv=1, budget=256)
+    scores, sel = run_indexer(case)
+    want = oracle.indexer_scores(case.info["iq"], case.info["ik"])
+    lim = limits(case)
+    budget = case.info["budget"]
+    inv = np.argsort(case.info["slot_of_pos"])
+    for t in range(case.T):
+        n = lim[t]
+        np.testing.assert_allclose(scores[t, :n], want[t, :n], rtol=1e-5, atol=2e-4)
+        got_blocks = set((inv[sel[t][:4 * min(n, budget)]] // 4).tolist())
+        ref = oracle.indexer_select(want[t:t + 1], case.info["positions"][t:t + 1],
+                                    case.info["slot_of_pos"], budget)[0]
+        ref_blocks = set((inv[ref[:4 * min(n, budget)]] // 4).tolist())
+        assert len(got_blocks) == min(n, budget)
+        diff = got_blocks ^ ref_blocks
+        if diff:
+            cut = np.sort(want[t, :n])[::-1][budget - 1]
+            assert all(abs(want[t, c] - cut) <= 4e-4 + 2e-5 * abs(cut) for c in diff)
+
+
+def test_edge_positions_tails_and_invalid_rows():
+    L, budget = 64, 3
+    case = qi.indexed_case(1120, L=L, T=12, Hq=4, Hkv=1, budget=budget, integer_keys=True)
+    case.info["positions"][:] = [0, 1, 2, 3, 4, 6, 7, 11, 62, 63, -1, 64]
+    scores, sel = run_indexer(case)
+    want = oracle.indexer_scores(case.info["iq"], case.info["ik"])
+    valid = slice(0, 10)
+    want_sel = oracle.indexer_select(want[valid], case.info["positions"][valid],
+                                     case.info["slot_of_pos"], budget)
+    np.testing.assert_array_equal(sel[valid], want_sel)
+    assert np.all(sel[10:] == -1)           # positions outside [0, L)
+
+
+def test_rows_longer_than_the_lds_stage():
+    """C > 16384 index keys: the select kernel reads scores from memory."""
+    case = qi.indexed_case(1130, L=80000, T=6, Hq=4, Hkv=1, budget=1000, integer_keys=True)
+    scores, sel = run_indexer(case)
+    want = oracle.indexer_scores(case.info["iq"], case.info["ik"])
+    want_sel = oracle.indexer_select(want, case.info["positions"], case.info["slot_of_pos"],
+                                     1000)
+    np.testing.assert_array_equal(sel, want_sel)
+
+
+def test_indexer_then_attention_end_to_end():
+    """Selection by the indexer feeds the prefill; with exact scores the
+    oracle selects the same slots, so its attention is the reference."""
+    case = qi.indexed_case(1140, L=6000, T=80, Hq=24, Hkv=2, budget=100, integer_keys=True)
+    iq, ik, pos, sop = dev_inputs(case)
+    sel = qsa.indexer_topk(iq, ik, pos, sop, 100)
+    q, k, v, _ = upload(case, DEV)
+    out = qsa.sparse_prefill(q, k, v, sel)
+    torch.cuda.synchronize()
+    want_sel = oracle.indexer_select(oracle.indexer_scores(case.info["iq"], case.info["ik"]),
+                                     case.info["positions"], case.info["slot_of_pos"], 100)
+    np.testing.assert_array_equal(sel.cpu().numpy(), want_sel)
+    want = oracle.prefill(case.q, case.k_cache, case.v_cache, want_sel, 1.0 / 16.0)
+    gate(bf16_tensor_to_f32(out), want, empty_row_mask(want_sel, case.S))
+
+
+def test_indexed_long_prefill_sampled_rows():
+    case = qi.indexed_long_prefill()
+    budget = case.info["budget"]
+    iq, ik, pos, sop = dev_inputs(case)
+    sel = qsa.indexer_topk(iq, ik, pos, sop, budget)
+    torch.cuda.synchronize()
+    rows = qi.sample_rows(case.T, 32)
+    sel_np = sel.cpu().numpy()
+    want_scores = oracle.indexer_scores(case.info["iq"][rows], case.info["ik"])
+    inv = np.argsort(case.info["slot_of_pos"])
+    lim = limits(case)
+    for i, t in enumerate(rows):
+        n = int(lim[t])
+        row = sel_np[t]
+        r = (int(case.info["positions"][t]) + 1) % 4
+        assert np.all(row[4 * budget + r:] == -1)
+        chosen = set((inv[row[:4 * budget]] // 4).tolist())
+        assert len(chosen) == budget and max(chosen) < n
+        cut = np.sort(want_scores[i, :n])[::-1][budget - 1]
+        assert all(want_scores[i, c] >= cut - 1e-3 for c in chosen)
+    # The attention at full size on the oracle's own selection for these rows.
+    want_sel = oracle.indexer_select(want_scores, case.info["positions"][rows],
+                                     case.info["slot_of_pos"], budget)
+    q, k, v, _ = upload(case, DEV)
+    out = qsa.sparse_prefill(q[torch.as_tensor(rows, device=DEV)].contiguous(), k, v,
+                             torch.from_numpy(want_sel).to(DEV))
+    torch.cuda.synchronize()
+    want = oracle.prefill(np.ascontiguousarray(case.q[rows]), case.k_cache, case.v_cache,
+                          want_sel, 1.0 / 16.0)
+    gate(bf16_tensor_to_f32(out), want, empty_row_mask(want_sel, case.S))

@@ -27,7 +27,8 @@ __all__ = [
     "compact_slot_range", "partials_bytes", "new_partials", "sparse_attend_partial",
     "merge_partials", "decode_splits", "decode_workspace_bytes", "sparse_decode",
     "sparse_attend_fp8kv", "sparse_prefill_fp8kv", "gather_ceiling_fp8kv",
-    "compact_blocks", "sparse_prefill_blocks",
+    "compact_blocks", "sparse_prefill_blocks", "indexer_scores", "indexer_select",
+    "indexer_topk",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -134,6 +135,16 @@ def load_library():
     lib.qsa_sparse_prefill_blocks.restype = ctypes.c_int
     lib.qsa_sparse_prefill_blocks.argtypes = [P(BF16View), P(BF16View), P(BF16View), P(I32View),
                                               ctypes.c_int32, f32, P(BF16View), vp, sz, vp]
+    lib.qsa_indexer_scores_bytes.restype = sz
+    lib.qsa_indexer_scores_bytes.argtypes = [i64, i64]
+    lib.qsa_indexer_scores.restype = ctypes.c_int
+    lib.qsa_indexer_scores.argtypes = [P(BF16View), P(BF16View), vp, vp, sz, vp]
+    lib.qsa_indexer_select.restype = ctypes.c_int
+    lib.qsa_indexer_select.argtypes = [vp, sz, i64, i64, vp, vp, i64, ctypes.c_int32,
+                                       P(I32View), vp]
+    lib.qsa_indexer_topk.restype = ctypes.c_int
+    lib.qsa_indexer_topk.argtypes = [P(BF16View), P(BF16View), vp, vp, i64, ctypes.c_int32, vp,
+                                     sz, P(I32View), vp]
     lib.qsa_gather_ceiling_fp8kv.restype = ctypes.c_int
     lib.qsa_gather_ceiling_fp8kv.argtypes = [P(BF16View), P(BF16View), i64, i64, vp, sz, vp, vp]
     _lib = lib
@@ -455,4 +466,65 @@ def sparse_prefill_blocks(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
         ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), ctypes.byref(bv), block_size,
         _default_scale(scale, q.shape[-1]), ctypes.byref(ov), workspace.data_ptr(),
         workspace.numel(), _stream(q.device)))
+    return out
+
+
+# ---------------------------------------------------------------- indexer + Top-K
+
+def _bf16_any(t: torch.Tensor, name: str) -> BF16View:
+    if t.dtype != torch.bfloat16 or t.dim() != 3:
+        raise TypeError(f"{name} must be a 3-D bfloat16 tensor")
+    return BF16View(t.data_ptr() if t.numel() else 0, (ctypes.c_int64 * 3)(*t.shape),
+                    (ctypes.c_int64 * 3)(*t.stride()))
+
+
+def _check_i32_1d(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous 1-D int32 tensor")
+
+
+def indexer_scores(iq: torch.Tensor, ik: torch.Tensor, positions: torch.Tensor,
+                   scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """FP32 [T, C] scores sum_h max(0, iq[t,h] . ik[c]); iq [T,4,128], ik [C,1,128]."""
+    _check_i32_1d(positions, "positions")
+    T, C = iq.shape[0], ik.shape[0]
+    if scores is None:
+        scores = torch.empty((T, C), dtype=torch.float32, device=iq.device)
+    _raise_on(load_library().qsa_indexer_scores(
+        ctypes.byref(_bf16_any(iq, "iq")), ctypes.byref(_bf16_any(ik, "ik")),
+        positions.data_ptr(), scores.data_ptr(), scores.numel() * 4, _stream(iq.device)))
+    return scores
+
+
+def indexer_select(scores: torch.Tensor, positions: torch.Tensor, slot_of_pos: torch.Tensor,
+                   budget: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-`budget` complete causal blocks per query, expanded to slots with
+    the causal tail: int32 [T, 4*budget + 3], -1 padded."""
+    _check_i32_1d(positions, "positions")
+    _check_i32_1d(slot_of_pos, "slot_of_pos")
+    T, C = scores.shape
+    if out is None:
+        out = torch.empty((T, 4 * budget + 3), dtype=torch.int32, device=scores.device)
+    ov = _i32_view(out, "slot_idx")
+    _raise_on(load_library().qsa_indexer_select(
+        scores.data_ptr(), scores.numel() * 4, T, C, positions.data_ptr(), slot_of_pos.data_ptr(),
+        slot_of_pos.numel(), budget, ctypes.byref(ov), _stream(scores.device)))
+    return out
+
+
+def indexer_topk(iq: torch.Tensor, ik: torch.Tensor, positions: torch.Tensor,
+                 slot_of_pos: torch.Tensor, budget: int, scores: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _check_i32_1d(positions, "positions")
+    _check_i32_1d(slot_of_pos, "slot_of_pos")
+    T, C = iq.shape[0], ik.shape[0]
+    if scores is None:
+        scores = torch.empty((T, C), dtype=torch.float32, device=iq.device)
+    if out is None:
+        out = torch.empty((T, 4 * budget + 3), dtype=torch.int32, device=iq.device)
+    ov = _i32_view(out, "slot_idx")
+    _raise_on(load_library().qsa_indexer_topk(
+        ctypes.byref(_bf16_any(iq, "iq")), ctypes.byref(_bf16_any(ik, "ik")),
+        positions.data_ptr(), slot_of_pos.data_ptr(), slot_of_pos.numel(), budget,
+        scores.data_ptr(), scores.numel() * 4, ctypes.byref(ov), _stream(iq.device)))
     return out

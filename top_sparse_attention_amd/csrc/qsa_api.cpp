@@ -433,6 +433,89 @@ qsa_status qsa_sparse_prefill_blocks(const qsa_bf16_view *q, const qsa_bf16_view
     return enqueue_attend(q, k_cache, v_cache, out, pr, scale, workspace, m, st);
 }
 
+// ---------------------------------------------------------------- indexer
+
+// iq [T, 4, 128] and ik [C, 1, 128] BF16 views (rows 16-byte aligned).
+qsa_status check_index_view(const qsa_bf16_view *v, const char *name, int64_t heads) {
+    if (!v) return fail(QSA_ERR_NULL, "%s: view pointer is NULL", name);
+    for (int i = 0; i < 3; ++i) {
+        if (v->size[i] < 0) return fail(QSA_ERR_SHAPE, "%s: negative size", name);
+        if (v->stride[i] < 0) return fail(QSA_ERR_STRIDE, "%s: negative stride", name);
+    }
+    if (v->size[1] != heads || v->size[2] != qsa::kIndexDim)
+        return fail(QSA_ERR_UNSUPPORTED, "%s must be [*, %lld, %d]", name, (long long)heads,
+                    qsa::kIndexDim);
+    if (any_empty(v)) return QSA_OK;
+    if (!v->data) return fail(QSA_ERR_NULL, "%s: data is NULL", name);
+    if (v->stride[2] != 1) return fail(QSA_ERR_STRIDE, "%s: innermost stride must be 1", name);
+    if ((uintptr_t)v->data % 16 || v->stride[0] % 8 || v->stride[1] % 8)
+        return fail(QSA_ERR_STRIDE, "%s: rows must be 16-byte aligned", name);
+    if (v->size[0] > kMax32) return fail(QSA_ERR_UNSUPPORTED, "%s: too many rows", name);
+    return QSA_OK;
+}
+
+qsa_status check_scores(const void *scores, size_t bytes, int64_t T, int64_t C) {
+    if (T > 0 && C > 0 && !scores) return fail(QSA_ERR_WORKSPACE, "scores buffer is NULL");
+    if ((uintptr_t)scores % 16) return fail(QSA_ERR_WORKSPACE, "scores must be 16-byte aligned");
+    if ((int64_t)bytes < T * C * 4)
+        return fail(QSA_ERR_WORKSPACE, "scores buffer holds %zu bytes, %lld needed", bytes,
+                    (long long)(T * C * 4));
+    return QSA_OK;
+}
+
+qsa_status enqueue_indexer_scores(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
+                                  const int32_t *positions, float *scores, hipStream_t stream) {
+    qsa::IndexerScoreParams p{};
+    p.iq = (const uint16_t *)iq->data;
+    p.q_st = iq->stride[0];
+    p.q_sh = iq->stride[1];
+    p.ik = (const uint16_t *)ik->data;
+    p.k_st = ik->stride[0];
+    p.T = iq->size[0];
+    p.C = ik->size[0];
+    p.positions = positions;
+    p.scores = scores;
+    hipError_t e = qsa::launch_indexer_scores(p, stream);
+    return e == hipSuccess ? QSA_OK : hip_fail(e, "indexer score launch");
+}
+
+qsa_status enqueue_indexer_select(const float *scores, int64_t T, int64_t C,
+                                  const int32_t *positions, const int32_t *slot_of_pos, int64_t L,
+                                  int32_t budget, const qsa_i32_view *out, hipStream_t stream) {
+    qsa::IndexerSelectParams p{};
+    p.scores = scores;
+    p.T = T;
+    p.C = C;
+    p.positions = positions;
+    p.slot_of_pos = slot_of_pos;
+    p.L = L;
+    p.budget = budget;
+    p.out = (int32_t *)out->data;
+    p.out_stride = out->stride[0];
+    hipError_t e = qsa::launch_indexer_select(p, stream);
+    return e == hipSuccess ? QSA_OK : hip_fail(e, "indexer select launch");
+}
+
+qsa_status check_select_args(int64_t T, int64_t C, const int32_t *positions,
+                             const int32_t *slot_of_pos, int64_t L, int32_t budget,
+                             const qsa_i32_view *out) {
+    if (T < 0 || C < 0 || L < 0) return fail(QSA_ERR_SHAPE, "negative size");
+    if (T > kMax32 || C > kMax32 || L > kMax32) return fail(QSA_ERR_UNSUPPORTED, "sizes beyond int32");
+    if (budget < 1 || (int64_t)budget * qsa::kIndexBlock + 3 > kMax32)
+        return fail(QSA_ERR_SHAPE, "budget must be positive");
+    if (C * qsa::kIndexBlock < L - (qsa::kIndexBlock - 1) || C * qsa::kIndexBlock > L + 3)
+        return fail(QSA_ERR_SHAPE, "need one index key per complete block: C = L / 4 (rounded)");
+    if (!out) return fail(QSA_ERR_NULL, "slot_idx: view pointer is NULL");
+    const int64_t width = (int64_t)budget * qsa::kIndexBlock + 3;
+    if (out->size[0] != T || out->size[1] != width)
+        return fail(QSA_ERR_SHAPE, "slot_idx must be [T, 4 * budget + 3]");
+    if (T > 0 && (!out->data || !positions)) return fail(QSA_ERR_NULL, "NULL output or positions");
+    if (T > 0 && L > 0 && !slot_of_pos) return fail(QSA_ERR_NULL, "slot_of_pos is NULL");
+    if (out->stride[1] != 1 || out->stride[0] < width)
+        return fail(QSA_ERR_STRIDE, "slot_idx rows must be contiguous and not overlap");
+    return QSA_OK;
+}
+
 qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S, void *workspace,
                              size_t workspace_bytes, void *stream) {
     return qsa_compact_slot_range(slot_idx, S, 0, S < 0 ? 0 : S, workspace, workspace_bytes,
@@ -669,6 +752,50 @@ qsa_status qsa_sparse_prefill_fp8kv(const qsa_bf16_view *q, const qsa_fp8_view *
     if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, 0, pr.S, workspace, m, st))) return s;
     KvKind kv{qsa::KvType::kFp8, k_scale, v_scale};
     return enqueue_attend(q, as_view(k8), as_view(v8), out, pr, scale, workspace, m, st, kv);
+}
+
+size_t qsa_indexer_scores_bytes(int64_t T, int64_t C) {
+    return (T < 0 || C < 0) ? 0 : (size_t)(T * C * 4);
+}
+
+qsa_status qsa_indexer_scores(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
+                              const int32_t *positions, float *scores, size_t scores_bytes,
+                              void *stream) {
+    qsa_status s;
+    if ((s = check_index_view(iq, "iq", qsa::kIndexHeads)) || (s = check_index_view(ik, "ik", 1)))
+        return s;
+    const int64_t T = iq->size[0], C = ik->size[0];
+    if ((s = check_scores(scores, scores_bytes, T, C))) return s;
+    if (T > 0 && !positions) return fail(QSA_ERR_NULL, "positions is NULL");
+    if (T == 0 || C == 0) return QSA_OK;
+    return enqueue_indexer_scores(iq, ik, positions, scores, (hipStream_t)stream);
+}
+
+qsa_status qsa_indexer_select(const float *scores, size_t scores_bytes, int64_t T, int64_t C,
+                              const int32_t *positions, const int32_t *slot_of_pos, int64_t L,
+                              int32_t budget, qsa_i32_view *slot_idx, void *stream) {
+    qsa_status s = check_select_args(T, C, positions, slot_of_pos, L, budget, slot_idx);
+    if (s) return s;
+    if ((s = check_scores(scores, scores_bytes, T, C))) return s;
+    if (T == 0) return QSA_OK;
+    return enqueue_indexer_select(scores, T, C, positions, slot_of_pos, L, budget, slot_idx,
+                                  (hipStream_t)stream);
+}
+
+qsa_status qsa_indexer_topk(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
+                            const int32_t *positions, const int32_t *slot_of_pos, int64_t L,
+                            int32_t budget, float *scores, size_t scores_bytes,
+                            qsa_i32_view *slot_idx, void *stream) {
+    qsa_status s;
+    if ((s = check_index_view(iq, "iq", qsa::kIndexHeads)) || (s = check_index_view(ik, "ik", 1)))
+        return s;
+    const int64_t T = iq->size[0], C = ik->size[0];
+    if ((s = check_select_args(T, C, positions, slot_of_pos, L, budget, slot_idx))) return s;
+    if ((s = check_scores(scores, scores_bytes, T, C))) return s;
+    if (T == 0) return QSA_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (C > 0 && (s = enqueue_indexer_scores(iq, ik, positions, scores, st))) return s;
+    return enqueue_indexer_select(scores, T, C, positions, slot_of_pos, L, budget, slot_idx, st);
 }
 
 }  // extern "C"

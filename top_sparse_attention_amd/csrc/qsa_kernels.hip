@@ -37,6 +37,8 @@
 #include <stdint.h>
 
 #include <hipcub/block/block_radix_sort.hpp>
+#include <hipcub/block/block_reduce.hpp>
+#include <hipcub/block/block_scan.hpp>
 
 #include "qsa_kernels.h"
 
@@ -544,7 +546,363 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void ceiling_kernel(const Ce
     }
 }
 
+// ---------------------------------------------------------------- indexer
+
+// score[t, c] = sum_h max(0, iq[t,h] . ik[c]) with bf16 MFMA.  A workgroup
+// takes 64 tokens (16 per wave, as 4 MFMA row tiles of 4 tokens x 4 heads)
+// and one range of kScoreSplit index keys, walked in tiles of 64 blocks
+// staged in LDS (swizzled like the attention tiles) and shared by all four
+// row tiles; it stops at the last block any of its tokens may select.  MFMA
+// rows are (token, head) pairs, so lane (c, j) of a 16x16 output holds the 4
+// heads of one token against block c and the head sum stays in the lane.
+constexpr int kScoreTokens = 64;
+constexpr int kScoreRowTiles = kScoreTokens / 4 / 4;   // per wave
+constexpr int kScoreTile = 64;
+constexpr int kScoreSplit = 4096;
+constexpr int kIndexRowBytes = kIndexDim * 2;   // 256 B
+
+__device__ __forceinline__ int idx_off(int r, int chunk) {
+    return r * kIndexRowBytes + ((chunk ^ swz(r)) << 4);
+}
+
+__global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreParams p) {
+    __shared__ __attribute__((aligned(16))) char tile[2][kScoreTile * kIndexRowBytes];
+    __shared__ int c_end_shared;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = lane & 15, j = lane >> 4;
+    const int64_t t0 = (int64_t)blockIdx.x * kScoreTokens;
+    const int c_begin = blockIdx.y * kScoreSplit;
+
+    if (threadIdx.x == 0) c_end_shared = 0;
+    __syncthreads();
+    if (threadIdx.x < kScoreTokens && t0 + threadIdx.x < p.T) {
+        const int64_t lim = ((int64_t)p.positions[t0 + threadIdx.x] + 1) / kIndexBlock;
+        atomicMax(&c_end_shared, (int)min<int64_t>(lim, p.C));
+    }
+    __syncthreads();
+    const int c_end = min(c_end_shared, c_begin + kScoreSplit);
+    if (c_begin >= c_end) return;
+
+    // A operands: row tile rt of this wave is tokens t0 + 16 wave + 4 rt ..+3;
+    // row r of a tile = (token r/4, head r%4), dims 32 ks + 8 j.
+    bf16x8_t qa[kScoreRowTiles][4];
+#pragma unroll
+    for (int rt = 0; rt < kScoreRowTiles; ++rt) {
+        const int64_t ta = t0 + 16 * wave + 4 * rt + (c >> 2);
+        const uint16_t *qrow =
+            ta < p.T ? p.iq + ta * p.q_st + (int64_t)(c & 3) * p.q_sh : kZeroRow;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qa[rt][ks] = ldg16<bf16x8_t>(qrow + 32 * ks + 8 * j);
+    }
+
+    // Staging: 64 rows x 16 chunks = 1024 chunks, 4 per thread.
+    auto load_tile = [&](int c0, u32x4_t (&r)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = threadIdx.x + 256 * u;
+            const int row = idx >> 4, ch = idx & 15;
+            const int64_t blk = c0 + row;
+            const uint16_t *src = blk < c_end ? p.ik + blk * p.k_st + ch * 8 : kZeroRow + ch * 8;
+            r[u] = ldg16<u32x4_t>(src);
+        }
+    };
+    auto store_tile = [&](char *dst, const u32x4_t (&r)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = threadIdx.x + 256 * u;
+            *LDS_PTR(u32x4_t, dst + idx_off(idx >> 4, idx & 15)) = r[u];
+        }
+    };
+
+    u32x4_t stage[4];
+    load_tile(c_begin, stage);
+    int buf = 0;
+    for (int c0 = c_begin; c0 < c_end; c0 += kScoreTile) {
+        store_tile(tile[buf], stage);
+        __syncthreads();
+        if (c0 + kScoreTile < c_end) load_tile(c0 + kScoreTile, stage);
+#pragma unroll
+        for (int ct = 0; ct < kScoreTile / 16; ++ct) {
+            bf16x8_t kb[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                kb[ks] = *LDS_PTR(bf16x8_t, tile[buf] + idx_off(16 * ct + c, 4 * ks + j));
+            const int64_t blk = c0 + 16 * ct + c;
+#pragma unroll
+            for (int rt = 0; rt < kScoreRowTiles; ++rt) {
+                f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], kb[ks], d, 0, 0, 0);
+                const float score = fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) +
+                                    fmaxf(d[3], 0.f);
+                const int64_t t_out = t0 + 16 * wave + 4 * rt + j;
+                if (t_out < p.T && blk < c_end) p.scores[t_out * p.C + blk] = score;
+            }
+        }
+        buf ^= 1;
+    }
+}
+
+// Order-preserving map of FP32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t score_key(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Find, among the keys of `n` scores that pass `in_set`, the `need`-th largest
+// key tau and how many keys equal to tau must be kept (written to sh_prefix /
+// sh_need), with four 8-bit-digit radix passes.  hist is 256 ints of LDS.
+template <typename ScoreAt, typename InSet>
+__device__ void radix_select(int n, int need, ScoreAt score_at, InSet in_set, int *hist,
+                             uint32_t *sh_prefix, int *sh_need) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, mask = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[tid] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += 256) {
+            const float x = score_at(i);
+            const uint32_t u = score_key(x);
+            if (in_set(x) && (u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+        }
+        __syncthreads();
+        if (tid < 64) {
+            // lane l owns digits 4l..4l+3; suffix sums from the top digit.
+            const int cnt = hist[4 * tid] + hist[4 * tid + 1] + hist[4 * tid + 2] + hist[4 * tid + 3];
+            int incl = cnt;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int v = __shfl_down(incl, off);
+                if (tid + off < 64) incl += v;
+            }
+            const int above = incl - cnt;   // keys with higher digits
+            if (above < need && need <= incl) {
+                int cum = above, d = 4 * tid + 3;
+                while (cum + hist[d] < need) cum += hist[d--];
+                *sh_prefix = prefix | ((uint32_t)d << shift);
+                *sh_need = need - cum;
+            }
+        }
+        __syncthreads();
+        prefix = *sh_prefix;
+        need = *sh_need;
+        mask |= 0xffu << shift;
+        __syncthreads();
+    }
+}
+
+// Per query token: keep the `budget` highest-scoring complete causal blocks
+// (ties to the lower block); write their positions in ascending block order,
+// the causal tail, slot-mapped, then -1 padding.
+//
+// The threshold is found in two steps: a histogram of 256 buckets that split
+// [min, max] of the row linearly (a monotone map, so whole buckets above the
+// threshold's bucket are kept and those below dropped), then an exact radix
+// select over the keys of that one bucket.  Scores of a row sit in a narrow
+// float range, so a radix pass over raw key bits would pile every key into
+// one or two bins; the linear buckets spread them.
+template <bool kInLds>
+__global__ __launch_bounds__(256) void indexer_select_kernel(const IndexerSelectParams p) {
+    using Scan = hipcub::BlockScan<int, 256>;
+    using Reduce = hipcub::BlockReduce<float, 256>;
+    __shared__ float vals[kInLds ? kSelectLdsBlocks : 1];
+    __shared__ int hist[256];
+    __shared__ int chunk_gt[256], chunk_eq[256];
+    __shared__ union {
+        typename Scan::TempStorage scan;
+        typename Reduce::TempStorage reduce;
+    } tmp;
+    __shared__ uint32_t sh_prefix;
+    __shared__ int sh_need;
+    __shared__ float sh_lo, sh_hi;
+
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t pos = p.positions[t];
+    int32_t *out = p.out + t * p.out_stride;
+    const int width = kIndexBlock * p.budget + 3;
+    if (pos < 0 || pos >= p.L) {
+        for (int i = tid; i < width; i += 256) out[i] = -1;
+        return;
+    }
+    const int n = (int)min<int64_t>((pos + 1) / kIndexBlock, p.C);
+    const float *row = p.scores + t * p.C;
+
+    // Row statistics (and the LDS copy): 16-byte loads, four in flight per
+    // thread, so the row arrives in a few memory round trips.
+    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+    const bool vec_ok = ((uintptr_t)row % 16) == 0;
+    const int n4 = vec_ok ? n / 4 : 0;
+    for (int base = 0; base < n4; base += 4 * 256) {
+        f32x4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i4 = base + u * 256 + tid;
+            v[u] = i4 < n4 ? *(const f32x4_t *)(row + 4 * i4)
+                           : f32x4_t{lo, lo, lo, lo};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i4 = base + u * 256 + tid;
+            if (i4 < n4) {
+                if (kInLds) *(f32x4_t *)(vals + 4 * i4) = v[u];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lo = fminf(lo, v[u][e]);
+                    hi = fmaxf(hi, v[u][e]);
+                }
+            }
+        }
+    }
+    for (int i = 4 * n4 + tid; i < n; i += 256) {
+        const float x = row[i];
+        if (kInLds) vals[i] = x;
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
+    }
+    auto score_at = [&](int i) -> float { return kInLds ? vals[i] : row[i]; };
+
+    // Threshold key tau and how many keys equal to tau to keep (`need`).
+    uint32_t tau = 0;
+    int need = n;   // n <= budget: every key (all > 0) is kept
+    if (n > p.budget) {
+        lo = Reduce(tmp.reduce).Reduce(lo, [](float a, float b) { return fminf(a, b); });
+        __syncthreads();
+        hi = Reduce(tmp.reduce).Reduce(hi, [](float a, float b) { return fmaxf(a, b); });
+        if (tid == 0) {
+            sh_lo = lo;
+            sh_hi = hi;
+        }
+        __syncthreads();
+        lo = sh_lo;
+        hi = sh_hi;
+        const float inv = hi > lo ? 256.0f / (hi - lo) : 0.0f;
+        auto bucket = [&](float x) { return min(255, (int)((x - lo) * inv)); };
+        // Step 1: the bucket holding the budget-th largest score.
+        hist[tid] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += 256) atomicAdd(&hist[bucket(score_at(i))], 1);
+        __syncthreads();
+        if (tid < 64) {
+            const int cnt = hist[4 * tid] + hist[4 * tid + 1] + hist[4 * tid + 2] + hist[4 * tid + 3];
+            int incl = cnt;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int v = __shfl_down(incl, off);
+                if (tid + off < 64) incl += v;
+            }
+            const int above = incl - cnt;
+            if (above < p.budget && p.budget <= incl) {
+                int cum = above, d = 4 * tid + 3;
+                while (cum + hist[d] < p.budget) cum += hist[d--];
+                sh_prefix = (uint32_t)d;
+                sh_need = p.budget - cum;
+            }
+        }
+        __syncthreads();
+        const int b_star = (int)sh_prefix;
+        need = sh_need;
+        __syncthreads();
+        // Step 2: exact select inside that bucket.
+        radix_select(n, need, score_at, [&](float x) { return bucket(x) == b_star; }, hist,
+                     &sh_prefix, &sh_need);
+        tau = sh_prefix;
+        need = sh_need;
+    }
+    __syncthreads();   // vals written by other threads are read below
+
+    // Keep key > tau, and the first `need` keys == tau in block order.  The
+    // row is read in chunks of 64 blocks (one per lane); per-chunk counts are
+    // scanned so every kept block knows its output position.  Chunks are
+    // handled in groups of 256 (one count per thread).
+    int gt_before = 0, eq_before = 0;   // keys > tau / == tau in earlier groups
+    const int nchunks = (n + 63) / 64;
+    for (int g0 = 0; g0 < nchunks; g0 += 256) {
+        const int gn = min(256, nchunks - g0);
+        for (int k = wave; k < gn; k += 4) {
+            const int i = (g0 + k) * 64 + lane;
+            const uint32_t u = i < n ? score_key(score_at(i)) : 0u;
+            const uint64_t gt = __ballot(i < n && u > tau);
+            const uint64_t eq = __ballot(i < n && u == tau);
+            if (lane == 0) {
+                chunk_gt[k] = __popcll(gt);
+                chunk_eq[k] = __popcll(eq);
+            }
+        }
+        __syncthreads();
+        int my_gt = tid < gn ? chunk_gt[tid] : 0, my_eq = tid < gn ? chunk_eq[tid] : 0;
+        int gt_pre, eq_pre, gt_tot, eq_tot;
+        Scan(tmp.scan).ExclusiveSum(my_gt, gt_pre, gt_tot);
+        __syncthreads();
+        Scan(tmp.scan).ExclusiveSum(my_eq, eq_pre, eq_tot);
+        __syncthreads();
+        if (tid < gn) {
+            chunk_gt[tid] = gt_pre;
+            chunk_eq[tid] = eq_pre;
+        }
+        __syncthreads();
+        const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+        for (int k = wave; k < gn; k += 4) {
+            const int i = (g0 + k) * 64 + lane;
+            const uint32_t u = i < n ? score_key(score_at(i)) : 0u;
+            const bool is_gt = i < n && u > tau, is_eq = i < n && u == tau;
+            const uint64_t eq_mask = __ballot(is_eq);
+            const int eq_rank = eq_before + chunk_eq[k] + __popcll(eq_mask & below);
+            const bool keep = is_gt || (is_eq && eq_rank < need);
+            const uint64_t keep_mask = __ballot(keep);
+            const int eq_prior = eq_before + chunk_eq[k];
+            // kept before this lane = all keys > tau before it + the first
+            // `need` keys == tau before it
+            const int w = gt_before + chunk_gt[k] + min(eq_prior, need) +
+                          __popcll(keep_mask & below);
+            if (keep) out[kIndexBlock * w] = i;   // block id for now, expanded below
+        }
+        gt_before += gt_tot;
+        eq_before += eq_tot;
+        __syncthreads();   // chunk counts are rewritten by the next group
+    }
+    // Expand every kept block into its slots; all the slot-table reads of the
+    // row are independent and in flight together.
+    const int kept = min(n, p.budget);
+    __threadfence_block();
+    __syncthreads();
+    for (int e = tid; e < kept; e += 256) {
+        const int64_t blk = out[kIndexBlock * e];
+        const int32_t *src = p.slot_of_pos + kIndexBlock * blk;
+        int32_t sl[kIndexBlock];
+#pragma unroll
+        for (int q = 0; q < kIndexBlock; ++q) sl[q] = src[q];
+#pragma unroll
+        for (int q = 0; q < kIndexBlock; ++q) out[kIndexBlock * e + q] = sl[q];
+    }
+    const int r = (int)((pos + 1) % kIndexBlock);
+    const int tail0 = kIndexBlock * kept;
+    for (int i = tid; i < width - tail0; i += 256)
+        out[tail0 + i] = i < r ? p.slot_of_pos[pos - r + 1 + i] : -1;
+}
+
 }  // namespace
+
+hipError_t launch_indexer_scores(const IndexerScoreParams &p, hipStream_t stream) {
+    if (p.T == 0 || p.C == 0) return hipSuccess;
+    const int64_t blocks = (p.T + kScoreTokens - 1) / kScoreTokens;
+    const int64_t splits = (p.C + kScoreSplit - 1) / kScoreSplit;
+    hipLaunchKernelGGL(indexer_scores_kernel, dim3((unsigned)blocks, (unsigned)splits), dim3(256),
+                       0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_indexer_select(const IndexerSelectParams &p, hipStream_t stream) {
+    if (p.T == 0) return hipSuccess;
+    if (p.C <= kSelectLdsBlocks)
+        hipLaunchKernelGGL(indexer_select_kernel<true>, dim3((unsigned)p.T), dim3(256), 0, stream,
+                           p);
+    else
+        hipLaunchKernelGGL(indexer_select_kernel<false>, dim3((unsigned)p.T), dim3(256), 0,
+                           stream, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_compact(const CompactParams &p, hipStream_t stream) {
     if (p.T == 0) return hipSuccess;
