@@ -271,15 +271,18 @@ qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes,
 /*
  * Measurement aid: reads exactly the K and V rows that qsa_sparse_attend
  * would read for this workspace (same slots, same KV heads, same load
- * pattern) and folds them into one checksum word per (token, KV head) in
- * sink[T * Hkv] (device memory, caller-owned), with no attention arithmetic.
- * Its duration is the practical gather ceiling for the workload.
+ * pattern, one wave per (token, KV head), same residency per CU) and folds
+ * them into one checksum word per (token, KV head) in sink[T * Hkv] (device
+ * memory, caller-owned): the XOR of the 32-bit words of every read row.  It
+ * issues the loads back to back with no attention arithmetic between them;
+ * its duration is the cost of the gathers alone issued that way, which the
+ * attention itself, pacing its requests, can beat.
  */
-qsa_status qsa_gather_ceiling(const qsa_bf16_view *k_cache,
-                              const qsa_bf16_view *v_cache, int64_t T,
-                              int64_t W, const void *workspace,
-                              size_t workspace_bytes, uint32_t *sink,
-                              void *stream);
+qsa_status qsa_gather_only(const qsa_bf16_view *k_cache,
+                           const qsa_bf16_view *v_cache, int64_t T,
+                           int64_t W, const void *workspace,
+                           size_t workspace_bytes, uint32_t *sink,
+                           void *stream);
 
 /*
  * FP8 KV-cache variant.  The page's section "Where this sits in the Qwen4Exp
@@ -305,13 +308,13 @@ qsa_status qsa_sparse_prefill_fp8kv(const qsa_bf16_view *q,
                                     void *workspace, size_t workspace_bytes,
                                     void *stream);
 
-/* qsa_gather_ceiling for an FP8 KV cache (same tiles, waves and loads as
+/* qsa_gather_only for an FP8 KV cache (same tiles, waves and loads as
  * qsa_sparse_attend_fp8kv; XOR of the 32-bit words of every read row). */
-qsa_status qsa_gather_ceiling_fp8kv(const qsa_fp8_view *k_cache,
-                                    const qsa_fp8_view *v_cache, int64_t T,
-                                    int64_t W, const void *workspace,
-                                    size_t workspace_bytes, uint32_t *sink,
-                                    void *stream);
+qsa_status qsa_gather_only_fp8kv(const qsa_fp8_view *k_cache,
+                                 const qsa_fp8_view *v_cache, int64_t T,
+                                 int64_t W, const void *workspace,
+                                 size_t workspace_bytes, uint32_t *sink,
+                                 void *stream);
 
 /*
  * QSA indexer and Top-K selection: the step that produces slot_idx (page,

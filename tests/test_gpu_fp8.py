@@ -92,13 +92,13 @@ def test_fp8_equals_bf16_path_for_power_of_two_scales(k_scale, v_scale):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_fp8_gather_ceiling_reads_exactly_the_selected_rows():
+def test_fp8_gather_only_reads_exactly_the_selected_rows():
     case = qi.with_fp8_kv(qi.random_case(950, T=21, S=2500, Hq=4, Hkv=2, W=150, pad_frac=0.3,
                                          interior=True))
     _, _, _, sl = upload(case, DEV)
     k8, v8, _, _ = upload_fp8(case, DEV)
     ws = qsa.compact_slots(sl, case.S)
-    sink = qsa.gather_ceiling_fp8kv(k8, v8, ws, case.T, case.W)
+    sink = qsa.gather_only_fp8kv(k8, v8, ws, case.T, case.W)
     torch.cuda.synchronize()
     got = sink.cpu().numpy().view(np.uint32)
     kw = np.ascontiguousarray(case.info["k8"]).view(np.uint32)

@@ -288,11 +288,11 @@ def test_large_scale_is_finite_and_matches_oracle():
     assert torch.isfinite(o.float()).all()
 
 
-def test_gather_ceiling_reads_exactly_the_selected_rows():
+def test_gather_only_reads_exactly_the_selected_rows():
     case = qi.random_case(710, T=37, S=3000, Hq=4, Hkv=2, W=200, pad_frac=0.25, interior=True)
     q, k, v, sl = upload(case, DEV)
     ws = qsa.compact_slots(sl, case.S)
-    sink = qsa.gather_ceiling(k, v, ws, case.T, case.W)
+    sink = qsa.gather_only(k, v, ws, case.T, case.W)
     torch.cuda.synchronize()
     got = sink.cpu().numpy().view(np.uint32)
     kw = np.ascontiguousarray(case.k_cache).view(np.uint32)   # [S, Hkv, 128] words

@@ -23,10 +23,10 @@ import torch
 __all__ = [
     "QsaError", "library_path", "load_library", "version", "workspace_bytes",
     "workspace_layout", "new_workspace", "compact_slots", "compacted_lists",
-    "sparse_attend", "sparse_prefill", "check_status", "gather_ceiling",
+    "sparse_attend", "sparse_prefill", "check_status", "gather_only",
     "compact_slot_range", "partials_bytes", "new_partials", "sparse_attend_partial",
     "merge_partials", "decode_splits", "decode_workspace_bytes", "sparse_decode",
-    "sparse_attend_fp8kv", "sparse_prefill_fp8kv", "gather_ceiling_fp8kv",
+    "sparse_attend_fp8kv", "sparse_prefill_fp8kv", "gather_only_fp8kv",
     "compact_blocks", "sparse_prefill_blocks", "indexer_scores", "indexer_select",
     "indexer_topk",
 ]
@@ -106,8 +106,8 @@ def load_library():
                                        f32, P(BF16View), vp, sz, vp]
     lib.qsa_check_status.restype = ctypes.c_int
     lib.qsa_check_status.argtypes = [vp, sz, i64, i64, vp, P(i64)]
-    lib.qsa_gather_ceiling.restype = ctypes.c_int
-    lib.qsa_gather_ceiling.argtypes = [P(BF16View), P(BF16View), i64, i64, vp, sz, vp, vp]
+    lib.qsa_gather_only.restype = ctypes.c_int
+    lib.qsa_gather_only.argtypes = [P(BF16View), P(BF16View), i64, i64, vp, sz, vp, vp]
     lib.qsa_compact_slot_range.restype = ctypes.c_int
     lib.qsa_compact_slot_range.argtypes = [P(I32View), i64, i64, i64, vp, sz, vp]
     lib.qsa_partials_bytes.restype = sz
@@ -145,8 +145,8 @@ def load_library():
     lib.qsa_indexer_topk.restype = ctypes.c_int
     lib.qsa_indexer_topk.argtypes = [P(BF16View), P(BF16View), vp, vp, i64, ctypes.c_int32, vp,
                                      sz, P(I32View), vp]
-    lib.qsa_gather_ceiling_fp8kv.restype = ctypes.c_int
-    lib.qsa_gather_ceiling_fp8kv.argtypes = [P(BF16View), P(BF16View), i64, i64, vp, sz, vp, vp]
+    lib.qsa_gather_only_fp8kv.restype = ctypes.c_int
+    lib.qsa_gather_only_fp8kv.argtypes = [P(BF16View), P(BF16View), i64, i64, vp, sz, vp, vp]
     _lib = lib
     return lib
 
@@ -283,14 +283,14 @@ def check_status(workspace: torch.Tensor, T: int, W: int) -> int:
     return n_bad.value
 
 
-def gather_ceiling(k_cache: torch.Tensor, v_cache: torch.Tensor, workspace: torch.Tensor,
-                   T: int, W: int, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+def gather_only(k_cache: torch.Tensor, v_cache: torch.Tensor, workspace: torch.Tensor,
+                T: int, W: int, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Run the gather-only measurement kernel; returns sink [T * Hkv] (int32 bits)."""
     Hkv = k_cache.shape[1]
     if sink is None:
         sink = torch.empty(max(T * Hkv, 1), dtype=torch.int32, device=k_cache.device)
     kv, vv = _bf16_view(k_cache, "k_cache"), _bf16_view(v_cache, "v_cache")
-    _raise_on(load_library().qsa_gather_ceiling(
+    _raise_on(load_library().qsa_gather_only(
         ctypes.byref(kv), ctypes.byref(vv), T, W, workspace.data_ptr(), workspace.numel(),
         sink.data_ptr(), _stream(k_cache.device)))
     return sink
@@ -422,13 +422,13 @@ def sparse_prefill_fp8kv(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, k_
     return out
 
 
-def gather_ceiling_fp8kv(k8: torch.Tensor, v8: torch.Tensor, workspace: torch.Tensor, T: int,
-                         W: int, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+def gather_only_fp8kv(k8: torch.Tensor, v8: torch.Tensor, workspace: torch.Tensor, T: int,
+                      W: int, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
     Hkv = k8.shape[1]
     if sink is None:
         sink = torch.empty(max(T * Hkv, 1), dtype=torch.int32, device=k8.device)
     kv, vv = _fp8_view(k8, "k_cache"), _fp8_view(v8, "v_cache")
-    _raise_on(load_library().qsa_gather_ceiling_fp8kv(
+    _raise_on(load_library().qsa_gather_only_fp8kv(
         ctypes.byref(kv), ctypes.byref(vv), T, W, workspace.data_ptr(), workspace.numel(),
         sink.data_ptr(), _stream(k8.device)))
     return sink

@@ -298,7 +298,7 @@ qsa_status enqueue_merge(const void *partials, const PartialsMap &pm, int64_t n_
 }
 
 // Splits per item for qsa_sparse_decode: enough workgroups to cover every
-// CU a few times over, at least 4 tiles (one per wave) per split, at most 64.
+// CU a few times over, at least kMinSplitTiles tiles per split, at most 64.
 // A pure function of the sizes, so results are reproducible.
 int32_t decode_splits(int64_t T, int64_t W, int32_t Hq, int32_t Hkv) {
     if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0) return 1;
@@ -307,7 +307,7 @@ int32_t decode_splits(int64_t T, int64_t W, int32_t Hq, int32_t Hkv) {
     const int64_t tiles = (W + qsa::kTileSlots - 1) / qsa::kTileSlots;
     const int64_t target_blocks = 2048;
     int64_t s = (target_blocks + items - 1) / items;
-    s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / qsa::kWavesPerItem));
+    s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / qsa::kMinSplitTiles));
     s = std::min<int64_t>(s, 64);
     return (int32_t)std::max<int64_t>(s, 1);
 }
@@ -666,10 +666,10 @@ qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes, int64
 
 namespace {
 
-qsa_status gather_ceiling_any(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_cache,
-                              int kv_bytes, qsa::KvType kv, int64_t T, int64_t W,
-                              const void *workspace, size_t workspace_bytes, uint32_t *sink,
-                              void *stream) {
+qsa_status gather_only_any(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_cache,
+                           int kv_bytes, qsa::KvType kv, int64_t T, int64_t W,
+                           const void *workspace, size_t workspace_bytes, uint32_t *sink,
+                           void *stream) {
     qsa_status s;
     if ((s = check_view(k_cache, "k_cache", kv_bytes)) ||
         (s = check_view(v_cache, "v_cache", kv_bytes)))
@@ -684,7 +684,7 @@ qsa_status gather_ceiling_any(const qsa_bf16_view *k_cache, const qsa_bf16_view 
     if ((s = check_workspace(workspace, workspace_bytes, T, W, &m))) return s;
     if (T == 0 || k_cache->size[1] == 0) return QSA_OK;
     if (!sink) return fail(QSA_ERR_NULL, "sink is NULL");
-    qsa::CeilingParams p{};
+    qsa::GatherParams p{};
     p.k = k_cache->data;
     p.k_ss = k_cache->stride[0];
     p.k_sh = k_cache->stride[1];
@@ -696,26 +696,26 @@ qsa_status gather_ceiling_any(const qsa_bf16_view *k_cache, const qsa_bf16_view 
     p.count = (const int32_t *)((const char *)workspace + m.count_offset);
     p.sink = sink;
     p.Hkv = (int32_t)k_cache->size[1];
-    hipError_t e = qsa::launch_ceiling(p, kv, T, (hipStream_t)stream);
-    return e == hipSuccess ? QSA_OK : hip_fail(e, "gather-ceiling launch");
+    hipError_t e = qsa::launch_gather_only(p, kv, T, (hipStream_t)stream);
+    return e == hipSuccess ? QSA_OK : hip_fail(e, "gather-only launch");
 }
 
 }  // namespace
 
 extern "C" {
 
-qsa_status qsa_gather_ceiling(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_cache,
-                              int64_t T, int64_t W, const void *workspace,
-                              size_t workspace_bytes, uint32_t *sink, void *stream) {
-    return gather_ceiling_any(k_cache, v_cache, 2, qsa::KvType::kBf16, T, W, workspace,
-                              workspace_bytes, sink, stream);
+qsa_status qsa_gather_only(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_cache,
+                           int64_t T, int64_t W, const void *workspace, size_t workspace_bytes,
+                           uint32_t *sink, void *stream) {
+    return gather_only_any(k_cache, v_cache, 2, qsa::KvType::kBf16, T, W, workspace,
+                           workspace_bytes, sink, stream);
 }
 
-qsa_status qsa_gather_ceiling_fp8kv(const qsa_fp8_view *k8, const qsa_fp8_view *v8, int64_t T,
-                                    int64_t W, const void *workspace, size_t workspace_bytes,
-                                    uint32_t *sink, void *stream) {
-    return gather_ceiling_any(as_view(k8), as_view(v8), 1, qsa::KvType::kFp8, T, W, workspace,
-                              workspace_bytes, sink, stream);
+qsa_status qsa_gather_only_fp8kv(const qsa_fp8_view *k8, const qsa_fp8_view *v8, int64_t T,
+                                 int64_t W, const void *workspace, size_t workspace_bytes,
+                                 uint32_t *sink, void *stream) {
+    return gather_only_any(as_view(k8), as_view(v8), 1, qsa::KvType::kFp8, T, W, workspace,
+                           workspace_bytes, sink, stream);
 }
 
 qsa_status qsa_sparse_attend_fp8kv(const qsa_bf16_view *q, const qsa_fp8_view *k8,

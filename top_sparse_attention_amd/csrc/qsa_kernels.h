@@ -13,10 +13,19 @@ constexpr int kHeadDim = 256;
 constexpr int kTileSlots = 16;
 // Compacted lists are padded with -1 to a multiple of this.
 constexpr int kListPad = 32;
-// Waves that share one (token, KV head, head block) work item.
-constexpr int kWavesPerItem = 4;
-// Work items resident per CU (sizes the LDS and register budget).
-constexpr int kItemsPerCU = 2;
+// Work items (one wave each) resident per CU.  Exactly 8 (2 per SIMD): the
+// attention kernel requests enough LDS per item that a 9th does not fit.
+// With every SIMD holding the same number of waves, the waves of a CU, and
+// of the whole chip, advance through their slot-sorted lists at the same
+// rate, so concurrent tokens read the same cache rows at about the same
+// time and share them in L2; an uneven split (7 or 9 waves per CU) lets the
+// waves drift apart and loses most of that sharing.
+constexpr int kItemsPerCU = 8;
+// Waves per SIMD the attention kernel's registers are budgeted for (up to
+// 256 registers per wave).
+constexpr int kWavesPerSimd = 2;
+// Fewest tiles a split of the decode path takes.
+constexpr int kMinSplitTiles = 4;
 // Entries of a selection row sorted together by the compaction pass.
 constexpr int kSortThreads = 256;
 constexpr int kSortItemsPerThread = 9;
@@ -79,7 +88,7 @@ struct MergeParams {
     int64_t o_st, o_sh;
 };
 
-struct CeilingParams {
+struct GatherParams {
     const void *k;
     int64_t k_ss, k_sh;
     const void *v;
@@ -128,6 +137,6 @@ hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_
 hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
                                  hipStream_t stream);
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
-hipError_t launch_ceiling(const CeilingParams &p, KvType kv, int64_t T, hipStream_t stream);
+hipError_t launch_gather_only(const GatherParams &p, KvType kv, int64_t T, hipStream_t stream);
 
 }  // namespace qsa

@@ -17,15 +17,15 @@
 //     large pages of the cache, which the memory system serves markedly
 //     faster than uniformly scattered rows.
 //  2. attend_kernel: one work item = (token t, KV head g, block of up to 16
-//     query heads of that group), kItemsPerCU items resident per CU.  The
-//     item's kWavesPerItem waves split its 16-slot tiles round-robin; each
-//     wave gathers a tile's K and V rows (512 B each, 16-byte coalesced
-//     loads, prefetched one tile ahead through registers), stages them in
-//     LDS, computes the 16x16 score tile with bf16 MFMA (K rows x query
-//     heads), runs an online softmax in FP32 and accumulates P.V with bf16
-//     MFMA fed by LDS transpose loads.  The waves' partial (max, sum, O) are
-//     merged through LDS at the end and the row is written in BF16.
-//
+//     query heads of that group) = one wave, kItemsPerCU items resident per
+//     CU.  The wave walks its item's 16-slot tiles in list order.  Per tile
+//     it loads the K rows straight into the registers of the score MFMA's A
+//     operand and the V rows (whole rows) into registers that it then writes
+//     to its LDS tile, both one tile ahead of use; computes the 16x16 score
+//     tile with bf16 MFMA (K rows x query heads, the query rows read from
+//     LDS), runs an online softmax in FP32 and accumulates P.V with bf16
+//     MFMA fed by LDS transpose loads, then writes the row in BF16.
+
 // MFMA orientation: scores are computed transposed, S^T = K_tile . Q^T, so
 // that one lane owns one query head (column) of the MFMA output: the row
 // maximum needs only two cross-lane steps and the O rescale is one scalar per
@@ -56,26 +56,39 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 #define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T *)(p))
 
-constexpr int kRowBytes = kHeadDim * 2;             // one BF16 K or V row in LDS: 512 B
+constexpr int kRowBytes = kHeadDim * 2;             // one BF16 row: 512 B
 constexpr int kChunksPerRow = kRowBytes / 16;       // 32 sixteen-byte chunks
-constexpr int kTileBytes = kTileSlots * kRowBytes;  // 8 KiB of K (or V)
-constexpr int kWaveLds = 2 * kTileBytes;            // K tile + V tile per wave
-constexpr int kThreads = 64 * kWavesPerItem;
-constexpr int kMaxLoadsPerTile = kTileBytes / (64 * 16);  // 8 dwordx4 per lane (BF16)
 
-// How one tile of a cache with this element type is gathered: a row of 256
-// elements is split into 16-byte chunks, one per lane, and one dwordx4 load
-// instruction covers kRowsPerLoad whole rows.
+// LDS row pitches.  Rows are padded rather than swizzled, so every LDS
+// access of the tile loop is one per-lane base address plus an immediate
+// offset.  V tile rows (544 B = 136 banks): the 4 rows one 16-lane group
+// reads with a transpose load fall in 4 different 32-byte bank windows, and
+// 8 lanes writing consecutive chunks of a row hit 8 different 16-byte bank
+// groups.  Query rows (528 B = 33 chunks): the 8 rows read by one phase of a
+// 16-byte read start in 8 different 16-byte bank groups.
+constexpr int kVPitch = kRowBytes + 32;
+constexpr int kQPitch = kRowBytes + 16;
+constexpr int kTileBytes = kTileSlots * kVPitch;    // the wave's V tile: 8.5 KiB
+
+// How one tile of a cache with this element type is gathered.
+//  K: 16 rows in MFMA A-operand layout; every lane loads 16 bytes per load
+//     instruction from its row (see gather_k for which bytes).
+//  V: whole rows, each row split into 16-byte chunks, one per lane,
+//     kRowsPerLoad rows per load instruction.
 template <KvType KV>
 struct KvGather {
     static constexpr int kElemBytes = KV == KvType::kFp8 ? 1 : 2;
     static constexpr int kRowBytesHbm = kHeadDim * kElemBytes;  // 512 or 256
+    static constexpr int kKLoads = kRowBytesHbm / 64;             // 8 or 4
     static constexpr int kLanesPerRow = kRowBytesHbm / 16;        // 32 or 16
     static constexpr int kRowsPerLoad = 64 / kLanesPerRow;        // 2 or 4
-    static constexpr int kLoads = kTileSlots / kRowsPerLoad;      // 8 or 4
+    static constexpr int kVLoads = kTileSlots / kRowsPerLoad;     // 8 or 4
 };
 constexpr int kHeadBlock = 16;                      // query heads per MFMA column block
 constexpr int kDimBlocks = kHeadDim / 16;           // 16 output blocks of 16 dims
+constexpr int kKSteps = kHeadDim / 32;              // 8 k-steps of the score MFMA
+constexpr int kQBytes = kHeadBlock * kQPitch;       // an item's query rows in LDS
+constexpr int kQChunksPerLane = kHeadBlock * kChunksPerRow / 64;   // 8
 constexpr float kNegInf = -__builtin_huge_valf();
 // A new running maximum is adopted only when it exceeds the current one by
 // more than this (log2 units); otherwise probabilities may reach 2^8, which
@@ -83,12 +96,14 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // rescales of the O accumulators.
 constexpr float kRescaleSlack = 8.0f;
 
-// Partial results of the waves of one item, merged at the end (reuses the
-// tile area): O [wave][db][lane] as f32x4, then max and sum [wave][head].
-constexpr int kMergeOBytes = kWavesPerItem * kDimBlocks * 64 * 16;
-constexpr int kAttendLds = kWavesPerItem * kWaveLds + 2 * kWavesPerItem * kHeadBlock * 4;
-static_assert(kMergeOBytes <= kWavesPerItem * kWaveLds, "merge area must fit in the tiles");
+// LDS of one item (one wave): its V tile and its query rows, in a block
+// sized so that kItemsPerCU items fit in the 160 KiB of a CU and one more
+// does not.
+constexpr int kAttendLdsUsed = kTileBytes + kQBytes;
+constexpr int kAttendLds = 160 * 1024 / kItemsPerCU - 1024;
+static_assert(kAttendLdsUsed <= kAttendLds, "item LDS");
 static_assert(kItemsPerCU * kAttendLds <= 160 * 1024, "LDS budget of a gfx950 CU");
+static_assert((kItemsPerCU + 1) * kAttendLds > 160 * 1024, "one more item must not fit");
 
 // A row of zeros: masked tile rows and absent query heads load from here, so
 // every load is unconditional and no select waits on loaded data.
@@ -100,16 +115,6 @@ __device__ __attribute__((aligned(16))) uint16_t kZeroRow[kHeadDim] = {};
 template <typename V>
 __device__ __forceinline__ V ldg16(const void *p) {
     return *GLOBAL_PTR(V, p);
-}
-
-// LDS byte offset of 16-byte chunk `chunk` of tile row `r`.  The chunk index
-// is XOR-swizzled by a bijection of r & 7 so that (a) the 8 rows read by one
-// ds_read_b128 phase of the score MFMA hit 8 different bank groups, and (b)
-// the 4 rows read by one 16-lane group of the V transpose loads hit 4
-// different 32-byte bank windows.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-__device__ __forceinline__ int lds_off(int r, int chunk) {
-    return r * kRowBytes + ((chunk ^ swz(r)) << 4);
 }
 
 // ---------------------------------------------------------------- compaction
@@ -177,74 +182,123 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
 
 // ---------------------------------------------------------------- gathers
 
-// Issue the dwordx4 loads of one tile of K and of V.  `slot` holds, in lane
-// r (and every lane congruent to r mod 16), the slot of tile row r (-1:
-// none).  Load q covers kRowsPerLoad consecutive tile rows, each one whole
-// row read by kLanesPerRow consecutive lanes, 16 bytes per lane, so every
-// row is one fully coalesced read.  kb/vb are byte pointers to head g of
-// slot 0; k_ss/v_ss are slot strides in bytes.
+// Start of the cache row of `slot`, or of the row of zeros for slot -1.
+// Both addresses are formed and one is selected, so no branch depends on
+// the slot.
+__device__ __forceinline__ const char *row_ptr(const char *base, int64_t ss, int slot) {
+    const uint64_t a = (uint64_t)(base + (int64_t)max(slot, 0) * ss);
+    const uint64_t z = (uint64_t)(const char *)kZeroRow;
+    return (const char *)(slot >= 0 ? a : z);
+}
+
+// K rows go straight from memory into the A operand of the score MFMA.  The
+// dims of the head are grouped into the 8 k-steps so that one 16-byte load
+// of FP8 codes feeds two k-steps: k-step ks = 2u + b of lane group j takes
+// dims 64 u + 16 j + 8 b .. +8.  BF16 keys use the same grouping (so both
+// cache types give the same sums), each lane loading those 8 dims (16
+// bytes) per k-step: the loads of k-steps 2u and 2u + 1 together read 128
+// contiguous bytes of each of the 16 rows.  FP8 keys: load u reads dims
+// 64 u + 16 j .. +16, converted just before use.  The query operand of each
+// k-step is read with the same map (q_chunk).  `slot` is the slot of tile
+// row (lane & 15), -1 for none (then the row of zeros is read).
 template <KvType KV>
-__device__ __forceinline__ void gather_tile(u32x4_t (&rk)[kMaxLoadsPerTile],
-                                            u32x4_t (&rv)[kMaxLoadsPerTile], int slot,
-                                            const char *kb, int64_t k_ss, const char *vb,
-                                            int64_t v_ss, int lane) {
+__device__ __forceinline__ void gather_k1(u32x4_t &r, int q, int slot, const char *kb,
+                                          int64_t k_ss, int lane) {
+    const int j = lane >> 4;
+    const char *row = row_ptr(kb, k_ss, slot);
+    if constexpr (KV == KvType::kBf16)
+        r = ldg16<u32x4_t>(row + 128 * (q >> 1) + 32 * j + 16 * (q & 1));
+    else
+        r = ldg16<u32x4_t>(row + 64 * q + 16 * j);
+}
+
+template <KvType KV>
+__device__ __forceinline__ void gather_k(u32x4_t (&rk)[KvGather<KV>::kKLoads], int slot,
+                                         const char *kb, int64_t k_ss, int lane) {
+#pragma unroll
+    for (int q = 0; q < KvGather<KV>::kKLoads; ++q) gather_k1<KV>(rk[q], q, slot, kb, k_ss, lane);
+}
+
+// The 16-byte chunk (8 dims) of a query row that pairs with k-step ks of
+// lane group j, following gather_k.
+__device__ __forceinline__ constexpr int q_chunk(int ks, int j) {
+    return 8 * (ks >> 1) + 2 * j + (ks & 1);
+}
+
+// 8 FP8 E4M3 codes (two dwords) -> 8 BF16 values (exact: every E4M3 value is
+// a BF16 value).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+    bf16x8_t x;
+    const uint32_t w[2] = {w0, w1};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+        const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+        x[4 * i] = (__bf16)a[0];
+        x[4 * i + 1] = (__bf16)a[1];
+        x[4 * i + 2] = (__bf16)b[0];
+        x[4 * i + 3] = (__bf16)b[1];
+    }
+    return x;
+}
+
+// A operand of k-step ks from the K registers.
+template <KvType KV>
+__device__ __forceinline__ bf16x8_t k_operand(const u32x4_t (&rk)[KvGather<KV>::kKLoads], int ks) {
+    if constexpr (KV == KvType::kBf16) {
+        return __builtin_bit_cast(bf16x8_t, rk[ks]);
+    } else {
+        const u32x4_t w = rk[ks >> 1];
+        return (ks & 1) ? fp8x8_to_bf16(w[2], w[3]) : fp8x8_to_bf16(w[0], w[1]);
+    }
+}
+
+// V rows are read whole: load q covers kRowsPerLoad consecutive tile rows,
+// each read by kLanesPerRow consecutive lanes, 16 bytes per lane, so every
+// row is one fully coalesced read.  The slot of each row is broadcast from
+// the lane that holds it.  Each load is issued right after its own address
+// work and nothing is moved across it: the loads of a wave reach the memory
+// system spread out rather than as one burst, which measured markedly faster
+// (a burst of whole-row loads from every wave delays the other waves'
+// requests and lets the waves of the chip fall out of step).
+template <KvType KV>
+__device__ __forceinline__ void gather_v(u32x4_t (&rv)[KvGather<KV>::kVLoads], int slot,
+                                         const char *vb, int64_t v_ss, int lane) {
     using G = KvGather<KV>;
     const int byte_in_row = (lane % G::kLanesPerRow) * 16;
     const int sub = lane / G::kLanesPerRow;   // which row of the load this lane reads
 #pragma unroll
-    for (int q = 0; q < G::kLoads; ++q) {
-        int s = __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q);
+    for (int q = 0; q < G::kVLoads; ++q) {
+        // The rows' addresses are wave-uniform (scalar registers); each lane
+        // then picks the one of its row.
+        const char *row = row_ptr(vb, v_ss, __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q));
 #pragma unroll
         for (int r = 1; r < G::kRowsPerLoad; ++r) {
-            const int sr = __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q + r);
-            s = sub == r ? sr : s;
+            const char *rr =
+                row_ptr(vb, v_ss, __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q + r));
+            row = sub == r ? rr : row;
         }
-        const char *zero = (const char *)kZeroRow + byte_in_row;
-        const char *kp = s >= 0 ? kb + (int64_t)s * k_ss + byte_in_row : zero;
-        const char *vp = s >= 0 ? vb + (int64_t)s * v_ss + byte_in_row : zero;
-        rk[q] = ldg16<u32x4_t>(kp);
-        rv[q] = ldg16<u32x4_t>(vp);
+        rv[q] = ldg16<u32x4_t>(row + byte_in_row);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// 16 FP8 E4M3 codes -> 16 BF16 values (exact: every E4M3 value is a BF16
-// value), as two 16-byte chunks.
-__device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t w, u32x4_t &lo, u32x4_t &hi) {
-    u32x2_t pk[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-        const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-        const bf16x4_t x = {(__bf16)a[0], (__bf16)a[1], (__bf16)b[0], (__bf16)b[1]};
-        pk[i] = __builtin_bit_cast(u32x2_t, x);
-    }
-    lo = u32x4_t{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
-    hi = u32x4_t{pk[2][0], pk[2][1], pk[3][0], pk[3][1]};
-}
-
-// Write a gathered tile into the wave's LDS tiles as BF16 rows (swizzled).
+// Write a gathered V tile into the wave's LDS tile as BF16 rows.
 template <KvType KV>
-__device__ __forceinline__ void stage_tile(const u32x4_t (&rk)[kMaxLoadsPerTile],
-                                           const u32x4_t (&rv)[kMaxLoadsPerTile],
-                                           char *ks, char *vs, int lane) {
+__device__ __forceinline__ void stage_v(const u32x4_t (&rv)[KvGather<KV>::kVLoads], char *vs,
+                                        int lane) {
     using G = KvGather<KV>;
     const int chunk = lane % G::kLanesPerRow;
     const int sub = lane / G::kLanesPerRow;
 #pragma unroll
-    for (int q = 0; q < G::kLoads; ++q) {
+    for (int q = 0; q < G::kVLoads; ++q) {
         const int r = G::kRowsPerLoad * q + sub;
         if constexpr (KV == KvType::kBf16) {
-            const int off = lds_off(r, chunk);
-            *LDS_PTR(u32x4_t, ks + off) = rk[q];
-            *LDS_PTR(u32x4_t, vs + off) = rv[q];
+            *LDS_PTR(u32x4_t, vs + r * kVPitch + 16 * chunk) = rv[q];
         } else {
-            u32x4_t k0, k1, v0, v1;
-            fp8x16_to_bf16(rk[q], k0, k1);
-            fp8x16_to_bf16(rv[q], v0, v1);
-            *LDS_PTR(u32x4_t, ks + lds_off(r, 2 * chunk)) = k0;
-            *LDS_PTR(u32x4_t, ks + lds_off(r, 2 * chunk + 1)) = k1;
-            *LDS_PTR(u32x4_t, vs + lds_off(r, 2 * chunk)) = v0;
-            *LDS_PTR(u32x4_t, vs + lds_off(r, 2 * chunk + 1)) = v1;
+            *LDS_PTR(bf16x8_t, vs + r * kVPitch + 32 * chunk) = fp8x8_to_bf16(rv[q][0], rv[q][1]);
+            *LDS_PTR(bf16x8_t, vs + r * kVPitch + 32 * chunk + 16) =
+                fp8x8_to_bf16(rv[q][2], rv[q][3]);
         }
     }
 }
@@ -262,18 +316,27 @@ __device__ __forceinline__ int tile_slot(const int32_t *list, int tile, int ntil
 
 // ---------------------------------------------------------------- attention
 
-// kSplit = false: workgroup = one item, all its tiles, BF16 output.
+// One wave per workgroup and per work item.
+// kSplit = false: the wave takes all tiles of its item and writes BF16.
 // kSplit = true: workgroup = (item, split s); it takes tiles s, s + splits,
 // s + 2 splits, ... and writes FP32 (O, m, l) of that share to part
 // part_base + s, for qsa_merge_partials (or another shard's partials) to
 // combine.
+//
+// Per tile: the score MFMAs consume K(i) from registers and the loads of
+// K(i+1) are issued into the same registers; the softmax runs; V(i) is
+// written from registers to the wave's LDS tile and the loads of V(i+1) are
+// issued; then P.V reads V(i) back with transpose loads.  So one tile of K
+// and V (16 KiB in BF16) is in flight per wave throughout, and the work
+// between the two halves of the loads paces the wave's requests.  Each wave
+// walks its own item's slot list in order, and the list is grouped by slot
+// range, so a wave's consecutive tiles fall in the same part of the cache.
 template <bool kSplit, KvType KV>
-__global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const AttendParams p) {
+__global__ __launch_bounds__(64, kWavesPerSimd) void attend_kernel(const AttendParams p) {
     using Gth = KvGather<KV>;
     __shared__ __attribute__((aligned(16))) char smem[kAttendLds];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x;
     const int c = lane & 15;   // MFMA column: query head within the block / A-operand row
     const int j = lane >> 4;   // MFMA lane group
 
@@ -293,42 +356,72 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
     const int64_t part_row = kSplit ? ((p.part_base + split) * p.T + t) * p.Hq + h0 : 0;
     if (kSplit && split >= ntiles) {
         // This share is empty: max -inf, sum 0, O 0.
-        for (int idx = threadIdx.x; idx < nh * (kHeadDim / 4); idx += kThreads) {
+        for (int idx = lane; idx < nh * (kHeadDim / 4); idx += 64) {
             const int hh = idx / (kHeadDim / 4), q4 = idx % (kHeadDim / 4);
             *(f32x4_t *)(p.part_o + (part_row + hh) * kHeadDim + 4 * q4) =
                 f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        if (threadIdx.x < nh) {
-            p.part_ml[(part_row + threadIdx.x) * 2] = kNegInf;
-            p.part_ml[(part_row + threadIdx.x) * 2 + 1] = 0.0f;
+        if (lane < nh) {
+            p.part_ml[(part_row + lane) * 2] = kNegInf;
+            p.part_ml[(part_row + lane) * 2 + 1] = 0.0f;
         }
         return;
     }
     uint16_t *out_t = kSplit ? nullptr : p.out + t * p.o_st + (int64_t)h0 * p.o_sh;
     if (!kSplit && n == 0) {
         // Nothing selected: the output row is exactly +0.0.
-        for (int idx = threadIdx.x; idx < nh * kChunksPerRow; idx += kThreads) {
+        for (int idx = lane; idx < nh * kChunksPerRow; idx += 64) {
             const int hh = idx / kChunksPerRow, ch = idx % kChunksPerRow;
             *(u32x4_t *)(out_t + hh * p.o_sh + ch * 8) = u32x4_t{0, 0, 0, 0};
         }
         return;
     }
 
-    // Query heads as the B operand of S^T = K . Q^T: lane (c, j) holds head c,
-    // dims 32 ks + 8 j .. +8 for k-step ks.
-    bf16x8_t qb[8];
-    {
-        const uint16_t *qrow = c < nh ? p.q + t * p.q_st + (int64_t)(h0 + c) * p.q_sh : kZeroRow;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qb[ks] = ldg16<bf16x8_t>(qrow + 32 * ks + 8 * j);
-    }
-
     const int32_t *list = p.list + t * p.list_stride;
     const char *kb = (const char *)p.k + (int64_t)g * p.k_sh * Gth::kElemBytes;
     const char *vb = (const char *)p.v + (int64_t)g * p.v_sh * Gth::kElemBytes;
     const int64_t k_ss = p.k_ss * Gth::kElemBytes, v_ss = p.v_ss * Gth::kElemBytes;
-    char *ks_lds = smem + wave * kWaveLds;
-    char *vs_lds = ks_lds + kTileBytes;
+    char *vs_lds = smem;
+    char *q_lds = smem + kTileBytes;
+
+    // The item's query rows (16 heads; absent heads are zero) go to LDS; their
+    // loads are issued before the first gathers and written after them.
+    u32x4_t qr[kQChunksPerLane];
+#pragma unroll
+    for (int u = 0; u < kQChunksPerLane; ++u) {
+        const int idx = lane + 64 * u;
+        const int r = idx / kChunksPerRow, ch = idx % kChunksPerRow;
+        const uint16_t *src =
+            r < nh ? p.q + t * p.q_st + (int64_t)(h0 + r) * p.q_sh + 8 * ch : kZeroRow + 8 * ch;
+        qr[u] = ldg16<u32x4_t>(src);
+    }
+
+    // This wave's tiles: split, split + splits, ...  The gathers run one
+    // tile ahead: rk and rv hold tile i while tile i+1 is in flight, and
+    // slot_next holds the slots of the next tile to gather (-1 past the list,
+    // where the gathers read the row of zeros: they are issued
+    // unconditionally, so the loaded registers need no copies).  Each slot
+    // vector is loaded before the V gathers of the tile ahead of it, so
+    // waiting for it never waits for those.  (Two tiles ahead measured no
+    // faster.)
+    const int step = splits;
+    u32x4_t rk[Gth::kKLoads], rv[Gth::kVLoads];
+    int tile = split;
+    int slot_next;
+    {
+        const int slot = tile_slot(list, tile, ntiles, lane);
+        gather_k<KV>(rk, slot, kb, k_ss, lane);
+        slot_next = tile_slot(list, tile + step, ntiles, lane);
+        gather_v<KV>(rv, slot, vb, v_ss, lane);
+    }
+
+#pragma unroll
+    for (int u = 0; u < kQChunksPerLane; ++u) {
+        const int idx = lane + 64 * u;
+        *LDS_PTR(u32x4_t, q_lds + (idx / kChunksPerRow) * kQPitch + 16 * (idx % kChunksPerRow)) =
+            qr[u];
+    }
+    wave_lds_fence();
 
     float m = kNegInf;   // running max (log2 domain) for head c
     float lsum = 0.0f;   // this lane's share of the softmax denominator
@@ -336,36 +429,41 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
 #pragma unroll
     for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // This wave's tiles: split + splits * (wave + kWavesPerItem * i).
-    const int step = splits * kWavesPerItem;
-    u32x4_t rk[kMaxLoadsPerTile], rv[kMaxLoadsPerTile];
-    int tile = split + splits * wave;
-    int slot_next = tile_slot(list, tile + step, ntiles, lane);
-    if (tile < ntiles)
-        gather_tile<KV>(rk, rv, tile_slot(list, tile, ntiles, lane), kb, k_ss, vb, v_ss, lane);
-
     const int tr_row = 4 * j + (c >> 2);    // V row this lane addresses in a transpose load
     const int tr_sub = c & 3;               // which 4 of the 16 dims of a block
 
     for (; tile < ntiles; tile += step) {
-        wave_lds_fence();   // the previous tile's LDS reads are done
-        stage_tile<KV>(rk, rv, ks_lds, vs_lds, lane);
-        const int nt = tile + step;
-        if (nt < ntiles) {
-            gather_tile<KV>(rk, rv, slot_next, kb, k_ss, vb, v_ss, lane);
-            slot_next = tile_slot(list, nt + step, ntiles, lane);
-        }
-        wave_lds_fence();   // other lanes of this wave wrote the rows read below
-
         // S^T for the tile: s[i] = score of tile slot 4j+i against head c.
-        bf16x8_t ka[8];
-#pragma unroll
-        for (int kstep = 0; kstep < 8; ++kstep)
-            ka[kstep] = *LDS_PTR(bf16x8_t, ks_lds + lds_off(c, 4 * kstep + j));
+        // The query operands are read from LDS in two halves to bound the
+        // registers they hold.
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kstep = 0; kstep < 8; ++kstep)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kstep], qb[kstep], s, 0, 0, 0);
+        for (int half = 0; half < 2; ++half) {
+            bf16x8_t qb[kKSteps / 2];
+#pragma unroll
+            for (int u = 0; u < kKSteps / 2; ++u)
+                qb[u] = *LDS_PTR(bf16x8_t,
+                                 q_lds + c * kQPitch + 16 * q_chunk(half * kKSteps / 2 + u, j));
+#pragma unroll
+            for (int u = 0; u < kKSteps / 2; ++u)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    k_operand<KV>(rk, half * kKSteps / 2 + u), qb[u], s, 0, 0, 0);
+        }
+        // Where the loads of the next tile's K go: FP8 tiles are short and
+        // latency-bound, so they are issued early, half before the softmax
+        // and half after its row maximum; BF16 loads are spread over the P.V
+        // MFMAs below, one per two MFMAs (measured fastest of the placements
+        // tried: all at once after the scores, spread over the softmax, or
+        // alternating with the V loads).
+        const int slot_g = slot_next;
+        __builtin_amdgcn_sched_barrier(0);   // K(i) is consumed before K(i+1) lands
+        if constexpr (KV == KvType::kFp8) {
+#pragma unroll
+            for (int q = 0; q < Gth::kKLoads / 2; ++q) {
+                gather_k1<KV>(rk[q], q, slot_g, kb, k_ss, lane);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
 
         // Online softmax in the log2 domain; slots at or past n are masked.
         const int first = tile * kTileSlots + 4 * j;
@@ -375,6 +473,14 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
         float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
+        if constexpr (KV == KvType::kFp8) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = Gth::kKLoads / 2; q < Gth::kKLoads; ++q) {
+                gather_k1<KV>(rk[q], q, slot_g, kb, k_ss, lane);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         const bool raise = mt > m + kRescaleSlack;
         const float m_new = raise ? mt : m;
         if (__ballot(raise)) {
@@ -392,73 +498,61 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void attend_kernel(const Att
             lsum += (float)pr;
         }
 
+        wave_lds_fence();   // the previous tile's transpose reads are done
+        stage_v<KV>(rv, vs_lds, lane);
+        __builtin_amdgcn_sched_barrier(0);   // V(i) is consumed before V(i+1) lands
+        slot_next = tile_slot(list, tile + 2 * step, ntiles, lane);
+        gather_v<KV>(rv, slot_g, vb, v_ss, lane);
+        wave_lds_fence();   // other lanes of this wave wrote the rows read below
+
         // O^T += V^T . P^T over the tile's 16 slots.  The k index of lane
         // group j is slots 4j..4j+3, matching pb.  ds_read_b64_tr_b16: lane i
         // of a 16-lane group addresses row 4j + i/4, dims 16 db + 4 (i%4);
         // lane c then receives V[4j + e][16 db + c] for e = 0..3.
-        bf16x4_t va[kDimBlocks];
 #pragma unroll
-        for (int db = 0; db < kDimBlocks; ++db) {
-            const int chunk = 2 * db + (tr_sub >> 1);
-            va[db] = __builtin_bit_cast(
-                bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(
-                              i16x4_t, vs_lds + lds_off(tr_row, chunk) + 8 * (tr_sub & 1))));
+        for (int half = 0; half < 2; ++half) {
+            bf16x4_t va[kDimBlocks / 2];
+#pragma unroll
+            for (int u = 0; u < kDimBlocks / 2; ++u) {
+                const int db = half * (kDimBlocks / 2) + u;
+                va[u] = __builtin_bit_cast(
+                    bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(
+                                  i16x4_t, vs_lds + tr_row * kVPitch + 32 * db + 8 * tr_sub)));
+            }
+#pragma unroll
+            for (int u = 0; u < kDimBlocks / 2; ++u) {
+                const int db = half * (kDimBlocks / 2) + u;
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[u], pb, o[db], 0, 0, 0);
+                constexpr int kEvery = kDimBlocks / Gth::kKLoads;
+                if (KV == KvType::kBf16 && db % kEvery == kEvery - 1) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    gather_k1<KV>(rk[db / kEvery], db / kEvery, slot_g, kb, k_ss, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
-#pragma unroll
-        for (int db = 0; db < kDimBlocks; ++db)
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[db], pb, o[db], 0, 0, 0);
     }
 
-    // Whole-head denominator of this wave: add the four lane groups.
+    // Whole-head denominator: add the four lane groups.
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
 
-    // Merge the waves' partial states through LDS (reusing the tile area).
-    __syncthreads();
-    f32x4_t *part_o = (f32x4_t *)smem;                                     // [wave][db][lane]
-    float *part_m = (float *)(smem + kWavesPerItem * kWaveLds);            // [wave][head]
-    float *part_l = part_m + kWavesPerItem * kHeadBlock;                   // [wave][head]
-#pragma unroll
-    for (int db = 0; db < kDimBlocks; ++db) part_o[(wave * kDimBlocks + db) * 64 + lane] = o[db];
-    if (j == 0) {
-        part_m[wave * kHeadBlock + c] = m;
-        part_l[wave * kHeadBlock + c] = lsum;
-    }
-    __syncthreads();
-
-    float mw[kWavesPerItem], fw[kWavesPerItem];
-    float mmax = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWavesPerItem; ++w) {
-        mw[w] = part_m[w * kHeadBlock + c];
-        mmax = fmaxf(mmax, mw[w]);
-    }
-    float l_tot = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWavesPerItem; ++w) {
-        fw[w] = __builtin_amdgcn_exp2f(mw[w] - mmax);   // 0 for waves without tiles
-        l_tot += fw[w] * part_l[w * kHeadBlock + c];
-    }
-    constexpr int kDbPerWave = kDimBlocks / kWavesPerItem;
+    // Lane (c, j) holds dims 16 db + 4 j .. +4 of head c.
     if (c < nh) {
-        if (kSplit && wave == 0 && j == 0) {
-            p.part_ml[(part_row + c) * 2] = mmax;
-            p.part_ml[(part_row + c) * 2 + 1] = l_tot;
+        if (kSplit && j == 0) {
+            p.part_ml[(part_row + c) * 2] = m;
+            p.part_ml[(part_row + c) * 2 + 1] = lsum;
         }
 #pragma unroll
-        for (int d = 0; d < kDbPerWave; ++d) {
-            const int db = wave * kDbPerWave + d;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int w = 0; w < kWavesPerItem; ++w)
-                acc += fw[w] * part_o[(w * kDimBlocks + db) * 64 + lane];
+        for (int db = 0; db < kDimBlocks; ++db) {
+            f32x4_t acc = o[db];
             if constexpr (KV == KvType::kFp8) acc *= p.v_scale;
             if (kSplit) {
                 *(f32x4_t *)(p.part_o + (part_row + c) * kHeadDim + 16 * db + 4 * j) = acc;
             } else {
                 bf16x4_t ob;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ob[i] = (__bf16)(acc[i] / l_tot);
+                for (int i = 0; i < 4; ++i) ob[i] = (__bf16)(acc[i] / lsum);
                 *(u32x2_t *)(out_t + (int64_t)c * p.o_sh + 16 * db + 4 * j) =
                     __builtin_bit_cast(u32x2_t, ob);
             }
@@ -496,18 +590,19 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
         __builtin_bit_cast(u32x2_t, ob);
 }
 
-// ---------------------------------------------------------------- gather ceiling
+// ---------------------------------------------------------------- gather only
 
-// Reads the same rows with the same tiles, waves, prefetch distance and
-// residency as attend_kernel, folds them with XOR and writes one word per
-// (t, g): the cost of the gathers alone.
+// Issues the same loads as attend_kernel (same load pattern, tiles, one wave
+// per (t, g), same residency per CU) with no arithmetic between them, folds
+// them with XOR and writes one word per (t, g).  It shows the cost of the
+// gathers issued back to back; the attention kernel, whose work between the
+// K and the V loads paces each wave's requests, can run faster than this.
 template <KvType KV>
-__global__ __launch_bounds__(kThreads, kItemsPerCU) void ceiling_kernel(const CeilingParams p) {
+__global__ __launch_bounds__(64, kWavesPerSimd) void gather_only_kernel(const GatherParams p) {
     using Gth = KvGather<KV>;
     // Same LDS footprint as attend_kernel, so the same number of items fit a CU.
-    __shared__ __attribute__((aligned(16))) char smem[kAttendLds];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) uint32_t smem[kAttendLds / 4];
+    const int lane = threadIdx.x;
     const int64_t item = blockIdx.x;
     const int64_t t = item / p.Hkv;
     const int g = (int)(item - t * p.Hkv);
@@ -519,31 +614,35 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void ceiling_kernel(const Ce
     const int64_t k_ss = p.k_ss * Gth::kElemBytes, v_ss = p.v_ss * Gth::kElemBytes;
 
     u32x4_t acc = {0, 0, 0, 0};
-    u32x4_t rk[kMaxLoadsPerTile], rv[kMaxLoadsPerTile];
-    int tile = wave;
-    int slot_next = tile_slot(list, tile + kWavesPerItem, ntiles, lane);
-    if (tile < ntiles)
-        gather_tile<KV>(rk, rv, tile_slot(list, tile, ntiles, lane), kb, k_ss, vb, v_ss, lane);
-    for (; tile < ntiles; tile += kWavesPerItem) {
+    u32x4_t rk[Gth::kKLoads], rv[Gth::kVLoads];
+    int tile = 0;
+    int slot_next;
+    {
+        const int slot = tile_slot(list, tile, ntiles, lane);
+        gather_k<KV>(rk, slot, kb, k_ss, lane);
+        slot_next = tile_slot(list, tile + 1, ntiles, lane);
+        gather_v<KV>(rv, slot, vb, v_ss, lane);
+    }
+    for (; tile < ntiles; ++tile) {
 #pragma unroll
-        for (int q = 0; q < Gth::kLoads; ++q) acc ^= rk[q] ^ rv[q];
-        const int nt = tile + kWavesPerItem;
-        if (nt < ntiles) {
-            gather_tile<KV>(rk, rv, slot_next, kb, k_ss, vb, v_ss, lane);
-            slot_next = tile_slot(list, nt + kWavesPerItem, ntiles, lane);
-        }
+        for (int q = 0; q < Gth::kKLoads; ++q) acc ^= rk[q];
+        __builtin_amdgcn_sched_barrier(0);
+        gather_k<KV>(rk, slot_next, kb, k_ss, lane);
+#pragma unroll
+        for (int q = 0; q < Gth::kVLoads; ++q) acc ^= rv[q];
+        __builtin_amdgcn_sched_barrier(0);
+        const int slot = slot_next;
+        slot_next = tile_slot(list, tile + 2, ntiles, lane);
+        gather_v<KV>(rv, slot, vb, v_ss, lane);
     }
     uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off);
-    uint32_t *fold = (uint32_t *)smem;
-    if (lane == 0) fold[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t y = 0;
-        for (int w = 0; w < kWavesPerItem; ++w) y ^= fold[w];
-        p.sink[item] = y;
-    }
+    // Every lane holds the fold; it reaches lane 0 through the LDS block (from
+    // lane 63), which keeps the block allocated.
+    smem[lane] = x;
+    wave_lds_fence();
+    if (lane == 0) p.sink[item] = smem[63];
 }
 
 // ---------------------------------------------------------------- indexer
@@ -551,7 +650,7 @@ __global__ __launch_bounds__(kThreads, kItemsPerCU) void ceiling_kernel(const Ce
 // score[t, c] = sum_h max(0, iq[t,h] . ik[c]) with bf16 MFMA.  A workgroup
 // takes 64 tokens (16 per wave, as 4 MFMA row tiles of 4 tokens x 4 heads)
 // and one range of kScoreSplit index keys, walked in tiles of 64 blocks
-// staged in LDS (swizzled like the attention tiles) and shared by all four
+// staged in LDS (swizzled) and shared by all four
 // row tiles; it stops at the last block any of its tokens may select.  MFMA
 // rows are (token, head) pairs, so lane (c, j) of a 16x16 output holds the 4
 // heads of one token against block c and the head sum stays in the lane.
@@ -561,6 +660,10 @@ constexpr int kScoreTile = 64;
 constexpr int kScoreSplit = 4096;
 constexpr int kIndexRowBytes = kIndexDim * 2;   // 256 B
 
+// LDS byte offset of 16-byte chunk `chunk` of index-key tile row `r`.  The
+// chunk index is XOR-swizzled by a bijection of r & 7 so that the 8 rows read
+// by one phase of a 16-byte read hit 8 different bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 __device__ __forceinline__ int idx_off(int r, int chunk) {
     return r * kIndexRowBytes + ((chunk ^ swz(r)) << 4);
 }
@@ -915,10 +1018,10 @@ hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_
     if (items == 0) return hipSuccess;
     if (kv == KvType::kFp8)
         hipLaunchKernelGGL((attend_kernel<false, KvType::kFp8>), dim3((unsigned)items),
-                           dim3(kThreads), 0, stream, p);
+                           dim3(64), 0, stream, p);
     else
         hipLaunchKernelGGL((attend_kernel<false, KvType::kBf16>), dim3((unsigned)items),
-                           dim3(kThreads), 0, stream, p);
+                           dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -928,10 +1031,10 @@ hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
     if (blocks == 0) return hipSuccess;
     if (kv == KvType::kFp8)
         hipLaunchKernelGGL((attend_kernel<true, KvType::kFp8>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, stream, p);
+                           dim3(64), 0, stream, p);
     else
         hipLaunchKernelGGL((attend_kernel<true, KvType::kBf16>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, stream, p);
+                           dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -942,14 +1045,14 @@ hipError_t launch_merge(const MergeParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_ceiling(const CeilingParams &p, KvType kv, int64_t T, hipStream_t stream) {
+hipError_t launch_gather_only(const GatherParams &p, KvType kv, int64_t T, hipStream_t stream) {
     const int64_t items = T * (int64_t)p.Hkv;
     if (items == 0) return hipSuccess;
     if (kv == KvType::kFp8)
-        hipLaunchKernelGGL(ceiling_kernel<KvType::kFp8>, dim3((unsigned)items), dim3(kThreads), 0,
+        hipLaunchKernelGGL(gather_only_kernel<KvType::kFp8>, dim3((unsigned)items), dim3(64), 0,
                            stream, p);
     else
-        hipLaunchKernelGGL(ceiling_kernel<KvType::kBf16>, dim3((unsigned)items), dim3(kThreads), 0,
+        hipLaunchKernelGGL(gather_only_kernel<KvType::kBf16>, dim3((unsigned)items), dim3(64), 0,
                            stream, p);
     return hipGetLastError();
 }
