@@ -152,3 +152,62 @@ def test_indexed_long_prefill_sampled_rows():
     want = oracle.prefill(np.ascontiguousarray(case.q[rows]), case.k_cache, case.v_cache,
                           want_sel, 1.0 / 16.0)
     gate(bf16_tensor_to_f32(out), want, empty_row_mask(want_sel, case.S))
+
+
+def select_on(scores_np, positions_np, slot_of_pos_np, budget):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    sel = qsa.indexer_select(t(scores_np), t(positions_np), t(slot_of_pos_np), budget)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy()
+
+
+@pytest.mark.parametrize("L,budget", [(80000, 8), (80000, 960), (80000, 961), (80000, 3000),
+                                      (20000, 300), (20000, 1500), (9000, 960)])
+def test_selection_paths_by_budget_and_row_length(L, budget):
+    """Budgets up to 960 take the sampled-threshold kernel, larger ones the
+    histogram kernel (rows staged in LDS up to 16,384 blocks, else read from
+    memory).  Integer scores with many ties: every path must match the
+    oracle exactly."""
+    rng = np.random.Generator(np.random.PCG64(1150 + L + budget))
+    C = -(-L // 4)
+    T = 9
+    scores = rng.integers(0, 40, size=(T, C)).astype(np.float32)
+    positions = np.sort(rng.choice(L, size=T, replace=False)).astype(np.int32)
+    positions[-1] = L - 1
+    slot_of_pos = rng.permutation(L).astype(np.int32)
+    got = select_on(scores, positions, slot_of_pos, budget)
+    want = oracle.indexer_select(scores, positions, slot_of_pos, budget)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_all_equal_scores_keep_the_lowest_blocks():
+    """Every score equal: the sampled threshold admits the whole row, more
+    than the candidate list holds, so the kernel takes its exact fallback; the
+    ties go to the lowest blocks."""
+    L, budget, T = 60000, 512, 5
+    C = L // 4
+    scores = np.zeros((T, C), dtype=np.float32)
+    positions = np.array([L - 1, 30000, 20000, 2100, 3], dtype=np.int32)
+    slot_of_pos = np.random.Generator(np.random.PCG64(1160)).permutation(L).astype(np.int32)
+    got = select_on(scores, positions, slot_of_pos, budget)
+    want = oracle.indexer_select(scores, positions, slot_of_pos, budget)
+    np.testing.assert_array_equal(got, want)
+    assert np.array_equal(got[0][:4 * budget], slot_of_pos[:4 * budget])
+
+
+def test_fractional_scores_with_one_tied_cut():
+    """Random scores with a block of exact ties straddling the cut: the first
+    tied blocks in block order are kept."""
+    rng = np.random.Generator(np.random.PCG64(1170))
+    L, budget, T = 65536, 512, 6
+    C = L // 4
+    scores = rng.random((T, C), dtype=np.float32)
+    for t in range(T):
+        cut = np.sort(scores[t])[::-1][budget - 1]
+        tied = rng.choice(C, size=300, replace=False)
+        scores[t, tied] = cut
+    positions = (L - 1 - np.arange(T) * 997).astype(np.int32)
+    slot_of_pos = rng.permutation(L).astype(np.int32)
+    got = select_on(scores, positions, slot_of_pos, budget)
+    want = oracle.indexer_select(scores, positions, slot_of_pos, budget)
+    np.testing.assert_array_equal(got, want)

@@ -755,19 +755,41 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 
 // Find, among the keys of `n` scores that pass `in_set`, the `need`-th largest
 // key tau and how many keys equal to tau must be kept (written to sh_prefix /
-// sh_need), with four 8-bit-digit radix passes.  hist is 256 ints of LDS.
-template <typename ScoreAt, typename InSet>
+// sh_need), with 8-bit-digit radix passes.  hist is 256 ints of LDS.  With
+// kPasses < 4 only the top 8 * kPasses bits are resolved: the result is the
+// need-th largest key with its other bits cleared (a lower bound of it).
+template <int kPasses = 4, typename ScoreAt, typename InSet>
 __device__ void radix_select(int n, int need, ScoreAt score_at, InSet in_set, int *hist,
                              uint32_t *sh_prefix, int *sh_need) {
     const int tid = threadIdx.x;
     uint32_t prefix = 0, mask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = 24; shift >= 32 - 8 * kPasses; shift -= 8) {
         hist[tid] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += 256) {
-            const float x = score_at(i);
-            const uint32_t u = score_key(x);
-            if (in_set(x) && (u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+        for (int i0 = 0; i0 < n; i0 += 256) {
+            const int i = i0 + tid;
+            bool hit = false;
+            int digit = 0;
+            if (i < n) {
+                const float x = score_at(i);
+                const uint32_t u = score_key(x);
+                hit = in_set(x) && (u & mask) == prefix;
+                digit = (u >> shift) & 255;
+            }
+            // The keys of a row share their leading digits, so most lanes
+            // of a wave hit the same bin: the lanes with the first active
+            // lane's digit add their count with one atomic.
+            const uint64_t active = __ballot(hit);
+            if (active) {
+                const int lead = __builtin_amdgcn_readlane(digit, __builtin_ctzll(active));
+                const uint64_t same = __ballot(hit && digit == lead);
+                if (hit && digit == lead) {
+                    if ((tid & 63) == __builtin_ctzll(same))
+                        atomicAdd(&hist[lead], (int)__popcll(same));
+                } else if (hit) {
+                    atomicAdd(&hist[digit], 1);
+                }
+            }
         }
         __syncthreads();
         if (tid < 64) {
@@ -806,7 +828,7 @@ __device__ void radix_select(int n, int need, ScoreAt score_at, InSet in_set, in
 // float range, so a radix pass over raw key bits would pile every key into
 // one or two bins; the linear buckets spread them.
 template <bool kInLds>
-__global__ __launch_bounds__(256) void indexer_select_kernel(const IndexerSelectParams p) {
+__device__ void select_exact(const IndexerSelectParams &p, int n, const float *row, int32_t *out) {
     using Scan = hipcub::BlockScan<int, 256>;
     using Reduce = hipcub::BlockReduce<float, 256>;
     __shared__ float vals[kInLds ? kSelectLdsBlocks : 1];
@@ -819,18 +841,7 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(const IndexerSelect
     __shared__ uint32_t sh_prefix;
     __shared__ int sh_need;
     __shared__ float sh_lo, sh_hi;
-
-    const int64_t t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t pos = p.positions[t];
-    int32_t *out = p.out + t * p.out_stride;
-    const int width = kIndexBlock * p.budget + 3;
-    if (pos < 0 || pos >= p.L) {
-        for (int i = tid; i < width; i += 256) out[i] = -1;
-        return;
-    }
-    const int n = (int)min<int64_t>((pos + 1) / kIndexBlock, p.C);
-    const float *row = p.scores + t * p.C;
 
     // Row statistics (and the LDS copy): 16-byte loads, four in flight per
     // thread, so the row arrives in a few memory round trips.
@@ -965,24 +976,207 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(const IndexerSelect
         eq_before += eq_tot;
         __syncthreads();   // chunk counts are rewritten by the next group
     }
-    // Expand every kept block into its slots; all the slot-table reads of the
-    // row are independent and in flight together.
-    const int kept = min(n, p.budget);
+}
+
+// Expand every kept block id (written at out[4 e], e < kept) into its 4 slots,
+// then write the causal tail and the -1 padding.  All the slot-table reads of
+// the row are independent and in flight together.
+__device__ void expand_row(const IndexerSelectParams &p, int64_t pos, int kept, int32_t *out,
+                           int width) {
+    const int tid = threadIdx.x;
     __threadfence_block();
     __syncthreads();
+    const bool vec_ok = ((uintptr_t)p.slot_of_pos % 16) == 0 && ((uintptr_t)out % 16) == 0;
     for (int e = tid; e < kept; e += 256) {
         const int64_t blk = out[kIndexBlock * e];
         const int32_t *src = p.slot_of_pos + kIndexBlock * blk;
-        int32_t sl[kIndexBlock];
+        if (vec_ok) {
+            *(u32x4_t *)(out + kIndexBlock * e) = *(const u32x4_t *)src;
+        } else {
+            int32_t sl[kIndexBlock];
 #pragma unroll
-        for (int q = 0; q < kIndexBlock; ++q) sl[q] = src[q];
+            for (int q = 0; q < kIndexBlock; ++q) sl[q] = src[q];
 #pragma unroll
-        for (int q = 0; q < kIndexBlock; ++q) out[kIndexBlock * e + q] = sl[q];
+            for (int q = 0; q < kIndexBlock; ++q) out[kIndexBlock * e + q] = sl[q];
+        }
     }
     const int r = (int)((pos + 1) % kIndexBlock);
     const int tail0 = kIndexBlock * kept;
     for (int i = tid; i < width - tail0; i += 256)
         out[tail0 + i] = i < r ? p.slot_of_pos[pos - r + 1 + i] : -1;
+}
+
+template <bool kInLds>
+__global__ __launch_bounds__(256) void indexer_select_kernel(const IndexerSelectParams p) {
+    const int64_t t = blockIdx.x;
+    const int64_t pos = p.positions[t];
+    int32_t *out = p.out + t * p.out_stride;
+    const int width = kIndexBlock * p.budget + 3;
+    if (pos < 0 || pos >= p.L) {
+        for (int i = threadIdx.x; i < width; i += 256) out[i] = -1;
+        return;
+    }
+    const int n = (int)min<int64_t>((pos + 1) / kIndexBlock, p.C);
+    select_exact<kInLds>(p, n, p.scores + t * p.C, out);
+    expand_row(p, pos, min(n, p.budget), out, width);
+}
+
+// The same selection, faster for budgets up to kSelCand / 4: the threshold
+// is first estimated from kSelSample scores spaced evenly over the row (the
+// top 16 bits of the key ranked about 2 * budget * kSelSample / n from the
+// top); one pass over the row then keeps, in block order, the scores whose
+// key is at least the estimate (about 2 * budget of them), and the exact
+// selection runs on that short list.  It is exact whenever at least `budget` scores pass the
+// estimate (the budget-th largest key and all its ties then pass); rows where
+// fewer pass, or more than kSelCand, take select_exact.
+constexpr int kSelSample = 1024;
+constexpr int kSelCand = 3840;   // a multiple of 256
+constexpr int kSelPerThread = 16;   // scores per thread per pass over the row
+// Candidate i is stored at i + i / 16: the output pass, where thread t reads
+// candidates 16 t .. 16 t + 15, then reads 64 different banks.
+__device__ __forceinline__ int cand_at(int i) { return i + (i >> 4); }
+constexpr int kSelCandPadded = kSelCand + kSelCand / 16;
+
+__global__ __launch_bounds__(256) void indexer_select_fast_kernel(const IndexerSelectParams p) {
+    using Scan = hipcub::BlockScan<int, 256>;
+    __shared__ float cval[kSelCandPadded];
+    __shared__ int cid[kSelCandPadded];
+    __shared__ int hist[256];
+    __shared__ typename Scan::TempStorage scan;
+    __shared__ uint32_t sh_prefix;
+    __shared__ int sh_need;
+
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t pos = p.positions[t];
+    int32_t *out = p.out + t * p.out_stride;
+    const int width = kIndexBlock * p.budget + 3;
+    if (pos < 0 || pos >= p.L) {
+        for (int i = tid; i < width; i += 256) out[i] = -1;
+        return;
+    }
+    const int n = (int)min<int64_t>((pos + 1) / kIndexBlock, p.C);
+    const float *row = p.scores + t * p.C;
+    auto all = [](float) { return true; };
+
+    // Scores [base, base + kSlice) of the row, kSelPerThread consecutive ones
+    // per thread (16-byte loads where aligned).
+    const bool vec_ok = ((uintptr_t)row % 16) == 0;
+    constexpr int kSlice = 256 * kSelPerThread;
+    auto load_slice = [&](int base, float (&v)[kSelPerThread]) {
+        const int i0 = base + kSelPerThread * tid;
+#pragma unroll
+        for (int u = 0; u < kSelPerThread / 4; ++u) {
+            const int i = i0 + 4 * u;
+            if (vec_ok && i + 3 < n) {
+                const f32x4_t x = *(const f32x4_t *)(row + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * u + e] = x[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * u + e] = i + e < n ? row[i + e] : 0.0f;
+            }
+        }
+    };
+
+    if (n <= p.budget) {
+        for (int e = tid; e < n; e += 256) out[kIndexBlock * e] = e;
+    } else {
+        // The first two slices are in flight while the threshold is estimated.
+        float v[kSelPerThread], v1[kSelPerThread];
+        load_slice(0, v);
+        if (kSlice < n) load_slice(kSlice, v1);
+        // 1. Estimated threshold (every key passes when the row fits the list).
+        uint32_t tau0 = 0;
+        if (n > kSelCand) {
+            for (int k = tid; k < kSelSample; k += 256)
+                cval[k] = row[(int64_t)k * n / kSelSample];
+            __syncthreads();
+            const int kth =
+                (int)min<int64_t>(kSelSample, (2 * (int64_t)p.budget * kSelSample + n - 1) / n);
+            radix_select<2>(kSelSample, kth, [&](int i) { return cval[i]; }, all, hist,
+                            &sh_prefix, &sh_need);
+            tau0 = sh_prefix;
+        }
+        // 2. Candidates in block order: each thread takes kSelPerThread
+        // consecutive scores per slice, the next two slices loading while
+        // this one is placed by a block scan of the per-thread counts.
+        int nc = 0;
+        for (int base = 0; base < n; base += kSlice) {
+            float v2[kSelPerThread];
+            if (base + 2 * kSlice < n) load_slice(base + 2 * kSlice, v2);
+            const int i0 = base + kSelPerThread * tid;
+            int cnt = 0;
+#pragma unroll
+            for (int e = 0; e < kSelPerThread; ++e)
+                cnt += i0 + e < n && score_key(v[e]) >= tau0;
+            int off, total;
+            Scan(scan).ExclusiveSum(cnt, off, total);
+            if (nc + total <= kSelCand) {
+                int w = nc + off;
+#pragma unroll
+                for (int e = 0; e < kSelPerThread; ++e) {
+                    if (i0 + e < n && score_key(v[e]) >= tau0) {
+                        cval[cand_at(w)] = v[e];
+                        cid[cand_at(w)] = i0 + e;
+                        ++w;
+                    }
+                }
+            }
+            nc += total;
+            __syncthreads();   // the scan storage is reused
+#pragma unroll
+            for (int e = 0; e < kSelPerThread; ++e) {
+                v[e] = v1[e];
+                v1[e] = v2[e];
+            }
+        }
+
+        if (nc < p.budget || nc > kSelCand) {
+            select_exact<false>(p, n, row, out);
+        } else {
+            // 3. Exact threshold key tau among the candidates and how many
+            // keys equal to tau to keep.
+            radix_select(nc, p.budget, [&](int i) { return cval[cand_at(i)]; }, all, hist,
+                         &sh_prefix, &sh_need);
+            const uint32_t tau = sh_prefix;
+            const int need = sh_need;
+            // 4. Output in block order.  Thread t owns candidates
+            // [kPer t, kPer (t + 1)); a kept candidate's position is the
+            // number of keys > tau before it plus the number of kept ties
+            // (the first `need` in block order) before it.
+            constexpr int kPer = kSelCand / 256;
+            int gt = 0, eq = 0;
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const int i = kPer * tid + k;
+                if (i < nc) {
+                    const uint32_t u = score_key(cval[cand_at(i)]);
+                    gt += u > tau;
+                    eq += u == tau;
+                }
+            }
+            int gt_pre, eq_pre, total;
+            Scan(scan).ExclusiveSum(gt, gt_pre, total);
+            __syncthreads();
+            Scan(scan).ExclusiveSum(eq, eq_pre, total);
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const int i = kPer * tid + k;
+                if (i < nc) {
+                    const uint32_t u = score_key(cval[cand_at(i)]);
+                    if (u > tau) {
+                        out[kIndexBlock * (gt_pre + min(eq_pre, need))] = cid[cand_at(i)];
+                        ++gt_pre;
+                    } else if (u == tau) {
+                        if (eq_pre < need) out[kIndexBlock * (gt_pre + eq_pre)] = cid[cand_at(i)];
+                        ++eq_pre;
+                    }
+                }
+            }
+        }
+    }
+    expand_row(p, pos, min(n, p.budget), out, width);
 }
 
 }  // namespace
@@ -998,7 +1192,10 @@ hipError_t launch_indexer_scores(const IndexerScoreParams &p, hipStream_t stream
 
 hipError_t launch_indexer_select(const IndexerSelectParams &p, hipStream_t stream) {
     if (p.T == 0) return hipSuccess;
-    if (p.C <= kSelectLdsBlocks)
+    if (4 * (int64_t)p.budget <= kSelCand)
+        hipLaunchKernelGGL(indexer_select_fast_kernel, dim3((unsigned)p.T), dim3(256), 0, stream,
+                           p);
+    else if (p.C <= kSelectLdsBlocks)
         hipLaunchKernelGGL(indexer_select_kernel<true>, dim3((unsigned)p.T), dim3(256), 0, stream,
                            p);
     else
