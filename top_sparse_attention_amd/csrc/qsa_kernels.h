@@ -13,17 +13,18 @@ constexpr int kHeadDim = 256;
 constexpr int kTileSlots = 16;
 // Compacted lists are padded with -1 to a multiple of this.
 constexpr int kListPad = 32;
-// Work items (one wave each) resident per CU.  Exactly 8 (2 per SIMD): the
-// attention kernel requests enough LDS per item that a 9th does not fit.
+// Work items (one wave each) resident per CU in the attention kernel's
+// general layout.  Exactly 8 (2 per SIMD): the kernel requests enough LDS per
+// item that a 9th does not fit.
 // With every SIMD holding the same number of waves, the waves of a CU, and
 // of the whole chip, advance through their slot-sorted lists at the same
 // rate, so concurrent tokens read the same cache rows at about the same
 // time and share them in L2; an uneven split (7 or 9 waves per CU) lets the
 // waves drift apart and loses most of that sharing.
 constexpr int kItemsPerCU = 8;
-// Waves per SIMD the attention kernel's registers are budgeted for (up to
-// 256 registers per wave).
-constexpr int kWavesPerSimd = 2;
+// Waves per SIMD the attention kernel's registers are budgeted for in that
+// layout (up to 256 registers per wave).
+constexpr int kAttendWavesPerSimd = 2;
 // Fewest tiles a split of the decode path takes.
 constexpr int kMinSplitTiles = 4;
 // Entries of a selection row sorted together by the compaction pass.

@@ -17,8 +17,8 @@
 //     large pages of the cache, which the memory system serves markedly
 //     faster than uniformly scattered rows.
 //  2. attend_kernel: one work item = (token t, KV head g, block of up to 16
-//     query heads of that group) = one wave, kItemsPerCU items resident per
-//     CU.  The wave walks its item's 16-slot tiles in list order.  Per tile
+//     query heads of that group) = one wave, 8 (or 12, see AttendLayout)
+//     items resident per CU.  The wave walks its item's 16-slot tiles in list order.  Per tile
 //     it loads the K rows straight into the registers of the score MFMA's A
 //     operand and the V rows (whole rows) into registers that it then writes
 //     to its LDS tile, both one tile ahead of use; computes the 16x16 score
@@ -47,11 +47,11 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 #define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T *)(p))
@@ -59,16 +59,11 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kRowBytes = kHeadDim * 2;             // one BF16 row: 512 B
 constexpr int kChunksPerRow = kRowBytes / 16;       // 32 sixteen-byte chunks
 
-// LDS row pitches.  Rows are padded rather than swizzled, so every LDS
-// access of the tile loop is one per-lane base address plus an immediate
-// offset.  V tile rows (544 B = 136 banks): the 4 rows one 16-lane group
-// reads with a transpose load fall in 4 different 32-byte bank windows, and
-// 8 lanes writing consecutive chunks of a row hit 8 different 16-byte bank
-// groups.  Query rows (528 B = 33 chunks): the 8 rows read by one phase of a
-// 16-byte read start in 8 different 16-byte bank groups.
-constexpr int kVPitch = kRowBytes + 32;
+// LDS row pitch of the query rows (528 B = 33 chunks: the 8 rows read by
+// one phase of a 16-byte read start in 8 different 16-byte bank groups).
+// Rows are padded rather than swizzled, so every LDS access of the tile loop
+// is one per-lane base address plus an immediate offset.
 constexpr int kQPitch = kRowBytes + 16;
-constexpr int kTileBytes = kTileSlots * kVPitch;    // the wave's V tile: 8.5 KiB
 
 // How one tile of a cache with this element type is gathered.
 //  K: 16 rows in MFMA A-operand layout; every lane loads 16 bytes per load
@@ -87,8 +82,6 @@ struct KvGather {
 constexpr int kHeadBlock = 16;                      // query heads per MFMA column block
 constexpr int kDimBlocks = kHeadDim / 16;           // 16 output blocks of 16 dims
 constexpr int kKSteps = kHeadDim / 32;              // 8 k-steps of the score MFMA
-constexpr int kQBytes = kHeadBlock * kQPitch;       // an item's query rows in LDS
-constexpr int kQChunksPerLane = kHeadBlock * kChunksPerRow / 64;   // 8
 constexpr float kNegInf = -__builtin_huge_valf();
 // A new running maximum is adopted only when it exceeds the current one by
 // more than this (log2 units); otherwise probabilities may reach 2^8, which
@@ -96,14 +89,34 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // rescales of the O accumulators.
 constexpr float kRescaleSlack = 8.0f;
 
-// LDS of one item (one wave): its V tile and its query rows, in a block
-// sized so that kItemsPerCU items fit in the 160 KiB of a CU and one more
-// does not.
-constexpr int kAttendLdsUsed = kTileBytes + kQBytes;
-constexpr int kAttendLds = 160 * 1024 / kItemsPerCU - 1024;
-static_assert(kAttendLdsUsed <= kAttendLds, "item LDS");
-static_assert(kItemsPerCU * kAttendLds <= 160 * 1024, "LDS budget of a gfx950 CU");
-static_assert((kItemsPerCU + 1) * kAttendLds > 160 * 1024, "one more item must not fit");
+// LDS layout and residency of one attention item (one wave): its V tile and
+// kQRows query rows.
+//  kQRows = 16 (any head ratio): V rows of 544 B (136 banks: the 4 rows one
+//    16-lane group reads with a transpose load fall in 4 different 32-byte
+//    bank windows; 8 lanes writing consecutive chunks of a row hit 8 different
+//    16-byte bank groups).  The item requests a block sized so that exactly
+//    kItemsPerCU items fit in the 160 KiB of a CU.
+//  kQRows = 8 (FP8 caches with at most 8 query heads per KV head): V rows of
+//    528 B; the 12.4 KiB item lets 12 items (3 per SIMD) fit a CU.  FP8
+//    tiles are short and their waves wait on load latency, which the extra
+//    items hide (BF16 measured slower this way).  MFMA columns 8..15 then
+//    repeat heads 0..7 and are not written out.
+template <int kQRows>
+struct AttendLayout {
+    static constexpr int kVPitch = kQRows == 16 ? kRowBytes + 32 : kRowBytes + 16;
+    static constexpr int kTileBytes = kTileSlots * kVPitch;
+    static constexpr int kQBytes = kQRows * kQPitch;
+    static constexpr int kUsed = kTileBytes + kQBytes;
+    static constexpr int kItems = kQRows == 16 ? kItemsPerCU : 12;
+    static constexpr int kLds = kQRows == 16 ? 160 * 1024 / kItemsPerCU - 1024 : kUsed;
+    static constexpr int kWavesPerSimd = kQRows == 16 ? kAttendWavesPerSimd : 3;
+    static constexpr int kQChunksPerLane = kQRows * kChunksPerRow / 64;
+    static_assert(kUsed <= kLds, "item LDS");
+    static_assert(kItems * kLds <= 160 * 1024, "LDS budget of a gfx950 CU");
+    // with the 1,280-byte LDS allocation granule
+    static_assert((kItems + 1) * ((kLds + 1279) / 1280 * 1280) > 160 * 1024,
+                  "one more item must not fit");
+};
 
 // A row of zeros: masked tile rows and absent query heads load from here, so
 // every load is unconditional and no select waits on loaded data.
@@ -226,20 +239,15 @@ __device__ __forceinline__ constexpr int q_chunk(int ks, int j) {
 }
 
 // 8 FP8 E4M3 codes (two dwords) -> 8 BF16 values (exact: every E4M3 value is
-// a BF16 value).
+// a BF16 value).  v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes
+// per instruction; it matches the two-step conversion through FP32 on all
+// 256 codes in every byte position (checked on the GPU).
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-    bf16x8_t x;
-    const uint32_t w[2] = {w0, w1};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-        const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-        x[4 * i] = (__bf16)a[0];
-        x[4 * i + 1] = (__bf16)a[1];
-        x[4 * i + 2] = (__bf16)b[0];
-        x[4 * i + 3] = (__bf16)b[1];
-    }
-    return x;
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // A operand of k-step ks from the K registers.
@@ -284,7 +292,7 @@ __device__ __forceinline__ void gather_v(u32x4_t (&rv)[KvGather<KV>::kVLoads], i
 }
 
 // Write a gathered V tile into the wave's LDS tile as BF16 rows.
-template <KvType KV>
+template <KvType KV, int kVPitch>
 __device__ __forceinline__ void stage_v(const u32x4_t (&rv)[KvGather<KV>::kVLoads], char *vs,
                                         int lane) {
     using G = KvGather<KV>;
@@ -331,10 +339,12 @@ __device__ __forceinline__ int tile_slot(const int32_t *list, int tile, int ntil
 // between the two halves of the loads paces the wave's requests.  Each wave
 // walks its own item's slot list in order, and the list is grouped by slot
 // range, so a wave's consecutive tiles fall in the same part of the cache.
-template <bool kSplit, KvType KV>
-__global__ __launch_bounds__(64, kWavesPerSimd) void attend_kernel(const AttendParams p) {
+template <bool kSplit, KvType KV, int kQRows>
+__global__ __launch_bounds__(64, AttendLayout<kQRows>::kWavesPerSimd) void attend_kernel(
+    const AttendParams p) {
     using Gth = KvGather<KV>;
-    __shared__ __attribute__((aligned(16))) char smem[kAttendLds];
+    using Lay = AttendLayout<kQRows>;
+    __shared__ __attribute__((aligned(16))) char smem[Lay::kLds];
 
     const int lane = threadIdx.x;
     const int c = lane & 15;   // MFMA column: query head within the block / A-operand row
@@ -382,13 +392,13 @@ __global__ __launch_bounds__(64, kWavesPerSimd) void attend_kernel(const AttendP
     const char *vb = (const char *)p.v + (int64_t)g * p.v_sh * Gth::kElemBytes;
     const int64_t k_ss = p.k_ss * Gth::kElemBytes, v_ss = p.v_ss * Gth::kElemBytes;
     char *vs_lds = smem;
-    char *q_lds = smem + kTileBytes;
+    char *q_lds = smem + Lay::kTileBytes;
 
     // The item's query rows (16 heads; absent heads are zero) go to LDS; their
     // loads are issued before the first gathers and written after them.
-    u32x4_t qr[kQChunksPerLane];
+    u32x4_t qr[Lay::kQChunksPerLane];
 #pragma unroll
-    for (int u = 0; u < kQChunksPerLane; ++u) {
+    for (int u = 0; u < Lay::kQChunksPerLane; ++u) {
         const int idx = lane + 64 * u;
         const int r = idx / kChunksPerRow, ch = idx % kChunksPerRow;
         const uint16_t *src =
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(64, kWavesPerSimd) void attend_kernel(const AttendP
     }
 
 #pragma unroll
-    for (int u = 0; u < kQChunksPerLane; ++u) {
+    for (int u = 0; u < Lay::kQChunksPerLane; ++u) {
         const int idx = lane + 64 * u;
         *LDS_PTR(u32x4_t, q_lds + (idx / kChunksPerRow) * kQPitch + 16 * (idx % kChunksPerRow)) =
             qr[u];
@@ -443,7 +453,8 @@ __global__ __launch_bounds__(64, kWavesPerSimd) void attend_kernel(const AttendP
 #pragma unroll
             for (int u = 0; u < kKSteps / 2; ++u)
                 qb[u] = *LDS_PTR(bf16x8_t,
-                                 q_lds + c * kQPitch + 16 * q_chunk(half * kKSteps / 2 + u, j));
+                                 q_lds + (c % kQRows) * kQPitch +
+                                     16 * q_chunk(half * kKSteps / 2 + u, j));
 #pragma unroll
             for (int u = 0; u < kKSteps / 2; ++u)
                 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -499,7 +510,7 @@ __global__ __launch_bounds__(64, kWavesPerSimd) void attend_kernel(const AttendP
         }
 
         wave_lds_fence();   // the previous tile's transpose reads are done
-        stage_v<KV>(rv, vs_lds, lane);
+        stage_v<KV, Lay::kVPitch>(rv, vs_lds, lane);
         __builtin_amdgcn_sched_barrier(0);   // V(i) is consumed before V(i+1) lands
         slot_next = tile_slot(list, tile + 2 * step, ntiles, lane);
         gather_v<KV>(rv, slot_g, vb, v_ss, lane);
@@ -517,7 +528,7 @@ __global__ __launch_bounds__(64, kWavesPerSimd) void attend_kernel(const AttendP
                 const int db = half * (kDimBlocks / 2) + u;
                 va[u] = __builtin_bit_cast(
                     bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(
-                                  i16x4_t, vs_lds + tr_row * kVPitch + 32 * db + 8 * tr_sub)));
+                                  i16x4_t, vs_lds + tr_row * Lay::kVPitch + 32 * db + 8 * tr_sub)));
             }
 #pragma unroll
             for (int u = 0; u < kDimBlocks / 2; ++u) {
@@ -598,10 +609,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 // gathers issued back to back; the attention kernel, whose work between the
 // K and the V loads paces each wave's requests, can run faster than this.
 template <KvType KV>
-__global__ __launch_bounds__(64, kWavesPerSimd) void gather_only_kernel(const GatherParams p) {
+__global__ __launch_bounds__(64, kAttendWavesPerSimd) void gather_only_kernel(const GatherParams p) {
     using Gth = KvGather<KV>;
-    // Same LDS footprint as attend_kernel, so the same number of items fit a CU.
-    __shared__ __attribute__((aligned(16))) uint32_t smem[kAttendLds / 4];
+    // Same LDS footprint as attend_kernel's general layout, so the same number
+    // of items fit a CU.
+    __shared__ __attribute__((aligned(16))) uint32_t smem[AttendLayout<16>::kLds / 4];
     const int lane = threadIdx.x;
     const int64_t item = blockIdx.x;
     const int64_t t = item / p.Hkv;
@@ -1210,15 +1222,25 @@ hipError_t launch_compact(const CompactParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// FP8 caches with at most 8 query heads per KV head take the 8-query-row
+// layout (12 items per CU); everything else the general one.
+template <bool kSplit>
+void launch_attend_any(const AttendParams &p, KvType kv, int64_t blocks, hipStream_t stream) {
+    if (kv == KvType::kFp8 && p.G <= 8)
+        hipLaunchKernelGGL((attend_kernel<kSplit, KvType::kFp8, 8>), dim3((unsigned)blocks),
+                           dim3(64), 0, stream, p);
+    else if (kv == KvType::kFp8)
+        hipLaunchKernelGGL((attend_kernel<kSplit, KvType::kFp8, 16>), dim3((unsigned)blocks),
+                           dim3(64), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attend_kernel<kSplit, KvType::kBf16, 16>), dim3((unsigned)blocks),
+                           dim3(64), 0, stream, p);
+}
+
 hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_t stream) {
     const int64_t items = T * (int64_t)p.Hkv * p.HB;
     if (items == 0) return hipSuccess;
-    if (kv == KvType::kFp8)
-        hipLaunchKernelGGL((attend_kernel<false, KvType::kFp8>), dim3((unsigned)items),
-                           dim3(64), 0, stream, p);
-    else
-        hipLaunchKernelGGL((attend_kernel<false, KvType::kBf16>), dim3((unsigned)items),
-                           dim3(64), 0, stream, p);
+    launch_attend_any<false>(p, kv, items, stream);
     return hipGetLastError();
 }
 
@@ -1226,12 +1248,7 @@ hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
                                  hipStream_t stream) {
     const int64_t blocks = T * (int64_t)p.Hkv * p.HB * p.splits;
     if (blocks == 0) return hipSuccess;
-    if (kv == KvType::kFp8)
-        hipLaunchKernelGGL((attend_kernel<true, KvType::kFp8>), dim3((unsigned)blocks),
-                           dim3(64), 0, stream, p);
-    else
-        hipLaunchKernelGGL((attend_kernel<true, KvType::kBf16>), dim3((unsigned)blocks),
-                           dim3(64), 0, stream, p);
+    launch_attend_any<true>(p, kv, blocks, stream);
     return hipGetLastError();
 }
 
