@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (for counter calibration)")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as replays of one captured HIP graph (the kernels' "
+                         "own times still come from the eager loop)")
     return ap.parse_args()
 
 
@@ -184,6 +187,30 @@ def main():
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / K
+    ms_step_eager = ms_step
+    if args.graph:
+        # The whole step captured once (the library records no memset and no
+        # synchronous call on these paths) and replayed K times.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(max(args.warmup, 1)):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(K):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_step = g0.elapsed_time(g1) / K
     attn_ms = [a0[i].elapsed_time(a1[i]) for i in range(K)]
     attn_avg = float(np.mean(attn_ms))
     select_ms = float(np.mean([(t0 if i == 0 else a1[i - 1]).elapsed_time(s1[i])
@@ -278,6 +305,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_eager": ms_step_eager,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -285,7 +313,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": case.name, "T": T, "S": S, "W": W, "Hq": Hq, "Hkv": Hkv,
                    "D": case.D, "scale": scale, "seed": case.info.get("seed"),
-                   "splits": splits, "block_size": bs, "parallelism": "none (1 GPU)"},
+                   "splits": splits, "block_size": bs, "parallelism": "none (1 GPU)",
+                   "launch": "hip_graph" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic},

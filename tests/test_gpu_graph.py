@@ -1,0 +1,91 @@
+"""The prefill, FP8 prefill, decode and indexer paths captured in a HIP graph.
+
+These paths record no memset and make no synchronous call, so a captured
+step replays exactly: every replay is compared bit for bit with the eager
+result.  Between replays the output is overwritten with a sentinel and other
+eager work and synchronizations run, so a replay that skipped a kernel, or
+read a stale buffer, shows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import qsa_inputs as qi
+import top_sparse_attention_amd as qsa
+from qsa_testutil import upload, upload_fp8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+REPLAYS = 4
+
+
+def replay_matches_eager(step, out):
+    """Run `step` (which writes `out`) eagerly, capture it, and check every
+    replay against the eager bits."""
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    scratch = torch.randn(512, 512, device=DEV)
+    for r in range(REPLAYS):
+        if out.dtype == torch.bfloat16:
+            out.view(torch.int16).fill_(0x3F3F)        # a sentinel the step never writes
+        else:
+            out.fill_(0x3F3F3F3F)
+        torch.cuda.synchronize()
+        graph.replay()
+        scratch = scratch @ scratch.T / 512.0      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                           eager.view(torch.int16) if eager.dtype == torch.bfloat16 else eager), \
+            f"replay {r} differs from the eager result"
+    assert torch.isfinite(scratch).all()
+
+
+def test_prefill_graph_replays_exactly():
+    case = qi.random_case(1201, T=300, S=20000, Hq=16, Hkv=2, W=700, pad_frac=0.1,
+                          interior=True)
+    q, k, v, sl = upload(case, DEV)
+    out = torch.empty_like(q)
+    ws = qsa.new_workspace(case.T, case.W, DEV)
+    replay_matches_eager(lambda: qsa.sparse_prefill(q, k, v, sl, out=out, workspace=ws), out)
+
+
+def test_fp8_prefill_graph_replays_exactly():
+    case = qi.with_fp8_kv(qi.random_case(1202, T=200, S=12000, Hq=8, Hkv=1, W=900))
+    q, _, _, sl = upload(case, DEV)
+    k8, v8, ks, vs = upload_fp8(case, DEV)
+    out = torch.empty_like(q)
+    ws = qsa.new_workspace(case.T, case.W, DEV)
+    replay_matches_eager(
+        lambda: qsa.sparse_prefill_fp8kv(q, k8, v8, ks, vs, sl, out=out, workspace=ws), out)
+
+
+def test_decode_graph_replays_exactly():
+    case = qi.random_case(1203, T=8, S=60000, Hq=24, Hkv=2, W=2048)
+    q, k, v, sl = upload(case, DEV)
+    out = torch.empty_like(q)
+    nbytes = qsa.decode_workspace_bytes(case.T, case.W, case.Hq, case.Hkv)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    replay_matches_eager(lambda: qsa.sparse_decode(q, k, v, sl, out=out, workspace=ws), out)
+
+
+def test_indexer_topk_graph_replays_exactly():
+    case = qi.indexed_case(1204, L=20000, T=64, Hq=8, Hkv=1, budget=256)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    iq = t(case.info["iq"].view(np.int16)).view(torch.bfloat16)
+    ik = t(case.info["ik"].view(np.int16)).view(torch.bfloat16)
+    pos, sop = t(case.info["positions"]), t(case.info["slot_of_pos"])
+    scores = torch.empty((case.T, ik.shape[0]), dtype=torch.float32, device=DEV)
+    sel = torch.empty((case.T, 4 * 256 + 3), dtype=torch.int32, device=DEV)
+    replay_matches_eager(lambda: qsa.indexer_topk(iq, ik, pos, sop, 256, scores=scores, out=sel),
+                         sel)

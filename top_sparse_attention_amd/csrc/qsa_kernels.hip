@@ -575,7 +575,9 @@ __global__ __launch_bounds__(64, AttendLayout<kQRows>::kWavesPerSimd) void atten
 
 // out[t, h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the parts s,
 // M = max_s m_s; exactly +0.0 when no part saw a slot.  One wave per (t, h)
-// row, 4 dims per lane.
+// row, 4 dims per lane.  Lane s of each run of 64 parts loads part s's (m, l)
+// and computes its weight; the O rows are then read 8 parts at a time, all 8
+// loads in flight together, each scaled by its part's weight (a readlane).
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -583,17 +585,43 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     if (row >= rows) return;
     const int64_t t = row / p.Hq;
     const int h = (int)(row - t * p.Hq);
+    const int64_t n = p.n_parts;
     float mmax = kNegInf;
-    for (int64_t s = 0; s < p.n_parts; ++s) mmax = fmaxf(mmax, p.part_ml[(s * rows + row) * 2]);
+    for (int64_t s0 = 0; s0 < n; s0 += 64) {
+        const int64_t s = s0 + lane;
+        if (s < n) mmax = fmaxf(mmax, p.part_ml[(s * rows + row) * 2]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
     bf16x4_t ob = {(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
     if (mmax != kNegInf) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        float l_tot = 0.0f;
-        for (int64_t s = 0; s < p.n_parts; ++s) {
-            const float w = __builtin_amdgcn_exp2f(p.part_ml[(s * rows + row) * 2] - mmax);
-            l_tot += w * p.part_ml[(s * rows + row) * 2 + 1];
-            acc += w * *(const f32x4_t *)(p.part_o + (s * rows + row) * kHeadDim + 4 * lane);
+        float l_part = 0.0f;
+        for (int64_t s0 = 0; s0 < n; s0 += 64) {
+            const int64_t s = s0 + lane;
+            float w = 0.0f;
+            if (s < n) {
+                w = __builtin_amdgcn_exp2f(p.part_ml[(s * rows + row) * 2] - mmax);
+                l_part += w * p.part_ml[(s * rows + row) * 2 + 1];
+            }
+            const int cnt = (int)min<int64_t>(64, n - s0);
+            for (int u = 0; u < cnt; u += 8) {
+                f32x4_t o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    o[e] = u + e < cnt ? *(const f32x4_t *)(p.part_o + ((s0 + u + e) * rows + row) *
+                                                                       kHeadDim + 4 * lane)
+                                       : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (u + e < cnt)   // lane u + e holds that part's weight
+                        acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u + e)) *
+                               o[e];
+            }
         }
+        float l_tot = l_part;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) l_tot += __shfl_xor(l_tot, off);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ob[i] = (__bf16)(acc[i] / l_tot);
     }
