@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <hipcub/block/block_load.hpp>
 #include <hipcub/block/block_radix_sort.hpp>
 #include <hipcub/block/block_reduce.hpp>
 #include <hipcub/block/block_scan.hpp>
@@ -144,50 +145,73 @@ __device__ __forceinline__ V ldg16(const void *p) {
 // slot ranges, stable inside a range, and appended to the compacted list.
 // Two radix passes; a full sort would cost more and buys no locality.
 __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactParams p) {
+    using Load = hipcub::BlockLoad<int32_t, kSortThreads, kSortItemsPerThread,
+                                   hipcub::BLOCK_LOAD_TRANSPOSE>;
     using Sort = hipcub::BlockRadixSort<uint32_t, kSortThreads, kSortItemsPerThread>;
-    __shared__ typename Sort::TempStorage sort_tmp;
-    __shared__ int chunk_valid, chunk_bad;
+    __shared__ union {
+        typename Load::TempStorage load;
+        typename Sort::TempStorage sort;
+    } tmp;
+    __shared__ int chunk_counts;   // valid entries | invalid entries << 16
 
     const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
     const int32_t *src = p.slot_idx + t * p.stride_t;
     int32_t *dst = p.list + t * p.row_stride;
     const uint32_t pad_key = 1u << (p.key_bits - 1);
     int n = 0, bad = 0;
     for (int64_t base = 0; base < p.W; base += kSortChunk) {
-        if (threadIdx.x == 0) chunk_valid = chunk_bad = 0;
-        __syncthreads();
+        if (tid == 0) chunk_counts = 0;
+        // Coalesced loads, handed to the sort in blocked order (thread t holds
+        // entries 9t .. 9t + 8 of the run), so the sort is stable in the
+        // row's order.
+        int32_t e[kSortItemsPerThread];
+        Load(tmp.load).Load(src + base, e, (int)min<int64_t>(kSortChunk, p.W - base), -1);
+        __syncthreads();   // the load's staging area is reused by the sort
         uint32_t key[kSortItemsPerThread];
         int my_valid = 0, my_bad = 0;
 #pragma unroll
         for (int u = 0; u < kSortItemsPerThread; ++u) {
-            const int64_t i = base + threadIdx.x * kSortItemsPerThread + u;
-            const int32_t e = i < p.W ? src[i] : -1;
-            const bool in_cache = e >= 0 && (int64_t)e < p.S;
-            const bool keep = in_cache && (int64_t)e >= p.lo && (int64_t)e < p.hi;
+            const bool in_cache = e[u] >= 0 && (int64_t)e[u] < p.S;
+            const bool keep = in_cache && (int64_t)e[u] >= p.lo && (int64_t)e[u] < p.hi;
             my_valid += keep;
-            my_bad += !in_cache && e != -1;
-            key[u] = keep ? (uint32_t)((int64_t)e - p.lo) : pad_key;
+            my_bad += !in_cache && e[u] != -1;
+            key[u] = keep ? (uint32_t)((int64_t)e[u] - p.lo) : pad_key;
         }
-        atomicAdd(&chunk_valid, my_valid);
-        atomicAdd(&chunk_bad, my_bad);
-        Sort(sort_tmp).Sort(key, max(p.key_bits - kSortKeyBits, 0), p.key_bits);
-        __syncthreads();   // the counters above are complete
-        const int nv = chunk_valid;
+        // Both counts (each < 2^16 per run) in one word, summed per wave.
+        int packed = my_valid | (my_bad << 16);
 #pragma unroll
-        for (int u = 0; u < kSortItemsPerThread; ++u) {
-            const int pos = threadIdx.x * kSortItemsPerThread + u;
-            if (pos < nv)
-                for (int i = 0; i < p.block; ++i)
-                    dst[(int64_t)(n + pos) * p.block + i] = (int32_t)key[u] * p.block + i;
+        for (int off = 32; off >= 1; off >>= 1) packed += __shfl_xor(packed, off);
+        if ((tid & 63) == 0) atomicAdd(&chunk_counts, packed);
+        // Sorted keys come back striped: thread t holds ranks t, t + 256, ...,
+        // so the stores below are coalesced.
+        Sort(tmp.sort).SortBlockedToStriped(key, max(p.key_bits - kSortKeyBits, 0), p.key_bits);
+        __syncthreads();   // the counts above are complete
+        const int nv = chunk_counts & 0xffff;
+        const int nb = chunk_counts >> 16;
+        if (p.block == 1) {
+#pragma unroll
+            for (int u = 0; u < kSortItemsPerThread; ++u) {
+                const int pos = tid + kSortThreads * u;
+                if (pos < nv) dst[n + pos] = (int32_t)key[u];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kSortItemsPerThread; ++u) {
+                const int pos = tid + kSortThreads * u;
+                if (pos < nv)
+                    for (int i = 0; i < p.block; ++i)
+                        dst[(int64_t)(n + pos) * p.block + i] = (int32_t)key[u] * p.block + i;
+            }
         }
         n += nv;
-        bad += chunk_bad;
-        __syncthreads();   // counters are reset by the next chunk
+        bad += nb;
+        __syncthreads();   // the counts are reset by the next run
     }
     const int slots = n * p.block;
     const int padded = (slots + kListPad - 1) / kListPad * kListPad;
-    for (int i = slots + threadIdx.x; i < padded; i += kSortThreads) dst[i] = -1;
-    if (threadIdx.x == 0) {
+    for (int i = slots + tid; i < padded; i += kSortThreads) dst[i] = -1;
+    if (tid == 0) {
         p.count[t] = slots;
         p.n_bad[t] = bad;
     }
