@@ -714,15 +714,17 @@ __global__ __launch_bounds__(64, kAttendWavesPerSimd) void gather_only_kernel(co
 // score[t, c] = sum_h max(0, iq[t,h] . ik[c]) with bf16 MFMA.  A workgroup
 // takes 64 tokens (16 per wave, as 4 MFMA row tiles of 4 tokens x 4 heads)
 // and one range of kScoreSplit index keys, walked in tiles of 64 blocks
-// staged in LDS (swizzled) and shared by all four
-// row tiles; it stops at the last block any of its tokens may select.  MFMA
-// rows are (token, head) pairs, so lane (c, j) of a 16x16 output holds the 4
-// heads of one token against block c and the head sum stays in the lane.
+// staged in LDS (swizzled) and shared by all four row tiles; it stops at the
+// last block any of its tokens may select.  MFMA rows are (token, head)
+// pairs, so lane (c, j) of a 16x16 output holds the 4 heads of one token
+// against block c and the head sum stays in the lane.  Each tile's 64 x 64
+// scores go through LDS and are stored as whole 256-byte row segments.
 constexpr int kScoreTokens = 64;
 constexpr int kScoreRowTiles = kScoreTokens / 4 / 4;   // per wave
 constexpr int kScoreTile = 64;
-constexpr int kScoreSplit = 4096;
+constexpr int kScoreSplit = 1024;
 constexpr int kIndexRowBytes = kIndexDim * 2;   // 256 B
+constexpr int kScoreOutPitch = kScoreTile + 4;  // floats per staged row (16-byte aligned)
 
 // LDS byte offset of 16-byte chunk `chunk` of index-key tile row `r`.  The
 // chunk index is XOR-swizzled by a bijection of r & 7 so that the 8 rows read
@@ -733,17 +735,21 @@ __device__ __forceinline__ int idx_off(int r, int chunk) {
 }
 
 __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreParams p) {
-    __shared__ __attribute__((aligned(16))) char tile[2][kScoreTile * kIndexRowBytes];
+    // One key tile: the barrier after each tile's scores also orders its reads
+    // before the next tile is written.
+    __shared__ __attribute__((aligned(16))) char tile[kScoreTile * kIndexRowBytes];
+    __shared__ __attribute__((aligned(16))) float out_tile[kScoreTokens * kScoreOutPitch];
     __shared__ int c_end_shared;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int c = lane & 15, j = lane >> 4;
     const int64_t t0 = (int64_t)blockIdx.x * kScoreTokens;
     const int c_begin = blockIdx.y * kScoreSplit;
 
-    if (threadIdx.x == 0) c_end_shared = 0;
+    if (tid == 0) c_end_shared = 0;
     __syncthreads();
-    if (threadIdx.x < kScoreTokens && t0 + threadIdx.x < p.T) {
-        const int64_t lim = ((int64_t)p.positions[t0 + threadIdx.x] + 1) / kIndexBlock;
+    if (tid < kScoreTokens && t0 + tid < p.T) {
+        const int64_t lim = ((int64_t)p.positions[t0 + tid] + 1) / kIndexBlock;
         atomicMax(&c_end_shared, (int)min<int64_t>(lim, p.C));
     }
     __syncthreads();
@@ -766,7 +772,7 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
     auto load_tile = [&](int c0, u32x4_t (&r)[4]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int idx = threadIdx.x + 256 * u;
+            const int idx = tid + 256 * u;
             const int row = idx >> 4, ch = idx & 15;
             const int64_t blk = c0 + row;
             const uint16_t *src = blk < c_end ? p.ik + blk * p.k_st + ch * 8 : kZeroRow + ch * 8;
@@ -776,25 +782,25 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
     auto store_tile = [&](char *dst, const u32x4_t (&r)[4]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int idx = threadIdx.x + 256 * u;
+            const int idx = tid + 256 * u;
             *LDS_PTR(u32x4_t, dst + idx_off(idx >> 4, idx & 15)) = r[u];
         }
     };
+    // The staged scores go out as 16-byte stores where the rows allow it.
+    const bool vec_out = (p.C % 4) == 0 && ((uintptr_t)p.scores % 16) == 0;
 
     u32x4_t stage[4];
     load_tile(c_begin, stage);
-    int buf = 0;
     for (int c0 = c_begin; c0 < c_end; c0 += kScoreTile) {
-        store_tile(tile[buf], stage);
-        __syncthreads();
+        store_tile(tile, stage);
+        __syncthreads();   // the key tile is staged; the previous scores are stored
         if (c0 + kScoreTile < c_end) load_tile(c0 + kScoreTile, stage);
 #pragma unroll
         for (int ct = 0; ct < kScoreTile / 16; ++ct) {
             bf16x8_t kb[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                kb[ks] = *LDS_PTR(bf16x8_t, tile[buf] + idx_off(16 * ct + c, 4 * ks + j));
-            const int64_t blk = c0 + 16 * ct + c;
+                kb[ks] = *LDS_PTR(bf16x8_t, tile + idx_off(16 * ct + c, 4 * ks + j));
 #pragma unroll
             for (int rt = 0; rt < kScoreRowTiles; ++rt) {
                 f32x4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -803,11 +809,27 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
                     d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], kb[ks], d, 0, 0, 0);
                 const float score = fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) +
                                     fmaxf(d[3], 0.f);
-                const int64_t t_out = t0 + 16 * wave + 4 * rt + j;
-                if (t_out < p.T && blk < c_end) p.scores[t_out * p.C + blk] = score;
+                out_tile[(16 * wave + 4 * rt + j) * kScoreOutPitch + 16 * ct + c] = score;
             }
         }
-        buf ^= 1;
+        __syncthreads();   // the tile's scores are complete
+        // 64 rows of 64 scores: 16 chunks of 4 per row, 4 chunks per thread.
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = tid + 256 * u;
+            const int r = idx >> 4, k4 = 4 * (idx & 15);
+            const int64_t t_out = t0 + r;
+            const int64_t blk = c0 + k4;
+            if (t_out < p.T && blk < c_end) {
+                const f32x4_t v = *(const f32x4_t *)(out_tile + r * kScoreOutPitch + k4);
+                float *dst = p.scores + t_out * p.C + blk;
+                if (vec_out && blk + 3 < c_end) {
+                    *(f32x4_t *)dst = v;
+                } else {
+                    for (int e = 0; e < 4 && blk + e < c_end; ++e) dst[e] = v[e];
+                }
+            }
+        }
     }
 }
 
