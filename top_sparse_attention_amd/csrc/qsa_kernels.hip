@@ -8,23 +8,28 @@
 // in place, takes any query/KV head ratio without padding it to a power of
 // two, and needs no host synchronisation.
 //
-// Two passes:
+// The prefill path is two passes:
 //  1. compact_kernel: per token row, keep the entries in [0, S) (counting
 //     the others as invalid), group them into ascending slot ranges (a
 //     partial radix sort), and pad the list with -1 to a multiple of
 //     kListPad.  The order does not change the result (the softmax sum is
 //     order-free) but makes each wave's consecutive gathers land in few
-//     large pages of the cache, which the memory system serves markedly
-//     faster than uniformly scattered rows.
+//     large pages of the cache, and lets the tokens running at one time
+//     read the same rows at about the same time.
 //  2. attend_kernel: one work item = (token t, KV head g, block of up to 16
 //     query heads of that group) = one wave, 8 (or 12, see AttendLayout)
-//     items resident per CU.  The wave walks its item's 16-slot tiles in list order.  Per tile
-//     it loads the K rows straight into the registers of the score MFMA's A
-//     operand and the V rows (whole rows) into registers that it then writes
-//     to its LDS tile, both one tile ahead of use; computes the 16x16 score
-//     tile with bf16 MFMA (K rows x query heads, the query rows read from
-//     LDS), runs an online softmax in FP32 and accumulates P.V with bf16
-//     MFMA fed by LDS transpose loads, then writes the row in BF16.
+//     items resident per CU.  The wave walks its item's 16-slot tiles in
+//     list order.  Per tile it loads the K rows straight into the registers
+//     of the score MFMA's A operand and the V rows (whole rows) into
+//     registers that it then writes to its LDS tile, both one tile ahead of
+//     use; computes the 16x16 score tile with bf16 MFMA (K rows x query
+//     heads, the query rows read from LDS), runs an online softmax in FP32
+//     and accumulates P.V with bf16 MFMA fed by LDS transpose loads, then
+//     writes the row in BF16.  Its split form writes FP32 (O, m, l) partials
+//     of a share of the tiles instead, which merge_kernel combines.
+// Also here: gather_only_kernel (the attention's loads alone, a measurement
+// aid), and the QSA indexer that produces the selection: indexer_scores_kernel
+// (index scores with bf16 MFMA) and the Top-K selection kernels.
 
 // MFMA orientation: scores are computed transposed, S^T = K_tile . Q^T, so
 // that one lane owns one query head (column) of the MFMA output: the row
@@ -355,14 +360,15 @@ __device__ __forceinline__ int tile_slot(const int32_t *list, int tile, int ntil
 // part_base + s, for qsa_merge_partials (or another shard's partials) to
 // combine.
 //
-// Per tile: the score MFMAs consume K(i) from registers and the loads of
-// K(i+1) are issued into the same registers; the softmax runs; V(i) is
-// written from registers to the wave's LDS tile and the loads of V(i+1) are
-// issued; then P.V reads V(i) back with transpose loads.  So one tile of K
-// and V (16 KiB in BF16) is in flight per wave throughout, and the work
-// between the two halves of the loads paces the wave's requests.  Each wave
-// walks its own item's slot list in order, and the list is grouped by slot
-// range, so a wave's consecutive tiles fall in the same part of the cache.
+// Per tile: the score MFMAs consume K(i) from registers; the softmax runs;
+// V(i) is written from registers to the wave's LDS tile and the loads of
+// V(i+1) are issued one by one; P.V reads V(i) back with transpose loads.
+// The loads of K(i+1) go into K(i)'s registers once the scores are done:
+// spread over the P.V MFMAs for BF16, around the softmax for FP8.  So about
+// one tile of K and V (16 KiB in BF16) is in flight per wave throughout, and
+// the wave's requests reach the memory system spread out.  Each wave walks
+// its own item's slot list in order, and the list is grouped by slot range,
+// so a wave's consecutive tiles fall in the same part of the cache.
 template <bool kSplit, KvType KV, int kQRows>
 __global__ __launch_bounds__(64, AttendLayout<kQRows>::kWavesPerSimd) void attend_kernel(
     const AttendParams p) {
@@ -907,7 +913,10 @@ __device__ void radix_select(int n, int need, ScoreAt score_at, InSet in_set, in
 // (ties to the lower block); write their positions in ascending block order,
 // the causal tail, slot-mapped, then -1 padding.
 //
-// The threshold is found in two steps: a histogram of 256 buckets that split
+// select_exact (the whole workgroup, one row of n >= 0 eligible scores)
+// writes the kept block ids, in ascending order, at out[4 e] for
+// e < min(n, budget); expand_row then turns them into slots.  Its threshold
+// is found in two steps: a histogram of 256 buckets that split
 // [min, max] of the row linearly (a monotone map, so whole buckets above the
 // threshold's bucket are kept and those below dropped), then an exact radix
 // select over the keys of that one bucket.  Scores of a row sit in a narrow
