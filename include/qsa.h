@@ -123,8 +123,9 @@ qsa_status qsa_workspace_layout(int64_t T, int64_t W, qsa_workspace_map *map);
  * [0, S) grouped into ascending slot ranges (see qsa_workspace_map for the
  * exact order), their count, and the number of invalid entries.  S is the
  * number of cache slots.  Duplicates are kept.  The attention result does
- * not depend on the order of a row; the grouping only makes the gathers of
- * one tile fall close together in memory.
+ * not depend on the order of a row; the grouping makes the gathers of one
+ * tile fall close together in memory and lets the tokens processed at one
+ * time read the same cache rows at about the same time.
  */
 qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S,
                              void *workspace, size_t workspace_bytes,
@@ -237,8 +238,8 @@ qsa_status qsa_merge_partials(const void *partials, size_t partials_bytes,
                               qsa_bf16_view *out, void *stream);
 
 /* Splits per item that qsa_sparse_decode uses for these sizes (a pure
- * function of the sizes: enough workgroups to cover the GPU, at least one
- * tile per wave per split, at most 64). */
+ * function of the sizes: enough workgroups to cover the GPU, at least four
+ * 16-slot tiles per split, at most 64). */
 int32_t qsa_decode_splits(int64_t T, int64_t W, int32_t Hq, int32_t Hkv);
 
 /* Workspace bytes for qsa_sparse_decode: the compaction area followed by the
