@@ -91,12 +91,15 @@ typedef struct qsa_i32_view {
  *          b = max(1, ceil(log2 S)) and r = max(0, b - 7) (at most 128 slot
  *          ranges, ascending; input order within a range);
  *   count: int32 [T], number of valid entries of row t;
- *   n_bad: int32 [T], entries of row t that were neither -1 nor in [0, S). */
+ *   n_bad: int32 [T], entries of row t that were neither -1 nor in [0, S);
+ *   share: 512 bytes the attention uses to pick its layout (see
+ *          qsa_sparse_attend); the compaction pass initialises them. */
 typedef struct qsa_workspace_map {
     int64_t list_offset;
     int64_t row_stride;
     int64_t count_offset;
     int64_t bad_offset;
+    int64_t share_offset;
     int64_t total_bytes;
 } qsa_workspace_map;
 
@@ -178,11 +181,20 @@ qsa_status qsa_sparse_prefill_blocks(const qsa_bf16_view *q,
  * paragraph, restricted to each token's listed slots).  Rows with count 0
  * receive +0.0.  q/out [T, Hq, 256], k_cache/v_cache [S, Hkv, 256]; W is the
  * selection width the workspace was compacted with; scale must be finite.
+ *
+ * Layout choice: the kernel runs 8 items (token, KV head) per CU, which lets
+ * the tokens running together share cache rows in L2.  Where the sizes allow
+ * little sharing (a cache large against W), a small estimate first samples
+ * pairs of neighbouring tokens' lists and counts their common slots; if the
+ * tokens share few rows, 4 items per CU are run instead.  Both layouts give
+ * the same bits.  The estimate writes the workspace's share words (the rest
+ * of the workspace is only read), so calls on one workspace must not
+ * overlap.
  */
 qsa_status qsa_sparse_attend(const qsa_bf16_view *q,
                              const qsa_bf16_view *k_cache,
                              const qsa_bf16_view *v_cache, int64_t W,
-                             float scale, const void *workspace,
+                             float scale, void *workspace,
                              size_t workspace_bytes, qsa_bf16_view *out,
                              void *stream);
 
@@ -298,7 +310,7 @@ qsa_status qsa_sparse_attend_fp8kv(const qsa_bf16_view *q,
                                    const qsa_fp8_view *k_cache,
                                    const qsa_fp8_view *v_cache, float k_scale,
                                    float v_scale, int64_t W, float scale,
-                                   const void *workspace, size_t workspace_bytes,
+                                   void *workspace, size_t workspace_bytes,
                                    qsa_bf16_view *out, void *stream);
 
 qsa_status qsa_sparse_prefill_fp8kv(const qsa_bf16_view *q,

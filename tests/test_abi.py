@@ -57,6 +57,8 @@ def test_workspace_layout():
     assert m["list_offset"] == 0
     assert m["count_offset"] >= 7810 * 2080 * 4 and m["count_offset"] % 256 == 0
     assert m["bad_offset"] >= m["count_offset"] + 7810 * 4
+    assert m["share_offset"] >= m["bad_offset"] + 7810 * 4 and m["share_offset"] % 256 == 0
+    assert m["total_bytes"] == m["share_offset"] + 512
     assert m["total_bytes"] == qsa.workspace_bytes(7810, 2051)
     assert qsa.workspace_bytes(0, 0) == 0
     assert qsa.workspace_bytes(-1, 3) == 0

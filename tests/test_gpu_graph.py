@@ -89,3 +89,13 @@ def test_indexer_topk_graph_replays_exactly():
     sel = torch.empty((case.T, 4 * 256 + 3), dtype=torch.int32, device=DEV)
     replay_matches_eager(lambda: qsa.indexer_topk(iq, ik, pos, sop, 256, scores=scores, out=sel),
                          sel)
+
+
+def test_prefill_with_sharing_estimate_graph_replays_exactly():
+    # A large cache against W: the sharing estimate runs, then the gated
+    # attention launches; its ticket must be left cleared by every replay.
+    case = qi.random_case(1205, T=4096, S=131072, Hq=3, Hkv=1, W=512)
+    q, k, v, sl = upload(case, DEV)
+    out = torch.empty_like(q)
+    ws = qsa.new_workspace(case.T, case.W, DEV)
+    replay_matches_eager(lambda: qsa.sparse_prefill(q, k, v, sl, out=out, workspace=ws), out)

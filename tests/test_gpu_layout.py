@@ -1,0 +1,121 @@
+"""The attention's layout choice (8 or 4 items per CU) and its sharing estimate.
+
+Where the sizes leave the cache large against the selection width, a small
+kernel samples pairs of neighbouring tokens, counts their common slots and
+picks 4 items per CU if the tokens running together share few cache rows.
+These tests check the choice the estimate writes into the workspace on
+selections of known sharing, that both layouts give the oracle's result
+within the gate, and that they give the same bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_inputs as qi
+import top_sparse_attention_amd as qsa
+from qsa_testutil import (bf16_tensor_bits, bf16_tensor_to_f32, empty_row_mask, gate, upload,
+                          upload_fp8)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+SHARE_PAIRS = 32          # token pairs the estimate samples
+# The choice word follows the pairs' (common, length) floats and the ticket.
+CHOICE_BYTE = SHARE_PAIRS * 8 + 4
+
+
+def choice_of(ws: torch.Tensor, T: int, W: int) -> int:
+    off = qsa.workspace_layout(T, W)["share_offset"] + CHOICE_BYTE
+    return int(ws[off:off + 4].view(torch.int32).item())
+
+
+def check_rows(out, q_np, k_np, v_np, sl_np, S, rows):
+    want = oracle.prefill(np.ascontiguousarray(q_np[rows]), k_np, v_np,
+                          np.ascontiguousarray(sl_np[rows]), 1.0 / 16.0)
+    got = bf16_tensor_to_f32(out[torch.as_tensor(rows, device=DEV)])
+    return gate(got, want, empty_row_mask(sl_np, S, rows))
+
+
+def prefill_with_choice(q, k, v, sl):
+    T, W = sl.shape
+    ws = qsa.new_workspace(T, W, DEV)
+    # A value the estimate never writes, so a missing write shows.
+    off = qsa.workspace_layout(T, W)["share_offset"] + CHOICE_BYTE
+    ws[off:off + 4].view(torch.int32).fill_(-7)
+    out = qsa.sparse_prefill(q, k, v, sl, workspace=ws)
+    torch.cuda.synchronize()
+    return out, choice_of(ws, T, W)
+
+
+def test_large_cache_with_little_sharing_takes_four_per_cu_and_same_bits():
+    # 2,048 random slots of 262,144 per token, one KV head: each row is read by
+    # about 2 of the 256 tokens an XCD runs at a time.
+    case = qi.random_case(1301, T=4096, S=262144, Hq=3, Hkv=1, W=2048)
+    q, k, v, sl = upload(case, DEV)
+    out, choice = prefill_with_choice(q, k, v, sl)
+    assert choice == 1
+    rows = qi.sample_rows(case.T, 24, seed=31)
+    print(check_rows(out, case.q, case.k_cache, case.v_cache, case.slot_idx, case.S, rows))
+    # The same selections padded to width 8,192 with -1: from the sizes
+    # alone the sharing is at least 256 * 8192 / 262144 = 8, so the general
+    # layout runs without an estimate.  Same valid entries, same bits.
+    padded = torch.full((case.T, 8192), -1, dtype=torch.int32, device=DEV)
+    padded[:, :case.W] = sl
+    out8 = qsa.sparse_prefill(q, k, v, padded)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_tensor_bits(out8), bf16_tensor_bits(out))
+
+
+def test_two_kv_heads_at_sharing_four_take_four_per_cu():
+    case = qi.random_case(1302, T=4096, S=131072, Hq=16, Hkv=2, W=2051)
+    q, k, v, sl = upload(case, DEV)
+    out, choice = prefill_with_choice(q, k, v, sl)
+    assert choice == 1
+    rows = qi.sample_rows(case.T, 16, seed=32)
+    print(check_rows(out, case.q, case.k_cache, case.v_cache, case.slot_idx, case.S, rows))
+
+
+def test_large_cache_with_a_small_referenced_part_keeps_eight_per_cu():
+    # The tokens select among 40,000 slots scattered over a 262,144-slot cache:
+    # the sizes suggest little sharing, the lists show about 13 readers per row.
+    base = qi.random_case(1303, T=4096, S=40000, Hq=3, Hkv=1, W=2048)
+    q, kb, vb, slb = upload(base, DEV)
+    S = 262144
+    new_of_old = torch.from_numpy(
+        np.random.Generator(np.random.PCG64(1304)).permutation(S)[:base.S].astype(np.int64)
+    ).to(DEV)
+    k = torch.zeros((S, 1, 256), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros_like(k)
+    k[new_of_old] = kb
+    v[new_of_old] = vb
+    sl = new_of_old[slb.long()].to(torch.int32)
+    out, choice = prefill_with_choice(q, k, v, sl)
+    assert choice == 0
+    rows = qi.sample_rows(base.T, 16, seed=33)
+    # Relocated rows: the oracle of the original cache gives the same result.
+    print(check_rows(out, base.q, base.k_cache, base.v_cache, base.slot_idx, base.S, rows))
+
+
+def test_fp8_cache_with_more_than_eight_heads_per_kv_head_takes_four_per_cu():
+    # FP8 caches with G > 8 run the general layout, so the estimate applies.
+    case = qi.with_fp8_kv(qi.random_case(1305, T=4096, S=131072, Hq=12, Hkv=1, W=1024))
+    q, _, _, sl = upload(case, DEV)
+    k8, v8, ks, vs = upload_fp8(case, DEV)
+    ws = qsa.new_workspace(case.T, case.W, DEV)
+    off = qsa.workspace_layout(case.T, case.W)["share_offset"] + CHOICE_BYTE
+    ws[off:off + 4].view(torch.int32).fill_(-7)
+    out = qsa.sparse_prefill_fp8kv(q, k8, v8, ks, vs, sl, workspace=ws)
+    torch.cuda.synchronize()
+    assert choice_of(ws, case.T, case.W) == 1
+    rows = qi.sample_rows(case.T, 16, seed=34)
+    want = oracle.prefill_fp8kv(case.q, case.info["k8"], case.info["v8"], ks, vs,
+                                case.slot_idx, 1.0 / 16.0, rows=rows)
+    got = bf16_tensor_to_f32(out[torch.as_tensor(rows, device=DEV)])
+    print(gate(got, want, empty_row_mask(case.slot_idx, case.S, rows)))
+    # Padded to width 8,192 the sizes bound the sharing at 16: general layout.
+    padded = torch.full((case.T, 8192), -1, dtype=torch.int32, device=DEV)
+    padded[:, :case.W] = sl
+    out8 = qsa.sparse_prefill_fp8kv(q, k8, v8, ks, vs, padded)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_tensor_bits(out8), bf16_tensor_bits(out))

@@ -64,7 +64,7 @@ class I32View(ctypes.Structure):
 class WorkspaceMap(ctypes.Structure):
     _fields_ = [("list_offset", ctypes.c_int64), ("row_stride", ctypes.c_int64),
                 ("count_offset", ctypes.c_int64), ("bad_offset", ctypes.c_int64),
-                ("total_bytes", ctypes.c_int64)]
+                ("share_offset", ctypes.c_int64), ("total_bytes", ctypes.c_int64)]
 
 
 _lib = None

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <numeric>
 #include <vector>
 
 #include "qsa.h"
@@ -28,6 +29,10 @@ qsa_status fail(qsa_status s, const char *fmt, ...) {
 
 constexpr int64_t kAlign = 256;
 constexpr int64_t kMax32 = 0x7fffffff;
+// The sharing estimate's words in the workspace: est [kSharePairs][2] floats,
+// then the ticket and the choice.
+constexpr int64_t kShareBytes = 512;
+static_assert(qsa::kSharePairs * 8 + 8 <= kShareBytes, "sharing words");
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -38,7 +43,8 @@ bool layout_of(int64_t T, int64_t W, qsa_workspace_map *m) {
     m->row_stride = row;
     m->count_offset = round_up(T * row * 4, kAlign);
     m->bad_offset = m->count_offset + round_up(T * 4, kAlign);
-    m->total_bytes = m->bad_offset + round_up(T * 4, kAlign);
+    m->share_offset = m->bad_offset + round_up(T * 4, kAlign);
+    m->total_bytes = m->share_offset + (T > 0 ? kShareBytes : 0);
     return true;
 }
 
@@ -211,6 +217,7 @@ qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t
     p.row_stride = m.row_stride;
     p.count = (int32_t *)((char *)ws + m.count_offset);
     p.n_bad = (int32_t *)((char *)ws + m.bad_offset);
+    p.share_ticket = (uint32_t *)((char *)ws + m.share_offset + qsa::kSharePairs * 8);
     hipError_t e = qsa::launch_compact(p, stream);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "compaction launch");
 }
@@ -225,9 +232,51 @@ struct KvKind {
     float k_scale = 1.0f, v_scale = 1.0f;
 };
 
+// Below this sharing bound from the sizes alone (rows full, every cache slot
+// referenced) the sharing estimate runs; at or above it the estimate could
+// only confirm the kItemsPerCU layout (full rows share at least this much).
+constexpr double kShareSizeBound = 6.0;
+
+// Parameters of the sharing estimate for an attention launch, or false where
+// the kItemsPerCU layout is taken without one: the sizes already bound the
+// sharing above kShareSizeBound, or there are fewer than two chip-fulls of
+// items for the layout to matter.
+bool sharing_of(const Problem &pr, int32_t HB, void *ws, const qsa_workspace_map &m,
+                qsa::SharingParams *sp) {
+    const int64_t per_t = (int64_t)pr.Hkv * HB;
+    const int64_t chip = (int64_t)qsa::kXcds * qsa::kCusPerXcd * qsa::kItemsPerCU;
+    if (pr.T < 2 || per_t <= 0 || pr.T * per_t < 2 * chip || pr.S <= 0) return false;
+    // KV heads among the items one XCD runs (items are dealt round robin).
+    const int64_t period = per_t * qsa::kXcds / std::gcd(per_t, (int64_t)qsa::kXcds);
+    std::vector<char> seen(pr.Hkv, 0);
+    int heads = 0;
+    for (int64_t i = 0; i < period; i += qsa::kXcds) {
+        const int64_t g = (i % per_t) / HB;
+        if (!seen[g]) {
+            seen[g] = 1;
+            ++heads;
+        }
+    }
+    const double per_xcd = (double)qsa::kCusPerXcd * qsa::kItemsPerCU / heads;
+    if (per_xcd * (double)m.row_stride >= kShareSizeBound * (double)pr.S) return false;
+    char *base = (char *)ws + m.share_offset;
+    sp->list = (const int32_t *)((const char *)ws + m.list_offset);
+    sp->row_stride = m.row_stride;
+    sp->count = (const int32_t *)((const char *)ws + m.count_offset);
+    sp->T = pr.T;
+    sp->pairs = qsa::kSharePairs;
+    sp->span = (int32_t)std::max<int64_t>(1, chip / per_t);   // tokens of one chip-full
+    sp->lambda_scale = (float)per_xcd;
+    sp->threshold = qsa::kShareThreshold;
+    sp->est = (float *)base;
+    sp->ticket = (uint32_t *)(base + qsa::kSharePairs * 8);
+    sp->choice = (int32_t *)(base + qsa::kSharePairs * 8 + 4);
+    return true;
+}
+
 qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
                           const qsa_bf16_view *v, const qsa_bf16_view *out, const Problem &pr,
-                          float scale, const void *ws, const qsa_workspace_map &m,
+                          float scale, void *ws, const qsa_workspace_map &m,
                           hipStream_t stream, KvKind kv = KvKind()) {
     if (pr.T == 0 || pr.Hq == 0) return QSA_OK;
     qsa::AttendParams p{};
@@ -236,7 +285,9 @@ qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
     p.out = (uint16_t *)out->data;
     p.o_st = out->stride[0];
     p.o_sh = out->stride[1];
-    hipError_t e = qsa::launch_attend(p, kv.type, pr.T, stream);
+    qsa::SharingParams sp{};
+    const bool share = sharing_of(pr, p.HB, ws, m, &sp);
+    hipError_t e = qsa::launch_attend(p, kv.type, pr.T, stream, share ? &sp : nullptr);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
 }
 
@@ -524,7 +575,7 @@ qsa_status qsa_compact_slots(const qsa_i32_view *slot_idx, int64_t S, void *work
 
 qsa_status qsa_sparse_attend(const qsa_bf16_view *q, const qsa_bf16_view *k_cache,
                              const qsa_bf16_view *v_cache, int64_t W, float scale,
-                             const void *workspace, size_t workspace_bytes,
+                             void *workspace, size_t workspace_bytes,
                              qsa_bf16_view *out, void *stream) {
     Problem pr;
     qsa_status s = check_attend(q, k_cache, v_cache, out, W, scale, &pr);
@@ -720,7 +771,7 @@ qsa_status qsa_gather_only_fp8kv(const qsa_fp8_view *k8, const qsa_fp8_view *v8,
 
 qsa_status qsa_sparse_attend_fp8kv(const qsa_bf16_view *q, const qsa_fp8_view *k8,
                                    const qsa_fp8_view *v8, float k_scale, float v_scale,
-                                   int64_t W, float scale, const void *workspace,
+                                   int64_t W, float scale, void *workspace,
                                    size_t workspace_bytes, qsa_bf16_view *out, void *stream) {
     Problem pr;
     qsa_status s = check_attend(q, as_view(k8), as_view(v8), out, W, scale, &pr, 1);

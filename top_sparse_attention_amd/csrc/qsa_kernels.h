@@ -25,6 +25,19 @@ constexpr int kItemsPerCU = 8;
 // Waves per SIMD the attention kernel's registers are budgeted for in that
 // layout (up to 256 registers per wave).
 constexpr int kAttendWavesPerSimd = 2;
+// Tiles of gathers each attention wave keeps in flight in that layout.
+constexpr int kAttendAhead = 1;
+// Items per CU of the general layout when the tokens running together share
+// few cache rows (see SharingParams).
+constexpr int kLowShareItemsPerCU = 4;
+// CUs per XCD of the MI355X (256 CUs in 8 XCDs); workgroups are dealt to the
+// XCDs round robin.
+constexpr int kCusPerXcd = 32;
+constexpr int kXcds = 8;
+// Token pairs the sharing estimate samples, and the estimated sharing below
+// which the low-sharing layout is chosen.
+constexpr int kSharePairs = 32;
+constexpr float kShareThreshold = 5.0f;
 // Fewest tiles a split of the decode path takes.
 constexpr int kMinSplitTiles = 4;
 // Entries of a selection row sorted together by the compaction pass.
@@ -47,6 +60,7 @@ struct CompactParams {
     int64_t row_stride;
     int32_t *count;
     int32_t *n_bad;
+    uint32_t *share_ticket;   // set to 0 by the workgroup of row 0 (null: left alone)
 };
 
 // Element type of the K/V cache: BF16, or FP8 E4M3 codes with one scale per
@@ -78,6 +92,34 @@ struct AttendParams {
     int32_t Hq;
     float *part_o;       // [n_parts][T][Hq][256], O not yet divided by l
     float *part_ml;      // [n_parts][T][Hq][2]: running max (log2 units) and sum
+    // Gated launch (non-null choice): the kernel does its work only if
+    // (*choice == 1) == (choice_value == 1), so of two launches with values 0
+    // and 1 exactly one works, whatever the word holds.
+    const int32_t *choice;
+    int32_t choice_value;
+};
+
+// Sharing estimate.  Items run kItemsPerCU to a CU and walk their slot lists
+// in ascending slot ranges at about the same rate, so a cache row one item
+// reads is read at about the same time by the other items on its XCD that
+// read it, and they share it in L2.  The expected number of such readers is
+//   lambda = (concurrent items of one KV head per XCD) x |L_a & L_b| / |L_b|
+// for tokens a, b that run together.  The estimate samples `pairs` token
+// pairs (b at most `span` tokens after a), counts each pair's common slots,
+// and writes choice = 1 (take the kLowShareItemsPerCU layout) if
+// lambda_scale * sum|L_a & L_b| < threshold * sum|L_b|, else 0.
+struct SharingParams {
+    const int32_t *list;
+    int64_t row_stride;
+    const int32_t *count;
+    int64_t T;
+    int32_t pairs;
+    int32_t span;
+    float lambda_scale;   // concurrent items of one KV head per XCD
+    float threshold;
+    float *est;           // [pairs][2]: common slots (scaled), |L_b|
+    uint32_t *ticket;     // 0 on entry (compaction clears it; each run leaves it 0)
+    int32_t *choice;
 };
 
 struct MergeParams {
@@ -134,7 +176,10 @@ struct IndexerSelectParams {
 hipError_t launch_compact(const CompactParams &p, hipStream_t stream);
 hipError_t launch_indexer_scores(const IndexerScoreParams &p, hipStream_t stream);
 hipError_t launch_indexer_select(const IndexerSelectParams &p, hipStream_t stream);
-hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_t stream);
+// With a non-null `share`, the sharing estimate runs first and picks the
+// layout (general-layout kernels only; others ignore it).
+hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_t stream,
+                         const SharingParams *share = nullptr);
 hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
                                  hipStream_t stream);
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream);

@@ -17,8 +17,10 @@
 //     large pages of the cache, and lets the tokens running at one time
 //     read the same rows at about the same time.
 //  2. attend_kernel: one work item = (token t, KV head g, block of up to 16
-//     query heads of that group) = one wave, 8 (or 12, see AttendLayout)
-//     items resident per CU.  The wave walks its item's 16-slot tiles in
+//     query heads of that group) = one wave, 8 items resident per CU (4
+//     where sharing_kernel estimates that the running tokens share few
+//     cache rows; 12 for FP8 caches with at most 8 heads per KV head; see
+//     AttendLayout).  The wave walks its item's 16-slot tiles in
 //     list order.  Per tile it loads the K rows straight into the registers
 //     of the score MFMA's A operand and the V rows (whole rows) into
 //     registers that it then writes to its LDS tile, both one tile ahead of
@@ -101,21 +103,23 @@ constexpr float kRescaleSlack = 8.0f;
 //    16-lane group reads with a transpose load fall in 4 different 32-byte
 //    bank windows; 8 lanes writing consecutive chunks of a row hit 8 different
 //    16-byte bank groups).  The item requests a block sized so that exactly
-//    kItemsPerCU items fit in the 160 KiB of a CU.
+//    kItems items fit in the 160 KiB of a CU: kItemsPerCU, or
+//    kLowShareItemsPerCU where the running tokens share few cache rows.
 //  kQRows = 8 (FP8 caches with at most 8 query heads per KV head): V rows of
 //    528 B; the 12.4 KiB item lets 12 items (3 per SIMD) fit a CU.  FP8
 //    tiles are short and their waves wait on load latency, which the extra
 //    items hide (BF16 measured slower this way).  MFMA columns 8..15 then
 //    repeat heads 0..7 and are not written out.
-template <int kQRows>
+template <int kQRows, int kItemsGeneral = kItemsPerCU>
 struct AttendLayout {
     static constexpr int kVPitch = kQRows == 16 ? kRowBytes + 32 : kRowBytes + 16;
     static constexpr int kTileBytes = kTileSlots * kVPitch;
     static constexpr int kQBytes = kQRows * kQPitch;
     static constexpr int kUsed = kTileBytes + kQBytes;
-    static constexpr int kItems = kQRows == 16 ? kItemsPerCU : 12;
-    static constexpr int kLds = kQRows == 16 ? 160 * 1024 / kItemsPerCU - 1024 : kUsed;
+    static constexpr int kItems = kQRows == 16 ? kItemsGeneral : 12;
+    static constexpr int kLds = kQRows == 16 ? 160 * 1024 / kItems - 1024 : kUsed;
     static constexpr int kWavesPerSimd = kQRows == 16 ? kAttendWavesPerSimd : 3;
+    static constexpr int kAhead = kQRows == 16 ? kAttendAhead : 1;   // tiles in flight per wave
     static constexpr int kQChunksPerLane = kQRows * kChunksPerRow / 64;
     static_assert(kUsed <= kLds, "item LDS");
     static_assert(kItems * kLds <= 160 * 1024, "LDS budget of a gfx950 CU");
@@ -161,6 +165,7 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
 
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
+    if (t == 0 && tid == 0 && p.share_ticket != nullptr) *p.share_ticket = 0;
     const int32_t *src = p.slot_idx + t * p.stride_t;
     int32_t *dst = p.list + t * p.row_stride;
     const uint32_t pad_key = 1u << (p.key_bits - 1);
@@ -369,12 +374,13 @@ __device__ __forceinline__ int tile_slot(const int32_t *list, int tile, int ntil
 // the wave's requests reach the memory system spread out.  Each wave walks
 // its own item's slot list in order, and the list is grouped by slot range,
 // so a wave's consecutive tiles fall in the same part of the cache.
-template <bool kSplit, KvType KV, int kQRows>
-__global__ __launch_bounds__(64, AttendLayout<kQRows>::kWavesPerSimd) void attend_kernel(
+template <bool kSplit, KvType KV, int kQRows, int kItems = kItemsPerCU>
+__global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) void attend_kernel(
     const AttendParams p) {
     using Gth = KvGather<KV>;
-    using Lay = AttendLayout<kQRows>;
+    using Lay = AttendLayout<kQRows, kItems>;
     __shared__ __attribute__((aligned(16))) char smem[Lay::kLds];
+    if (p.choice != nullptr && ((*p.choice == 1) != (p.choice_value == 1))) return;
 
     const int lane = threadIdx.x;
     const int c = lane & 15;   // MFMA column: query head within the block / A-operand row
@@ -444,15 +450,17 @@ __global__ __launch_bounds__(64, AttendLayout<kQRows>::kWavesPerSimd) void atten
     // vector is loaded before the V gathers of the tile ahead of it, so
     // waiting for it never waits for those.  (Two tiles ahead measured no
     // faster.)
+    constexpr int kAhead = Lay::kAhead;
     const int step = splits;
-    u32x4_t rk[Gth::kKLoads], rv[Gth::kVLoads];
+    u32x4_t rkb[kAhead][Gth::kKLoads], rvb[kAhead][Gth::kVLoads];
     int tile = split;
-    int slot_next;
-    {
-        const int slot = tile_slot(list, tile, ntiles, lane);
-        gather_k<KV>(rk, slot, kb, k_ss, lane);
-        slot_next = tile_slot(list, tile + step, ntiles, lane);
-        gather_v<KV>(rv, slot, vb, v_ss, lane);
+    int slot_next = tile_slot(list, tile, ntiles, lane);
+#pragma unroll
+    for (int b = 0; b < kAhead; ++b) {
+        const int slot = slot_next;
+        gather_k<KV>(rkb[b], slot, kb, k_ss, lane);
+        slot_next = tile_slot(list, tile + (b + 1) * step, ntiles, lane);
+        gather_v<KV>(rvb[b], slot, vb, v_ss, lane);
     }
 
 #pragma unroll
@@ -472,7 +480,10 @@ __global__ __launch_bounds__(64, AttendLayout<kQRows>::kWavesPerSimd) void atten
     const int tr_row = 4 * j + (c >> 2);    // V row this lane addresses in a transpose load
     const int tr_sub = c & 3;               // which 4 of the 16 dims of a block
 
-    for (; tile < ntiles; tile += step) {
+    // One tile: consumes K(tile) and V(tile) from rk and rv and issues the
+    // gathers of tile + kAhead * step into the same registers.
+    auto tile_body = [&](const int tile, u32x4_t (&rk)[Gth::kKLoads],
+                         u32x4_t (&rv)[Gth::kVLoads]) {
         // S^T for the tile: s[i] = score of tile slot 4j+i against head c.
         // The query operands are read from LDS in two halves to bound the
         // registers they hold.
@@ -542,7 +553,7 @@ __global__ __launch_bounds__(64, AttendLayout<kQRows>::kWavesPerSimd) void atten
         wave_lds_fence();   // the previous tile's transpose reads are done
         stage_v<KV, Lay::kVPitch>(rv, vs_lds, lane);
         __builtin_amdgcn_sched_barrier(0);   // V(i) is consumed before V(i+1) lands
-        slot_next = tile_slot(list, tile + 2 * step, ntiles, lane);
+        slot_next = tile_slot(list, tile + (kAhead + 1) * step, ntiles, lane);
         gather_v<KV>(rv, slot_g, vb, v_ss, lane);
         wave_lds_fence();   // other lanes of this wave wrote the rows read below
 
@@ -571,6 +582,13 @@ __global__ __launch_bounds__(64, AttendLayout<kQRows>::kWavesPerSimd) void atten
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+        }
+    };
+    for (; tile < ntiles; tile += kAhead * step) {
+#pragma unroll
+        for (int b = 0; b < kAhead; ++b) {
+            if (b > 0 && tile + b * step >= ntiles) break;
+            tile_body(tile + b * step, rkb[b], rvb[b]);
         }
     }
 
@@ -657,6 +675,87 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     }
     *(u32x2_t *)(p.out + t * p.o_st + (int64_t)h * p.o_sh + 4 * lane) =
         __builtin_bit_cast(u32x2_t, ob);
+}
+
+// ---------------------------------------------------------------- sharing estimate
+
+// One workgroup per sampled token pair (a, b): a's list (at most
+// kShareTable / 2 entries of it) goes into an open-addressing hash set in
+// LDS, b's list is looked up in it.  The count of common slots, scaled by
+// the share of a's list that was hashed, and |L_b| go to est[pair]; the
+// workgroup that finishes last adds them up and writes the choice (see
+// SharingParams), then clears the ticket for the next call.
+constexpr int kShareTable = 4096;
+
+__device__ __forceinline__ uint32_t share_hash(int32_t key) {
+    return ((uint32_t)key * 2654435761u) >> (32 - 12);
+}
+static_assert(kShareTable == 1 << 12, "share_hash yields 12 bits");
+
+__global__ __launch_bounds__(256) void sharing_kernel(const SharingParams p) {
+    __shared__ int32_t table[kShareTable];
+    __shared__ int wave_hits[4];
+    const int tid = threadIdx.x;
+    const int k = blockIdx.x;
+    // a spread over [0, T - 2], b within `span` tokens after it.
+    const int64_t a = (int64_t)k * (p.T - 2) / max(p.pairs - 1, 1);
+    const int64_t b = min(a + 1 + (int64_t)((k * 37) % p.span), p.T - 1);
+    for (int i = tid; i < kShareTable; i += 256) table[i] = -1;
+    __syncthreads();
+    const int32_t *la = p.list + a * p.row_stride;
+    const int32_t *lb = p.list + b * p.row_stride;
+    const int na = p.count[a], nb = p.count[b];
+    const int nh = min(na, kShareTable / 2);   // at most half full: every probe ends
+    for (int i = tid; i < nh; i += 256) {
+        const int32_t key = la[i];
+        uint32_t h = share_hash(key);
+        for (;;) {
+            const int32_t prev = atomicCAS(&table[h], -1, key);
+            if (prev == -1 || prev == key) break;
+            h = (h + 1) & (kShareTable - 1);
+        }
+    }
+    __syncthreads();
+    int hits = 0;
+    for (int i = tid; i < nb; i += 256) {
+        const int32_t key = lb[i];
+        uint32_t h = share_hash(key);
+        for (int32_t e; (e = table[h]) != -1; h = (h + 1) & (kShareTable - 1)) {
+            if (e == key) {
+                ++hits;
+                break;
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) hits += __shfl_xor(hits, off);
+    if ((tid & 63) == 0) wave_hits[tid >> 6] = hits;
+    __syncthreads();
+    if (tid >= 64) return;
+    int last = 0;
+    if (tid == 0) {
+        const int total = wave_hits[0] + wave_hits[1] + wave_hits[2] + wave_hits[3];
+        p.est[2 * k] = nh > 0 ? (float)total * ((float)na / (float)nh) : 0.0f;
+        p.est[2 * k + 1] = (float)nb;
+        __threadfence();
+        last = atomicAdd(p.ticket, 1u) == (uint32_t)(p.pairs - 1);
+    }
+    if (!__shfl(last, 0)) return;
+    __threadfence();
+    float common = 0.0f, len = 0.0f;
+    if (tid < p.pairs) {
+        common = __hip_atomic_load(&p.est[2 * tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        len = __hip_atomic_load(&p.est[2 * tid + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        common += __shfl_xor(common, off);
+        len += __shfl_xor(len, off);
+    }
+    if (tid == 0) {
+        *p.choice = (len > 0.0f && p.lambda_scale * common < p.threshold * len) ? 1 : 0;
+        *p.ticket = 0;
+    }
 }
 
 // ---------------------------------------------------------------- gather only
@@ -1320,10 +1419,33 @@ void launch_attend_any(const AttendParams &p, KvType kv, int64_t blocks, hipStre
                            dim3(64), 0, stream, p);
 }
 
-hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_t stream) {
+hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_t stream,
+                         const SharingParams *share) {
     const int64_t items = T * (int64_t)p.Hkv * p.HB;
     if (items == 0) return hipSuccess;
-    launch_attend_any<false>(p, kv, items, stream);
+    if (share == nullptr || (kv == KvType::kFp8 && p.G <= 8)) {
+        launch_attend_any<false>(p, kv, items, stream);
+        return hipGetLastError();
+    }
+    // The estimate picks one of two launches of the general layout; the other
+    // returns at once.  Both compute the same bits.
+    hipLaunchKernelGGL(sharing_kernel, dim3((unsigned)share->pairs), dim3(256), 0, stream, *share);
+    AttendParams g = p;
+    g.choice = share->choice;
+    g.choice_value = 0;
+    if (kv == KvType::kFp8)
+        hipLaunchKernelGGL((attend_kernel<false, KvType::kFp8, 16>), dim3((unsigned)items),
+                           dim3(64), 0, stream, g);
+    else
+        hipLaunchKernelGGL((attend_kernel<false, KvType::kBf16, 16>), dim3((unsigned)items),
+                           dim3(64), 0, stream, g);
+    g.choice_value = 1;
+    if (kv == KvType::kFp8)
+        hipLaunchKernelGGL((attend_kernel<false, KvType::kFp8, 16, kLowShareItemsPerCU>),
+                           dim3((unsigned)items), dim3(64), 0, stream, g);
+    else
+        hipLaunchKernelGGL((attend_kernel<false, KvType::kBf16, 16, kLowShareItemsPerCU>),
+                           dim3((unsigned)items), dim3(64), 0, stream, g);
     return hipGetLastError();
 }
 
