@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (for counter calibration)")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache steps and the device-copy reference (they add "
+                         "kernel instances to a profile)")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as replays of one captured HIP graph (the kernels' "
                          "own times still come from the eager loop)")
@@ -230,6 +233,47 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     gather_only_ms = c0.elapsed_time(c1) / K
+    peak_mib = torch.cuda.max_memory_allocated(dev) / 2**20
+
+    # Cold steps: before each, a 1 GiB write (untimed) evicts the L2s and the
+    # 256 MB Infinity Cache, so the step starts with its inputs in HBM only.
+    # Then a device-to-device copy as the streaming reference of this GPU.
+    cold, copy_ref = None, None
+    if not args.no_cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        steps_ms, attend_ms_cold = [], []
+        for _ in range(min(K, 10)):
+            flush.fill_(1)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
+            select()
+            compact()
+            ev[1].record()
+            attend()
+            ev[2].record()
+            finish()
+            ev[3].record()
+            torch.cuda.synchronize()
+            steps_ms.append(ev[0].elapsed_time(ev[3]))
+            attend_ms_cold.append(ev[1].elapsed_time(ev[2]))
+        cold = {"ms_per_step_median": float(np.median(steps_ms)),
+                "attend_kernel_ms_median": float(np.median(attend_ms_cold)),
+                "steps": len(steps_ms), "flush_bytes": 1 << 30}
+        del flush
+        src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        dst.copy_(src)
+        x0 = torch.cuda.Event(enable_timing=True)
+        x1 = torch.cuda.Event(enable_timing=True)
+        x0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        x1.record()
+        torch.cuda.synchronize()
+        copy_ref = {"GBps": 5 * 2 * src.numel() / (x0.elapsed_time(x1) * 1e-3) / 1e9,
+                    "what": "torch device-to-device copy of 2 GiB; read + write bytes / time"}
+        del src, dst
 
     if indexed:
         # 4 positions per kept block (at most `budget` complete causal blocks)
@@ -322,6 +366,9 @@ def main():
         "attend_kernel_ms": attn_avg,
         "indexer_topk_ms": select_ms,
         "attend_kernel_ms_min": float(np.min(attn_ms)),
+        "attend_kernel_ms_median": float(np.median(attn_ms)),
+        "cold": cold,
+        "device_copy": copy_ref,
         "gather_GBps": gather_bytes / (attn_avg * 1e-3) / 1e9,
         "gather_only": {"ms": gather_only_ms,
                         "GBps": gather_bytes / (gather_only_ms * 1e-3) / 1e9},
@@ -329,7 +376,7 @@ def main():
         "attend_bytes_per_launch": attn_bytes,
         "parity": {"rows": int(rows.size), **{k_: v_ for k_, v_ in parity.items()
                                               if k_ != "rows"}},
-        "peak_allocated_MiB": torch.cuda.max_memory_allocated(dev) / 2**20,
+        "peak_allocated_MiB": peak_mib,
     }
     print(json.dumps(record), flush=True)
 

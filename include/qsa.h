@@ -92,8 +92,8 @@ typedef struct qsa_i32_view {
  *          ranges, ascending; input order within a range);
  *   count: int32 [T], number of valid entries of row t;
  *   n_bad: int32 [T], entries of row t that were neither -1 nor in [0, S);
- *   share: 512 bytes the attention uses to pick its layout (see
- *          qsa_sparse_attend); the compaction pass initialises them. */
+ *   share: 512 bytes the attention writes to pick its layout (see
+ *          qsa_sparse_attend). */
 typedef struct qsa_workspace_map {
     int64_t list_offset;
     int64_t row_stride;

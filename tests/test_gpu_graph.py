@@ -93,7 +93,7 @@ def test_indexer_topk_graph_replays_exactly():
 
 def test_prefill_with_sharing_estimate_graph_replays_exactly():
     # A large cache against W: the sharing estimate runs, then the gated
-    # attention launches; its ticket must be left cleared by every replay.
+    # attention launches.
     case = qi.random_case(1205, T=4096, S=131072, Hq=3, Hkv=1, W=512)
     q, k, v, sl = upload(case, DEV)
     out = torch.empty_like(q)

@@ -21,8 +21,8 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 SHARE_PAIRS = 32          # token pairs the estimate samples
-# The choice word follows the pairs' (common, length) floats and the ticket.
-CHOICE_BYTE = SHARE_PAIRS * 8 + 4
+# The choice word follows the pairs' (common, length) floats.
+CHOICE_BYTE = SHARE_PAIRS * 8
 
 
 def choice_of(ws: torch.Tensor, T: int, W: int) -> int:

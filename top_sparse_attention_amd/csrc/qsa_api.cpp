@@ -30,9 +30,9 @@ qsa_status fail(qsa_status s, const char *fmt, ...) {
 constexpr int64_t kAlign = 256;
 constexpr int64_t kMax32 = 0x7fffffff;
 // The sharing estimate's words in the workspace: est [kSharePairs][2] floats,
-// then the ticket and the choice.
+// then the choice.
 constexpr int64_t kShareBytes = 512;
-static_assert(qsa::kSharePairs * 8 + 8 <= kShareBytes, "sharing words");
+static_assert(qsa::kSharePairs * 8 + 4 <= kShareBytes && qsa::kSharePairs <= 64, "sharing words");
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -217,7 +217,6 @@ qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t
     p.row_stride = m.row_stride;
     p.count = (int32_t *)((char *)ws + m.count_offset);
     p.n_bad = (int32_t *)((char *)ws + m.bad_offset);
-    p.share_ticket = (uint32_t *)((char *)ws + m.share_offset + qsa::kSharePairs * 8);
     hipError_t e = qsa::launch_compact(p, stream);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "compaction launch");
 }
@@ -245,7 +244,8 @@ bool sharing_of(const Problem &pr, int32_t HB, void *ws, const qsa_workspace_map
                 qsa::SharingParams *sp) {
     const int64_t per_t = (int64_t)pr.Hkv * HB;
     const int64_t chip = (int64_t)qsa::kXcds * qsa::kCusPerXcd * qsa::kItemsPerCU;
-    if (pr.T < 2 || per_t <= 0 || pr.T * per_t < 2 * chip || pr.S <= 0) return false;
+    if (pr.T < 2 || pr.T > kMax32 || per_t <= 0 || pr.T * per_t < 2 * chip || pr.S <= 0)
+        return false;
     // KV heads among the items one XCD runs (items are dealt round robin).
     const int64_t period = per_t * qsa::kXcds / std::gcd(per_t, (int64_t)qsa::kXcds);
     std::vector<char> seen(pr.Hkv, 0);
@@ -263,14 +263,19 @@ bool sharing_of(const Problem &pr, int32_t HB, void *ws, const qsa_workspace_map
     sp->list = (const int32_t *)((const char *)ws + m.list_offset);
     sp->row_stride = m.row_stride;
     sp->count = (const int32_t *)((const char *)ws + m.count_offset);
-    sp->T = pr.T;
+    // Pairs: a spread over [0, T - 2], b at most one chip-full of items later
+    // (tokens that run at about the same time).
+    const int64_t span = std::max<int64_t>(1, chip / per_t);
     sp->pairs = qsa::kSharePairs;
-    sp->span = (int32_t)std::max<int64_t>(1, chip / per_t);   // tokens of one chip-full
+    for (int i = 0; i < qsa::kSharePairs; ++i) {
+        const int64_t a = (int64_t)i * (pr.T - 2) / (qsa::kSharePairs - 1);
+        sp->pair_a[i] = (int32_t)a;
+        sp->pair_b[i] = (int32_t)std::min<int64_t>(a + 1 + (i * 37) % span, pr.T - 1);
+    }
     sp->lambda_scale = (float)per_xcd;
     sp->threshold = qsa::kShareThreshold;
     sp->est = (float *)base;
-    sp->ticket = (uint32_t *)(base + qsa::kSharePairs * 8);
-    sp->choice = (int32_t *)(base + qsa::kSharePairs * 8 + 4);
+    sp->choice = (int32_t *)(base + qsa::kSharePairs * 8);
     return true;
 }
 

@@ -34,8 +34,8 @@ constexpr int kLowShareItemsPerCU = 4;
 // XCDs round robin.
 constexpr int kCusPerXcd = 32;
 constexpr int kXcds = 8;
-// Token pairs the sharing estimate samples, and the estimated sharing below
-// which the low-sharing layout is chosen.
+// Token pairs the sharing estimate samples (at most 64: one wave adds them
+// up), and the estimated sharing below which the low-sharing layout is chosen.
 constexpr int kSharePairs = 32;
 constexpr float kShareThreshold = 5.0f;
 // Fewest tiles a split of the decode path takes.
@@ -60,7 +60,6 @@ struct CompactParams {
     int64_t row_stride;
     int32_t *count;
     int32_t *n_bad;
-    uint32_t *share_ticket;   // set to 0 by the workgroup of row 0 (null: left alone)
 };
 
 // Element type of the K/V cache: BF16, or FP8 E4M3 codes with one scale per
@@ -104,21 +103,19 @@ struct AttendParams {
 // reads is read at about the same time by the other items on its XCD that
 // read it, and they share it in L2.  The expected number of such readers is
 //   lambda = (concurrent items of one KV head per XCD) x |L_a & L_b| / |L_b|
-// for tokens a, b that run together.  The estimate samples `pairs` token
-// pairs (b at most `span` tokens after a), counts each pair's common slots,
-// and writes choice = 1 (take the kLowShareItemsPerCU layout) if
+// for tokens a, b that run together.  The estimate takes `pairs` token
+// pairs (pair_a[i], pair_b[i]), counts each pair's common slots, and writes
+// choice = 1 (take the kLowShareItemsPerCU layout) if
 // lambda_scale * sum|L_a & L_b| < threshold * sum|L_b|, else 0.
 struct SharingParams {
     const int32_t *list;
     int64_t row_stride;
     const int32_t *count;
-    int64_t T;
     int32_t pairs;
-    int32_t span;
+    int32_t pair_a[kSharePairs], pair_b[kSharePairs];   // token rows, a != b
     float lambda_scale;   // concurrent items of one KV head per XCD
     float threshold;
     float *est;           // [pairs][2]: common slots (scaled), |L_b|
-    uint32_t *ticket;     // 0 on entry (compaction clears it; each run leaves it 0)
     int32_t *choice;
 };
 

@@ -60,6 +60,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 #define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T *)(p))
@@ -165,7 +166,6 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
 
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
-    if (t == 0 && tid == 0 && p.share_ticket != nullptr) *p.share_ticket = 0;
     const int32_t *src = p.slot_idx + t * p.stride_t;
     int32_t *dst = p.list + t * p.row_stride;
     const uint32_t pad_key = 1u << (p.key_bits - 1);
@@ -679,83 +679,129 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 
 // ---------------------------------------------------------------- sharing estimate
 
-// One workgroup per sampled token pair (a, b): a's list (at most
-// kShareTable / 2 entries of it) goes into an open-addressing hash set in
-// LDS, b's list is looked up in it.  The count of common slots, scaled by
-// the share of a's list that was hashed, and |L_b| go to est[pair]; the
-// workgroup that finishes last adds them up and writes the choice (see
-// SharingParams), then clears the ticket for the next call.
-constexpr int kShareTable = 4096;
+// One workgroup per sampled token pair (a, b): a's list (at most kShareKeys
+// entries of it) goes into a hash set in LDS, b's list is looked up in it.
+// The set is kShareBuckets buckets of 8 entries (2 keys per bucket on
+// average), filled through per-bucket counters; a key that finds its bucket
+// full goes on to the next.  A lookup reads one 32-byte bucket, so every
+// lane of a wave finishes in about the same number of steps.  The count of
+// common slots, scaled by the share of a's list that was hashed, and |L_b|
+// go to est[pair]; sharing_choice_kernel then adds them up and writes the
+// choice (see SharingParams).
+constexpr int kShareKeys = 2048;
+constexpr int kShareBuckets = 1024;
+constexpr int kShareBucketSize = 8;
 
-__device__ __forceinline__ uint32_t share_hash(int32_t key) {
-    return ((uint32_t)key * 2654435761u) >> (32 - 12);
+__device__ __forceinline__ uint32_t share_bucket(int32_t key) {
+    return ((uint32_t)key * 2654435761u) >> (32 - 10);
 }
-static_assert(kShareTable == 1 << 12, "share_hash yields 12 bits");
+static_assert(kShareBuckets == 1 << 10, "share_bucket yields 10 bits");
+
+// True if `key` is in bucket bk; *full says whether the bucket has no free
+// entry (then a key of this home bucket may have moved on to the next).
+__device__ __forceinline__ bool share_in_bucket(const int32_t *table, uint32_t bk, int32_t key,
+                                                bool *full) {
+    const i32x4_t e0 = *(const i32x4_t *)&table[bk * kShareBucketSize];
+    const i32x4_t e1 = *(const i32x4_t *)&table[bk * kShareBucketSize + 4];
+    *full = e1[3] != -1;
+    return e0[0] == key || e0[1] == key || e0[2] == key || e0[3] == key || e1[0] == key ||
+           e1[1] == key || e1[2] == key || e1[3] == key;
+}
 
 __global__ __launch_bounds__(256) void sharing_kernel(const SharingParams p) {
-    __shared__ int32_t table[kShareTable];
+    constexpr int kPerThread = kShareKeys / 256;
+    __shared__ __attribute__((aligned(16))) int32_t table[kShareBuckets * kShareBucketSize];
+    __shared__ int32_t fill[kShareBuckets];
     __shared__ int wave_hits[4];
     const int tid = threadIdx.x;
     const int k = blockIdx.x;
-    // a spread over [0, T - 2], b within `span` tokens after it.
-    const int64_t a = (int64_t)k * (p.T - 2) / max(p.pairs - 1, 1);
-    const int64_t b = min(a + 1 + (int64_t)((k * 37) % p.span), p.T - 1);
-    for (int i = tid; i < kShareTable; i += 256) table[i] = -1;
+    const int32_t *la = p.list + (int64_t)p.pair_a[k] * p.row_stride;
+    const int32_t *lb = p.list + (int64_t)p.pair_b[k] * p.row_stride;
+    const int na = p.count[p.pair_a[k]], nb = p.count[p.pair_b[k]];
+    // Entry tid + 256 u of each row, all loads in flight at once (rows are
+    // row_stride long; entries past a row's count are never used).
+    int32_t ka[kPerThread], kb[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        const int i = tid + 256 * u;
+        ka[u] = i < p.row_stride ? la[i] : -1;
+        kb[u] = i < p.row_stride ? lb[i] : -1;
+    }
+    for (int i = tid; i < kShareBuckets * kShareBucketSize / 4; i += 256)
+        *(i32x4_t *)&table[4 * i] = i32x4_t{-1, -1, -1, -1};
+    for (int i = tid; i < kShareBuckets; i += 256) fill[i] = 0;
     __syncthreads();
-    const int32_t *la = p.list + a * p.row_stride;
-    const int32_t *lb = p.list + b * p.row_stride;
-    const int na = p.count[a], nb = p.count[b];
-    const int nh = min(na, kShareTable / 2);   // at most half full: every probe ends
-    for (int i = tid; i < nh; i += 256) {
-        const int32_t key = la[i];
-        uint32_t h = share_hash(key);
-        for (;;) {
-            const int32_t prev = atomicCAS(&table[h], -1, key);
-            if (prev == -1 || prev == key) break;
-            h = (h + 1) & (kShareTable - 1);
+    // At most kShareKeys keys in kShareBuckets * 8 entries: a free entry is
+    // always found.  The home buckets of a thread's keys are claimed
+    // together; the rare key whose home bucket is full walks on.
+    const int nh = min(na, kShareKeys);
+    int pos[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u)
+        pos[u] = tid + 256 * u < nh ? atomicAdd(&fill[share_bucket(ka[u])], 1) : 0;
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        if (tid + 256 * u >= nh) continue;
+        uint32_t bk = share_bucket(ka[u]);
+        int at = pos[u];
+        while (at >= kShareBucketSize) {
+            bk = (bk + 1) & (kShareBuckets - 1);
+            at = atomicAdd(&fill[bk], 1);
         }
+        table[bk * kShareBucketSize + at] = ka[u];
     }
     __syncthreads();
     int hits = 0;
-    for (int i = tid; i < nb; i += 256) {
-        const int32_t key = lb[i];
-        uint32_t h = share_hash(key);
-        for (int32_t e; (e = table[h]) != -1; h = (h + 1) & (kShareTable - 1)) {
-            if (e == key) {
-                ++hits;
-                break;
-            }
+    bool found[kPerThread], full[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u)
+        found[u] = share_in_bucket(table, share_bucket(kb[u]), kb[u], &full[u]);
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        if (tid + 256 * u >= nb) continue;
+        bool hit = found[u], more = full[u];
+        for (uint32_t bk = share_bucket(kb[u]); !hit && more;) {
+            bk = (bk + 1) & (kShareBuckets - 1);
+            hit = share_in_bucket(table, bk, kb[u], &more);
         }
+        hits += hit;
+    }
+    // Rows longer than kShareKeys entries: the rest of b, one at a time.
+#pragma unroll 1
+    for (int i = kShareKeys + tid; i < nb; i += 256) {
+        const int32_t key = lb[i];
+        bool hit = false, more = true;
+        for (uint32_t bk = share_bucket(key); !hit && more; bk = (bk + 1) & (kShareBuckets - 1))
+            hit = share_in_bucket(table, bk, key, &more);
+        hits += hit;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) hits += __shfl_xor(hits, off);
     if ((tid & 63) == 0) wave_hits[tid >> 6] = hits;
     __syncthreads();
-    if (tid >= 64) return;
-    int last = 0;
     if (tid == 0) {
         const int total = wave_hits[0] + wave_hits[1] + wave_hits[2] + wave_hits[3];
         p.est[2 * k] = nh > 0 ? (float)total * ((float)na / (float)nh) : 0.0f;
         p.est[2 * k + 1] = (float)nb;
-        __threadfence();
-        last = atomicAdd(p.ticket, 1u) == (uint32_t)(p.pairs - 1);
     }
-    if (!__shfl(last, 0)) return;
-    __threadfence();
+}
+
+// One wave: adds up the pairs' counts and writes the choice (the launch
+// boundary after sharing_kernel makes its stores visible).
+__global__ __launch_bounds__(64) void sharing_choice_kernel(const SharingParams p) {
+    const int lane = threadIdx.x;
     float common = 0.0f, len = 0.0f;
-    if (tid < p.pairs) {
-        common = __hip_atomic_load(&p.est[2 * tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        len = __hip_atomic_load(&p.est[2 * tid + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane < p.pairs) {
+        common = p.est[2 * lane];
+        len = p.est[2 * lane + 1];
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         common += __shfl_xor(common, off);
         len += __shfl_xor(len, off);
     }
-    if (tid == 0) {
+    if (lane == 0)
         *p.choice = (len > 0.0f && p.lambda_scale * common < p.threshold * len) ? 1 : 0;
-        *p.ticket = 0;
-    }
 }
 
 // ---------------------------------------------------------------- gather only
@@ -1430,6 +1476,7 @@ hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_
     // The estimate picks one of two launches of the general layout; the other
     // returns at once.  Both compute the same bits.
     hipLaunchKernelGGL(sharing_kernel, dim3((unsigned)share->pairs), dim3(256), 0, stream, *share);
+    hipLaunchKernelGGL(sharing_choice_kernel, dim3(1), dim3(64), 0, stream, *share);
     AttendParams g = p;
     g.choice = share->choice;
     g.choice_value = 0;
