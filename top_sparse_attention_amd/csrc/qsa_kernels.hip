@@ -129,8 +129,8 @@ struct AttendLayout {
                   "one more item must not fit");
 };
 
-// A row of zeros: masked tile rows and absent query heads load from here, so
-// every load is unconditional and no select waits on loaded data.
+// A row of zeros: absent query heads (and index rows past the end) load from
+// here, so every load is unconditional and no select waits on loaded data.
 __device__ __attribute__((aligned(16))) uint16_t kZeroRow[kHeadDim] = {};
 
 // 16-byte load through the global address space (all operands of the
@@ -229,13 +229,9 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
 
 // ---------------------------------------------------------------- gathers
 
-// Start of the cache row of `slot`, or of the row of zeros for slot -1.
-// Both addresses are formed and one is selected, so no branch depends on
-// the slot.
+// Start of the cache row of `slot` (a valid slot: see stand_in).
 __device__ __forceinline__ const char *row_ptr(const char *base, int64_t ss, int slot) {
-    const uint64_t a = (uint64_t)(base + (int64_t)max(slot, 0) * ss);
-    const uint64_t z = (uint64_t)(const char *)kZeroRow;
-    return (const char *)(slot >= 0 ? a : z);
+    return base + (int64_t)slot * ss;
 }
 
 // K rows go straight from memory into the A operand of the score MFMA.  The
@@ -247,7 +243,7 @@ __device__ __forceinline__ const char *row_ptr(const char *base, int64_t ss, int
 // contiguous bytes of each of the 16 rows.  FP8 keys: load u reads dims
 // 64 u + 16 j .. +16, converted just before use.  The query operand of each
 // k-step is read with the same map (q_chunk).  `slot` is the slot of tile
-// row (lane & 15), -1 for none (then the row of zeros is read).
+// row (lane & 15), from stand_in.
 template <KvType KV>
 __device__ __forceinline__ void gather_k1(u32x4_t &r, int q, int slot, const char *kb,
                                           int64_t k_ss, int lane) {
@@ -303,7 +299,7 @@ __device__ __forceinline__ bf16x8_t k_operand(const u32x4_t (&rk)[KvGather<KV>::
 // system spread out rather than as one burst, which measured markedly faster
 // (a burst of whole-row loads from every wave delays the other waves'
 // requests and lets the waves of the chip fall out of step).
-template <KvType KV>
+template <KvType KV, bool kScalarAddr>
 __device__ __forceinline__ void gather_v(u32x4_t (&rv)[KvGather<KV>::kVLoads], int slot,
                                          const char *vb, int64_t v_ss, int lane) {
     using G = KvGather<KV>;
@@ -311,16 +307,34 @@ __device__ __forceinline__ void gather_v(u32x4_t (&rv)[KvGather<KV>::kVLoads], i
     const int sub = lane / G::kLanesPerRow;   // which row of the load this lane reads
 #pragma unroll
     for (int q = 0; q < G::kVLoads; ++q) {
-        // The rows' addresses are wave-uniform (scalar registers); each lane
-        // then picks the one of its row.
-        const char *row = row_ptr(vb, v_ss, __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q));
+        // The slots of the load's rows are wave-uniform (read from the lanes
+        // that hold them).  kScalarAddr: each row's address is formed in
+        // scalar registers (the empty asm keeps it there) and each lane picks
+        // the one of its row.  Otherwise each lane picks its row's slot and
+        // forms the address with vector instructions.  Which is faster
+        // depends on the layout (see the attention kernel).
+        uint64_t row;
+        if constexpr (kScalarAddr) {
+            uint64_t addr[G::kRowsPerLoad];
 #pragma unroll
-        for (int r = 1; r < G::kRowsPerLoad; ++r) {
-            const char *rr =
-                row_ptr(vb, v_ss, __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q + r));
-            row = sub == r ? rr : row;
+            for (int r = 0; r < G::kRowsPerLoad; ++r) {
+                addr[r] = (uint64_t)row_ptr(
+                    vb, v_ss, __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q + r));
+                asm volatile("" : "+s"(addr[r]));
+            }
+            row = addr[0];
+#pragma unroll
+            for (int r = 1; r < G::kRowsPerLoad; ++r) row = sub == r ? addr[r] : row;
+        } else {
+            int s = __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q);
+#pragma unroll
+            for (int r = 1; r < G::kRowsPerLoad; ++r) {
+                const int sr = __builtin_amdgcn_readlane(slot, G::kRowsPerLoad * q + r);
+                s = sub == r ? sr : s;
+            }
+            row = (uint64_t)row_ptr(vb, v_ss, s);
         }
-        rv[q] = ldg16<u32x4_t>(row + byte_in_row);
+        rv[q] = ldg16<u32x4_t>((const char *)row + byte_in_row);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -351,9 +365,23 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Slot of tile row (lane & 15) for tile `tile`, or -1 past the list.
+// List entry of tile row (lane & 15) for tile `tile`: -1 for the padding of
+// the last tile, 0 for a tile past the list (a prefetch that is never used).
 __device__ __forceinline__ int tile_slot(const int32_t *list, int tile, int ntiles, int lane) {
-    return tile < ntiles ? list[tile * kTileSlots + (lane & 15)] : -1;
+    return tile < ntiles ? list[tile * kTileSlots + (lane & 15)] : 0;
+}
+
+// The slot a tile row gathers, from its tile_slot entry: padding rows take
+// the tile's first slot (row 0, held by lane 0; valid whenever the tile is
+// in the list), so every gather reads a row of the cache and is issued
+// unconditionally, with no select on the row address.  The scores of such
+// rows are masked to -inf, so their softmax weights are exactly zero and what
+// they read never reaches the output.  Called with all lanes active (the
+// lane-0 read must not run under a mask of the padding lanes), and where the
+// entry was loaded a tile earlier, so it waits for nothing recent.
+__device__ __forceinline__ int stand_in(int entry) {
+    const int first = max(__builtin_amdgcn_readfirstlane(entry), 0);
+    return entry >= 0 ? entry : first;
 }
 
 // ---------------------------------------------------------------- attention
@@ -444,23 +472,29 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
 
     // This wave's tiles: split, split + splits, ...  The gathers run one
     // tile ahead: rk and rv hold tile i while tile i+1 is in flight, and
-    // slot_next holds the slots of the next tile to gather (-1 past the list,
-    // where the gathers read the row of zeros: they are issued
-    // unconditionally, so the loaded registers need no copies).  Each slot
+    // slot_next holds the list entries of the next tile to gather (turned
+    // into slots by stand_in: the gathers are issued unconditionally, so the
+    // loaded registers need no copies).  Each slot
     // vector is loaded before the V gathers of the tile ahead of it, so
     // waiting for it never waits for those.  (Two tiles ahead measured no
     // faster.)
     constexpr int kAhead = Lay::kAhead;
+    // V row addresses in scalar registers for BF16 at 8 items per CU (the
+    // vector form measured 4% slower there: its 64-bit multiplies take vector
+    // issue slots); in vector registers for the FP8 layout (12 items per CU,
+    // whose waves share the scalar unit of the CU) and at 4 items per CU,
+    // where the vector form measured 2-5% faster.
+    constexpr bool kScalarVAddr = KV == KvType::kBf16 && Lay::kItems == 8;
     const int step = splits;
     u32x4_t rkb[kAhead][Gth::kKLoads], rvb[kAhead][Gth::kVLoads];
     int tile = split;
     int slot_next = tile_slot(list, tile, ntiles, lane);
 #pragma unroll
     for (int b = 0; b < kAhead; ++b) {
-        const int slot = slot_next;
+        const int slot = stand_in(slot_next);
         gather_k<KV>(rkb[b], slot, kb, k_ss, lane);
         slot_next = tile_slot(list, tile + (b + 1) * step, ntiles, lane);
-        gather_v<KV>(rvb[b], slot, vb, v_ss, lane);
+        gather_v<KV, kScalarVAddr>(rvb[b], slot, vb, v_ss, lane);
     }
 
 #pragma unroll
@@ -507,7 +541,11 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         // MFMAs below, one per two MFMAs (measured fastest of the placements
         // tried: all at once after the scores, spread over the softmax, or
         // alternating with the V loads).
-        const int slot_g = slot_next;
+        // The next tile's slots: FP8 needs them here; BF16 resolves them after
+        // V(i) is staged, where that wait has already covered their load (a
+        // resolve here would wait for V(i) before the scores).
+        int slot_g = 0;
+        if constexpr (KV == KvType::kFp8) slot_g = stand_in(slot_next);
         __builtin_amdgcn_sched_barrier(0);   // K(i) is consumed before K(i+1) lands
         if constexpr (KV == KvType::kFp8) {
 #pragma unroll
@@ -553,8 +591,9 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         wave_lds_fence();   // the previous tile's transpose reads are done
         stage_v<KV, Lay::kVPitch>(rv, vs_lds, lane);
         __builtin_amdgcn_sched_barrier(0);   // V(i) is consumed before V(i+1) lands
+        if constexpr (KV == KvType::kBf16) slot_g = stand_in(slot_next);
         slot_next = tile_slot(list, tile + (kAhead + 1) * step, ntiles, lane);
-        gather_v<KV>(rv, slot_g, vb, v_ss, lane);
+        gather_v<KV, kScalarVAddr>(rv, slot_g, vb, v_ss, lane);
         wave_lds_fence();   // other lanes of this wave wrote the rows read below
 
         // O^T += V^T . P^T over the tile's 16 slots.  The k index of lane
@@ -833,22 +872,26 @@ __global__ __launch_bounds__(64, kAttendWavesPerSimd) void gather_only_kernel(co
     int tile = 0;
     int slot_next;
     {
-        const int slot = tile_slot(list, tile, ntiles, lane);
+        const int slot = stand_in(tile_slot(list, tile, ntiles, lane));
         gather_k<KV>(rk, slot, kb, k_ss, lane);
         slot_next = tile_slot(list, tile + 1, ntiles, lane);
-        gather_v<KV>(rv, slot, vb, v_ss, lane);
+        gather_v<KV, KV == KvType::kBf16>(rv, slot, vb, v_ss, lane);
     }
+    const u32x4_t zero = {0, 0, 0, 0};
     for (; tile < ntiles; ++tile) {
+        // Only the rows of the list are folded (padding rows read stand-ins).
+        const int rows = n - tile * kTileSlots;
 #pragma unroll
-        for (int q = 0; q < Gth::kKLoads; ++q) acc ^= rk[q];
+        for (int q = 0; q < Gth::kKLoads; ++q) acc ^= (lane & 15) < rows ? rk[q] : zero;
+        const int slot = stand_in(slot_next);
         __builtin_amdgcn_sched_barrier(0);
-        gather_k<KV>(rk, slot_next, kb, k_ss, lane);
+        gather_k<KV>(rk, slot, kb, k_ss, lane);
 #pragma unroll
-        for (int q = 0; q < Gth::kVLoads; ++q) acc ^= rv[q];
+        for (int q = 0; q < Gth::kVLoads; ++q)
+            acc ^= Gth::kRowsPerLoad * q + lane / Gth::kLanesPerRow < rows ? rv[q] : zero;
         __builtin_amdgcn_sched_barrier(0);
-        const int slot = slot_next;
         slot_next = tile_slot(list, tile + 2, ntiles, lane);
-        gather_v<KV>(rv, slot, vb, v_ss, lane);
+        gather_v<KV, KV == KvType::kBf16>(rv, slot, vb, v_ss, lane);
     }
     uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 #pragma unroll
