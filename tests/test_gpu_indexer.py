@@ -211,3 +211,20 @@ def test_fractional_scores_with_one_tied_cut():
     got = select_on(scores, positions, slot_of_pos, budget)
     want = oracle.indexer_select(scores, positions, slot_of_pos, budget)
     np.testing.assert_array_equal(got, want)
+
+
+def test_deferred_rows_do_not_disturb_the_others():
+    """Budgets up to 512 defer the rows whose sampled threshold admits too
+    many candidates to a second, exact launch.  Rows of all-equal scores
+    (deferred) interleaved with random rows (selected at once) must each
+    match the oracle."""
+    rng = np.random.Generator(np.random.PCG64(1180))
+    L, budget, T = 40000, 400, 8
+    C = L // 4
+    scores = rng.random((T, C), dtype=np.float32)
+    scores[1::2] = 0.5
+    positions = (L - 1 - np.arange(T) * 1201).astype(np.int32)
+    slot_of_pos = rng.permutation(L).astype(np.int32)
+    got = select_on(scores, positions, slot_of_pos, budget)
+    want = oracle.indexer_select(scores, positions, slot_of_pos, budget)
+    np.testing.assert_array_equal(got, want)

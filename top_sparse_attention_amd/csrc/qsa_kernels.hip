@@ -119,7 +119,7 @@ struct AttendLayout {
     static constexpr int kUsed = kTileBytes + kQBytes;
     static constexpr int kItems = kQRows == 16 ? kItemsGeneral : 12;
     static constexpr int kLds = kQRows == 16 ? 160 * 1024 / kItems - 1024 : kUsed;
-    static constexpr int kWavesPerSimd = kQRows == 16 ? kAttendWavesPerSimd : 3;
+    static constexpr int kWavesPerSimd = kQRows == 16 ? (kItems >= 8 ? kAttendWavesPerSimd : 1) : 3;
     static constexpr int kAhead = kQRows == 16 ? kAttendAhead : 1;   // tiles in flight per wave
     static constexpr int kQChunksPerLane = kQRows * kChunksPerRow / 64;
     static_assert(kUsed <= kLds, "item LDS");
@@ -1289,12 +1289,22 @@ __device__ void expand_row(const IndexerSelectParams &p, int64_t pos, int kept, 
         out[tail0 + i] = i < r ? p.slot_of_pos[pos - r + 1 + i] : -1;
 }
 
-template <bool kInLds>
+// Marks, in the first output word, a row that indexer_select_fast_kernel
+// left to the exact selection (no output word holds a value below -1).
+constexpr int32_t kSelDeferred = INT32_MIN;
+
+// kDeferredOnly: a second launch after indexer_select_fast_kernel that
+// selects only the rows it deferred (the others return at once).
+template <bool kInLds, bool kDeferredOnly = false>
 __global__ __launch_bounds__(256) void indexer_select_kernel(const IndexerSelectParams p) {
     const int64_t t = blockIdx.x;
     const int64_t pos = p.positions[t];
     int32_t *out = p.out + t * p.out_stride;
     const int width = kIndexBlock * p.budget + 3;
+    if (kDeferredOnly) {
+        if (out[0] != kSelDeferred) return;   // the same word for every thread
+        __syncthreads();                       // read by all before it is rewritten
+    }
     if (pos < 0 || pos >= p.L) {
         for (int i = threadIdx.x; i < width; i += 256) out[i] = -1;
         return;
@@ -1304,26 +1314,36 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(const IndexerSelect
     expand_row(p, pos, min(n, p.budget), out, width);
 }
 
-// The same selection, faster for budgets up to kSelCand / 4: the threshold
+// The same selection, faster for budgets up to kCand / 4: the threshold
 // is first estimated from kSelSample scores spaced evenly over the row (the
 // top 16 bits of the key ranked about 2 * budget * kSelSample / n from the
 // top); one pass over the row then keeps, in block order, the scores whose
 // key is at least the estimate (about 2 * budget of them), and the exact
 // selection runs on that short list.  It is exact whenever at least `budget` scores pass the
 // estimate (the budget-th largest key and all its ties then pass); rows where
-// fewer pass, or more than kSelCand, take select_exact.
+// fewer pass, or more than kCand, take select_exact.  Two sizes: kSelCandSmall
+// (budgets up to 512, the page's budget) takes 19.5 KB of LDS and 94
+// registers, 5 workgroups per CU, and defers those rows (kDefer: it marks
+// them with kSelDeferred and a second launch selects them), since the exact
+// selection inlined here would take 4 KB more LDS and 30 more registers;
+// kSelCand takes budgets up to 960 at 4 per CU and selects them in place.
+// (Held to 64 registers for 8 per CU the small kernel ran twice as slowly.)
 constexpr int kSelSample = 1024;
-constexpr int kSelCand = 3840;   // a multiple of 256
+constexpr int kSelCand = 3840;        // multiples of 256
+constexpr int kSelCandSmall = 2048;
 constexpr int kSelPerThread = 16;   // scores per thread per pass over the row
 // Candidate i is stored at i + i / 16: the output pass, where thread t reads
-// candidates 16 t .. 16 t + 15, then reads 64 different banks.
+// candidates kPer t .. kPer t + kPer - 1, then reads different banks.
 __device__ __forceinline__ int cand_at(int i) { return i + (i >> 4); }
-constexpr int kSelCandPadded = kSelCand + kSelCand / 16;
 
-__global__ __launch_bounds__(256) void indexer_select_fast_kernel(const IndexerSelectParams p) {
+template <int kCand, int kWavesPerSimd, bool kDefer>
+__global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel(
+    const IndexerSelectParams p) {
+    static_assert(kCand % 256 == 0 && kCand >= kSelSample, "candidate list");
+    constexpr int kCandPadded = kCand + kCand / 16;
     using Scan = hipcub::BlockScan<int, 256>;
-    __shared__ float cval[kSelCandPadded];
-    __shared__ int cid[kSelCandPadded];
+    __shared__ float cval[kCandPadded];
+    __shared__ int cid[kCandPadded];
     __shared__ int hist[256];
     __shared__ typename Scan::TempStorage scan;
     __shared__ uint32_t sh_prefix;
@@ -1371,7 +1391,7 @@ __global__ __launch_bounds__(256) void indexer_select_fast_kernel(const IndexerS
         if (kSlice < n) load_slice(kSlice, v1);
         // 1. Estimated threshold (every key passes when the row fits the list).
         uint32_t tau0 = 0;
-        if (n > kSelCand) {
+        if (n > kCand) {
             for (int k = tid; k < kSelSample; k += 256)
                 cval[k] = row[(int64_t)k * n / kSelSample];
             __syncthreads();
@@ -1395,7 +1415,7 @@ __global__ __launch_bounds__(256) void indexer_select_fast_kernel(const IndexerS
                 cnt += i0 + e < n && score_key(v[e]) >= tau0;
             int off, total;
             Scan(scan).ExclusiveSum(cnt, off, total);
-            if (nc + total <= kSelCand) {
+            if (nc + total <= kCand) {
                 int w = nc + off;
 #pragma unroll
                 for (int e = 0; e < kSelPerThread; ++e) {
@@ -1415,8 +1435,13 @@ __global__ __launch_bounds__(256) void indexer_select_fast_kernel(const IndexerS
             }
         }
 
-        if (nc < p.budget || nc > kSelCand) {
-            select_exact<false>(p, n, row, out);
+        if (nc < p.budget || nc > kCand) {
+            if constexpr (kDefer) {
+                if (tid == 0) out[0] = kSelDeferred;
+                return;
+            } else {
+                select_exact<false>(p, n, row, out);
+            }
         } else {
             // 3. Exact threshold key tau among the candidates and how many
             // keys equal to tau to keep.
@@ -1428,7 +1453,7 @@ __global__ __launch_bounds__(256) void indexer_select_fast_kernel(const IndexerS
             // [kPer t, kPer (t + 1)); a kept candidate's position is the
             // number of keys > tau before it plus the number of kept ties
             // (the first `need` in block order) before it.
-            constexpr int kPer = kSelCand / 256;
+            constexpr int kPer = kCand / 256;
             int gt = 0, eq = 0;
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
@@ -1475,9 +1500,14 @@ hipError_t launch_indexer_scores(const IndexerScoreParams &p, hipStream_t stream
 
 hipError_t launch_indexer_select(const IndexerSelectParams &p, hipStream_t stream) {
     if (p.T == 0) return hipSuccess;
-    if (4 * (int64_t)p.budget <= kSelCand)
-        hipLaunchKernelGGL(indexer_select_fast_kernel, dim3((unsigned)p.T), dim3(256), 0, stream,
-                           p);
+    if (4 * (int64_t)p.budget <= kSelCandSmall) {
+        hipLaunchKernelGGL((indexer_select_fast_kernel<kSelCandSmall, 4, true>),
+                           dim3((unsigned)p.T), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((indexer_select_kernel<false, true>), dim3((unsigned)p.T), dim3(256),
+                           0, stream, p);
+    } else if (4 * (int64_t)p.budget <= kSelCand)
+        hipLaunchKernelGGL((indexer_select_fast_kernel<kSelCand, 4, false>), dim3((unsigned)p.T),
+                           dim3(256), 0, stream, p);
     else if (p.C <= kSelectLdsBlocks)
         hipLaunchKernelGGL(indexer_select_kernel<true>, dim3((unsigned)p.T), dim3(256), 0, stream,
                            p);
