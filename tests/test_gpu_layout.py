@@ -119,3 +119,44 @@ def test_fp8_cache_with_more_than_eight_heads_per_kv_head_takes_four_per_cu():
     out8 = qsa.sparse_prefill_fp8kv(q, k8, v8, ks, vs, padded)
     torch.cuda.synchronize()
     assert np.array_equal(bf16_tensor_bits(out8), bf16_tensor_bits(out))
+
+
+def test_block_selections_on_a_large_cache_take_the_estimate():
+    """Micro-block selections reach the estimate through the block compaction
+    (list width 512 blocks x 4 slots against 262,144 slots)."""
+    T, S, bs, nblocks = 4096, 262144, 4, 512
+    sel = qi.random_case(1306, T=T, S=S // bs, Hq=3, Hkv=1, W=nblocks)
+    rng = np.random.Generator(np.random.PCG64(1307))
+    k_np = qi.normal_bf16(rng, (S, 1, 256))
+    v_np = qi.normal_bf16(rng, (S, 1, 256))
+    q = torch.from_numpy(sel.q.view(np.int16)).to(DEV).view(torch.bfloat16)
+    k = torch.from_numpy(k_np.view(np.int16)).to(DEV).view(torch.bfloat16)
+    v = torch.from_numpy(v_np.view(np.int16)).to(DEV).view(torch.bfloat16)
+    bl = torch.from_numpy(sel.slot_idx.astype(np.int32)).to(DEV)
+    Wl = nblocks * bs
+    ws = qsa.new_workspace(T, Wl, DEV)
+    off = qsa.workspace_layout(T, Wl)["share_offset"] + CHOICE_BYTE
+    ws[off:off + 4].view(torch.int32).fill_(-7)
+    out = qsa.sparse_prefill_blocks(q, k, v, bl, bs, workspace=ws)
+    torch.cuda.synchronize()
+    assert choice_of(ws, T, Wl) == 1
+    rows = qi.sample_rows(T, 12, seed=35)
+    slots = oracle.expand_blocks(sel.slot_idx[rows], bs)
+    want = oracle.prefill(np.ascontiguousarray(sel.q[rows]), k_np, v_np, slots, 1.0 / 16.0)
+    got = bf16_tensor_to_f32(out[torch.as_tensor(rows, device=DEV)])
+    print(gate(got, want, empty_row_mask(slots, S)))
+
+
+def test_mostly_empty_rows_with_the_estimate():
+    """Nine rows in ten select nothing: sampled pairs with empty lists count
+    nothing, and every output row is right whichever layout is taken (empty
+    rows exactly +0.0)."""
+    case = qi.random_case(1308, T=4096, S=262144, Hq=6, Hkv=1, W=2048)
+    empty = np.arange(case.T) % 10 != 3
+    case.slot_idx[empty] = -1
+    q, k, v, sl = upload(case, DEV)
+    out, choice = prefill_with_choice(q, k, v, sl)
+    assert choice in (0, 1)
+    rows = np.unique(np.concatenate([qi.sample_rows(case.T, 10, seed=36), [3, 13, 4093]]))
+    print(check_rows(out, case.q, case.k_cache, case.v_cache, case.slot_idx, case.S, rows))
+    assert torch.count_nonzero(out[torch.as_tensor(np.flatnonzero(empty), device=DEV)]) == 0
