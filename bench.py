@@ -293,7 +293,7 @@ def main():
     flops = pairs * 4 * case.D
     achieved = attn_bytes / (attn_avg * 1e-3) / 1e9
 
-    # Parity of this very output on a sample of rows (the oracle is the judge).
+    # Parity of this very output on a sample of rows, checked against the oracle.
     import oracle
 
     def run_oracle(rows_, nthreads=0):
