@@ -273,7 +273,8 @@ bool sharing_of(const Problem &pr, int32_t HB, void *ws, const qsa_workspace_map
         sp->pair_b[i] = (int32_t)std::min<int64_t>(a + 1 + (i * 37) % span, pr.T - 1);
     }
     sp->lambda_scale = (float)per_xcd;
-    sp->threshold = qsa::kShareThreshold;
+    sp->threshold = m.row_stride >= qsa::kShareLongList ? qsa::kShareThreshold
+                                                        : qsa::kShareThresholdShort;
     sp->est = (float *)base;
     sp->choice = (int32_t *)(base + qsa::kSharePairs * 8);
     return true;

@@ -35,9 +35,14 @@ constexpr int kLowShareItemsPerCU = 4;
 constexpr int kCusPerXcd = 32;
 constexpr int kXcds = 8;
 // Token pairs the sharing estimate samples (at most 64: one wave adds them
-// up), and the estimated sharing below which the low-sharing layout is chosen.
+// up), and the estimated sharing below which the low-sharing layout is chosen:
+// kShareThreshold for lists of at least kShareLongList entries, else
+// kShareThresholdShort (measured crossovers: between 4 and 8 at 1,024 and
+// 2,048 entries, between 2 and 4 at 512).
 constexpr int kSharePairs = 32;
 constexpr float kShareThreshold = 5.0f;
+constexpr float kShareThresholdShort = 3.0f;
+constexpr int kShareLongList = 1024;
 // Fewest tiles a split of the decode path takes.
 constexpr int kMinSplitTiles = 4;
 // Entries of a selection row sorted together by the compaction pass.
