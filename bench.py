@@ -3,8 +3,8 @@
 One step = the whole hot path on one batch of resident synthetic input:
 index validation/compaction (qsa_compact_slots) followed by the gather
 attention (qsa_sparse_attend), both through the C ABI on torch's current
-stream.  Other workloads: `decode_batch` runs the split path (compaction,
-qsa_sparse_attend_partial, qsa_merge_partials), `long_prefill_fp8kv` the
+stream.  Other workloads: `decode_batch` runs qsa_sparse_decode (split
+attention over the raw selection rows, then the merge), `long_prefill_fp8kv` the
 FP8 E4M3 KV-cache variant (qsa_sparse_attend_fp8kv) and `long_prefill_block4`
 micro-block selections (qsa_compact_blocks, then qsa_sparse_attend);
 `indexed_long_prefill` makes the selection inside the step with the QSA
@@ -136,13 +136,16 @@ def main():
         if indexed:
             qsa.indexer_topk(iq, ik, ipos, isop, budget, scores=iscores, out=sl)
 
-    # Few-token workloads run the split path (qsa_sparse_decode's steps):
-    # compaction, split attention into FP32 partials, merge.
+    # Few-token workloads run qsa_sparse_decode: split attention over the raw
+    # selection rows into FP32 partials, then the merge (no compaction pass).
     split = args.workload == "decode_batch"
     splits = qsa.decode_splits(T, W, Hq, Hkv) if split else 1
-    parts = qsa.new_partials(splits, T, Hq, dev) if split else None
+    dws = (torch.empty(qsa.decode_workspace_bytes(T, W, Hq, Hkv), dtype=torch.uint8, device=dev)
+           if split else None)
 
     def compact():
+        if split:
+            return
         if bs > 1:
             qsa.compact_blocks(sl, S, bs, ws)
         else:
@@ -150,15 +153,14 @@ def main():
 
     def attend():
         if split:
-            qsa.sparse_attend_partial(q, k, v, ws, W, splits, 0, splits, parts, scale=scale)
+            qsa.sparse_decode(q, k, v, sl, scale=scale, out=out, workspace=dws)
         elif fp8:
             qsa.sparse_attend_fp8kv(q, k, v, k_scale, v_scale, ws, W, scale=scale, out=out)
         else:
             qsa.sparse_attend(q, k, v, ws, Wl, scale=scale, out=out)
 
     def finish():
-        if split:
-            qsa.merge_partials(parts, splits, T, Hq, out=out)
+        pass
 
     def step():
         select()
@@ -223,6 +225,8 @@ def main():
     # the loads issued back to back.
     sink = torch.empty(T * Hkv, dtype=torch.int32, device=dev)
     gather_only = qsa.gather_only_fp8kv if fp8 else qsa.gather_only
+    if split:   # the decode step compacts nothing; the reference needs the lists
+        qsa.compact_slots(sl, S, ws)
     for _ in range(2):
         gather_only(k, v, ws, T, Wl, sink)
     c0 = torch.cuda.Event(enable_timing=True)

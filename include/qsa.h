@@ -254,15 +254,21 @@ qsa_status qsa_merge_partials(const void *partials, size_t partials_bytes,
  * 16-slot tiles per split, at most 64). */
 int32_t qsa_decode_splits(int64_t T, int64_t W, int32_t Hq, int32_t Hkv);
 
-/* Workspace bytes for qsa_sparse_decode: the compaction area followed by the
+/* Workspace bytes for qsa_sparse_decode: the area of qsa_workspace_bytes(T, W)
+ * (qsa_check_status reads the invalid-entry counts there) followed by the
  * partials of qsa_decode_splits(T, W, Hq, Hkv) shares. */
 size_t qsa_decode_workspace_bytes(int64_t T, int64_t W, int32_t Hq, int32_t Hkv);
 
 /*
  * The same operation as qsa_sparse_prefill, organised for few tokens
- * (decode steps, short batches): compaction, split attention over
- * qsa_decode_splits shares per item, merge.  Same arguments and conventions
- * as qsa_sparse_prefill; the workspace must hold qsa_decode_workspace_bytes.
+ * (decode steps, short batches): split attention over qsa_decode_splits
+ * shares per item, then the merge.  There is no compaction pass: each share
+ * reads its part of the selection row itself, skips -1 and drops (and
+ * counts) entries outside [0, S).  Same arguments and conventions as
+ * qsa_sparse_prefill; the workspace must hold qsa_decode_workspace_bytes, and
+ * qsa_check_status(workspace, ..., T, W, ...) reports the invalid entries.
+ * Entries are summed in row order rather than grouped by slot range, so the
+ * result can differ from qsa_sparse_prefill's in the last bits.
  */
 qsa_status qsa_sparse_decode(const qsa_bf16_view *q,
                              const qsa_bf16_view *k_cache,

@@ -159,3 +159,51 @@ def test_split_path_on_the_long_prefill_sampled_rows():
     rows = qi.sample_rows(case.T, 32)
     check(case, out, rows)
     assert torch.isfinite(out.float()).all()
+
+
+def test_decode_drops_and_counts_invalid_entries():
+    """The decode shares read the selection rows themselves: entries that are
+    neither -1 nor in [0, S) are dropped (the result equals the attention over
+    the valid entries) and their number reaches qsa_check_status."""
+    case = qi.random_case(830, T=8, S=5000, Hq=8, Hkv=1, W=300, pad_frac=0.1, interior=True)
+    # Token 0 starts with 40 padding entries: the first tiles of several shares
+    # hold no valid row, ahead of tiles that do.
+    case.slot_idx[0, :40] = -1
+    rng = np.random.Generator(np.random.PCG64(831))
+    bad_pos = np.stack([rng.choice(300, size=3, replace=False) for _ in range(case.T)])
+    raw = case.slot_idx.copy()
+    for t in range(case.T):
+        raw[t, bad_pos[t]] = [5000, -7, 1 << 30]
+    valid_only = np.where((raw >= 0) & (raw < case.S), raw, -1).astype(np.int32)
+    q, k, v, _ = upload(case, DEV)
+    sl = torch.from_numpy(raw.astype(np.int32)).to(DEV)
+    nbytes = qsa.decode_workspace_bytes(case.T, case.W, case.Hq, case.Hkv)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    out = qsa.sparse_decode(q, k, v, sl, workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.prefill(case.q, case.k_cache, case.v_cache, valid_only, 1.0 / 16.0)
+    print(gate(bf16_tensor_to_f32(out), want, empty_row_mask(valid_only, case.S)))
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.check_status(ws, case.T, case.W)
+    assert e.value.status == 6 and f"{3 * case.T} selection entries" in str(e.value)
+
+
+def test_decode_over_an_empty_cache_is_zero_and_counts_entries():
+    """S = 0: no entry is valid; the output is exactly +0.0 and every entry
+    other than -1 is counted as out of range."""
+    T, Hq, Hkv, W = 3, 4, 2, 40
+    g = torch.Generator().manual_seed(840)
+    q = torch.randn(T, Hq, 256, generator=g).to(torch.bfloat16).to(DEV)
+    k = torch.empty(0, Hkv, 256, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty(0, Hkv, 256, dtype=torch.bfloat16, device=DEV)
+    sl = torch.full((T, W), -1, dtype=torch.int32)
+    sl[0, 3] = 0
+    sl[2, 10:15] = 7
+    sl = sl.to(DEV)
+    ws = torch.empty(qsa.decode_workspace_bytes(T, W, Hq, Hkv), dtype=torch.uint8, device=DEV)
+    out = qsa.sparse_decode(q, k, v, sl, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(out.view(torch.int16) == 0)
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.check_status(ws, T, W)
+    assert e.value.status == 6 and "6 selection entries" in str(e.value)

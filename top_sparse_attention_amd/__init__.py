@@ -355,7 +355,8 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                   slot_idx: torch.Tensor, scale: Optional[float] = None,
                   out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Sparse attention for few tokens: compaction, split attention, merge."""
+    """Sparse attention for few tokens: split attention over the raw selection
+    rows (no compaction pass), then the merge."""
     T, W = slot_idx.shape
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)

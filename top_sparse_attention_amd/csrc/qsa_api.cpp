@@ -321,13 +321,24 @@ qsa_status check_partials(const void *buf, size_t bytes, int64_t n_parts, int64_
     return QSA_OK;
 }
 
+// raw (optional): read the selection rows themselves instead of the compacted
+// list in ws, and write each share's invalid-entry count to bad_part.
 qsa_status enqueue_partial(const qsa_bf16_view *q, const qsa_bf16_view *k,
                            const qsa_bf16_view *v, const Problem &pr, float scale, const void *ws,
                            const qsa_workspace_map &m, int32_t splits, int64_t part_base,
-                           void *partials, const PartialsMap &pm, hipStream_t stream) {
+                           void *partials, const PartialsMap &pm, hipStream_t stream,
+                           const qsa_i32_view *raw = nullptr, int32_t *bad_part = nullptr) {
     if (pr.T == 0 || pr.Hq == 0) return QSA_OK;
     qsa::AttendParams p{};
     fill_attend(p, q, k, v, pr, scale, ws, m);
+    if (raw != nullptr) {
+        p.raw_rows = 1;
+        p.raw = raw->data;
+        p.raw_stride = raw->stride[0];
+        p.W_raw = (int32_t)raw->size[1];
+        p.S_rows = pr.S;
+        p.bad_part = bad_part;
+    }
     p.v_scale = 1.0f;
     p.splits = splits;
     p.part_base = part_base;
@@ -340,8 +351,11 @@ qsa_status enqueue_partial(const qsa_bf16_view *q, const qsa_bf16_view *k,
 }
 
 qsa_status enqueue_merge(const void *partials, const PartialsMap &pm, int64_t n_parts, int64_t T,
-                         int32_t Hq, const qsa_bf16_view *out, hipStream_t stream) {
+                         int32_t Hq, const qsa_bf16_view *out, hipStream_t stream,
+                         const int32_t *bad_part = nullptr, int32_t *n_bad = nullptr) {
     qsa::MergeParams p{};
+    p.bad_part = bad_part;
+    p.n_bad = n_bad;
     p.part_o = (const float *)partials;
     p.part_ml = (const float *)((const char *)partials + pm.ml_offset);
     p.n_parts = n_parts;
@@ -691,11 +705,27 @@ qsa_status qsa_sparse_decode(const qsa_bf16_view *q, const qsa_bf16_view *k_cach
     PartialsMap pm;
     partials_of(splits, pr.T, pr.Hq, &pm);
     hipStream_t st = (hipStream_t)stream;
-    if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, 0, pr.S, workspace, m, st))) return s;
+    if (pr.S == 0) {
+        // An empty cache: no entry is valid and there is no row for a stand-in
+        // slot to read, so the compacted (empty) lists serve instead.
+        if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, 0, pr.S, workspace, m, st))) return s;
+        if ((s = enqueue_partial(q, k_cache, v_cache, pr, scale, workspace, m, splits, 0, partials,
+                                 pm, st)))
+            return s;
+        return enqueue_merge(partials, pm, splits, pr.T, pr.Hq, out, st);
+    }
+    // No compaction pass: the shares read the selection rows themselves (for
+    // a few tokens the grouping by slot range buys nothing) and count their
+    // invalid entries in the list area of the workspace; the merge adds them
+    // up into n_bad, where qsa_check_status reads them.
+    if ((int64_t)splits * pr.T * 4 > m.bad_offset - m.list_offset)
+        return fail(QSA_ERR_WORKSPACE, "decode workspace too small for the per-share counts");
+    int32_t *bad_part = (int32_t *)((char *)workspace + m.list_offset);
     if ((s = enqueue_partial(q, k_cache, v_cache, pr, scale, workspace, m, splits, 0, partials, pm,
-                             st)))
+                             st, slot_idx, bad_part)))
         return s;
-    return enqueue_merge(partials, pm, splits, pr.T, pr.Hq, out, st);
+    return enqueue_merge(partials, pm, splits, pr.T, pr.Hq, out, st, bad_part,
+                         (int32_t *)((char *)workspace + m.bad_offset));
 }
 
 qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes, int64_t T,

@@ -101,6 +101,19 @@ struct AttendParams {
     // and 1 exactly one works, whatever the word holds.
     const int32_t *choice;
     int32_t choice_value;
+    // Split mode over raw selection rows (raw_rows = 1; BF16 only): each share
+    // reads slot_idx row t itself (W_raw entries, -1 and invalid entries
+    // included; valid means in [0, S_rows)) instead of a compacted list, and
+    // the share with g = 0 and head block 0 writes its count of invalid
+    // entries to bad_part[split * T + t].
+    // (The mode is the flag, not raw's nullness: a zero-width row set has no
+    // data pointer, and its shares read nothing.)
+    int32_t raw_rows;
+    const int32_t *raw;
+    int64_t raw_stride;
+    int32_t W_raw;
+    int64_t S_rows;
+    int32_t *bad_part;
 };
 
 // Sharing estimate.  Items run kItemsPerCU to a CU and walk their slot lists
@@ -131,6 +144,9 @@ struct MergeParams {
     int32_t Hq;
     uint16_t *out;
     int64_t o_st, o_sh;
+    // Non-null after raw-row shares: n_bad[t] = sum over parts of bad_part[s * T + t].
+    const int32_t *bad_part;
+    int32_t *n_bad;
 };
 
 struct GatherParams {

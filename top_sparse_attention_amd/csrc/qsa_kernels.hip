@@ -384,6 +384,28 @@ __device__ __forceinline__ int stand_in(int entry) {
     return entry >= 0 ? entry : first;
 }
 
+// Raw selection rows (decode shares): entry of tile row (lane & 15), -1 past
+// the row's W entries, 0 for a tile past the row (a prefetch never used).
+__device__ __forceinline__ int tile_entry_raw(const int32_t *row, int tile, int ntiles, int W,
+                                              int lane) {
+    const int i = tile * kTileSlots + (lane & 15);
+    return tile < ntiles ? (i < W ? row[i] : -1) : 0;
+}
+
+// stand_in for raw rows: valid entries (in [0, S)) keep their slot; the others
+// read the tile's first valid slot, or slot 0 when it has none.  Also returns
+// the tile's valid-row mask (bit r for tile row r) and its count of invalid
+// entries other than -1.  Called with every lane active.
+__device__ __forceinline__ int stand_in_raw(int entry, int64_t S, uint32_t *valid_rows,
+                                            int *n_bad) {
+    const bool valid = entry >= 0 && entry < S;
+    const uint32_t vm = (uint32_t)(__ballot(valid) & 0xffffu);
+    *valid_rows = vm;
+    *n_bad = __popcll(__ballot(!valid && entry != -1) & 0xffffu);
+    const int first = vm ? __builtin_amdgcn_readlane(entry, __builtin_ctz(vm)) : 0;
+    return valid ? entry : first;
+}
+
 // ---------------------------------------------------------------- attention
 
 // One wave per workgroup and per work item.
@@ -402,11 +424,12 @@ __device__ __forceinline__ int stand_in(int entry) {
 // the wave's requests reach the memory system spread out.  Each wave walks
 // its own item's slot list in order, and the list is grouped by slot range,
 // so a wave's consecutive tiles fall in the same part of the cache.
-template <bool kSplit, KvType KV, int kQRows, int kItems = kItemsPerCU>
+template <bool kSplit, KvType KV, int kQRows, int kItems = kItemsPerCU, bool kRaw = false>
 __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) void attend_kernel(
     const AttendParams p) {
     using Gth = KvGather<KV>;
     using Lay = AttendLayout<kQRows, kItems>;
+    static_assert(!kRaw || (kSplit && Lay::kAhead == 1), "raw rows: split shares, one tile ahead");
     __shared__ __attribute__((aligned(16))) char smem[Lay::kLds];
     if (p.choice != nullptr && ((*p.choice == 1) != (p.choice_value == 1))) return;
 
@@ -424,9 +447,13 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
     const int hb = rem - g * p.HB;
     const int h0 = g * p.G + hb * kHeadBlock;
     const int nh = min(kHeadBlock, p.G - hb * kHeadBlock);
-    const int n = p.count[t];
+    // Entries of the item's row: the compacted list's count, or (raw rows)
+    // the selection width, -1 and invalid entries included.
+    const int n = kRaw ? p.W_raw : p.count[t];
 
     const int ntiles = (n + kTileSlots - 1) / kTileSlots;
+    // Raw rows: the share of (g = 0, head block 0) reports the invalid entries.
+    const bool report_bad = kRaw && g == 0 && hb == 0;
     const int64_t part_row = kSplit ? ((p.part_base + split) * p.T + t) * p.Hq + h0 : 0;
     if (kSplit && split >= ntiles) {
         // This share is empty: max -inf, sum 0, O 0.
@@ -439,6 +466,7 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
             p.part_ml[(part_row + lane) * 2] = kNegInf;
             p.part_ml[(part_row + lane) * 2 + 1] = 0.0f;
         }
+        if (report_bad && lane == 0) p.bad_part[split * p.T + t] = 0;
         return;
     }
     uint16_t *out_t = kSplit ? nullptr : p.out + t * p.o_st + (int64_t)h0 * p.o_sh;
@@ -451,7 +479,19 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         return;
     }
 
-    const int32_t *list = p.list + t * p.list_stride;
+    const int32_t *list = kRaw ? p.raw + t * p.raw_stride : p.list + t * p.list_stride;
+    // The next list entries of this lane's tile row (compacted list or raw row).
+    auto entry_at = [&](int tl) {
+        return kRaw ? tile_entry_raw(list, tl, ntiles, n, lane) : tile_slot(list, tl, ntiles, lane);
+    };
+    // Raw rows: the valid-row mask and invalid count of the tile being
+    // computed (cur) and of the tile whose gathers were issued last (next).
+    uint32_t valid_cur = 0xffffu, valid_next = 0xffffu;
+    int bad_next = 0, bad_total = 0;
+    auto resolve = [&](int entry) {
+        if constexpr (kRaw) return stand_in_raw(entry, p.S_rows, &valid_next, &bad_next);
+        else return stand_in(entry);
+    };
     const char *kb = (const char *)p.k + (int64_t)g * p.k_sh * Gth::kElemBytes;
     const char *vb = (const char *)p.v + (int64_t)g * p.v_sh * Gth::kElemBytes;
     const int64_t k_ss = p.k_ss * Gth::kElemBytes, v_ss = p.v_ss * Gth::kElemBytes;
@@ -488,12 +528,12 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
     const int step = splits;
     u32x4_t rkb[kAhead][Gth::kKLoads], rvb[kAhead][Gth::kVLoads];
     int tile = split;
-    int slot_next = tile_slot(list, tile, ntiles, lane);
+    int slot_next = entry_at(tile);
 #pragma unroll
     for (int b = 0; b < kAhead; ++b) {
-        const int slot = stand_in(slot_next);
+        const int slot = resolve(slot_next);
         gather_k<KV>(rkb[b], slot, kb, k_ss, lane);
-        slot_next = tile_slot(list, tile + (b + 1) * step, ntiles, lane);
+        slot_next = entry_at(tile + (b + 1) * step);
         gather_v<KV, kScalarVAddr>(rvb[b], slot, vb, v_ss, lane);
     }
 
@@ -544,8 +584,12 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         // The next tile's slots: FP8 needs them here; BF16 resolves them after
         // V(i) is staged, where that wait has already covered their load (a
         // resolve here would wait for V(i) before the scores).
+        if constexpr (kRaw) {   // this tile's mask and count, resolved a tile ago
+            valid_cur = valid_next;
+            bad_total += bad_next;
+        }
         int slot_g = 0;
-        if constexpr (KV == KvType::kFp8) slot_g = stand_in(slot_next);
+        if constexpr (KV == KvType::kFp8) slot_g = resolve(slot_next);
         __builtin_amdgcn_sched_barrier(0);   // K(i) is consumed before K(i+1) lands
         if constexpr (KV == KvType::kFp8) {
 #pragma unroll
@@ -559,7 +603,10 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         const int first = tile * kTileSlots + 4 * j;
         float x[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = first + i < n ? s[i] * p.scale_log2e : kNegInf;
+        for (int i = 0; i < 4; ++i) {
+            const bool keep = kRaw ? ((valid_cur >> (4 * j + i)) & 1u) != 0 : first + i < n;
+            x[i] = keep ? s[i] * p.scale_log2e : kNegInf;
+        }
         float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -583,7 +630,11 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         bf16x4_t pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const __bf16 pr = (__bf16)__builtin_amdgcn_exp2f(x[i] - m);
+            // (Raw rows: a tile with no valid row, before any valid one, has
+            // m = -inf and x = -inf, whose difference is not a number.)
+            const __bf16 pr = (kRaw && valid_cur == 0)
+                                  ? (__bf16)0.0f
+                                  : (__bf16)__builtin_amdgcn_exp2f(x[i] - m);
             pb[i] = pr;
             lsum += (float)pr;
         }
@@ -591,8 +642,8 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         wave_lds_fence();   // the previous tile's transpose reads are done
         stage_v<KV, Lay::kVPitch>(rv, vs_lds, lane);
         __builtin_amdgcn_sched_barrier(0);   // V(i) is consumed before V(i+1) lands
-        if constexpr (KV == KvType::kBf16) slot_g = stand_in(slot_next);
-        slot_next = tile_slot(list, tile + (kAhead + 1) * step, ntiles, lane);
+        if constexpr (KV == KvType::kBf16) slot_g = resolve(slot_next);
+        slot_next = entry_at(tile + (kAhead + 1) * step);
         gather_v<KV, kScalarVAddr>(rv, slot_g, vb, v_ss, lane);
         wave_lds_fence();   // other lanes of this wave wrote the rows read below
 
@@ -641,6 +692,7 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
             p.part_ml[(part_row + c) * 2] = m;
             p.part_ml[(part_row + c) * 2 + 1] = lsum;
         }
+        if (report_bad && lane == 0) p.bad_part[split * p.T + t] = bad_total;
 #pragma unroll
         for (int db = 0; db < kDimBlocks; ++db) {
             f32x4_t acc = o[db];
@@ -673,6 +725,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     const int64_t t = row / p.Hq;
     const int h = (int)(row - t * p.Hq);
     const int64_t n = p.n_parts;
+    if (p.bad_part != nullptr && h == 0) {
+        // The invalid entries of token t's row, reported by its raw-row shares.
+        int bad = 0;
+        for (int64_t s = lane; s < n; s += 64) bad += p.bad_part[s * p.T + t];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) bad += __shfl_xor(bad, off);
+        if (lane == 0) p.n_bad[t] = bad;
+    }
     float mmax = kNegInf;
     for (int64_t s0 = 0; s0 < n; s0 += 64) {
         const int64_t s = s0 + lane;
@@ -1573,6 +1633,12 @@ hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
                                  hipStream_t stream) {
     const int64_t blocks = T * (int64_t)p.Hkv * p.HB * p.splits;
     if (blocks == 0) return hipSuccess;
+    if (p.raw_rows) {
+        if (kv != KvType::kBf16 || (p.raw == nullptr && p.W_raw > 0)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((attend_kernel<true, KvType::kBf16, 16, kItemsPerCU, true>),
+                           dim3((unsigned)blocks), dim3(64), 0, stream, p);
+        return hipGetLastError();
+    }
     launch_attend_any<true>(p, kv, blocks, stream);
     return hipGetLastError();
 }
