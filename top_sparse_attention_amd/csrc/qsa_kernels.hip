@@ -1375,7 +1375,7 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(const IndexerSelect
 }
 
 // The same selection, faster for budgets up to kCand / 4: the threshold
-// is first estimated from kSelSample scores spaced evenly over the row (the
+// is first estimated from kSelSample scores in runs spaced evenly over the row (the
 // top 16 bits of the key ranked about 2 * budget * kSelSample / n from the
 // top); one pass over the row then keeps, in block order, the scores whose
 // key is at least the estimate (about 2 * budget of them), and the exact
@@ -1400,6 +1400,8 @@ template <int kCand, int kWavesPerSimd, bool kDefer>
 __global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel(
     const IndexerSelectParams p) {
     static_assert(kCand % 256 == 0 && kCand >= kSelSample, "candidate list");
+    // One 16-byte sample load per thread; runs 16 apart or more once n > kCand >= kSelSample.
+    static_assert(kSelSample == 4 * 256, "sample runs");
     constexpr int kCandPadded = kCand + kCand / 16;
     using Scan = hipcub::BlockScan<int, 256>;
     __shared__ float cval[kCandPadded];
@@ -1452,8 +1454,24 @@ __global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel
         // 1. Estimated threshold (every key passes when the row fits the list).
         uint32_t tau0 = 0;
         if (n > kCand) {
-            for (int k = tid; k < kSelSample; k += 256)
-                cval[k] = row[(int64_t)k * n / kSelSample];
+            // The sample: kSelSample / 16 runs of 16 consecutive scores (64
+            // bytes), evenly spaced over the row and aligned to 16 scores.  A
+            // strided sample would touch every cache line of the row, which
+            // the pass below then fetches a second time.  Thread k loads
+            // scores 4 (k % 4) .. + 3 of run k / 4 (n > kCand keeps the runs
+            // distinct and inside the row).
+            constexpr int kRuns = kSelSample / 16;
+            const int start = (int)((int64_t)(tid >> 2) * (n - 16) / (kRuns - 1)) & ~15;
+            const int i = start + 4 * (tid & 3);
+            f32x4_t x;
+            if (vec_ok) {
+                x = *(const f32x4_t *)(row + i);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = row[i + e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cval[4 * tid + e] = x[e];
             __syncthreads();
             const int kth =
                 (int)min<int64_t>(kSelSample, (2 * (int64_t)p.budget * kSelSample + n - 1) / n);
