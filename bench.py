@@ -6,7 +6,8 @@ attention (qsa_sparse_attend), both through the C ABI on torch's current
 stream.  Other workloads: `decode_batch` runs qsa_sparse_decode (split
 attention over the raw selection rows, then the merge), `long_prefill_fp8kv` the
 FP8 E4M3 KV-cache variant (qsa_sparse_attend_fp8kv) and `long_prefill_block4`
-micro-block selections (qsa_compact_blocks, then qsa_sparse_attend);
+micro-block selections (qsa_sparse_prefill_blocks: compaction into aligned
+block lists, then the attention);
 `indexed_long_prefill` makes the selection inside the step with the QSA
 indexer and Top-K (qsa_indexer_topk) before the same two passes.  The default workload is the long prefill of the page "Qwen4-Exp QSA
 comes to Huawei's Ascend: inside SGLang's opt-in CANN prefill PR" (section
@@ -143,17 +144,22 @@ def main():
     dws = (torch.empty(qsa.decode_workspace_bytes(T, W, Hq, Hkv), dtype=torch.uint8, device=dev)
            if split else None)
 
+    # Micro-block workloads run qsa_sparse_prefill_blocks (its compaction
+    # writes the aligned block lists when the workspace has room for them),
+    # so their attend time includes the compaction.
+    bws = (torch.empty(qsa.prefill_blocks_workspace_bytes(T, W, bs), dtype=torch.uint8,
+                       device=dev) if bs > 1 else None)
+
     def compact():
-        if split:
+        if split or bs > 1:
             return
-        if bs > 1:
-            qsa.compact_blocks(sl, S, bs, ws)
-        else:
-            qsa.compact_slots(sl, S, ws)
+        qsa.compact_slots(sl, S, ws)
 
     def attend():
         if split:
             qsa.sparse_decode(q, k, v, sl, scale=scale, out=out, workspace=dws)
+        elif bs > 1:
+            qsa.sparse_prefill_blocks(q, k, v, sl, bs, scale=scale, out=out, workspace=bws)
         elif fp8:
             qsa.sparse_attend_fp8kv(q, k, v, k_scale, v_scale, ws, W, scale=scale, out=out)
         else:
@@ -227,6 +233,8 @@ def main():
     gather_only = qsa.gather_only_fp8kv if fp8 else qsa.gather_only
     if split:   # the decode step compacts nothing; the reference needs the lists
         qsa.compact_slots(sl, S, ws)
+    elif bs > 1:   # plain (unaligned) block lists
+        qsa.compact_blocks(sl, S, bs, ws)
     for _ in range(2):
         gather_only(k, v, ws, T, Wl, sink)
     c0 = torch.cuda.Event(enable_timing=True)

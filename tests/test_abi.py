@@ -42,6 +42,18 @@ def test_library_exports_every_declared_entry_point():
         assert hasattr(lib, name), f"{name} declared in qsa.h but not exported"
 
 
+def test_prefill_blocks_workspace_has_room_for_aligned_lists():
+    _lib()
+    base = qsa.workspace_bytes(7810, 513 * 4)
+    room = -(-(2052 * 3 // 2) // 32) * 32          # 1.5 x the row's slots, in list pads
+    want = -(-base // 256) * 256 + -(-(7810 * room * 4) // 256) * 256
+    assert qsa.prefill_blocks_workspace_bytes(7810, 513, 4) == want
+    assert qsa.prefill_blocks_workspace_bytes(3, 0, 4) >= qsa.workspace_bytes(3, 0)
+    assert qsa.prefill_blocks_workspace_bytes(-1, 5, 4) == 0
+    assert qsa.prefill_blocks_workspace_bytes(3, 5, 0) == 0
+    assert qsa.prefill_blocks_workspace_bytes(3, 5, 65) == 0
+
+
 def test_version_and_status_strings():
     lib = _lib()
     assert qsa.version().startswith("libqsa")

@@ -63,11 +63,97 @@ def test_block_path_equals_slot_path_on_the_expanded_selection():
     by slot id, so both paths sum in the same order: bit-identical outputs."""
     case = block_case(1030, T=23, S=8192, Hq=16, Hkv=2, nblocks=200, bs=4, pad_frac=0.1,
                       interior=True)
-    out, (q, k, v, sl) = check_blocks(case)
+    q, k, v, sl = upload(case, DEV)
+    plain_ws = qsa.new_workspace(case.T, case.W * 4, DEV)   # no room for aligned lists
+    out = qsa.sparse_prefill_blocks(q, k, v, sl, 4, scale=case.scale, workspace=plain_ws)
     slots = torch.from_numpy(oracle.expand_blocks(case.slot_idx, 4)).to(DEV)
     ref = qsa.sparse_prefill(q, k, v, slots)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def _key_bits(n):
+    bits = 1
+    while bits < 31 and (1 << bits) < n:
+        bits += 1
+    return bits + 1
+
+
+def aligned_lists_model(block_idx, S, bs):
+    """The aligned lists, written out from their rule: valid blocks grouped by
+    the compaction's 128 slot ranges (stable), super-ranges of at most 2,048
+    slots (unions of those ranges); super-range k starts at
+    max(previous end, min(k * F, room - slots still to place)), F =
+    ceil(1.25 * slots / ranges), room = 1.5 x the row's width in list pads."""
+    T, W = block_idx.shape
+    nb = S // bs
+    group_shift = max(_key_bits(nb) - 8, 0)
+    by_size = 0
+    while (bs << (by_size + 1)) <= 2048:
+        by_size += 1
+    shift = max(group_shift, by_size)
+    R = -(-nb // (1 << shift))
+    room = -(-((W * bs * 3 + 1) // 2) // 32) * 32
+    rows = []
+    for r in block_idx.astype(np.int64):
+        valid = r[(r >= 0) & (r < nb)]
+        valid = valid[np.argsort(valid >> group_shift, kind="stable")]
+        slots = len(valid) * bs
+        F = (5 * slots + 4 * R - 1) // (4 * R)
+        end, rem, out = 0, slots, []
+        for kk in range(R):
+            seg = valid[(valid >> shift) == kk]
+            cs = len(seg) * bs
+            start = max(end, min(kk * F, room - rem)) if cs else end
+            out += [-1] * (start - end)
+            out += (seg[:, None] * bs + np.arange(bs)[None, :]).ravel().tolist()
+            end, rem = start + cs, rem - cs
+        rows.append(np.array(out, dtype=np.int64))
+    return rows, room
+
+
+@pytest.mark.parametrize("bs,S,nblocks", [(4, 8192, 200), (8, 16384, 120), (16, 4096, 40)])
+def test_aligned_block_lists_follow_their_rule(bs, S, nblocks):
+    """Index work, so bit-exact: the aligned rows the prefill writes into the
+    workspace equal the rule's, and the output meets the gate."""
+    case = block_case(1050 + bs, T=19, S=S, Hq=16, Hkv=2, nblocks=nblocks, bs=bs, pad_frac=0.15,
+                      interior=True)
+    case.slot_idx[3] = -1                                  # an empty row
+    q, k, v, sl = upload(case, DEV)
+    nbytes = qsa.prefill_blocks_workspace_bytes(case.T, case.W, bs)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV)
+    out = qsa.sparse_prefill_blocks(q, k, v, sl, bs, scale=case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    m = qsa.workspace_layout(case.T, case.W * bs)
+    ext = -(-m["total_bytes"] // 256) * 256
+    want, room = aligned_lists_model(case.slot_idx, S, bs)
+    ws32 = ws.view(torch.int32)
+    rows = ws32[ext // 4: ext // 4 + case.T * room].view(case.T, room).cpu().numpy()
+    count = ws32[m["count_offset"] // 4: m["count_offset"] // 4 + case.T].cpu().numpy()
+    gaps = 0
+    for t in range(case.T):
+        assert count[t] == len(want[t]), t
+        assert np.array_equal(rows[t, :count[t]], want[t]), t
+        padded = -(-count[t] // 32) * 32
+        assert np.all(rows[t, count[t]:padded] == -1), t
+        gaps += int((want[t] == -1).sum())
+    assert gaps > 0                                         # the rule did insert gaps
+    scale = case.scale if case.scale is not None else 1.0 / 16.0
+    ref = oracle.prefill_blocks(case.q, case.k_cache, case.v_cache, case.slot_idx, bs, scale)
+    print(gate(bf16_tensor_to_f32(out), ref, empty_blocks(case)), "gaps", gaps)
+
+
+def test_aligned_and_plain_block_paths_agree_within_rounding():
+    case = block_case(1060, T=40, S=8192, Hq=24, Hkv=2, nblocks=300, bs=4, pad_frac=0.05)
+    q, k, v, sl = upload(case, DEV)
+    aligned = qsa.sparse_prefill_blocks(q, k, v, sl, 4)
+    plain = qsa.sparse_prefill_blocks(q, k, v, sl, 4,
+                                      workspace=qsa.new_workspace(case.T, case.W * 4, DEV))
+    torch.cuda.synchronize()
+    a, p = bf16_tensor_to_f32(aligned), bf16_tensor_to_f32(plain)
+    assert np.all(np.abs(a - p) <= 2.0 ** -7 * np.abs(p) + 1e-4)
+    ref = oracle.prefill_blocks(case.q, case.k_cache, case.v_cache, case.slot_idx, 4, 1.0 / 16.0)
+    print(gate(a, ref, empty_blocks(case)))
 
 
 def test_block_compaction_counts_slots_and_invalid_blocks():

@@ -130,6 +130,8 @@ def load_library():
     lib.qsa_sparse_prefill_fp8kv.restype = ctypes.c_int
     lib.qsa_sparse_prefill_fp8kv.argtypes = [P(BF16View), P(BF16View), P(BF16View), f32, f32,
                                              P(I32View), f32, P(BF16View), vp, sz, vp]
+    lib.qsa_prefill_blocks_workspace_bytes.restype = sz
+    lib.qsa_prefill_blocks_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32]
     lib.qsa_compact_blocks.restype = ctypes.c_int
     lib.qsa_compact_blocks.argtypes = [P(I32View), i64, ctypes.c_int32, vp, sz, vp]
     lib.qsa_sparse_prefill_blocks.restype = ctypes.c_int
@@ -451,6 +453,13 @@ def compact_blocks(block_idx: torch.Tensor, S: int, block_size: int,
     return workspace
 
 
+def prefill_blocks_workspace_bytes(T: int, W: int, block_size: int) -> int:
+    """Workspace bytes for sparse_prefill_blocks with room for the aligned
+    block lists (a workspace of workspace_bytes(T, W * block_size) also works,
+    with plain lists)."""
+    return int(load_library().qsa_prefill_blocks_workspace_bytes(T, W, block_size))
+
+
 def sparse_prefill_blocks(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                           block_idx: torch.Tensor, block_size: int,
                           scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
@@ -459,7 +468,8 @@ def sparse_prefill_blocks(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if workspace is None:
-        workspace = new_workspace(T, W * block_size, q.device)
+        nbytes = prefill_blocks_workspace_bytes(T, W, block_size)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     qv, kv, vv, ov = (_bf16_view(q, "q"), _bf16_view(k_cache, "k_cache"),
                       _bf16_view(v_cache, "v_cache"), _bf16_view(out, "out"))
     bv = _i32_view(block_idx, "block_idx")

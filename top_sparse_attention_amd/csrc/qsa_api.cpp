@@ -198,10 +198,26 @@ qsa_status hip_fail(hipError_t e, const char *what) {
     return fail(QSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Width of the compaction's sort key for entries in [0, n): the bits of
+// n - 1 (at least one) plus the bit that marks invalid entries.
+int32_t sort_key_bits(int64_t n) {
+    int bits = 1;
+    while (bits < 31 && ((int64_t)1 << bits) < n) ++bits;
+    return bits + 1;
+}
+
+// Aligned block lists (see CompactParams): the super-range shift, their
+// number and the row room, or shift -1 for the plain list.
+struct AlignSpec {
+    int32_t shift = -1, ranges = 0, cap = 0;
+    int64_t list_offset = 0;   // of the aligned rows in the workspace
+};
+
 qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t S, int64_t lo,
                            int64_t hi, void *ws, const qsa_workspace_map &m, hipStream_t stream,
-                           int32_t block = 1) {
+                           int32_t block = 1, const AlignSpec *align = nullptr) {
     qsa::CompactParams p{};
+    p.align_shift = -1;
     p.block = block;
     p.slot_idx = sl->data;
     p.stride_t = sl->stride[0];
@@ -210,11 +226,16 @@ qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t
     p.S = S;
     p.lo = lo;
     p.hi = hi;
-    int bits = 1;   // width of hi - lo - 1, at least one bit
-    while (bits < 31 && ((int64_t)1 << bits) < hi - lo) ++bits;
-    p.key_bits = bits + 1;   // one more bit for the key that marks invalid entries
+    p.key_bits = sort_key_bits(hi - lo);
     p.list = (int32_t *)((char *)ws + m.list_offset);
     p.row_stride = m.row_stride;
+    if (align != nullptr && align->shift >= 0) {
+        p.align_shift = align->shift;
+        p.align_ranges = align->ranges;
+        p.align_cap = align->cap;
+        p.list = (int32_t *)((char *)ws + align->list_offset);
+        p.row_stride = align->cap;
+    }
     p.count = (int32_t *)((char *)ws + m.count_offset);
     p.n_bad = (int32_t *)((char *)ws + m.bad_offset);
     hipError_t e = qsa::launch_compact(p, stream);
@@ -283,7 +304,8 @@ bool sharing_of(const Problem &pr, int32_t HB, void *ws, const qsa_workspace_map
 qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
                           const qsa_bf16_view *v, const qsa_bf16_view *out, const Problem &pr,
                           float scale, void *ws, const qsa_workspace_map &m,
-                          hipStream_t stream, KvKind kv = KvKind()) {
+                          hipStream_t stream, KvKind kv = KvKind(),
+                          const AlignSpec *align = nullptr) {
     if (pr.T == 0 || pr.Hq == 0) return QSA_OK;
     qsa::AttendParams p{};
     fill_attend(p, q, k, v, pr, scale * kv.k_scale, ws, m);
@@ -291,10 +313,64 @@ qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
     p.out = (uint16_t *)out->data;
     p.o_st = out->stride[0];
     p.o_sh = out->stride[1];
+    if (align != nullptr && align->shift >= 0) {
+        // Aligned block lists: -1 gaps inside the rows, masked per tile.
+        p.list = (const int32_t *)((const char *)ws + align->list_offset);
+        p.list_stride = align->cap;
+        p.masked = 1;
+        p.S_rows = pr.S;
+        hipError_t e = qsa::launch_attend(p, kv.type, pr.T, stream, nullptr);
+        return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
+    }
     qsa::SharingParams sp{};
     const bool share = sharing_of(pr, p.HB, ws, m, &sp);
     hipError_t e = qsa::launch_attend(p, kv.type, pr.T, stream, share ? &sp : nullptr);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
+}
+
+// Room (slots) of an aligned row for a selection of Ws slots.
+int64_t align_room(int64_t Ws) {
+    return round_up((Ws * qsa::kAlignRoomNum + qsa::kAlignRoomDen - 1) / qsa::kAlignRoomDen,
+                    qsa::kListPad);
+}
+
+// The standard layout for Ws slots, then the aligned rows (at *ext_offset).
+bool blocks_layout(int64_t T, int64_t Ws, qsa_workspace_map *m, int64_t *ext_offset,
+                   int64_t *total) {
+    if (!layout_of(T, Ws, m)) return false;
+    *ext_offset = round_up(m->total_bytes, kAlign);
+    *total = *ext_offset + round_up(T * align_room(Ws) * 4, kAlign);
+    return true;
+}
+
+// Whether a micro-block prefill takes the aligned lists, and their spec:
+// blocks of kAlignMinBlock slots or more, rows of one sort run, room in the
+// workspace, and enough sharing that the general layout runs without an
+// estimate (the lists only help tokens that share the L2).
+AlignSpec align_of(const Problem &pr, int64_t W, int32_t block_size, void *ws,
+                   size_t ws_bytes, const qsa_workspace_map &m) {
+    AlignSpec al;
+    const int64_t Ws = W * block_size, nb = pr.S / block_size;
+    if (block_size < qsa::kAlignMinBlock || W > qsa::kSortChunk || Ws <= 0 || nb <= 0 ||
+        pr.Hkv <= 0)
+        return al;
+    qsa_workspace_map mb;
+    int64_t ext = 0, total = 0;
+    if (!blocks_layout(pr.T, Ws, &mb, &ext, &total) || (int64_t)ws_bytes < total) return al;
+    qsa::SharingParams sp{};
+    const int32_t HB = (pr.Hq / pr.Hkv + 15) / 16;
+    if (sharing_of(pr, HB, ws, m, &sp)) return al;
+    int32_t shift = std::max(sort_key_bits(nb) - qsa::kSortKeyBits, 0);
+    int32_t by_size = 0;   // largest with 2^by_size blocks <= kAlignSlots slots
+    while (((int64_t)block_size << (by_size + 1)) <= qsa::kAlignSlots) ++by_size;
+    shift = std::max(shift, by_size);
+    const int64_t ranges = (nb + ((int64_t)1 << shift) - 1) >> shift;
+    if (ranges > qsa::kAlignMaxRanges) return al;
+    al.shift = shift;
+    al.ranges = (int32_t)ranges;
+    al.cap = (int32_t)align_room(Ws);
+    al.list_offset = ext;
+    return al;
 }
 
 // Partials buffer: O [n_parts][T][Hq][256] FP32, then (m, l) [n_parts][T][Hq][2] FP32.
@@ -500,8 +576,18 @@ qsa_status qsa_sparse_prefill_blocks(const qsa_bf16_view *q, const qsa_bf16_view
     if (pr.T == 0) return QSA_OK;
     hipStream_t st = (hipStream_t)stream;
     const int64_t nb = pr.S / block_size;
-    if ((s = enqueue_compact(block_idx, pr.T, W, nb, 0, nb, workspace, m, st, block_size))) return s;
-    return enqueue_attend(q, k_cache, v_cache, out, pr, scale, workspace, m, st);
+    const AlignSpec al = align_of(pr, W, block_size, workspace, workspace_bytes, m);
+    if ((s = enqueue_compact(block_idx, pr.T, W, nb, 0, nb, workspace, m, st, block_size, &al)))
+        return s;
+    return enqueue_attend(q, k_cache, v_cache, out, pr, scale, workspace, m, st, KvKind(), &al);
+}
+
+size_t qsa_prefill_blocks_workspace_bytes(int64_t T, int64_t W, int32_t block_size) {
+    if (T < 0 || W < 0 || block_size < 1 || block_size > 64 || W * block_size > kMax32) return 0;
+    qsa_workspace_map m;
+    int64_t ext = 0, total = 0;
+    if (!blocks_layout(T, W * block_size, &m, &ext, &total)) return 0;
+    return (size_t)total;
 }
 
 // ---------------------------------------------------------------- indexer

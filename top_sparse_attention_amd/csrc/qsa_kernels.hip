@@ -154,6 +154,11 @@ __device__ __forceinline__ V ldg16(const void *p) {
 // 2^(key_bits-1), so they sort last), i.e. grouped into at most 128 ascending
 // slot ranges, stable inside a range, and appended to the compacted list.
 // Two radix passes; a full sort would cost more and buys no locality.
+// Aligned lists (align_shift >= 0, one run per row) place each super-range of
+// about kAlignSlots slots near a fixed position of the row instead, the gaps
+// holding -1: the tokens running at one time, whose lists have different
+// counts per range, then reach each part of the cache after about the same
+// number of tiles (their gathers share the L2), at about 25% more tiles.
 __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactParams p) {
     using Load = hipcub::BlockLoad<int32_t, kSortThreads, kSortItemsPerThread,
                                    hipcub::BLOCK_LOAD_TRANSPOSE>;
@@ -163,13 +168,19 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
         typename Sort::TempStorage sort;
     } tmp;
     __shared__ int chunk_counts;   // valid entries | invalid entries << 16
+    // Aligned lists: per super-range its entry count, first rank, the start
+    // of the gap before it and its start (slot positions); the row's end.
+    __shared__ int sr_cnt[kAlignMaxRanges], sr_first[kAlignMaxRanges];
+    __shared__ int sr_gap[kAlignMaxRanges], sr_start[kAlignMaxRanges];
+    __shared__ int sh_end;
 
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
     const int32_t *src = p.slot_idx + t * p.stride_t;
     int32_t *dst = p.list + t * p.row_stride;
     const uint32_t pad_key = 1u << (p.key_bits - 1);
-    int n = 0, bad = 0;
+    const bool aligned = p.align_shift >= 0 && p.W <= kSortChunk;
+    int n = 0, bad = 0, aligned_end = 0;
     for (int64_t base = 0; base < p.W; base += kSortChunk) {
         if (tid == 0) chunk_counts = 0;
         // Coalesced loads, handed to the sort in blocked order (thread t holds
@@ -199,7 +210,50 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
         __syncthreads();   // the counts above are complete
         const int nv = chunk_counts & 0xffff;
         const int nb = chunk_counts >> 16;
-        if (p.block == 1) {
+        if (aligned) {
+            // One run holds the row.  Entries per super-range, then (one
+            // thread, at most kAlignMaxRanges steps) where each starts.
+            for (int i = tid; i < kAlignMaxRanges; i += kSortThreads) sr_cnt[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < kSortItemsPerThread; ++u) {
+                const int pos = tid + kSortThreads * u;
+                if (pos < nv) atomicAdd(&sr_cnt[min((int)(key[u] >> p.align_shift), p.align_ranges - 1)], 1);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                const int slots = nv * p.block, R = p.align_ranges;
+                const int F = (5 * slots + 4 * R - 1) / (4 * R);   // 1.25 x the mean, rounded up
+                int end = 0, first = 0, rem = slots;
+                for (int k = 0; k < R; ++k) {
+                    const int cs = sr_cnt[k] * p.block;
+                    // end + rem <= align_cap holds before and after each step.
+                    const int start = cs > 0 ? max(end, min(k * F, p.align_cap - rem)) : end;
+                    sr_gap[k] = end;
+                    sr_start[k] = start;
+                    sr_first[k] = first;
+                    end = start + cs;
+                    first += sr_cnt[k];
+                    rem -= cs;
+                }
+                sh_end = end;
+            }
+            __syncthreads();
+            for (int k = 0; k < p.align_ranges; ++k)
+                for (int i = sr_gap[k] + tid; i < sr_start[k]; i += kSortThreads) dst[i] = -1;
+#pragma unroll
+            for (int u = 0; u < kSortItemsPerThread; ++u) {
+                const int pos = tid + kSortThreads * u;
+                if (pos < nv) {
+                    const int k = min((int)(key[u] >> p.align_shift), p.align_ranges - 1);
+                    const int at = sr_start[k] + (pos - sr_first[k]) * p.block;
+                    for (int i = 0; i < p.block; ++i)
+                        if ((unsigned)(at + i) < (unsigned)p.align_cap)
+                            dst[at + i] = (int32_t)key[u] * p.block + i;
+                }
+            }
+            aligned_end = sh_end;
+        } else if (p.block == 1) {
 #pragma unroll
             for (int u = 0; u < kSortItemsPerThread; ++u) {
                 const int pos = tid + kSortThreads * u;
@@ -218,7 +272,7 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
         bad += nb;
         __syncthreads();   // the counts are reset by the next run
     }
-    const int slots = n * p.block;
+    const int slots = aligned ? aligned_end : n * p.block;
     const int padded = (slots + kListPad - 1) / kListPad * kListPad;
     for (int i = slots + tid; i < padded; i += kSortThreads) dst[i] = -1;
     if (tid == 0) {
@@ -384,20 +438,21 @@ __device__ __forceinline__ int stand_in(int entry) {
     return entry >= 0 ? entry : first;
 }
 
-// Raw selection rows (decode shares): entry of tile row (lane & 15), -1 past
-// the row's W entries, 0 for a tile past the row (a prefetch never used).
-__device__ __forceinline__ int tile_entry_raw(const int32_t *row, int tile, int ntiles, int W,
-                                              int lane) {
+// Masked rows (raw selection rows of decode shares, or aligned block lists):
+// entry of tile row (lane & 15), -1 past the row's W entries, 0 for a tile
+// past the row (a prefetch never used).
+__device__ __forceinline__ int tile_entry_masked(const int32_t *row, int tile, int ntiles, int W,
+                                                 int lane) {
     const int i = tile * kTileSlots + (lane & 15);
     return tile < ntiles ? (i < W ? row[i] : -1) : 0;
 }
 
-// stand_in for raw rows: valid entries (in [0, S)) keep their slot; the others
-// read the tile's first valid slot, or slot 0 when it has none.  Also returns
-// the tile's valid-row mask (bit r for tile row r) and its count of invalid
-// entries other than -1.  Called with every lane active.
-__device__ __forceinline__ int stand_in_raw(int entry, int64_t S, uint32_t *valid_rows,
-                                            int *n_bad) {
+// stand_in for masked rows: valid entries (in [0, S)) keep their slot; the
+// others read the tile's first valid slot, or slot 0 when it has none.  Also
+// returns the tile's valid-row mask (bit r for tile row r) and its count of
+// invalid entries other than -1.  Called with every lane active.
+__device__ __forceinline__ int stand_in_masked(int entry, int64_t S, uint32_t *valid_rows,
+                                               int *n_bad) {
     const bool valid = entry >= 0 && entry < S;
     const uint32_t vm = (uint32_t)(__ballot(valid) & 0xffffu);
     *valid_rows = vm;
@@ -424,12 +479,18 @@ __device__ __forceinline__ int stand_in_raw(int entry, int64_t S, uint32_t *vali
 // the wave's requests reach the memory system spread out.  Each wave walks
 // its own item's slot list in order, and the list is grouped by slot range,
 // so a wave's consecutive tiles fall in the same part of the cache.
-template <bool kSplit, KvType KV, int kQRows, int kItems = kItemsPerCU, bool kRaw = false>
+//
+// kMasked: a row's entries outside [0, S) (-1 included) may stand anywhere in
+// it; each tile masks them with a ballot of its rows.  Split shares then read
+// the raw selection rows (W_raw entries each); unsplit items read a
+// compacted list with -1 gaps (count[t] entries, the aligned block lists).
+template <bool kSplit, KvType KV, int kQRows, int kItems = kItemsPerCU, bool kMasked = false>
 __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) void attend_kernel(
     const AttendParams p) {
     using Gth = KvGather<KV>;
     using Lay = AttendLayout<kQRows, kItems>;
-    static_assert(!kRaw || (kSplit && Lay::kAhead == 1), "raw rows: split shares, one tile ahead");
+    static_assert(!kMasked || Lay::kAhead == 1, "masked rows: one tile ahead");
+    constexpr bool kRawRows = kMasked && kSplit;
     __shared__ __attribute__((aligned(16))) char smem[Lay::kLds];
     if (p.choice != nullptr && ((*p.choice == 1) != (p.choice_value == 1))) return;
 
@@ -449,11 +510,11 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
     const int nh = min(kHeadBlock, p.G - hb * kHeadBlock);
     // Entries of the item's row: the compacted list's count, or (raw rows)
     // the selection width, -1 and invalid entries included.
-    const int n = kRaw ? p.W_raw : p.count[t];
+    const int n = kRawRows ? p.W_raw : p.count[t];
 
     const int ntiles = (n + kTileSlots - 1) / kTileSlots;
     // Raw rows: the share of (g = 0, head block 0) reports the invalid entries.
-    const bool report_bad = kRaw && g == 0 && hb == 0;
+    const bool report_bad = kRawRows && g == 0 && hb == 0;
     const int64_t part_row = kSplit ? ((p.part_base + split) * p.T + t) * p.Hq + h0 : 0;
     if (kSplit && split >= ntiles) {
         // This share is empty: max -inf, sum 0, O 0.
@@ -479,17 +540,17 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         return;
     }
 
-    const int32_t *list = kRaw ? p.raw + t * p.raw_stride : p.list + t * p.list_stride;
+    const int32_t *list = kRawRows ? p.raw + t * p.raw_stride : p.list + t * p.list_stride;
     // The next list entries of this lane's tile row (compacted list or raw row).
     auto entry_at = [&](int tl) {
-        return kRaw ? tile_entry_raw(list, tl, ntiles, n, lane) : tile_slot(list, tl, ntiles, lane);
+        return kMasked ? tile_entry_masked(list, tl, ntiles, n, lane) : tile_slot(list, tl, ntiles, lane);
     };
-    // Raw rows: the valid-row mask and invalid count of the tile being
+    // Masked rows: the valid-row mask and invalid count of the tile being
     // computed (cur) and of the tile whose gathers were issued last (next).
     uint32_t valid_cur = 0xffffu, valid_next = 0xffffu;
     int bad_next = 0, bad_total = 0;
     auto resolve = [&](int entry) {
-        if constexpr (kRaw) return stand_in_raw(entry, p.S_rows, &valid_next, &bad_next);
+        if constexpr (kMasked) return stand_in_masked(entry, p.S_rows, &valid_next, &bad_next);
         else return stand_in(entry);
     };
     const char *kb = (const char *)p.k + (int64_t)g * p.k_sh * Gth::kElemBytes;
@@ -584,7 +645,7 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         // The next tile's slots: FP8 needs them here; BF16 resolves them after
         // V(i) is staged, where that wait has already covered their load (a
         // resolve here would wait for V(i) before the scores).
-        if constexpr (kRaw) {   // this tile's mask and count, resolved a tile ago
+        if constexpr (kMasked) {   // this tile's mask and count, resolved a tile ago
             valid_cur = valid_next;
             bad_total += bad_next;
         }
@@ -604,7 +665,7 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool keep = kRaw ? ((valid_cur >> (4 * j + i)) & 1u) != 0 : first + i < n;
+            const bool keep = kMasked ? ((valid_cur >> (4 * j + i)) & 1u) != 0 : first + i < n;
             x[i] = keep ? s[i] * p.scale_log2e : kNegInf;
         }
         float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -630,9 +691,9 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
         bf16x4_t pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            // (Raw rows: a tile with no valid row, before any valid one, has
-            // m = -inf and x = -inf, whose difference is not a number.)
-            const __bf16 pr = (kRaw && valid_cur == 0)
+            // (Masked rows: a tile with no valid row, before any valid one,
+            // has m = -inf and x = -inf, whose difference is not a number.)
+            const __bf16 pr = (kMasked && valid_cur == 0)
                                   ? (__bf16)0.0f
                                   : (__bf16)__builtin_amdgcn_exp2f(x[i] - m);
             pb[i] = pr;
@@ -1620,6 +1681,12 @@ hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_
                          const SharingParams *share) {
     const int64_t items = T * (int64_t)p.Hkv * p.HB;
     if (items == 0) return hipSuccess;
+    if (p.masked) {   // aligned block lists: BF16, the general layout
+        if (kv != KvType::kBf16 || share != nullptr) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((attend_kernel<false, KvType::kBf16, 16, kItemsPerCU, true>),
+                           dim3((unsigned)items), dim3(64), 0, stream, p);
+        return hipGetLastError();
+    }
     if (share == nullptr || (kv == KvType::kFp8 && p.G <= 8)) {
         launch_attend_any<false>(p, kv, items, stream);
         return hipGetLastError();
