@@ -189,3 +189,25 @@ def test_long_prefill_block4_sampled_rows():
     rows = qi.sample_rows(case.T, 64)
     out, _ = check_blocks(case, rows)
     assert torch.isfinite(out.float()).all()
+
+
+def test_aligned_block_prefill_reports_invalid_blocks():
+    """The aligned path keeps the standard layout's status words: qsa_check_status
+    (width W * block_size) counts the blocks that were neither -1 nor in range."""
+    case = block_case(1070, T=30, S=8192, Hq=16, Hkv=2, nblocks=150, bs=4, pad_frac=0.1,
+                      interior=True)
+    case.slot_idx[4, 7] = 2048            # one past the last block
+    case.slot_idx[9, 0] = -3
+    case.slot_idx[9, 1] = 1 << 29
+    q, k, v, sl = upload(case, DEV)
+    ws = torch.empty(qsa.prefill_blocks_workspace_bytes(case.T, case.W, 4), dtype=torch.uint8,
+                     device=DEV)
+    out = qsa.sparse_prefill_blocks(q, k, v, sl, 4, workspace=ws)
+    torch.cuda.synchronize()
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.check_status(ws, case.T, case.W * 4)
+    assert e.value.status == 6 and "3 selection entries" in str(e.value)
+    valid = np.where((case.slot_idx >= 0) & (case.slot_idx < 2048), case.slot_idx, -1)
+    ref = oracle.prefill_blocks(case.q, case.k_cache, case.v_cache, valid.astype(np.int32), 4,
+                                1.0 / 16.0)
+    print(gate(bf16_tensor_to_f32(out), ref, ~np.any(valid >= 0, axis=1)))

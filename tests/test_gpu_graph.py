@@ -1,4 +1,5 @@
-"""The prefill, FP8 prefill, decode and indexer paths captured in a HIP graph.
+"""The prefill, FP8 prefill, micro-block prefill, decode and indexer paths
+captured in a HIP graph.
 
 These paths record no memset and make no synchronous call, so a captured
 step replays exactly: every replay is compared bit for bit with the eager
@@ -68,6 +69,21 @@ def test_fp8_prefill_graph_replays_exactly():
     ws = qsa.new_workspace(case.T, case.W, DEV)
     replay_matches_eager(
         lambda: qsa.sparse_prefill_fp8kv(q, k8, v8, ks, vs, sl, out=out, workspace=ws), out)
+
+
+def test_block_prefill_with_aligned_lists_graph_replays_exactly():
+    case = qi.random_case(1206, T=150, S=4096, Hq=16, Hkv=2, W=300, pad_frac=0.1,
+                          interior=True)                  # block ids in [0, 4096), blocks of 4
+    rng = np.random.Generator(np.random.PCG64(1207))
+    q, _, _, sl = upload(case, DEV)
+    k = torch.from_numpy(qi.normal_bf16(rng, (4 * case.S, case.Hkv, 256)).view(np.int16)).to(DEV)
+    v = torch.from_numpy(qi.normal_bf16(rng, (4 * case.S, case.Hkv, 256)).view(np.int16)).to(DEV)
+    k, v = k.view(torch.bfloat16), v.view(torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = torch.empty(qsa.prefill_blocks_workspace_bytes(case.T, case.W, 4), dtype=torch.uint8,
+                     device=DEV)
+    replay_matches_eager(
+        lambda: qsa.sparse_prefill_blocks(q, k, v, sl, 4, out=out, workspace=ws), out)
 
 
 def test_decode_graph_replays_exactly():
