@@ -47,9 +47,10 @@ def check_blocks(case, rows=None):
     return out, (q, k, v, sl)
 
 
-@pytest.mark.parametrize("bs", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("bs", [1, 2, 4, 5, 8, 16, 64])
 def test_block_sizes(bs):
-    check_blocks(block_case(1000 + bs, T=29, S=8192, Hq=16, Hkv=2, nblocks=400 // bs + 3, bs=bs,
+    S = 8000 if bs == 5 else 8192          # a multiple of the block size
+    check_blocks(block_case(1000 + bs, T=29, S=S, Hq=16, Hkv=2, nblocks=400 // bs + 3, bs=bs,
                             pad_frac=0.2, interior=True))
 
 
@@ -112,7 +113,8 @@ def aligned_lists_model(block_idx, S, bs):
     return rows, room
 
 
-@pytest.mark.parametrize("bs,S,nblocks", [(4, 8192, 200), (8, 16384, 120), (16, 4096, 40)])
+@pytest.mark.parametrize("bs,S,nblocks", [(4, 8192, 200), (8, 16384, 120), (16, 4096, 40),
+                                          (5, 20000, 300), (64, 65536, 40)])
 def test_aligned_block_lists_follow_their_rule(bs, S, nblocks):
     """Index work, so bit-exact: the aligned rows the prefill writes into the
     workspace equal the rule's, and the output meets the gate."""
