@@ -120,6 +120,9 @@ struct AttendParams {
     // and 1 exactly one works, whatever the word holds.
     const int32_t *choice;
     int32_t choice_value;
+    // Work units of the launch (items, times splits in split mode); set by
+    // the launcher, which sizes the grid.
+    int64_t units;
     // Unsplit items over a compacted list with -1 gaps (the aligned block
     // lists; masked = 1, BF16, S_rows = S): entries are masked per tile row.
     int32_t masked;
