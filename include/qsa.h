@@ -282,7 +282,8 @@ size_t qsa_decode_workspace_bytes(int64_t T, int64_t W, int32_t Hq, int32_t Hkv)
  * qsa_sparse_prefill; the workspace must hold qsa_decode_workspace_bytes, and
  * qsa_check_status(workspace, ..., T, W, ...) reports the invalid entries.
  * Entries are summed in row order rather than grouped by slot range, so the
- * result can differ from qsa_sparse_prefill's in the last bits.
+ * result can differ from qsa_sparse_prefill's in the last bits.  (An empty
+ * cache, S = 0, where no entry is valid, runs the compaction pass instead.)
  */
 qsa_status qsa_sparse_decode(const qsa_bf16_view *q,
                              const qsa_bf16_view *k_cache,
@@ -293,7 +294,8 @@ qsa_status qsa_sparse_decode(const qsa_bf16_view *q,
 
 /*
  * Synchronizes `stream`, then reads the invalid-entry counts that the last
- * compaction into `workspace` (for T, W) left.  Writes their total to
+ * compaction into `workspace` (for T, W), or the last qsa_sparse_decode with
+ * it, left.  Writes their total to
  * *n_bad (if not NULL) and returns QSA_ERR_SLOT_RANGE if it is non-zero.
  * This is the only entry point that waits for the device.
  */
