@@ -344,9 +344,10 @@ bool blocks_layout(int64_t T, int64_t Ws, qsa_workspace_map *m, int64_t *ext_off
 }
 
 // Whether a micro-block prefill takes the aligned lists, and their spec:
-// blocks of kAlignMinBlock slots or more, rows of one sort run, room in the
-// workspace, and enough sharing that the general layout runs without an
-// estimate (the lists only help tokens that share the L2).
+// blocks of kAlignMinBlock slots or more, rows of one sort run whose room fits
+// kAlignRoomMax, room in the workspace, and enough sharing that the general
+// layout runs without an estimate (the lists only help tokens that share the
+// L2).
 AlignSpec align_of(const Problem &pr, int64_t W, int32_t block_size, void *ws,
                    size_t ws_bytes, const qsa_workspace_map &m) {
     AlignSpec al;
@@ -365,7 +366,7 @@ AlignSpec align_of(const Problem &pr, int64_t W, int32_t block_size, void *ws,
     while (((int64_t)block_size << (by_size + 1)) <= qsa::kAlignSlots) ++by_size;
     shift = std::max(shift, by_size);
     const int64_t ranges = (nb + ((int64_t)1 << shift) - 1) >> shift;
-    if (ranges > qsa::kAlignMaxRanges) return al;
+    if (ranges > qsa::kAlignMaxRanges || align_room(Ws) > qsa::kAlignRoomMax) return al;
     al.shift = shift;
     al.ranges = (int32_t)ranges;
     al.cap = (int32_t)align_room(Ws);

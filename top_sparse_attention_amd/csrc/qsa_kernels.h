@@ -59,6 +59,9 @@ constexpr int kSortKeyBits = 8;
 constexpr int kAlignSlots = 2048;
 constexpr int kAlignMaxRanges = 1 << (kSortKeyBits - 1);
 constexpr int kAlignRoomNum = 3, kAlignRoomDen = 2;
+// Largest room of an aligned row (entries): the compaction builds the row in
+// LDS before storing it.
+constexpr int kAlignRoomMax = 4096;
 // Smallest block size that takes the aligned lists (2-slot blocks measured
 // within 2%, single slots 4% slower with them).
 constexpr int kAlignMinBlock = 4;

@@ -164,6 +164,7 @@ __device__ __forceinline__ V ldg16(const void *p) {
 // holding -1: the tokens running at one time, whose lists have different
 // counts per range, then reach each part of the cache after about the same
 // number of tiles (their gathers share the L2), at about 25% more tiles.
+template <bool kAligned>
 __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactParams p) {
     using Load = hipcub::BlockLoad<int32_t, kSortThreads, kSortItemsPerThread,
                                    hipcub::BLOCK_LOAD_TRANSPOSE>;
@@ -178,13 +179,15 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
     __shared__ int sr_cnt[kAlignMaxRanges], sr_first[kAlignMaxRanges];
     __shared__ int sr_gap[kAlignMaxRanges], sr_start[kAlignMaxRanges];
     __shared__ int sh_end;
+    // Aligned lists: the row is built here (gaps -1) and stored in one pass.
+    __shared__ int row_stage[kAligned ? kAlignRoomMax : 1];
 
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
     const int32_t *src = p.slot_idx + t * p.stride_t;
     int32_t *dst = p.list + t * p.row_stride;
     const uint32_t pad_key = 1u << (p.key_bits - 1);
-    const bool aligned = p.align_shift >= 0 && p.W <= kSortChunk;
+    const bool aligned = kAligned && p.W <= kSortChunk && p.align_cap <= kAlignRoomMax;
     int n = 0, bad = 0, aligned_end = 0;
     for (int64_t base = 0; base < p.W; base += kSortChunk) {
         if (tid == 0) chunk_counts = 0;
@@ -244,8 +247,11 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
                 sh_end = end;
             }
             __syncthreads();
-            for (int k = 0; k < p.align_ranges; ++k)
-                for (int i = sr_gap[k] + tid; i < sr_start[k]; i += kSortThreads) dst[i] = -1;
+            // The row up to its padded end: -1 everywhere, then the entries at
+            // their places, then one coalesced store of the whole row.
+            const int row_end = (sh_end + kListPad - 1) / kListPad * kListPad;   // <= align_cap
+            for (int i = tid; i < row_end; i += kSortThreads) row_stage[i] = -1;
+            __syncthreads();
 #pragma unroll
             for (int u = 0; u < kSortItemsPerThread; ++u) {
                 const int pos = tid + kSortThreads * u;
@@ -253,10 +259,12 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
                     const int k = min((int)(key[u] >> p.align_shift), p.align_ranges - 1);
                     const int at = sr_start[k] + (pos - sr_first[k]) * p.block;
                     for (int i = 0; i < p.block; ++i)
-                        if ((unsigned)(at + i) < (unsigned)p.align_cap)
-                            dst[at + i] = (int32_t)key[u] * p.block + i;
+                        if ((unsigned)(at + i) < (unsigned)row_end)
+                            row_stage[at + i] = (int32_t)key[u] * p.block + i;
                 }
             }
+            __syncthreads();
+            for (int i = tid; i < row_end; i += kSortThreads) dst[i] = row_stage[i];
             aligned_end = sh_end;
         } else if (p.block == 1) {
 #pragma unroll
@@ -1687,7 +1695,14 @@ hipError_t launch_indexer_select(const IndexerSelectParams &p, hipStream_t strea
 
 hipError_t launch_compact(const CompactParams &p, hipStream_t stream) {
     if (p.T == 0) return hipSuccess;
-    hipLaunchKernelGGL(compact_kernel, dim3((unsigned)p.T), dim3(kSortThreads), 0, stream, p);
+    if (p.align_shift >= 0) {
+        if (p.W > kSortChunk || p.align_cap > kAlignRoomMax) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(compact_kernel<true>, dim3((unsigned)p.T), dim3(kSortThreads), 0,
+                           stream, p);
+    } else {
+        hipLaunchKernelGGL(compact_kernel<false>, dim3((unsigned)p.T), dim3(kSortThreads), 0,
+                           stream, p);
+    }
     return hipGetLastError();
 }
 
