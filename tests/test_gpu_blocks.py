@@ -213,3 +213,21 @@ def test_aligned_block_prefill_reports_invalid_blocks():
     ref = oracle.prefill_blocks(case.q, case.k_cache, case.v_cache, valid.astype(np.int32), 4,
                                 1.0 / 16.0)
     print(gate(bf16_tensor_to_f32(out), ref, ~np.any(valid >= 0, axis=1)))
+
+
+def test_wide_block_rows_take_the_plain_lists():
+    """Rows whose aligned room would exceed 4,096 entries (here 200 blocks of 16:
+    3,200 slots) run the plain lists: the aligned area stays as it was, and the
+    output meets the gate."""
+    case = block_case(1080, T=21, S=16384, Hq=16, Hkv=2, nblocks=200, bs=16, pad_frac=0.1,
+                      interior=True)
+    q, k, v, sl = upload(case, DEV)
+    nbytes = qsa.prefill_blocks_workspace_bytes(case.T, case.W, 16)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV)
+    out = qsa.sparse_prefill_blocks(q, k, v, sl, 16, scale=case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    m = qsa.workspace_layout(case.T, case.W * 16)
+    ext = -(-m["total_bytes"] // 256) * 256
+    assert torch.all(ws[ext:] == 0x7F)
+    ref = oracle.prefill_blocks(case.q, case.k_cache, case.v_cache, case.slot_idx, 16, 1.0 / 16.0)
+    print(gate(bf16_tensor_to_f32(out), ref, empty_blocks(case)))
