@@ -54,7 +54,7 @@ def test_block_sizes(bs):
                             pad_frac=0.2, interior=True))
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(24, 2), (12, 1), (3, 1)])
+@pytest.mark.parametrize("Hq,Hkv", [(24, 2), (12, 1), (3, 1), (32, 1)])
 def test_block4_head_shapes(Hq, Hkv):
     check_blocks(block_case(1020 + Hq, T=17, S=4096, Hq=Hq, Hkv=Hkv, nblocks=129, bs=4))
 
