@@ -207,3 +207,27 @@ def test_decode_over_an_empty_cache_is_zero_and_counts_entries():
     with pytest.raises(qsa.QsaError) as e:
         qsa.check_status(ws, T, W)
     assert e.value.status == 6 and "6 selection entries" in str(e.value)
+
+
+def test_decode_with_one_share_per_item():
+    """Enough tokens for one share per item (qsa_decode_splits gives 1): each
+    share reads a whole raw row, -1 padding and invalid entries included."""
+    case = qi.random_case(850, T=1100, S=5000, Hq=8, Hkv=2, W=70, pad_frac=0.2, interior=True)
+    assert qsa.decode_splits(case.T, case.W, case.Hq, case.Hkv) == 1
+    raw = case.slot_idx.copy()
+    raw[5, 3] = 5000
+    raw[700, 69] = -2
+    valid_only = np.where((raw >= 0) & (raw < case.S), raw, -1).astype(np.int32)
+    q, k, v, _ = upload(case, DEV)
+    sl = torch.from_numpy(raw).to(DEV)
+    ws = torch.empty(qsa.decode_workspace_bytes(case.T, case.W, case.Hq, case.Hkv),
+                     dtype=torch.uint8, device=DEV)
+    out = qsa.sparse_decode(q, k, v, sl, workspace=ws)
+    torch.cuda.synchronize()
+    rows = sorted(set(qi.sample_rows(case.T, 48, seed=851).tolist()) | {5, 700})
+    want = oracle.prefill(case.q, case.k_cache, case.v_cache, valid_only, 1.0 / 16.0, rows=rows)
+    got = bf16_tensor_to_f32(out[torch.as_tensor(rows, device=DEV)])
+    print(gate(got, want, empty_row_mask(valid_only, case.S, rows)))
+    with pytest.raises(qsa.QsaError) as e:
+        qsa.check_status(ws, case.T, case.W)
+    assert "2 selection entries" in str(e.value)
