@@ -118,16 +118,10 @@ struct AttendParams {
     int32_t Hq;
     float *part_o;       // [n_parts][T][Hq][256], O not yet divided by l
     float *part_ml;      // [n_parts][T][Hq][2]: running max (log2 units) and sum
-    // Gated launch (non-null share_est): each workgroup sums the sharing
-    // estimate's share_pairs (common, length) pairs and takes choice = 1 (4
-    // items per CU) if share_lambda * common < share_threshold * length; it
-    // does its work only if (choice == 1) == (choice_value == 1), so of two
-    // launches with values 0 and 1 exactly one works.  The first workgroup of
-    // the launch with value 0 stores the choice at *choice.
-    const float *share_est;
-    int32_t share_pairs;
-    float share_lambda, share_threshold;
-    int32_t *choice;
+    // Gated launch (non-null choice): the kernel does its work only if
+    // (*choice == 1) == (choice_value == 1), so of two launches with values 0
+    // and 1 exactly one works, whatever the word holds.
+    const int32_t *choice;
     int32_t choice_value;
     // Work units of the launch (items, times splits in split mode); set by
     // the launcher, which sizes the grid.

@@ -797,28 +797,7 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
     const AttendParams p) {
     using Lay = AttendLayout<kQRows, kItems>;
     __shared__ __attribute__((aligned(16))) char smem[Lay::kLds];
-    if (p.share_est != nullptr) {
-        // The layout choice from the estimate's pairs (the same sums in every
-        // workgroup of both gated launches).
-        const int lane = threadIdx.x;
-        float common = 0.0f, len = 0.0f;
-        if (lane < p.share_pairs) {
-            common = p.share_est[2 * lane];
-            len = p.share_est[2 * lane + 1];
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            common += __shfl_xor(common, off);
-            len += __shfl_xor(len, off);
-        }
-        // Every lane holds the same sums; read with the full wave active, the
-        // choice is a scalar and the return below a scalar branch (no exec
-        // mask over the rest of the kernel).
-        const int choice = __builtin_amdgcn_readfirstlane(
-            (len > 0.0f && p.share_lambda * common < p.share_threshold * len) ? 1 : 0);
-        if (p.choice_value == 0 && blockIdx.x == 0 && lane == 0) *p.choice = choice;
-        if ((choice == 1) != (p.choice_value == 1)) return;
-    }
+    if (p.choice != nullptr && ((*p.choice == 1) != (p.choice_value == 1))) return;
     if constexpr (Lay::kPersistent) {
         for (int64_t unit = blockIdx.x; unit < p.units; unit += gridDim.x) {
             wave_lds_fence();   // the previous unit's LDS reads are done
@@ -904,8 +883,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 // full goes on to the next.  A lookup reads one 32-byte bucket, so every
 // lane of a wave finishes in about the same number of steps.  The count of
 // common slots, scaled by the share of a's list that was hashed, and |L_b|
-// go to est[pair]; each workgroup of the attention's two gated launches then
-// adds them up and takes the choice (see AttendParams).
+// go to est[pair]; sharing_choice_kernel then adds them up and writes the
+// choice (see SharingParams).
 constexpr int kShareKeys = 2048;
 constexpr int kShareBuckets = 1024;
 constexpr int kShareBucketSize = 8;
@@ -1004,6 +983,23 @@ __global__ __launch_bounds__(256) void sharing_kernel(const SharingParams p) {
     }
 }
 
+// One wave: adds up the pairs' counts and writes the choice (the launch
+// boundary after sharing_kernel makes its stores visible).
+__global__ __launch_bounds__(64) void sharing_choice_kernel(const SharingParams p) {
+    const int lane = threadIdx.x;
+    float common = 0.0f, len = 0.0f;
+    if (lane < p.pairs) {
+        common = p.est[2 * lane];
+        len = p.est[2 * lane + 1];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        common += __shfl_xor(common, off);
+        len += __shfl_xor(len, off);
+    }
+    if (lane == 0)
+        *p.choice = (len > 0.0f && p.lambda_scale * common < p.threshold * len) ? 1 : 0;
+}
 
 // ---------------------------------------------------------------- gather only
 
@@ -1770,11 +1766,8 @@ hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_
     // The estimate picks one of two launches of the general layout; the other
     // returns at once.  Both compute the same bits.
     hipLaunchKernelGGL(sharing_kernel, dim3((unsigned)share->pairs), dim3(256), 0, stream, *share);
+    hipLaunchKernelGGL(sharing_choice_kernel, dim3(1), dim3(64), 0, stream, *share);
     AttendParams g = p;
-    g.share_est = share->est;
-    g.share_pairs = share->pairs;
-    g.share_lambda = share->lambda_scale;
-    g.share_threshold = share->threshold;
     g.choice = share->choice;
     g.choice_value = 0;
     if (kv == KvType::kFp8)
