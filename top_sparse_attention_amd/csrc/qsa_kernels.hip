@@ -1064,14 +1064,15 @@ __global__ __launch_bounds__(64, kAttendWavesPerSimd) void gather_only_kernel(co
 // ---------------------------------------------------------------- indexer
 
 // score[t, c] = sum_h max(0, iq[t,h] . ik[c]) with bf16 MFMA.  A workgroup
-// takes 64 tokens (16 per wave, as 4 MFMA row tiles of 4 tokens x 4 heads)
-// and one range of kScoreSplit index keys, walked in tiles of 64 blocks
-// staged in LDS (swizzled) and shared by all four row tiles; it stops at the
+// takes 128 tokens (32 per wave, as 8 MFMA row tiles of 4 tokens x 4 heads;
+// 64 measured 2% slower, each key tile then read from LDS by twice as many
+// waves per token) and one range of kScoreSplit index keys, walked in tiles
+// of 64 blocks staged in LDS (swizzled) and shared by all row tiles; it stops at the
 // last block any of its tokens may select.  MFMA rows are (token, head)
 // pairs, so lane (c, j) of a 16x16 output holds the 4 heads of one token
-// against block c and the head sum stays in the lane.  Each tile's 64 x 64
+// against block c and the head sum stays in the lane.  Each tile's 128 x 64
 // scores go through LDS and are stored as whole 256-byte row segments.
-constexpr int kScoreTokens = 64;
+constexpr int kScoreTokens = 128;
 constexpr int kScoreRowTiles = kScoreTokens / 4 / 4;   // per wave
 constexpr int kScoreTile = 64;
 constexpr int kScoreSplit = 1024;
@@ -1108,12 +1109,12 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
     const int c_end = min(c_end_shared, c_begin + kScoreSplit);
     if (c_begin >= c_end) return;
 
-    // A operands: row tile rt of this wave is tokens t0 + 16 wave + 4 rt ..+3;
+    // A operands: row tile rt of this wave is tokens t0 + 32 wave + 4 rt ..+3;
     // row r of a tile = (token r/4, head r%4), dims 32 ks + 8 j.
     bf16x8_t qa[kScoreRowTiles][4];
 #pragma unroll
     for (int rt = 0; rt < kScoreRowTiles; ++rt) {
-        const int64_t ta = t0 + 16 * wave + 4 * rt + (c >> 2);
+        const int64_t ta = t0 + (kScoreTokens / 4) * wave + 4 * rt + (c >> 2);
         const uint16_t *qrow =
             ta < p.T ? p.iq + ta * p.q_st + (int64_t)(c & 3) * p.q_sh : kZeroRow;
 #pragma unroll
@@ -1161,13 +1162,13 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
                     d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], kb[ks], d, 0, 0, 0);
                 const float score = fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) +
                                     fmaxf(d[3], 0.f);
-                out_tile[(16 * wave + 4 * rt + j) * kScoreOutPitch + 16 * ct + c] = score;
+                out_tile[((kScoreTokens / 4) * wave + 4 * rt + j) * kScoreOutPitch + 16 * ct + c] = score;
             }
         }
         __syncthreads();   // the tile's scores are complete
-        // 64 rows of 64 scores: 16 chunks of 4 per row, 4 chunks per thread.
+        // kScoreTokens rows of 64 scores: 16 chunks of 4 per row.
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kScoreTokens * (kScoreTile / 4) / 256; ++u) {
             const int idx = tid + 256 * u;
             const int r = idx >> 4, k4 = 4 * (idx & 15);
             const int64_t t_out = t0 + r;
