@@ -30,10 +30,10 @@ def kernel_asm(tmp_path_factory):
     hipcc = _hipcc()
     if hipcc is None:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "qsa_kernels.s"
+    out = tmp_path_factory.mktemp("asm") / "qsa_attend.s"
     cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
            "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "--cuda-device-only", "-S", os.path.join(CSRC, "qsa_kernels.hip"), "-o", str(out)]
+           "--cuda-device-only", "-S", os.path.join(CSRC, "qsa_attend.hip"), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True, timeout=600)
     funcs, cur = {}, None
     for line in out.read_text().splitlines():

@@ -1,4 +1,4 @@
-// HIP kernels for QSA sparse main-attention prefill on gfx950 (MI355X, CDNA4).
+// Attention kernels for QSA sparse main-attention prefill on gfx950 (MI355X, CDNA4).
 //
 // The operation is the one on the page "Qwen4-Exp QSA comes to Huawei's
 // Ascend: inside SGLang's opt-in CANN prefill PR", section "What the pull
@@ -29,9 +29,11 @@
 //     and accumulates P.V with bf16 MFMA fed by LDS transpose loads, then
 //     writes the row in BF16.  Its split form writes FP32 (O, m, l) partials
 //     of a share of the tiles instead, which merge_kernel combines.
-// Also here: gather_only_kernel (the attention's loads alone, a measurement
-// aid), and the QSA indexer that produces the selection: indexer_scores_kernel
-// (index scores with bf16 MFMA) and the Top-K selection kernels.
+// This file holds the attention kernels, their merge, the sharing estimate
+// and gather_only_kernel (the attention's loads alone, a measurement aid);
+// qsa_compact.hip holds the compaction pass and qsa_indexer.hip the QSA
+// indexer that produces the selection (index scores with bf16 MFMA and the
+// Top-K selection kernels).
 
 // MFMA orientation: scores are computed transposed, S^T = K_tile . Q^T, so
 // that one lane owns one query head (column) of the MFMA output: the row
@@ -46,27 +48,11 @@
 #include <atomic>
 #include <stdint.h>
 
-#include <hipcub/block/block_load.hpp>
-#include <hipcub/block/block_radix_sort.hpp>
-#include <hipcub/block/block_reduce.hpp>
-#include <hipcub/block/block_scan.hpp>
-
+#include "qsa_device.h"
 #include "qsa_kernels.h"
 
 namespace qsa {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
-#define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T *)(p))
 
 constexpr int kRowBytes = kHeadDim * 2;             // one BF16 row: 512 B
 constexpr int kChunksPerRow = kRowBytes / 16;       // 32 sixteen-byte chunks
@@ -94,7 +80,6 @@ struct KvGather {
 constexpr int kHeadBlock = 16;                      // query heads per MFMA column block
 constexpr int kDimBlocks = kHeadDim / 16;           // 16 output blocks of 16 dims
 constexpr int kKSteps = kHeadDim / 32;              // 8 k-steps of the score MFMA
-constexpr float kNegInf = -__builtin_huge_valf();
 // A new running maximum is adopted only when it exceeds the current one by
 // more than this (log2 units); otherwise probabilities may reach 2^8, which
 // FP32 sums and BF16 probabilities hold exactly as well.  This skips most
@@ -133,166 +118,6 @@ struct AttendLayout {
     static_assert((kItems + 1) * ((kLds + 1279) / 1280 * 1280) > 160 * 1024,
                   "one more item must not fit");
 };
-
-// A row of zeros: absent query heads (and index rows past the end) load from
-// here, so every load is unconditional and no select waits on loaded data.
-__device__ __attribute__((aligned(16))) uint16_t kZeroRow[kHeadDim] = {};
-
-// 16-byte load through the global address space (all operands of the
-// gathers, including kZeroRow, are global memory; a generic pointer would
-// turn the loads into flat loads).
-template <typename V>
-__device__ __forceinline__ V ldg16(const void *p) {
-    return *GLOBAL_PTR(V, p);
-}
-
-// ---------------------------------------------------------------- compaction
-
-// One workgroup per token row.  Entries in [lo, hi) are kept and stored as
-// slot - lo (a cache shard's local numbering; lo = 0, hi = S keeps them
-// all); entries that are neither -1 nor in [0, S) are counted as invalid.
-// With block > 1 an entry names a micro-block of `block` consecutive slots
-// (S, lo, hi then count blocks) and expands to those slots in order.
-// The row is processed in chunks of
-// kSortChunk entries; each chunk's valid slots are radix-sorted on the top
-// kSortKeyBits bits of a key_bits-wide key (invalid entries carry the key
-// 2^(key_bits-1), so they sort last), i.e. grouped into at most 128 ascending
-// slot ranges, stable inside a range, and appended to the compacted list.
-// Two radix passes; a full sort would cost more and buys no locality.
-// Aligned lists (align_shift >= 0, one run per row) place each super-range of
-// about kAlignSlots slots near a fixed position of the row instead, the gaps
-// holding -1: the tokens running at one time, whose lists have different
-// counts per range, then reach each part of the cache after about the same
-// number of tiles (their gathers share the L2), at about 25% more tiles.
-template <bool kAligned>
-__global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactParams p) {
-    using Load = hipcub::BlockLoad<int32_t, kSortThreads, kSortItemsPerThread,
-                                   hipcub::BLOCK_LOAD_TRANSPOSE>;
-    using Sort = hipcub::BlockRadixSort<uint32_t, kSortThreads, kSortItemsPerThread>;
-    __shared__ union {
-        typename Load::TempStorage load;
-        typename Sort::TempStorage sort;
-    } tmp;
-    __shared__ int chunk_counts;   // valid entries | invalid entries << 16
-    // Aligned lists: per super-range its entry count, first rank, the start
-    // of the gap before it and its start (slot positions); the row's end.
-    __shared__ int sr_cnt[kAlignMaxRanges], sr_first[kAlignMaxRanges];
-    __shared__ int sr_gap[kAlignMaxRanges], sr_start[kAlignMaxRanges];
-    __shared__ int sh_end;
-    // Aligned lists: the row is built here (gaps -1) and stored in one pass.
-    __shared__ int row_stage[kAligned ? kAlignRoomMax : 1];
-
-    const int64_t t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int32_t *src = p.slot_idx + t * p.stride_t;
-    int32_t *dst = p.list + t * p.row_stride;
-    const uint32_t pad_key = 1u << (p.key_bits - 1);
-    const bool aligned = kAligned && p.W <= kSortChunk && p.align_cap <= kAlignRoomMax;
-    int n = 0, bad = 0, aligned_end = 0;
-    for (int64_t base = 0; base < p.W; base += kSortChunk) {
-        if (tid == 0) chunk_counts = 0;
-        // Coalesced loads, handed to the sort in blocked order (thread t holds
-        // entries 9t .. 9t + 8 of the run), so the sort is stable in the
-        // row's order.
-        int32_t e[kSortItemsPerThread];
-        Load(tmp.load).Load(src + base, e, (int)min<int64_t>(kSortChunk, p.W - base), -1);
-        __syncthreads();   // the load's staging area is reused by the sort
-        uint32_t key[kSortItemsPerThread];
-        int my_valid = 0, my_bad = 0;
-#pragma unroll
-        for (int u = 0; u < kSortItemsPerThread; ++u) {
-            const bool in_cache = e[u] >= 0 && (int64_t)e[u] < p.S;
-            const bool keep = in_cache && (int64_t)e[u] >= p.lo && (int64_t)e[u] < p.hi;
-            my_valid += keep;
-            my_bad += !in_cache && e[u] != -1;
-            key[u] = keep ? (uint32_t)((int64_t)e[u] - p.lo) : pad_key;
-        }
-        // Both counts (each < 2^16 per run) in one word, summed per wave.
-        int packed = my_valid | (my_bad << 16);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) packed += __shfl_xor(packed, off);
-        if ((tid & 63) == 0) atomicAdd(&chunk_counts, packed);
-        // Sorted keys come back striped: thread t holds ranks t, t + 256, ...,
-        // so the stores below are coalesced.
-        Sort(tmp.sort).SortBlockedToStriped(key, max(p.key_bits - kSortKeyBits, 0), p.key_bits);
-        __syncthreads();   // the counts above are complete
-        const int nv = chunk_counts & 0xffff;
-        const int nb = chunk_counts >> 16;
-        if (aligned) {
-            // One run holds the row.  Entries per super-range, then (one
-            // thread, at most kAlignMaxRanges steps) where each starts.
-            for (int i = tid; i < kAlignMaxRanges; i += kSortThreads) sr_cnt[i] = 0;
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < kSortItemsPerThread; ++u) {
-                const int pos = tid + kSortThreads * u;
-                if (pos < nv) atomicAdd(&sr_cnt[min((int)(key[u] >> p.align_shift), p.align_ranges - 1)], 1);
-            }
-            __syncthreads();
-            if (tid == 0) {
-                const int slots = nv * p.block, R = p.align_ranges;
-                const int F = (5 * slots + 4 * R - 1) / (4 * R);   // 1.25 x the mean, rounded up
-                int end = 0, first = 0, rem = slots;
-                for (int k = 0; k < R; ++k) {
-                    const int cs = sr_cnt[k] * p.block;
-                    // end + rem <= align_cap holds before and after each step.
-                    const int start = cs > 0 ? max(end, min(k * F, p.align_cap - rem)) : end;
-                    sr_gap[k] = end;
-                    sr_start[k] = start;
-                    sr_first[k] = first;
-                    end = start + cs;
-                    first += sr_cnt[k];
-                    rem -= cs;
-                }
-                sh_end = end;
-            }
-            __syncthreads();
-            // The row up to its padded end: -1 everywhere, then the entries at
-            // their places, then one coalesced store of the whole row.
-            const int row_end = (sh_end + kListPad - 1) / kListPad * kListPad;   // <= align_cap
-            for (int i = tid; i < row_end; i += kSortThreads) row_stage[i] = -1;
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < kSortItemsPerThread; ++u) {
-                const int pos = tid + kSortThreads * u;
-                if (pos < nv) {
-                    const int k = min((int)(key[u] >> p.align_shift), p.align_ranges - 1);
-                    const int at = sr_start[k] + (pos - sr_first[k]) * p.block;
-                    for (int i = 0; i < p.block; ++i)
-                        if ((unsigned)(at + i) < (unsigned)row_end)
-                            row_stage[at + i] = (int32_t)key[u] * p.block + i;
-                }
-            }
-            __syncthreads();
-            for (int i = tid; i < row_end; i += kSortThreads) dst[i] = row_stage[i];
-            aligned_end = sh_end;
-        } else if (p.block == 1) {
-#pragma unroll
-            for (int u = 0; u < kSortItemsPerThread; ++u) {
-                const int pos = tid + kSortThreads * u;
-                if (pos < nv) dst[n + pos] = (int32_t)key[u];
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < kSortItemsPerThread; ++u) {
-                const int pos = tid + kSortThreads * u;
-                if (pos < nv)
-                    for (int i = 0; i < p.block; ++i)
-                        dst[(int64_t)(n + pos) * p.block + i] = (int32_t)key[u] * p.block + i;
-            }
-        }
-        n += nv;
-        bad += nb;
-        __syncthreads();   // the counts are reset by the next run
-    }
-    const int slots = aligned ? aligned_end : n * p.block;
-    const int padded = (slots + kListPad - 1) / kListPad * kListPad;
-    for (int i = slots + tid; i < padded; i += kSortThreads) dst[i] = -1;
-    if (tid == 0) {
-        p.count[t] = slots;
-        p.n_bad[t] = bad;
-    }
-}
 
 // ---------------------------------------------------------------- gathers
 
@@ -426,11 +251,6 @@ __device__ __forceinline__ void stage_v(const u32x4_t (&rv)[KvGather<KV>::kVLoad
     }
 }
 
-__device__ __forceinline__ void wave_lds_fence() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // List entry of tile row (lane & 15) for tile `tile`: -1 for the padding of
 // the last tile, 0 for a tile past the list (a prefetch that is never used).
@@ -1061,653 +881,8 @@ __global__ __launch_bounds__(64, kAttendWavesPerSimd) void gather_only_kernel(co
     if (lane == 0) p.sink[item] = smem[63];
 }
 
-// ---------------------------------------------------------------- indexer
-
-// score[t, c] = sum_h max(0, iq[t,h] . ik[c]) with bf16 MFMA.  A workgroup
-// takes 128 tokens (32 per wave, as 8 MFMA row tiles of 4 tokens x 4 heads;
-// 64 measured 2% slower, each key tile then read from LDS by twice as many
-// waves per token) and one range of kScoreSplit index keys, walked in tiles
-// of 64 blocks staged in LDS (swizzled) and shared by all row tiles; it stops at the
-// last block any of its tokens may select.  MFMA rows are (token, head)
-// pairs, so lane (c, j) of a 16x16 output holds the 4 heads of one token
-// against block c and the head sum stays in the lane.  Each tile's 128 x 64
-// scores go through LDS and are stored as whole 256-byte row segments.
-constexpr int kScoreTokens = 128;
-constexpr int kScoreRowTiles = kScoreTokens / 4 / 4;   // per wave
-constexpr int kScoreTile = 64;
-constexpr int kScoreSplit = 1024;
-constexpr int kIndexRowBytes = kIndexDim * 2;   // 256 B
-constexpr int kScoreOutPitch = kScoreTile + 4;  // floats per staged row (16-byte aligned)
-
-// LDS byte offset of 16-byte chunk `chunk` of index-key tile row `r`.  The
-// chunk index is XOR-swizzled by a bijection of r & 7 so that the 8 rows read
-// by one phase of a 16-byte read hit 8 different bank groups.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-__device__ __forceinline__ int idx_off(int r, int chunk) {
-    return r * kIndexRowBytes + ((chunk ^ swz(r)) << 4);
-}
-
-__global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreParams p) {
-    // One key tile: the barrier after each tile's scores also orders its reads
-    // before the next tile is written.
-    __shared__ __attribute__((aligned(16))) char tile[kScoreTile * kIndexRowBytes];
-    __shared__ __attribute__((aligned(16))) float out_tile[kScoreTokens * kScoreOutPitch];
-    __shared__ int c_end_shared;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int c = lane & 15, j = lane >> 4;
-    const int64_t t0 = (int64_t)blockIdx.x * kScoreTokens;
-    const int c_begin = blockIdx.y * kScoreSplit;
-
-    if (tid == 0) c_end_shared = 0;
-    __syncthreads();
-    if (tid < kScoreTokens && t0 + tid < p.T) {
-        const int64_t lim = ((int64_t)p.positions[t0 + tid] + 1) / kIndexBlock;
-        atomicMax(&c_end_shared, (int)min<int64_t>(lim, p.C));
-    }
-    __syncthreads();
-    const int c_end = min(c_end_shared, c_begin + kScoreSplit);
-    if (c_begin >= c_end) return;
-
-    // A operands: row tile rt of this wave is tokens t0 + 32 wave + 4 rt ..+3;
-    // row r of a tile = (token r/4, head r%4), dims 32 ks + 8 j.
-    bf16x8_t qa[kScoreRowTiles][4];
-#pragma unroll
-    for (int rt = 0; rt < kScoreRowTiles; ++rt) {
-        const int64_t ta = t0 + (kScoreTokens / 4) * wave + 4 * rt + (c >> 2);
-        const uint16_t *qrow =
-            ta < p.T ? p.iq + ta * p.q_st + (int64_t)(c & 3) * p.q_sh : kZeroRow;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qa[rt][ks] = ldg16<bf16x8_t>(qrow + 32 * ks + 8 * j);
-    }
-
-    // Staging: 64 rows x 16 chunks = 1024 chunks, 4 per thread.
-    auto load_tile = [&](int c0, u32x4_t (&r)[4]) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = tid + 256 * u;
-            const int row = idx >> 4, ch = idx & 15;
-            const int64_t blk = c0 + row;
-            const uint16_t *src = blk < c_end ? p.ik + blk * p.k_st + ch * 8 : kZeroRow + ch * 8;
-            r[u] = ldg16<u32x4_t>(src);
-        }
-    };
-    auto store_tile = [&](char *dst, const u32x4_t (&r)[4]) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = tid + 256 * u;
-            *LDS_PTR(u32x4_t, dst + idx_off(idx >> 4, idx & 15)) = r[u];
-        }
-    };
-    // The staged scores go out as 16-byte stores where the rows allow it.
-    const bool vec_out = (p.C % 4) == 0 && ((uintptr_t)p.scores % 16) == 0;
-
-    u32x4_t stage[4];
-    load_tile(c_begin, stage);
-    for (int c0 = c_begin; c0 < c_end; c0 += kScoreTile) {
-        store_tile(tile, stage);
-        __syncthreads();   // the key tile is staged; the previous scores are stored
-        if (c0 + kScoreTile < c_end) load_tile(c0 + kScoreTile, stage);
-#pragma unroll
-        for (int ct = 0; ct < kScoreTile / 16; ++ct) {
-            bf16x8_t kb[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                kb[ks] = *LDS_PTR(bf16x8_t, tile + idx_off(16 * ct + c, 4 * ks + j));
-#pragma unroll
-            for (int rt = 0; rt < kScoreRowTiles; ++rt) {
-                f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], kb[ks], d, 0, 0, 0);
-                const float score = fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) +
-                                    fmaxf(d[3], 0.f);
-                out_tile[((kScoreTokens / 4) * wave + 4 * rt + j) * kScoreOutPitch + 16 * ct + c] = score;
-            }
-        }
-        __syncthreads();   // the tile's scores are complete
-        // kScoreTokens rows of 64 scores: 16 chunks of 4 per row.
-#pragma unroll
-        for (int u = 0; u < kScoreTokens * (kScoreTile / 4) / 256; ++u) {
-            const int idx = tid + 256 * u;
-            const int r = idx >> 4, k4 = 4 * (idx & 15);
-            const int64_t t_out = t0 + r;
-            const int64_t blk = c0 + k4;
-            if (t_out < p.T && blk < c_end) {
-                const f32x4_t v = *(const f32x4_t *)(out_tile + r * kScoreOutPitch + k4);
-                float *dst = p.scores + t_out * p.C + blk;
-                if (vec_out && blk + 3 < c_end) {
-                    *(f32x4_t *)dst = v;
-                } else {
-                    for (int e = 0; e < 4 && blk + e < c_end; ++e) dst[e] = v[e];
-                }
-            }
-        }
-    }
-}
-
-// Order-preserving map of FP32 to uint32 (larger float -> larger key).
-__device__ __forceinline__ uint32_t score_key(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Find, among the keys of `n` scores that pass `in_set`, the `need`-th largest
-// key tau and how many keys equal to tau must be kept (written to sh_prefix /
-// sh_need), with 8-bit-digit radix passes.  hist is 256 ints of LDS.  With
-// kPasses < 4 only the top 8 * kPasses bits are resolved: the result is the
-// need-th largest key with its other bits cleared (a lower bound of it).
-template <int kPasses = 4, typename ScoreAt, typename InSet>
-__device__ void radix_select(int n, int need, ScoreAt score_at, InSet in_set, int *hist,
-                             uint32_t *sh_prefix, int *sh_need) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0, mask = 0;
-    for (int shift = 24; shift >= 32 - 8 * kPasses; shift -= 8) {
-        hist[tid] = 0;
-        __syncthreads();
-        for (int i0 = 0; i0 < n; i0 += 256) {
-            const int i = i0 + tid;
-            bool hit = false;
-            int digit = 0;
-            if (i < n) {
-                const float x = score_at(i);
-                const uint32_t u = score_key(x);
-                hit = in_set(x) && (u & mask) == prefix;
-                digit = (u >> shift) & 255;
-            }
-            // The keys of a row share their leading digits, so most lanes
-            // of a wave hit the same bin: the lanes with the first active
-            // lane's digit add their count with one atomic.
-            const uint64_t active = __ballot(hit);
-            if (active) {
-                const int lead = __builtin_amdgcn_readlane(digit, __builtin_ctzll(active));
-                const uint64_t same = __ballot(hit && digit == lead);
-                if (hit && digit == lead) {
-                    if ((tid & 63) == __builtin_ctzll(same))
-                        atomicAdd(&hist[lead], (int)__popcll(same));
-                } else if (hit) {
-                    atomicAdd(&hist[digit], 1);
-                }
-            }
-        }
-        __syncthreads();
-        if (tid < 64) {
-            // lane l owns digits 4l..4l+3; suffix sums from the top digit.
-            const int cnt = hist[4 * tid] + hist[4 * tid + 1] + hist[4 * tid + 2] + hist[4 * tid + 3];
-            int incl = cnt;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int v = __shfl_down(incl, off);
-                if (tid + off < 64) incl += v;
-            }
-            const int above = incl - cnt;   // keys with higher digits
-            if (above < need && need <= incl) {
-                int cum = above, d = 4 * tid + 3;
-                while (cum + hist[d] < need) cum += hist[d--];
-                *sh_prefix = prefix | ((uint32_t)d << shift);
-                *sh_need = need - cum;
-            }
-        }
-        __syncthreads();
-        prefix = *sh_prefix;
-        need = *sh_need;
-        mask |= 0xffu << shift;
-        __syncthreads();
-    }
-}
-
-// Per query token: keep the `budget` highest-scoring complete causal blocks
-// (ties to the lower block); write their positions in ascending block order,
-// the causal tail, slot-mapped, then -1 padding.
-//
-// select_exact (the whole workgroup, one row of n >= 0 eligible scores)
-// writes the kept block ids, in ascending order, at out[4 e] for
-// e < min(n, budget); expand_row then turns them into slots.  Its threshold
-// is found in two steps: a histogram of 256 buckets that split
-// [min, max] of the row linearly (a monotone map, so whole buckets above the
-// threshold's bucket are kept and those below dropped), then an exact radix
-// select over the keys of that one bucket.  Scores of a row sit in a narrow
-// float range, so a radix pass over raw key bits would pile every key into
-// one or two bins; the linear buckets spread them.
-template <bool kInLds>
-__device__ void select_exact(const IndexerSelectParams &p, int n, const float *row, int32_t *out) {
-    using Scan = hipcub::BlockScan<int, 256>;
-    using Reduce = hipcub::BlockReduce<float, 256>;
-    __shared__ float vals[kInLds ? kSelectLdsBlocks : 1];
-    __shared__ int hist[256];
-    __shared__ int chunk_gt[256], chunk_eq[256];
-    __shared__ union {
-        typename Scan::TempStorage scan;
-        typename Reduce::TempStorage reduce;
-    } tmp;
-    __shared__ uint32_t sh_prefix;
-    __shared__ int sh_need;
-    __shared__ float sh_lo, sh_hi;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    // Row statistics (and the LDS copy): 16-byte loads, four in flight per
-    // thread, so the row arrives in a few memory round trips.
-    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
-    const bool vec_ok = ((uintptr_t)row % 16) == 0;
-    const int n4 = vec_ok ? n / 4 : 0;
-    for (int base = 0; base < n4; base += 4 * 256) {
-        f32x4_t v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i4 = base + u * 256 + tid;
-            v[u] = i4 < n4 ? *(const f32x4_t *)(row + 4 * i4)
-                           : f32x4_t{lo, lo, lo, lo};
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i4 = base + u * 256 + tid;
-            if (i4 < n4) {
-                if (kInLds) *(f32x4_t *)(vals + 4 * i4) = v[u];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lo = fminf(lo, v[u][e]);
-                    hi = fmaxf(hi, v[u][e]);
-                }
-            }
-        }
-    }
-    for (int i = 4 * n4 + tid; i < n; i += 256) {
-        const float x = row[i];
-        if (kInLds) vals[i] = x;
-        lo = fminf(lo, x);
-        hi = fmaxf(hi, x);
-    }
-    auto score_at = [&](int i) -> float { return kInLds ? vals[i] : row[i]; };
-
-    // Threshold key tau and how many keys equal to tau to keep (`need`).
-    uint32_t tau = 0;
-    int need = n;   // n <= budget: every key (all > 0) is kept
-    if (n > p.budget) {
-        lo = Reduce(tmp.reduce).Reduce(lo, [](float a, float b) { return fminf(a, b); });
-        __syncthreads();
-        hi = Reduce(tmp.reduce).Reduce(hi, [](float a, float b) { return fmaxf(a, b); });
-        if (tid == 0) {
-            sh_lo = lo;
-            sh_hi = hi;
-        }
-        __syncthreads();
-        lo = sh_lo;
-        hi = sh_hi;
-        const float inv = hi > lo ? 256.0f / (hi - lo) : 0.0f;
-        auto bucket = [&](float x) { return min(255, (int)((x - lo) * inv)); };
-        // Step 1: the bucket holding the budget-th largest score.
-        hist[tid] = 0;
-        __syncthreads();
-        for (int i = tid; i < n; i += 256) atomicAdd(&hist[bucket(score_at(i))], 1);
-        __syncthreads();
-        if (tid < 64) {
-            const int cnt = hist[4 * tid] + hist[4 * tid + 1] + hist[4 * tid + 2] + hist[4 * tid + 3];
-            int incl = cnt;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int v = __shfl_down(incl, off);
-                if (tid + off < 64) incl += v;
-            }
-            const int above = incl - cnt;
-            if (above < p.budget && p.budget <= incl) {
-                int cum = above, d = 4 * tid + 3;
-                while (cum + hist[d] < p.budget) cum += hist[d--];
-                sh_prefix = (uint32_t)d;
-                sh_need = p.budget - cum;
-            }
-        }
-        __syncthreads();
-        const int b_star = (int)sh_prefix;
-        need = sh_need;
-        __syncthreads();
-        // Step 2: exact select inside that bucket.
-        radix_select(n, need, score_at, [&](float x) { return bucket(x) == b_star; }, hist,
-                     &sh_prefix, &sh_need);
-        tau = sh_prefix;
-        need = sh_need;
-    }
-    __syncthreads();   // vals written by other threads are read below
-
-    // Keep key > tau, and the first `need` keys == tau in block order.  The
-    // row is read in chunks of 64 blocks (one per lane); per-chunk counts are
-    // scanned so every kept block knows its output position.  Chunks are
-    // handled in groups of 256 (one count per thread).
-    int gt_before = 0, eq_before = 0;   // keys > tau / == tau in earlier groups
-    const int nchunks = (n + 63) / 64;
-    for (int g0 = 0; g0 < nchunks; g0 += 256) {
-        const int gn = min(256, nchunks - g0);
-        for (int k = wave; k < gn; k += 4) {
-            const int i = (g0 + k) * 64 + lane;
-            const uint32_t u = i < n ? score_key(score_at(i)) : 0u;
-            const uint64_t gt = __ballot(i < n && u > tau);
-            const uint64_t eq = __ballot(i < n && u == tau);
-            if (lane == 0) {
-                chunk_gt[k] = __popcll(gt);
-                chunk_eq[k] = __popcll(eq);
-            }
-        }
-        __syncthreads();
-        int my_gt = tid < gn ? chunk_gt[tid] : 0, my_eq = tid < gn ? chunk_eq[tid] : 0;
-        int gt_pre, eq_pre, gt_tot, eq_tot;
-        Scan(tmp.scan).ExclusiveSum(my_gt, gt_pre, gt_tot);
-        __syncthreads();
-        Scan(tmp.scan).ExclusiveSum(my_eq, eq_pre, eq_tot);
-        __syncthreads();
-        if (tid < gn) {
-            chunk_gt[tid] = gt_pre;
-            chunk_eq[tid] = eq_pre;
-        }
-        __syncthreads();
-        const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-        for (int k = wave; k < gn; k += 4) {
-            const int i = (g0 + k) * 64 + lane;
-            const uint32_t u = i < n ? score_key(score_at(i)) : 0u;
-            const bool is_gt = i < n && u > tau, is_eq = i < n && u == tau;
-            const uint64_t eq_mask = __ballot(is_eq);
-            const int eq_rank = eq_before + chunk_eq[k] + __popcll(eq_mask & below);
-            const bool keep = is_gt || (is_eq && eq_rank < need);
-            const uint64_t keep_mask = __ballot(keep);
-            const int eq_prior = eq_before + chunk_eq[k];
-            // kept before this lane = all keys > tau before it + the first
-            // `need` keys == tau before it
-            const int w = gt_before + chunk_gt[k] + min(eq_prior, need) +
-                          __popcll(keep_mask & below);
-            if (keep) out[kIndexBlock * w] = i;   // block id for now, expanded below
-        }
-        gt_before += gt_tot;
-        eq_before += eq_tot;
-        __syncthreads();   // chunk counts are rewritten by the next group
-    }
-}
-
-// Expand every kept block id (written at out[4 e], e < kept) into its 4 slots,
-// then write the causal tail and the -1 padding.  All the slot-table reads of
-// the row are independent and in flight together.
-__device__ void expand_row(const IndexerSelectParams &p, int64_t pos, int kept, int32_t *out,
-                           int width) {
-    const int tid = threadIdx.x;
-    __threadfence_block();
-    __syncthreads();
-    const bool vec_ok = ((uintptr_t)p.slot_of_pos % 16) == 0 && ((uintptr_t)out % 16) == 0;
-    for (int e = tid; e < kept; e += 256) {
-        const int64_t blk = out[kIndexBlock * e];
-        const int32_t *src = p.slot_of_pos + kIndexBlock * blk;
-        if (vec_ok) {
-            *(u32x4_t *)(out + kIndexBlock * e) = *(const u32x4_t *)src;
-        } else {
-            int32_t sl[kIndexBlock];
-#pragma unroll
-            for (int q = 0; q < kIndexBlock; ++q) sl[q] = src[q];
-#pragma unroll
-            for (int q = 0; q < kIndexBlock; ++q) out[kIndexBlock * e + q] = sl[q];
-        }
-    }
-    const int r = (int)((pos + 1) % kIndexBlock);
-    const int tail0 = kIndexBlock * kept;
-    for (int i = tid; i < width - tail0; i += 256)
-        out[tail0 + i] = i < r ? p.slot_of_pos[pos - r + 1 + i] : -1;
-}
-
-// Marks, in the first output word, a row that indexer_select_fast_kernel
-// left to the exact selection (no output word holds a value below -1).
-constexpr int32_t kSelDeferred = INT32_MIN;
-
-// kDeferredOnly: a second launch after indexer_select_fast_kernel that
-// selects only the rows it deferred (the others return at once).
-template <bool kInLds, bool kDeferredOnly = false>
-__global__ __launch_bounds__(256) void indexer_select_kernel(const IndexerSelectParams p) {
-    const int64_t t = blockIdx.x;
-    const int64_t pos = p.positions[t];
-    int32_t *out = p.out + t * p.out_stride;
-    const int width = kIndexBlock * p.budget + 3;
-    if (kDeferredOnly) {
-        if (out[0] != kSelDeferred) return;   // the same word for every thread
-        __syncthreads();                       // read by all before it is rewritten
-    }
-    if (pos < 0 || pos >= p.L) {
-        for (int i = threadIdx.x; i < width; i += 256) out[i] = -1;
-        return;
-    }
-    const int n = (int)min<int64_t>((pos + 1) / kIndexBlock, p.C);
-    select_exact<kInLds>(p, n, p.scores + t * p.C, out);
-    expand_row(p, pos, min(n, p.budget), out, width);
-}
-
-// The same selection, faster for budgets up to kCand / 4: the threshold
-// is first estimated from kSelSample scores in runs spaced evenly over the row (the
-// top 16 bits of the key ranked about 2 * budget * kSelSample / n from the
-// top); one pass over the row then keeps, in block order, the scores whose
-// key is at least the estimate (about 2 * budget of them), and the exact
-// selection runs on that short list.  It is exact whenever at least `budget` scores pass the
-// estimate (the budget-th largest key and all its ties then pass); rows where
-// fewer pass, or more than kCand, take select_exact.  Two sizes: kSelCandSmall
-// (budgets up to 512, the page's budget) takes 19.5 KB of LDS and 94
-// registers, 5 workgroups per CU, and defers those rows (kDefer: it marks
-// them with kSelDeferred and a second launch selects them), since the exact
-// selection inlined here would take 4 KB more LDS and 30 more registers;
-// kSelCand takes budgets up to 960 at 4 per CU and selects them in place.
-// (Held to 64 registers for 8 per CU the small kernel ran twice as slowly.)
-constexpr int kSelSample = 1024;
-constexpr int kSelCand = 3840;        // multiples of 256
-constexpr int kSelCandSmall = 2048;
-constexpr int kSelPerThread = 16;   // scores per thread per pass over the row
-// Candidate i is stored at i + i / 16: the output pass, where thread t reads
-// candidates kPer t .. kPer t + kPer - 1, then reads different banks.
-__device__ __forceinline__ int cand_at(int i) { return i + (i >> 4); }
-
-template <int kCand, int kWavesPerSimd, bool kDefer>
-__global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel(
-    const IndexerSelectParams p) {
-    static_assert(kCand % 256 == 0 && kCand >= kSelSample, "candidate list");
-    // One 16-byte sample load per thread; runs 16 apart or more once n > kCand >= kSelSample.
-    static_assert(kSelSample == 4 * 256, "sample runs");
-    constexpr int kCandPadded = kCand + kCand / 16;
-    using Scan = hipcub::BlockScan<int, 256>;
-    __shared__ float cval[kCandPadded];
-    __shared__ int cid[kCandPadded];
-    __shared__ int hist[256];
-    __shared__ typename Scan::TempStorage scan;
-    __shared__ uint32_t sh_prefix;
-    __shared__ int sh_need;
-
-    const int64_t t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int64_t pos = p.positions[t];
-    int32_t *out = p.out + t * p.out_stride;
-    const int width = kIndexBlock * p.budget + 3;
-    if (pos < 0 || pos >= p.L) {
-        for (int i = tid; i < width; i += 256) out[i] = -1;
-        return;
-    }
-    const int n = (int)min<int64_t>((pos + 1) / kIndexBlock, p.C);
-    const float *row = p.scores + t * p.C;
-    auto all = [](float) { return true; };
-
-    // Scores [base, base + kSlice) of the row, kSelPerThread consecutive ones
-    // per thread (16-byte loads where aligned).
-    const bool vec_ok = ((uintptr_t)row % 16) == 0;
-    constexpr int kSlice = 256 * kSelPerThread;
-    auto load_slice = [&](int base, float (&v)[kSelPerThread]) {
-        const int i0 = base + kSelPerThread * tid;
-#pragma unroll
-        for (int u = 0; u < kSelPerThread / 4; ++u) {
-            const int i = i0 + 4 * u;
-            if (vec_ok && i + 3 < n) {
-                const f32x4_t x = *(const f32x4_t *)(row + i);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * u + e] = x[e];
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[4 * u + e] = i + e < n ? row[i + e] : 0.0f;
-            }
-        }
-    };
-
-    if (n <= p.budget) {
-        for (int e = tid; e < n; e += 256) out[kIndexBlock * e] = e;
-    } else {
-        // The first two slices are in flight while the threshold is estimated.
-        float v[kSelPerThread], v1[kSelPerThread];
-        load_slice(0, v);
-        if (kSlice < n) load_slice(kSlice, v1);
-        // 1. Estimated threshold (every key passes when the row fits the list).
-        uint32_t tau0 = 0;
-        if (n > kCand) {
-            // The sample: kSelSample / 16 runs of 16 consecutive scores (64
-            // bytes), evenly spaced over the row and aligned to 16 scores.  A
-            // strided sample would touch every cache line of the row, which
-            // the pass below then fetches a second time.  Thread k loads
-            // scores 4 (k % 4) .. + 3 of run k / 4 (n > kCand keeps the runs
-            // distinct and inside the row).
-            constexpr int kRuns = kSelSample / 16;
-            const int start = (int)((int64_t)(tid >> 2) * (n - 16) / (kRuns - 1)) & ~15;
-            const int i = start + 4 * (tid & 3);
-            f32x4_t x;
-            if (vec_ok) {
-                x = *(const f32x4_t *)(row + i);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = row[i + e];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) cval[4 * tid + e] = x[e];
-            __syncthreads();
-            const int kth =
-                (int)min<int64_t>(kSelSample, (2 * (int64_t)p.budget * kSelSample + n - 1) / n);
-            radix_select<2>(kSelSample, kth, [&](int i) { return cval[i]; }, all, hist,
-                            &sh_prefix, &sh_need);
-            tau0 = sh_prefix;
-        }
-        // 2. Candidates in block order: each thread takes kSelPerThread
-        // consecutive scores per slice, the next two slices loading while
-        // this one is placed by a block scan of the per-thread counts.
-        int nc = 0;
-        for (int base = 0; base < n; base += kSlice) {
-            float v2[kSelPerThread];
-            if (base + 2 * kSlice < n) load_slice(base + 2 * kSlice, v2);
-            const int i0 = base + kSelPerThread * tid;
-            int cnt = 0;
-#pragma unroll
-            for (int e = 0; e < kSelPerThread; ++e)
-                cnt += i0 + e < n && score_key(v[e]) >= tau0;
-            int off, total;
-            Scan(scan).ExclusiveSum(cnt, off, total);
-            if (nc + total <= kCand) {
-                int w = nc + off;
-#pragma unroll
-                for (int e = 0; e < kSelPerThread; ++e) {
-                    if (i0 + e < n && score_key(v[e]) >= tau0) {
-                        cval[cand_at(w)] = v[e];
-                        cid[cand_at(w)] = i0 + e;
-                        ++w;
-                    }
-                }
-            }
-            nc += total;
-            __syncthreads();   // the scan storage is reused
-#pragma unroll
-            for (int e = 0; e < kSelPerThread; ++e) {
-                v[e] = v1[e];
-                v1[e] = v2[e];
-            }
-        }
-
-        if (nc < p.budget || nc > kCand) {
-            if constexpr (kDefer) {
-                if (tid == 0) out[0] = kSelDeferred;
-                return;
-            } else {
-                select_exact<false>(p, n, row, out);
-            }
-        } else {
-            // 3. Exact threshold key tau among the candidates and how many
-            // keys equal to tau to keep.
-            radix_select(nc, p.budget, [&](int i) { return cval[cand_at(i)]; }, all, hist,
-                         &sh_prefix, &sh_need);
-            const uint32_t tau = sh_prefix;
-            const int need = sh_need;
-            // 4. Output in block order.  Thread t owns candidates
-            // [kPer t, kPer (t + 1)); a kept candidate's position is the
-            // number of keys > tau before it plus the number of kept ties
-            // (the first `need` in block order) before it.
-            constexpr int kPer = kCand / 256;
-            int gt = 0, eq = 0;
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                const int i = kPer * tid + k;
-                if (i < nc) {
-                    const uint32_t u = score_key(cval[cand_at(i)]);
-                    gt += u > tau;
-                    eq += u == tau;
-                }
-            }
-            int gt_pre, eq_pre, total;
-            Scan(scan).ExclusiveSum(gt, gt_pre, total);
-            __syncthreads();
-            Scan(scan).ExclusiveSum(eq, eq_pre, total);
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                const int i = kPer * tid + k;
-                if (i < nc) {
-                    const uint32_t u = score_key(cval[cand_at(i)]);
-                    if (u > tau) {
-                        out[kIndexBlock * (gt_pre + min(eq_pre, need))] = cid[cand_at(i)];
-                        ++gt_pre;
-                    } else if (u == tau) {
-                        if (eq_pre < need) out[kIndexBlock * (gt_pre + eq_pre)] = cid[cand_at(i)];
-                        ++eq_pre;
-                    }
-                }
-            }
-        }
-    }
-    expand_row(p, pos, min(n, p.budget), out, width);
-}
-
 }  // namespace
 
-hipError_t launch_indexer_scores(const IndexerScoreParams &p, hipStream_t stream) {
-    if (p.T == 0 || p.C == 0) return hipSuccess;
-    const int64_t blocks = (p.T + kScoreTokens - 1) / kScoreTokens;
-    const int64_t splits = (p.C + kScoreSplit - 1) / kScoreSplit;
-    hipLaunchKernelGGL(indexer_scores_kernel, dim3((unsigned)blocks, (unsigned)splits), dim3(256),
-                       0, stream, p);
-    return hipGetLastError();
-}
-
-hipError_t launch_indexer_select(const IndexerSelectParams &p, hipStream_t stream) {
-    if (p.T == 0) return hipSuccess;
-    if (4 * (int64_t)p.budget <= kSelCandSmall) {
-        hipLaunchKernelGGL((indexer_select_fast_kernel<kSelCandSmall, 4, true>),
-                           dim3((unsigned)p.T), dim3(256), 0, stream, p);
-        hipLaunchKernelGGL((indexer_select_kernel<false, true>), dim3((unsigned)p.T), dim3(256),
-                           0, stream, p);
-    } else if (4 * (int64_t)p.budget <= kSelCand)
-        hipLaunchKernelGGL((indexer_select_fast_kernel<kSelCand, 4, false>), dim3((unsigned)p.T),
-                           dim3(256), 0, stream, p);
-    else if (p.C <= kSelectLdsBlocks)
-        hipLaunchKernelGGL(indexer_select_kernel<true>, dim3((unsigned)p.T), dim3(256), 0, stream,
-                           p);
-    else
-        hipLaunchKernelGGL(indexer_select_kernel<false>, dim3((unsigned)p.T), dim3(256), 0,
-                           stream, p);
-    return hipGetLastError();
-}
-
-hipError_t launch_compact(const CompactParams &p, hipStream_t stream) {
-    if (p.T == 0) return hipSuccess;
-    if (p.align_shift >= 0) {
-        if (p.W > kSortChunk || p.align_cap > kAlignRoomMax) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(compact_kernel<true>, dim3((unsigned)p.T), dim3(kSortThreads), 0,
-                           stream, p);
-    } else {
-        hipLaunchKernelGGL(compact_kernel<false>, dim3((unsigned)p.T), dim3(kSortThreads), 0,
-                           stream, p);
-    }
-    return hipGetLastError();
-}
-
-// CUs of the current device, queried once per device.
 int device_cus() {
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cached[kMaxDevices];
