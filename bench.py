@@ -14,9 +14,14 @@ comes to Huawei's Ascend: inside SGLang's opt-in CANN prefill PR" (section
 "Nine tests that passed, ..."): 7,810 query tokens, a 65,536-slot cache,
 2,051 selected slots per token, (Hq, Hkv) = (16, 2), D = 256, BF16.
 
-Prints one JSON line: selected (query-head, slot) pairs per second, the
-attention kernel's achieved bytes against the HBM roofline, and the FP32 CPU
-oracle timed on a bounded sample of the same workload on the host cores.
+Prints one JSON line: selected (query-head, slot) pairs per second; the
+attention kernel's memory traffic against the HBM roofline (`roofline`: the
+bytes it moves beyond the L2s, from rocprofv3 counters recorded for this
+version of the kernel, over its live time) and its algorithmic bytes over its
+time (`algorithmic_GBps`, which passes the HBM peak because the L2s serve
+most of the gathers); the read ceilings of the L2s, the Infinity Cache and
+HBM measured in the same run with a plain streaming read; and the FP32 CPU
+oracle timed on bounded samples of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -24,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -33,8 +39,12 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_long_prefill_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "top_sparse_attention_amd", "csrc", "qsa_kernels.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attend_counters.json")
+CSRC = os.path.join(ROOT, "top_sparse_attention_amd", "csrc")
+# The sources the attention kernel is compiled from: counters recorded for
+# another version of any of them are not used.
+KERNEL_SOURCES = [os.path.join(CSRC, n) for n in ("qsa_attend.hip", "qsa_device.h",
+                                                   "qsa_kernels.h")]
 
 
 def parse():
@@ -54,8 +64,8 @@ def parse():
                     help="run a 1 GiB device copy first (for counter calibration)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold-cache steps and the device-copy reference (they add "
-                         "kernel instances to a profile)")
+                    help="skip the cold-cache steps, the device-copy reference and the read "
+                         "ceilings (they add kernel instances to a profile)")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as replays of one captured HIP graph (the kernels' "
                          "own times still come from the eager loop)")
@@ -63,21 +73,70 @@ def parse():
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM-side bytes per attention launch from the committed counter summary,
-    or None if it is missing or was taken on another version of the kernel."""
+def recorded_counters(workload: str):
+    """The attention kernel's counters per launch for this workload from the
+    committed rocprofv3 summary (calibrated FETCH_SIZE + WRITE_SIZE bytes,
+    L2 hits and misses), or None if they were taken on another version of the
+    kernel's sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_sha") != kernel_sha() or rec.get("workload") != workload:
+    if not rec or rec.get("source_sha") != kernel_sha():
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def read_ceilings(qsa, torch, dev, reps=10):
+    """Read bandwidth of the L2s, the Infinity Cache and HBM, measured with
+    the library's streaming-read kernel (16-byte coalesced loads), in GB/s.
+
+    Workgroups go to the 8 XCDs round robin.  L2: a 16 MiB footprint read
+    64 KiB per workgroup, so each XCD reads its own 2 MiB (half its 4 MB L2)
+    over and over.  Infinity Cache: 128 MiB read 256 KiB per workgroup, 16 MiB
+    per XCD (4x its L2; all of it fits the 256 MB cache), each byte 8 times.
+    HBM: 2 GiB (8x the Infinity Cache) read once per launch."""
+    buf = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    buf.fill_(3)
+    cases = [("hbm", 1 << 31, 1 << 19, 4096),
+             ("infinity_cache", 1 << 27, 1 << 18, 4096),
+             ("l2", 1 << 24, 1 << 16, 16384)]
+    out = {}
+    for name, foot, per_wg, wgs in cases:
+        sink = torch.empty(wgs, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            qsa.stream_read(buf, foot, per_wg, wgs, sink)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            qsa.stream_read(buf, foot, per_wg, wgs, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"GBps": per_wg * wgs / (ms * 1e-3) / 1e9, "footprint_MiB": foot >> 20,
+                     "read_MiB": (per_wg * wgs) >> 20, "us": ms * 1e3}
+    del buf
+    return out
 
 
 def main():
@@ -286,6 +345,7 @@ def main():
         copy_ref = {"GBps": 5 * 2 * src.numel() / (x0.elapsed_time(x1) * 1e-3) / 1e9,
                     "what": "torch device-to-device copy of 2 GiB; read + write bytes / time"}
         del src, dst
+    ceilings = None if args.no_cold else read_ceilings(qsa, torch, dev)
 
     if indexed:
         # 4 positions per kept block (at most `budget` complete causal blocks)
@@ -297,13 +357,40 @@ def main():
         valid = (case.slot_idx >= 0) & (case.slot_idx < S // bs)
         n_t = valid.sum(axis=1).astype(np.int64) * bs      # selected slots per token
     pairs = int(n_t.sum()) * Hq
-    # Algorithmic bytes of one attention launch: every selected K and V row of
-    # every (token, KV head) once, its slot index, Q in and O out.
+    # Algorithmic bytes of one pass: every selected K and V row of every
+    # (token, KV head) once, Q in, O out, and the selection rows (T x W int32).
     kv_bytes = 1 if fp8 else 2
-    attn_bytes = int(n_t.sum()) * Hkv * (2 * case.D * kv_bytes + 4) + 2 * T * Hq * case.D * 2
+    attn_bytes = (int(n_t.sum()) * Hkv * 2 * case.D * kv_bytes + 2 * T * Hq * case.D * 2
+                  + T * W * 4)
     gather_bytes = int(n_t.sum()) * Hkv * 2 * case.D * kv_bytes
     flops = pairs * 4 * case.D
-    achieved = attn_bytes / (attn_avg * 1e-3) / 1e9
+    algorithmic_gbps = attn_bytes / (attn_avg * 1e-3) / 1e9
+
+    # The roofline: bytes the attention kernel moves beyond the L2s (calibrated
+    # FETCH_SIZE + WRITE_SIZE counters recorded for this version of its
+    # sources; they count Infinity-Cache hits too, so this bounds its HBM
+    # traffic from above) over its live time, against the HBM peak.
+    counters = recorded_counters(args.workload)
+    traffic = counters["fetch_write_bytes_per_launch"] if counters else None
+    achieved = traffic / (attn_avg * 1e-3) / 1e9 if traffic else None
+    hierarchy = None
+    if counters:
+        l2_req = counters["l2_requests_per_launch"] * 128
+        beyond = counters["l2_misses_per_launch"] * 128
+        hierarchy = {
+            "l2_request_bytes": l2_req, "l2_request_GBps": l2_req / (attn_avg * 1e-3) / 1e9,
+            "l2_hit_rate": 1.0 - counters["l2_misses_per_launch"] /
+            counters["l2_requests_per_launch"],
+            "beyond_l2_bytes": beyond, "beyond_l2_GBps": beyond / (attn_avg * 1e-3) / 1e9,
+            "counters": "rocprofv3 TCC_HIT_sum + TCC_MISS_sum (128-byte requests), "
+                        "FETCH_SIZE/WRITE_SIZE; " + os.path.relpath(COUNTERS_FILE, ROOT)}
+        if ceilings:
+            hierarchy["l2_request_frac_of_l2_ceiling"] = \
+                hierarchy["l2_request_GBps"] / ceilings["l2"]["GBps"]
+            hierarchy["beyond_l2_frac_of_infinity_cache_ceiling"] = \
+                hierarchy["beyond_l2_GBps"] / ceilings["infinity_cache"]["GBps"]
+            hierarchy["beyond_l2_frac_of_hbm_ceiling"] = \
+                hierarchy["beyond_l2_GBps"] / ceilings["hbm"]["GBps"]
 
     # Parity of this very output on a sample of rows, checked against the oracle.
     import oracle
@@ -348,11 +435,22 @@ def main():
         run_oracle(cpu_rows, threads)
         c_dt = time.perf_counter() - c_t0
         cpu_pairs = int(n_t[cpu_rows].sum()) * Hq
+        # The same oracle on one core, over a sixteenth of those rows.
+        one_rows = qi.sample_rows(T, max(2, min(args.cpu_rows, T) // 16), seed=13)
+        c_t0 = time.perf_counter()
+        run_oracle(one_rows, 1)
+        one_dt = time.perf_counter() - c_t0
+        one_pairs = int(n_t[one_rows].sum()) * Hq
         cpu = {"value": cpu_pairs / c_dt, "unit": "pairs/s", "cores": threads, "kind": "oracle",
                "sample": f"{cpu_rows.size} of {T} token rows (all {Hq} heads, seeded, incl. first "
-                         f"and last), {cpu_pairs} pairs in {c_dt:.2f} s"}
+                         f"and last), {cpu_pairs} pairs in {c_dt:.2f} s",
+               "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+               "one_core": {"value": one_pairs / one_dt, "unit": "pairs/s",
+                            "sample": f"{one_rows.size} token rows, {one_pairs} pairs in "
+                                      f"{one_dt:.2f} s"},
+               "full_config_s_extrapolated": pairs / (cpu_pairs / c_dt),
+               "full_config_s_one_core_extrapolated": pairs / (one_pairs / one_dt)}
 
-    traffic = measured_traffic(args.workload)
     record = {
         "metric": "selected (query-head,slot) pairs/sec + achieved gather GB/s & % HBM roofline",
         "value": pairs / (ms_step * 1e-3),
@@ -372,8 +470,14 @@ def main():
                    "splits": splits, "block_size": bs, "parallelism": "none (1 GPU)",
                    "launch": "hip_graph" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic},
+                     "frac": achieved / HBM_PEAK_GBS if achieved else None,
+                     "traffic": traffic,
+                     "basis": "bytes beyond the L2s per attention launch (calibrated rocprofv3 "
+                              "FETCH_SIZE + WRITE_SIZE, an upper bound of its HBM bytes) / "
+                              "attend_kernel_ms"},
+        "algorithmic_GBps": algorithmic_gbps,
+        "hierarchy": hierarchy,
+        "read_ceilings": ceilings,
         "cpu_baseline": cpu,
         "attend_kernel_ms": attn_avg,
         "indexer_topk_ms": select_ms,

@@ -34,6 +34,12 @@
  *    dereferenced) and counted; qsa_check_status reports them.
  *  - Calls on different streams with different workspaces may run
  *    concurrently; calls sharing a workspace must be stream-ordered.
+ *  - A problem whose kernel launches would exceed the 2^32 - 1 work-items
+ *    one grid dimension counts (for instance more than 16,777,215 tokens for
+ *    the compaction pass, or more than 67,108,863 attention work items of
+ *    (token, KV head, block of 16 query heads), times the splits of split
+ *    attention) is refused with QSA_ERR_UNSUPPORTED before anything is
+ *    enqueued; split such a call.
  */
 #ifndef QSA_H
 #define QSA_H
@@ -92,8 +98,11 @@ typedef struct qsa_i32_view {
  *          ranges, ascending; input order within a range);
  *   count: int32 [T], number of valid entries of row t;
  *   n_bad: int32 [T], entries of row t that were neither -1 nor in [0, S);
- *   share: 512 bytes the attention writes to pick its layout (see
- *          qsa_sparse_attend). */
+ *   share: 512 bytes: words the attention writes to pick its layout (see
+ *          qsa_sparse_attend), and at byte 384 two int32 words the
+ *          compaction writes: the number of cache slots its lists index (S,
+ *          or hi - lo for a shard) and a flag it clears, which an attention
+ *          over K/V views of fewer slots sets (see qsa_check_status). */
 typedef struct qsa_workspace_map {
     int64_t list_offset;
     int64_t row_stride;
@@ -115,6 +124,10 @@ const char *qsa_last_error(void);
 /* Workspace bytes needed for T tokens of W selection entries (T, W >= 0).
  * Returns 0 for negative sizes. */
 size_t qsa_workspace_bytes(int64_t T, int64_t W);
+
+/* The same size under the name of the prefill it serves (qsa_sparse_prefill,
+ * qsa_compact_slots, qsa_sparse_attend). */
+size_t qsa_sparse_prefill_workspace_bytes(int64_t T, int64_t W);
 
 /* Fill *map with the workspace layout for T, W (see qsa_workspace_map). */
 qsa_status qsa_workspace_layout(int64_t T, int64_t W, qsa_workspace_map *map);
@@ -197,6 +210,10 @@ qsa_status qsa_sparse_prefill_blocks(const qsa_bf16_view *q,
  * paragraph, restricted to each token's listed slots).  Rows with count 0
  * receive +0.0.  q/out [T, Hq, 256], k_cache/v_cache [S, Hkv, 256]; W is the
  * selection width the workspace was compacted with; scale must be finite.
+ * The workspace must have been compacted for at most S cache slots (the S
+ * of the compaction, or hi - lo of a shard): every listed slot then lies in
+ * the views.  Lists compacted for more slots are not read: the call writes
+ * +0.0 rows instead and qsa_check_status reports QSA_ERR_WORKSPACE.
  *
  * Layout choice: the kernel runs 8 items (token, KV head) per CU, which lets
  * the tokens running together share cache rows in L2.  Where the sizes allow
@@ -299,6 +316,9 @@ qsa_status qsa_sparse_decode(const qsa_bf16_view *q,
  * compaction into `workspace` (for T, W), or the last qsa_sparse_decode with
  * it, left.  Writes their total to
  * *n_bad (if not NULL) and returns QSA_ERR_SLOT_RANGE if it is non-zero.
+ * Returns QSA_ERR_WORKSPACE instead if an attention since that compaction
+ * found the workspace's lists compacted for more cache slots than its K/V
+ * views held (and wrote zero rows).
  * This is the only entry point that waits for the device.
  */
 qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes,
@@ -320,6 +340,23 @@ qsa_status qsa_gather_only(const qsa_bf16_view *k_cache,
                            int64_t W, const void *workspace,
                            size_t workspace_bytes, uint32_t *sink,
                            void *stream);
+
+/*
+ * Measurement aid: a plain streaming read.  `workgroups` workgroups of 256
+ * threads each read bytes_per_workgroup consecutive bytes of the first
+ * footprint_bytes of buf with 16-byte loads (workgroup w starting at byte
+ * w * bytes_per_workgroup modulo footprint_bytes and wrapping at the end of
+ * the footprint), and write the XOR of the 32-bit words they read to
+ * sink[w] (device memory, caller-owned, `workgroups` words).  buf must be
+ * 16-byte aligned; footprint_bytes and bytes_per_workgroup positive multiples
+ * of 16, bytes_per_workgroup <= footprint_bytes.  With a footprint that stays
+ * in the L2s, one that fits only the Infinity Cache, and one larger than that,
+ * the duration gives the read bandwidth of each level for the attention's
+ * 16-byte loads.
+ */
+qsa_status qsa_stream_read(const void *buf, size_t footprint_bytes,
+                           size_t bytes_per_workgroup, int64_t workgroups,
+                           uint32_t *sink, void *stream);
 
 /*
  * FP8 KV-cache variant.  The page's section "Where this sits in the Qwen4Exp

@@ -244,3 +244,68 @@ def test_indexer_entry_points_reject_bad_arguments():
     assert topk(out_=ivew((8, 22), (22, 1), FAKE + (2 << 24))) == "QSA_ERR_SHAPE"
     assert topk(sc_bytes=8 * 16 * 4 - 1) == "QSA_ERR_WORKSPACE"
     assert qsa.indexer_scores.__doc__ and lib.qsa_indexer_scores_bytes(8, 16) == 512
+
+
+def far_views(T, Hq, S, Hkv, W):
+    """Views of made-up addresses 1 TiB apart, so that even huge shapes pass
+    the overlap checks and reach the launch-size checks."""
+    tib = 1 << 40
+    q = view((T, Hq, 256), (Hq * 256, 256, 1), tib)
+    k = view((S, Hkv, 256), (Hkv * 256, 256, 1), 2 * tib)
+    v = view((S, Hkv, 256), (Hkv * 256, 256, 1), 3 * tib)
+    o = view((T, Hq, 256), (Hq * 256, 256, 1), 4 * tib)
+    s = ivew((T, W), (W, 1), 5 * tib)
+    return q, k, v, o, s, 6 * tib
+
+
+@host_only
+def test_launches_beyond_the_work_item_limit_are_refused():
+    """A launch covers at most 2^32 - 1 work-items per grid dimension; larger
+    problems are refused as unsupported before anything is enqueued."""
+    lib = _lib()
+    r = ctypes.byref
+    huge = (1 << 62)
+
+    def name(status):
+        return qsa.STATUS_NAMES[status]
+
+    # the compaction pass: 256 threads per token, so 2^24 tokens are too many
+    q, k, v, o, s, ws = far_views(1 << 24, 1, 64, 1, 1)
+    assert name(lib.qsa_sparse_prefill(r(q), r(k), r(v), r(s), 0.0625, r(o), ws, huge,
+                                       None)) == "QSA_ERR_UNSUPPORTED"
+    assert "work-items" in lib.qsa_last_error().decode()
+    assert name(lib.qsa_compact_slots(r(s), 64, ws, huge, None)) == "QSA_ERR_UNSUPPORTED"
+    assert name(lib.qsa_compact_blocks(r(s), 64, 4, ws, huge, None)) == "QSA_ERR_UNSUPPORTED"
+    # attention: one 64-thread wave per (token, KV head, 16-head block);
+    # 2^25 tokens x 2 KV heads = 2^26 waves = 2^32 work-items
+    q, k, v, o, s, ws = far_views(1 << 25, 16, 64, 2, 1)
+    assert name(lib.qsa_sparse_attend(r(q), r(k), r(v), 1, 0.0625, ws, huge, r(o),
+                                      None)) == "QSA_ERR_UNSUPPORTED"
+    # one fewer token fits: the call gets as far as the launch, which fails
+    # on a host without a GPU
+    q, k, v, o, s, ws = far_views((1 << 25) - 1, 16, 64, 2, 1)
+    assert name(lib.qsa_sparse_attend(r(q), r(k), r(v), 1, 0.0625, ws, huge, r(o), None)) == \
+        "QSA_ERR_HIP"
+    assert "work-items" not in lib.qsa_last_error().decode()
+    # split attention multiplies by the splits
+    q, k, v, o, s, ws = far_views(1 << 20, 1, 64, 1, 1)
+    part = 7 << 40
+    assert name(lib.qsa_sparse_attend_partial(r(q), r(k), r(v), 1, 0.0625, ws, huge, 4096, 0,
+                                              4096, part, huge, None)) == "QSA_ERR_UNSUPPORTED"
+    # the merge: one wave per (token, head), 4 per workgroup of 256
+    mo = view((1 << 24, 16, 256), (16 * 256, 256, 1), 4 << 40)
+    assert name(lib.qsa_merge_partials(part, huge, 2, 1 << 24, 16, r(mo), None)) == \
+        "QSA_ERR_UNSUPPORTED"
+    # the indexer's key ranges of 1,024 along y stop at 65,535
+    C = 1 << 27
+    iq = view((8, 4, 128), (512, 128, 1), 1 << 40)
+    ik = view((C, 1, 128), (128, 128, 1), 2 << 40)
+    out = ivew((8, 23), (23, 1), 3 << 40)
+    assert name(lib.qsa_indexer_topk(r(iq), r(ik), 4 << 40, 5 << 40, 4 * C, 5, 6 << 40, huge,
+                                     r(out), None)) == "QSA_ERR_UNSUPPORTED"
+
+
+def test_prefill_workspace_alias():
+    lib = _lib()
+    for T, W in ((7810, 2051), (0, 0), (3, 5), (-1, 2)):
+        assert lib.qsa_sparse_prefill_workspace_bytes(T, W) == qsa.workspace_bytes(T, W)

@@ -28,7 +28,7 @@ __all__ = [
     "merge_partials", "decode_splits", "decode_workspace_bytes", "sparse_decode",
     "sparse_attend_fp8kv", "sparse_prefill_fp8kv", "gather_only_fp8kv",
     "compact_blocks", "sparse_prefill_blocks", "indexer_scores", "indexer_select",
-    "indexer_topk",
+    "indexer_topk", "stream_read",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -94,6 +94,8 @@ def load_library():
     lib.qsa_last_error.argtypes = []
     lib.qsa_workspace_bytes.restype = sz
     lib.qsa_workspace_bytes.argtypes = [i64, i64]
+    lib.qsa_sparse_prefill_workspace_bytes.restype = sz
+    lib.qsa_sparse_prefill_workspace_bytes.argtypes = [i64, i64]
     lib.qsa_workspace_layout.restype = ctypes.c_int
     lib.qsa_workspace_layout.argtypes = [i64, i64, P(WorkspaceMap)]
     lib.qsa_compact_slots.restype = ctypes.c_int
@@ -147,6 +149,8 @@ def load_library():
     lib.qsa_indexer_topk.restype = ctypes.c_int
     lib.qsa_indexer_topk.argtypes = [P(BF16View), P(BF16View), vp, vp, i64, ctypes.c_int32, vp,
                                      sz, P(I32View), vp]
+    lib.qsa_stream_read.restype = ctypes.c_int
+    lib.qsa_stream_read.argtypes = [vp, sz, sz, i64, vp, vp]
     lib.qsa_gather_only_fp8kv.restype = ctypes.c_int
     lib.qsa_gather_only_fp8kv.argtypes = [P(BF16View), P(BF16View), i64, i64, vp, sz, vp, vp]
     _lib = lib
@@ -295,6 +299,20 @@ def gather_only(k_cache: torch.Tensor, v_cache: torch.Tensor, workspace: torch.T
     _raise_on(load_library().qsa_gather_only(
         ctypes.byref(kv), ctypes.byref(vv), T, W, workspace.data_ptr(), workspace.numel(),
         sink.data_ptr(), _stream(k_cache.device)))
+    return sink
+
+
+def stream_read(buf: torch.Tensor, footprint_bytes: int, bytes_per_workgroup: int,
+                workgroups: int, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Run the streaming-read measurement kernel over the first
+    ``footprint_bytes`` of ``buf``; returns sink [workgroups] (int32 bits)."""
+    if footprint_bytes > buf.numel() * buf.element_size():
+        raise ValueError("footprint larger than the buffer")
+    if sink is None:
+        sink = torch.empty(max(workgroups, 1), dtype=torch.int32, device=buf.device)
+    _raise_on(load_library().qsa_stream_read(
+        buf.data_ptr(), footprint_bytes, bytes_per_workgroup, workgroups, sink.data_ptr(),
+        _stream(buf.device)))
     return sink
 
 

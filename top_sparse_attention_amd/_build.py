@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["qsa_attend.hip", "qsa_compact.hip", "qsa_indexer.hip", "qsa_api.cpp"]
+SOURCES = ["qsa_attend.hip", "qsa_compact.hip", "qsa_indexer.hip", "qsa_measure.hip",
+           "qsa_api.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -32,9 +32,30 @@ constexpr int64_t kMax32 = 0x7fffffff;
 // The sharing estimate's words in the workspace: est [kSharePairs][2] floats,
 // then the choice.
 constexpr int64_t kShareBytes = 512;
-static_assert(qsa::kSharePairs * 8 + 4 <= kShareBytes && qsa::kSharePairs <= 64, "sharing words");
+// Also in the share area: the compaction's extent words (the number of cache
+// slots its lists index, and the flag an attention over a smaller cache view
+// sets; see qsa::CompactParams).
+constexpr int64_t kExtentOffset = 384;
+static_assert(qsa::kSharePairs * 8 + 4 <= kExtentOffset && kExtentOffset + 8 <= kShareBytes &&
+                  qsa::kSharePairs <= 64,
+              "share-area words");
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// a * b for non-negative operands, saturated at INT64_MAX.
+int64_t mul_sat(int64_t a, int64_t b) {
+    if (a <= 0 || b <= 0) return 0;
+    return a > INT64_MAX / b ? INT64_MAX : a * b;
+}
+
+// HIP counts the work-items of a launch along one grid dimension in 32 bits.
+constexpr int64_t kMaxWorkItems = 0xffffffffLL;
+// Largest grid along y (the indexer's key ranges).
+constexpr int64_t kMaxGridY = 65535;
+
+int32_t *extent_words(const void *ws, const qsa_workspace_map &m) {
+    return (int32_t *)((char *)ws + m.share_offset + kExtentOffset);
+}
 
 bool layout_of(int64_t T, int64_t W, qsa_workspace_map *m) {
     if (T < 0 || W < 0) return false;
@@ -198,6 +219,35 @@ qsa_status hip_fail(hipError_t e, const char *what) {
     return fail(QSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// A launch of `blocks` workgroups of `threads` threads must stay within the
+// work-items one grid dimension counts; larger problems are refused before
+// anything is enqueued (the launch would otherwise fail or cover part of the
+// work).
+qsa_status check_grid(int64_t blocks, int64_t threads, const char *what) {
+    if (mul_sat(blocks, threads) > kMaxWorkItems)
+        return fail(QSA_ERR_UNSUPPORTED,
+                    "%s: %lld workgroups of %lld threads exceed the 2^32 - 1 work-items of one "
+                    "launch; split the call",
+                    what, (long long)blocks, (long long)threads);
+    return QSA_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+
+qsa_status check_compact_grid(int64_t T) { return check_grid(T, qsa::kSortThreads, "compaction"); }
+
+// Attention items (token, KV head, block of 16 query heads), times splits.
+qsa_status check_attend_grid(int64_t T, int64_t Hq, int64_t Hkv, int64_t splits) {
+    if (Hkv <= 0) return QSA_OK;
+    const int64_t HB = ceil_div(Hq / Hkv, 16);
+    return check_grid(mul_sat(mul_sat(mul_sat(T, Hkv), HB), splits), 64, "attention");
+}
+
+// One wave per (token, head) row, four rows per workgroup.
+qsa_status check_merge_grid(int64_t T, int64_t Hq) {
+    return check_grid(ceil_div(mul_sat(T, Hq), 4), 256, "merge");
+}
+
 // Width of the compaction's sort key for entries in [0, n): the bits of
 // n - 1 (at least one) plus the bit that marks invalid entries.
 int32_t sort_key_bits(int64_t n) {
@@ -238,6 +288,7 @@ qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t
     }
     p.count = (int32_t *)((char *)ws + m.count_offset);
     p.n_bad = (int32_t *)((char *)ws + m.bad_offset);
+    p.extent = extent_words(ws, m);
     hipError_t e = qsa::launch_compact(p, stream);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "compaction launch");
 }
@@ -429,10 +480,12 @@ qsa_status enqueue_partial(const qsa_bf16_view *q, const qsa_bf16_view *k,
 
 qsa_status enqueue_merge(const void *partials, const PartialsMap &pm, int64_t n_parts, int64_t T,
                          int32_t Hq, const qsa_bf16_view *out, hipStream_t stream,
-                         const int32_t *bad_part = nullptr, int32_t *n_bad = nullptr) {
+                         const int32_t *bad_part = nullptr, int32_t *n_bad = nullptr,
+                         int32_t *clear_flag = nullptr) {
     qsa::MergeParams p{};
     p.bad_part = bad_part;
     p.n_bad = n_bad;
+    p.clear_flag = clear_flag;
     p.part_o = (const float *)partials;
     p.part_ml = (const float *)((const char *)partials + pm.ml_offset);
     p.n_parts = n_parts;
@@ -475,6 +528,8 @@ void fill_attend(qsa::AttendParams &p, const qsa_bf16_view *q, const qsa_bf16_vi
     p.list = (const int32_t *)((const char *)ws + m.list_offset);
     p.list_stride = m.row_stride;
     p.count = (const int32_t *)((const char *)ws + m.count_offset);
+    p.extent = extent_words(ws, m);
+    p.S_rows = pr.S;
     p.Hkv = pr.Hkv;
     p.G = pr.Hq / pr.Hkv;
     p.HB = (p.G + 15) / 16;
@@ -511,6 +566,8 @@ size_t qsa_workspace_bytes(int64_t T, int64_t W) {
     return layout_of(T, W, &m) ? (size_t)m.total_bytes : 0;
 }
 
+size_t qsa_sparse_prefill_workspace_bytes(int64_t T, int64_t W) { return qsa_workspace_bytes(T, W); }
+
 qsa_status qsa_workspace_layout(int64_t T, int64_t W, qsa_workspace_map *map) {
     if (!map) return fail(QSA_ERR_NULL, "map is NULL");
     if (!layout_of(T, W, map)) return fail(QSA_ERR_SHAPE, "negative T or W");
@@ -529,6 +586,7 @@ qsa_status qsa_compact_slot_range(const qsa_i32_view *slot_idx, int64_t S, int64
     if (lo < 0 || hi < lo || hi > S) return fail(QSA_ERR_SHAPE, "need 0 <= lo <= hi <= S");
     qsa_workspace_map m;
     if ((s = check_workspace(workspace, workspace_bytes, T, W, &m))) return s;
+    if ((s = check_compact_grid(T))) return s;
     return enqueue_compact(slot_idx, T, W, S, lo, hi, workspace, m, (hipStream_t)stream);
 }
 
@@ -556,6 +614,7 @@ qsa_status qsa_compact_blocks(const qsa_i32_view *block_idx, int64_t S, int32_t 
     if ((s = check_blocks(block_size, S, W, &Ws))) return s;
     qsa_workspace_map m;
     if ((s = check_workspace(workspace, workspace_bytes, T, Ws, &m))) return s;
+    if ((s = check_compact_grid(T))) return s;
     const int64_t nb = S / block_size;
     return enqueue_compact(block_idx, T, W, nb, 0, nb, workspace, m, (hipStream_t)stream,
                            block_size);
@@ -574,6 +633,8 @@ qsa_status qsa_sparse_prefill_blocks(const qsa_bf16_view *q, const qsa_bf16_view
     if ((s = check_blocks(block_size, pr.S, W, &Ws))) return s;
     qsa_workspace_map m;
     if ((s = check_workspace(workspace, workspace_bytes, pr.T, Ws, &m))) return s;
+    if ((s = check_compact_grid(pr.T)) || (s = check_attend_grid(pr.T, pr.Hq, pr.Hkv, 1)))
+        return s;
     if (pr.T == 0) return QSA_OK;
     hipStream_t st = (hipStream_t)stream;
     const int64_t nb = pr.S / block_size;
@@ -609,6 +670,17 @@ qsa_status check_index_view(const qsa_bf16_view *v, const char *name, int64_t he
     if ((uintptr_t)v->data % 16 || v->stride[0] % 8 || v->stride[1] % 8)
         return fail(QSA_ERR_STRIDE, "%s: rows must be 16-byte aligned", name);
     if (v->size[0] > kMax32) return fail(QSA_ERR_UNSUPPORTED, "%s: too many rows", name);
+    return QSA_OK;
+}
+
+// The score kernel: one workgroup of 256 per 128 tokens along x, one per
+// 1,024 keys along y.
+qsa_status check_scores_grid(int64_t T, int64_t C) {
+    qsa_status s = check_grid(ceil_div(T, 128), 256, "indexer scores");
+    if (s) return s;
+    if (ceil_div(C, 1024) > kMaxGridY)
+        return fail(QSA_ERR_UNSUPPORTED, "indexer scores: %lld keys exceed %lld key ranges",
+                    (long long)C, (long long)kMaxGridY);
     return QSA_OK;
 }
 
@@ -689,6 +761,7 @@ qsa_status qsa_sparse_attend(const qsa_bf16_view *q, const qsa_bf16_view *k_cach
     if (s) return s;
     qsa_workspace_map m;
     if ((s = check_workspace(workspace, workspace_bytes, pr.T, W, &m))) return s;
+    if ((s = check_attend_grid(pr.T, pr.Hq, pr.Hkv, 1))) return s;
     return enqueue_attend(q, k_cache, v_cache, out, pr, scale, workspace, m, (hipStream_t)stream);
 }
 
@@ -704,6 +777,8 @@ qsa_status qsa_sparse_prefill(const qsa_bf16_view *q, const qsa_bf16_view *k_cac
     if ((s = check_slots(slot_idx, pr.T, &W))) return s;
     qsa_workspace_map m;
     if ((s = check_workspace(workspace, workspace_bytes, pr.T, W, &m))) return s;
+    if ((s = check_compact_grid(pr.T)) || (s = check_attend_grid(pr.T, pr.Hq, pr.Hkv, 1)))
+        return s;
     if (pr.T == 0) return QSA_OK;
     hipStream_t st = (hipStream_t)stream;
     if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, 0, pr.S, workspace, m, st))) return s;
@@ -733,6 +808,7 @@ qsa_status qsa_sparse_attend_partial(const qsa_bf16_view *q, const qsa_bf16_view
     if ((s = check_no_overlap((uintptr_t)partials, (uintptr_t)partials + (uintptr_t)pm.total_bytes,
                               q, k_cache, v_cache, "partials")))
         return s;
+    if ((s = check_attend_grid(pr.T, pr.Hq, pr.Hkv, splits))) return s;
     return enqueue_partial(q, k_cache, v_cache, pr, scale, workspace, m, splits, part_base,
                            partials, pm, (hipStream_t)stream);
 }
@@ -753,6 +829,7 @@ qsa_status qsa_merge_partials(const void *partials, size_t partials_bytes, int64
         const uintptr_t plo = (uintptr_t)partials, phi = plo + (uintptr_t)pm.total_bytes;
         if (olo < phi && plo < ohi) return fail(QSA_ERR_ALIAS, "out overlaps the partials");
     }
+    if ((s = check_merge_grid(T, Hq))) return s;
     if (T == 0 || Hq == 0) return QSA_OK;
     return enqueue_merge(partials, pm, n_parts, T, (int32_t)Hq, out, (hipStream_t)stream);
 }
@@ -784,6 +861,10 @@ qsa_status qsa_sparse_decode(const qsa_bf16_view *q, const qsa_bf16_view *k_cach
     if ((uintptr_t)workspace % kAlign) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if (workspace_bytes < need)
         return fail(QSA_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+    if ((s = check_compact_grid(pr.T)) ||
+        (s = check_attend_grid(pr.T, pr.Hq, pr.Hkv, decode_splits(pr.T, W, pr.Hq, pr.Hkv))) ||
+        (s = check_merge_grid(pr.T, pr.Hq)))
+        return s;
     if (pr.T == 0) return QSA_OK;
     qsa_workspace_map m;
     layout_of(pr.T, W, &m);
@@ -812,7 +893,8 @@ qsa_status qsa_sparse_decode(const qsa_bf16_view *q, const qsa_bf16_view *k_cach
                              st, slot_idx, bad_part)))
         return s;
     return enqueue_merge(partials, pm, splits, pr.T, pr.Hq, out, st, bad_part,
-                         (int32_t *)((char *)workspace + m.bad_offset));
+                         (int32_t *)((char *)workspace + m.bad_offset),
+                         extent_words(workspace, m) + 1);
 }
 
 qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes, int64_t T,
@@ -823,14 +905,22 @@ qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes, int64
     if (n_bad) *n_bad = 0;
     if (T == 0) return QSA_OK;
     std::vector<int32_t> bad((size_t)T);
+    int32_t extent[2] = {0, 0};
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "stream synchronize");
     e = hipMemcpy(bad.data(), (const char *)workspace + m.bad_offset, (size_t)T * 4,
                   hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+        e = hipMemcpy(extent, extent_words(workspace, m), sizeof extent, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "status copy");
     int64_t total = 0;
     for (int32_t b : bad) total += b;
     if (n_bad) *n_bad = total;
+    if (extent[1])
+        return fail(QSA_ERR_WORKSPACE,
+                    "the workspace's lists index %d cache slots, more than the K/V views of the "
+                    "attention held; its rows were written as zeros",
+                    extent[0]);
     if (total) return fail(QSA_ERR_SLOT_RANGE, "%lld selection entries were neither -1 nor in [0, S)",
                            (long long)total);
     return QSA_OK;
@@ -858,6 +948,7 @@ qsa_status gather_only_any(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_
     if ((s = check_workspace(workspace, workspace_bytes, T, W, &m))) return s;
     if (T == 0 || k_cache->size[1] == 0) return QSA_OK;
     if (!sink) return fail(QSA_ERR_NULL, "sink is NULL");
+    if ((s = check_grid(mul_sat(T, k_cache->size[1]), 64, "gather-only"))) return s;
     qsa::GatherParams p{};
     p.k = k_cache->data;
     p.k_ss = k_cache->stride[0];
@@ -870,6 +961,8 @@ qsa_status gather_only_any(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_
     p.count = (const int32_t *)((const char *)workspace + m.count_offset);
     p.sink = sink;
     p.Hkv = (int32_t)k_cache->size[1];
+    p.S_rows = k_cache->size[0];
+    p.extent = extent_words(workspace, m);
     hipError_t e = qsa::launch_gather_only(p, kv, T, (hipStream_t)stream);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "gather-only launch");
 }
@@ -883,6 +976,27 @@ qsa_status qsa_gather_only(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_
                            uint32_t *sink, void *stream) {
     return gather_only_any(k_cache, v_cache, 2, qsa::KvType::kBf16, T, W, workspace,
                            workspace_bytes, sink, stream);
+}
+
+qsa_status qsa_stream_read(const void *buf, size_t footprint_bytes, size_t bytes_per_workgroup,
+                           int64_t workgroups, uint32_t *sink, void *stream) {
+    if (workgroups < 0) return fail(QSA_ERR_SHAPE, "negative workgroup count");
+    if (workgroups == 0) return QSA_OK;
+    if (!buf || !sink) return fail(QSA_ERR_NULL, "buffer or sink is NULL");
+    if ((uintptr_t)buf % 16) return fail(QSA_ERR_STRIDE, "buffer must be 16-byte aligned");
+    if (footprint_bytes == 0 || footprint_bytes % 16 || bytes_per_workgroup == 0 ||
+        bytes_per_workgroup % 16 || bytes_per_workgroup > footprint_bytes)
+        return fail(QSA_ERR_SHAPE,
+                    "need 0 < bytes_per_workgroup <= footprint_bytes, both multiples of 16");
+    qsa_status s = check_grid(workgroups, 256, "stream read");
+    if (s) return s;
+    qsa::StreamParams p{};
+    p.buf = buf;
+    p.footprint_chunks = (int64_t)(footprint_bytes / 16);
+    p.chunks_per_wg = (int64_t)(bytes_per_workgroup / 16);
+    p.sink = sink;
+    hipError_t e = qsa::launch_stream_read(p, workgroups, (hipStream_t)stream);
+    return e == hipSuccess ? QSA_OK : hip_fail(e, "stream read launch");
 }
 
 qsa_status qsa_gather_only_fp8kv(const qsa_fp8_view *k8, const qsa_fp8_view *v8, int64_t T,
@@ -921,6 +1035,8 @@ qsa_status qsa_sparse_prefill_fp8kv(const qsa_bf16_view *q, const qsa_fp8_view *
     if ((s = check_slots(slot_idx, pr.T, &W))) return s;
     qsa_workspace_map m;
     if ((s = check_workspace(workspace, workspace_bytes, pr.T, W, &m))) return s;
+    if ((s = check_compact_grid(pr.T)) || (s = check_attend_grid(pr.T, pr.Hq, pr.Hkv, 1)))
+        return s;
     if (pr.T == 0) return QSA_OK;
     hipStream_t st = (hipStream_t)stream;
     if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, 0, pr.S, workspace, m, st))) return s;
@@ -941,6 +1057,7 @@ qsa_status qsa_indexer_scores(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
     const int64_t T = iq->size[0], C = ik->size[0];
     if ((s = check_scores(scores, scores_bytes, T, C))) return s;
     if (T > 0 && !positions) return fail(QSA_ERR_NULL, "positions is NULL");
+    if ((s = check_scores_grid(T, C))) return s;
     if (T == 0 || C == 0) return QSA_OK;
     return enqueue_indexer_scores(iq, ik, positions, scores, (hipStream_t)stream);
 }
@@ -951,6 +1068,7 @@ qsa_status qsa_indexer_select(const float *scores, size_t scores_bytes, int64_t 
     qsa_status s = check_select_args(T, C, positions, slot_of_pos, L, budget, slot_idx);
     if (s) return s;
     if ((s = check_scores(scores, scores_bytes, T, C))) return s;
+    if ((s = check_grid(T, 256, "indexer select"))) return s;
     if (T == 0) return QSA_OK;
     return enqueue_indexer_select(scores, T, C, positions, slot_of_pos, L, budget, slot_idx,
                                   (hipStream_t)stream);
@@ -966,6 +1084,7 @@ qsa_status qsa_indexer_topk(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
     const int64_t T = iq->size[0], C = ik->size[0];
     if ((s = check_select_args(T, C, positions, slot_of_pos, L, budget, slot_idx))) return s;
     if ((s = check_scores(scores, scores_bytes, T, C))) return s;
+    if ((s = check_scores_grid(T, C)) || (s = check_grid(T, 256, "indexer select"))) return s;
     if (T == 0) return QSA_OK;
     hipStream_t st = (hipStream_t)stream;
     if (C > 0 && (s = enqueue_indexer_scores(iq, ik, positions, scores, st))) return s;

@@ -344,8 +344,18 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     const int h0 = g * p.G + hb * kHeadBlock;
     const int nh = min(kHeadBlock, p.G - hb * kHeadBlock);
     // Entries of the item's row: the compacted list's count, or (raw rows)
-    // the selection width, -1 and invalid entries included.
-    const int n = kRawRows ? p.W_raw : p.count[t];
+    // the selection width, -1 and invalid entries included.  Lists compacted
+    // for more cache slots than the views hold are refused: the item reads
+    // nothing (a zero row, or an empty share) and flags the workspace.
+    int n;
+    if constexpr (kRawRows) {
+        n = p.W_raw;
+    } else {
+        const int cnt = p.count[t];
+        const bool fits = (int64_t)p.extent[0] <= p.S_rows;
+        n = fits ? cnt : 0;
+        if (!fits && lane == 0) p.extent[1] = 1;
+    }
 
     const int ntiles = (n + kTileSlots - 1) / kTileSlots;
     // Raw rows: the share of (g = 0, head block 0) reports the invalid entries.
@@ -643,6 +653,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     const int64_t t = row / p.Hq;
     const int h = (int)(row - t * p.Hq);
     const int64_t n = p.n_parts;
+    if (p.clear_flag != nullptr && row == 0 && lane == 0) *p.clear_flag = 0;
     if (p.bad_part != nullptr && h == 0) {
         // The invalid entries of token t's row, reported by its raw-row shares.
         int bad = 0;
@@ -838,8 +849,14 @@ __global__ __launch_bounds__(64, kAttendWavesPerSimd) void gather_only_kernel(co
     const int64_t item = blockIdx.x;
     const int64_t t = item / p.Hkv;
     const int g = (int)(item - t * p.Hkv);
-    const int n = p.count[t];
+    const int cnt = p.count[t];
+    // Lists compacted for more slots than the views hold are not read.
+    const int n = (int64_t)p.extent[0] <= p.S_rows ? cnt : 0;
     const int ntiles = (n + kTileSlots - 1) / kTileSlots;
+    if (ntiles == 0) {   // nothing to read (and maybe no cache row to stand in)
+        if (lane == 0) p.sink[item] = 0;
+        return;
+    }
     const int32_t *list = p.list + t * p.list_stride;
     const char *kb = (const char *)p.k + (int64_t)g * p.k_sh * Gth::kElemBytes;
     const char *vb = (const char *)p.v + (int64_t)g * p.v_sh * Gth::kElemBytes;

@@ -52,6 +52,12 @@ __global__ __launch_bounds__(kSortThreads) void compact_kernel(const CompactPara
 
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
+    if (t == 0 && tid == 0) {
+        // Every list entry is below this; an attention over a cache view with
+        // fewer slots refuses the lists (and sets the flag cleared here).
+        p.extent[0] = (int32_t)((p.hi - p.lo) * p.block);
+        p.extent[1] = 0;
+    }
     const int32_t *src = p.slot_idx + t * p.stride_t;
     int32_t *dst = p.list + t * p.row_stride;
     const uint32_t pad_key = 1u << (p.key_bits - 1);

@@ -87,6 +87,10 @@ struct CompactParams {
     int64_t row_stride;
     int32_t *count;
     int32_t *n_bad;
+    // Workspace words [2], written by workgroup 0: the number of cache slots
+    // the lists index, (hi - lo) * block (every list entry is below it), and
+    // a cleared flag that an attention over a smaller cache view sets.
+    int32_t *extent;
 };
 
 // Element type of the K/V cache: BF16, or FP8 E4M3 codes with one scale per
@@ -140,8 +144,12 @@ struct AttendParams {
     const int32_t *raw;
     int64_t raw_stride;
     int32_t W_raw;
-    int64_t S_rows;
+    int64_t S_rows;      // slots of the k/v views
     int32_t *bad_part;
+    // Compacted lists: the workspace's extent words (see CompactParams).  An
+    // item whose lists index more slots than S_rows reads nothing, writes a
+    // zero row (or an empty share) and sets extent[1].  Unused for raw rows.
+    int32_t *extent;
 };
 
 // Sharing estimate.  Items run kItemsPerCU to a CU and walk their slot lists
@@ -175,6 +183,9 @@ struct MergeParams {
     // Non-null after raw-row shares: n_bad[t] = sum over parts of bad_part[s * T + t].
     const int32_t *bad_part;
     int32_t *n_bad;
+    // Non-null: workgroup 0 writes 0 here (the workspace's extent flag, which
+    // no compaction of a decode step clears).
+    int32_t *clear_flag;
 };
 
 struct GatherParams {
@@ -187,6 +198,8 @@ struct GatherParams {
     const int32_t *count;
     uint32_t *sink;
     int32_t Hkv;
+    int64_t S_rows;              // slots of the k/v views
+    const int32_t *extent;       // the workspace's extent word (see CompactParams)
 };
 
 // QSA indexer: 4 query heads sharing one key head, head dim 128, one key per
@@ -219,7 +232,17 @@ struct IndexerSelectParams {
     int64_t out_stride;
 };
 
+// Streaming read (measurement only): `workgroups` workgroups each read
+// chunks_per_wg 16-byte chunks of a footprint of footprint_chunks chunks.
+struct StreamParams {
+    const void *buf;
+    int64_t footprint_chunks;
+    int64_t chunks_per_wg;   // <= footprint_chunks
+    uint32_t *sink;          // [workgroups]
+};
+
 hipError_t launch_compact(const CompactParams &p, hipStream_t stream);
+hipError_t launch_stream_read(const StreamParams &p, int64_t workgroups, hipStream_t stream);
 hipError_t launch_indexer_scores(const IndexerScoreParams &p, hipStream_t stream);
 hipError_t launch_indexer_select(const IndexerSelectParams &p, hipStream_t stream);
 // With a non-null `share`, the sharing estimate runs first and picks the
