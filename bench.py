@@ -112,14 +112,17 @@ def read_ceilings(qsa, torch, dev, reps=10):
 
     Workgroups go to the 8 XCDs round robin.  L2: a 16 MiB footprint read
     64 KiB per workgroup, so each XCD reads its own 2 MiB (half its 4 MB L2)
-    over and over.  Infinity Cache: 128 MiB read 256 KiB per workgroup, 16 MiB
-    per XCD (4x its L2; all of it fits the 256 MB cache), each byte 8 times.
-    HBM: 2 GiB (8x the Infinity Cache) read once per launch."""
+    over and over, 4 GiB in all.  Infinity Cache: 128 MiB read 256 KiB per
+    workgroup, 16 MiB per XCD (4x its L2; all of it fits the 256 MB cache),
+    each byte 8 times.  HBM: 2 GiB (8x the Infinity Cache) read once per
+    launch, 128 KiB per workgroup.  (Grid and slice sizes are the fastest of a
+    sweep; slices of 1 MiB let workgroups running together on an XCD read the
+    same lines and measure L2 sharing instead.)"""
     buf = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     buf.fill_(3)
-    cases = [("hbm", 1 << 31, 1 << 19, 4096),
+    cases = [("hbm", 1 << 31, 1 << 17, 16384),
              ("infinity_cache", 1 << 27, 1 << 18, 4096),
-             ("l2", 1 << 24, 1 << 16, 16384)]
+             ("l2", 1 << 24, 1 << 16, 65536)]
     out = {}
     for name, foot, per_wg, wgs in cases:
         sink = torch.empty(wgs, dtype=torch.int32, device=dev)
