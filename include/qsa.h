@@ -312,6 +312,27 @@ qsa_status qsa_sparse_decode(const qsa_bf16_view *q,
                              size_t workspace_bytes, void *stream);
 
 /*
+ * qsa_sparse_prefill for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments and results without the
+ * workspace arguments.  Its workspace is a fixed scratch array of
+ * qsa_noalloc_scratch_bytes() bytes (64 MiB: enough for 7,810 tokens of 2,051
+ * entries) that the library holds in the memory of every GPU it runs on until
+ * the process ends; the call allocates nothing.  A selection whose workspace
+ * (qsa_workspace_bytes(T, W)) exceeds it is refused with QSA_ERR_UNSUPPORTED.
+ * All calls on one GPU share that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from different threads) race and must not be
+ * made.  The array keeps the last call's contents.
+ */
+size_t qsa_noalloc_scratch_bytes(void);
+
+qsa_status qsa_sparse_prefill_noalloc(const qsa_bf16_view *q,
+                                      const qsa_bf16_view *k_cache,
+                                      const qsa_bf16_view *v_cache,
+                                      const qsa_i32_view *slot_idx, float scale,
+                                      qsa_bf16_view *out, void *stream);
+
+/*
  * Synchronizes `stream`, then reads the invalid-entry counts that the last
  * compaction into `workspace` (for T, W), or the last qsa_sparse_decode with
  * it, left.  Writes their total to

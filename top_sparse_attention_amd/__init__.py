@@ -28,7 +28,7 @@ __all__ = [
     "merge_partials", "decode_splits", "decode_workspace_bytes", "sparse_decode",
     "sparse_attend_fp8kv", "sparse_prefill_fp8kv", "gather_only_fp8kv",
     "compact_blocks", "sparse_prefill_blocks", "indexer_scores", "indexer_select",
-    "indexer_topk", "stream_read",
+    "indexer_topk", "stream_read", "sparse_prefill_noalloc", "noalloc_scratch_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -149,6 +149,11 @@ def load_library():
     lib.qsa_indexer_topk.restype = ctypes.c_int
     lib.qsa_indexer_topk.argtypes = [P(BF16View), P(BF16View), vp, vp, i64, ctypes.c_int32, vp,
                                      sz, P(I32View), vp]
+    lib.qsa_noalloc_scratch_bytes.restype = sz
+    lib.qsa_noalloc_scratch_bytes.argtypes = []
+    lib.qsa_sparse_prefill_noalloc.restype = ctypes.c_int
+    lib.qsa_sparse_prefill_noalloc.argtypes = [P(BF16View), P(BF16View), P(BF16View),
+                                               P(I32View), f32, P(BF16View), vp]
     lib.qsa_stream_read.restype = ctypes.c_int
     lib.qsa_stream_read.argtypes = [vp, sz, sz, i64, vp, vp]
     lib.qsa_gather_only_fp8kv.restype = ctypes.c_int
@@ -275,6 +280,29 @@ def sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         workspace.numel(), stream))
     if check:
         check_status(workspace, T, W)
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the fixed scratch array qsa_sparse_prefill_noalloc works in."""
+    return int(load_library().qsa_noalloc_scratch_bytes())
+
+
+def sparse_prefill_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           slot_idx: torch.Tensor, scale: Optional[float] = None,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sparse_prefill without a workspace argument: the library works in its
+    fixed per-GPU scratch array and allocates nothing (calls that overlap on
+    one GPU race on that array).  ``out`` must be given to allocate nothing
+    here either."""
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    qv, kv, vv, ov = (_bf16_view(q, "q"), _bf16_view(k_cache, "k_cache"),
+                      _bf16_view(v_cache, "v_cache"), _bf16_view(out, "out"))
+    sv = _i32_view(slot_idx, "slot_idx")
+    _raise_on(load_library().qsa_sparse_prefill_noalloc(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), ctypes.byref(sv),
+        _default_scale(scale, q.shape[-1]), ctypes.byref(ov), _stream(q.device)))
     return out
 
 

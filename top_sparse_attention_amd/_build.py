@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libqsa.so")
 ARCH = "gfx950"
 
 SOURCES = ["qsa_attend.hip", "qsa_compact.hip", "qsa_indexer.hip", "qsa_measure.hip",
-           "qsa_api.cpp"]
+           "qsa_noalloc.hip", "qsa_api.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

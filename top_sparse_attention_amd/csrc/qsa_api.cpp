@@ -27,6 +27,18 @@ qsa_status fail(qsa_status s, const char *fmt, ...) {
     return s;
 }
 
+}  // namespace
+
+int qsa::set_error(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+namespace {
+
 constexpr int64_t kAlign = 256;
 constexpr int64_t kMax32 = 0x7fffffff;
 // The sharing estimate's words in the workspace: est [kSharePairs][2] floats,
@@ -318,17 +330,12 @@ bool sharing_of(const Problem &pr, int32_t HB, void *ws, const qsa_workspace_map
     const int64_t chip = (int64_t)qsa::kXcds * qsa::kCusPerXcd * qsa::kItemsPerCU;
     if (pr.T < 2 || pr.T > kMax32 || per_t <= 0 || pr.T * per_t < 2 * chip || pr.S <= 0)
         return false;
-    // KV heads among the items one XCD runs (items are dealt round robin).
-    const int64_t period = per_t * qsa::kXcds / std::gcd(per_t, (int64_t)qsa::kXcds);
-    std::vector<char> seen(pr.Hkv, 0);
-    int heads = 0;
-    for (int64_t i = 0; i < period; i += qsa::kXcds) {
-        const int64_t g = (i % per_t) / HB;
-        if (!seen[g]) {
-            seen[g] = 1;
-            ++heads;
-        }
-    }
+    // KV heads among the items one XCD runs (items are dealt round robin, so
+    // XCD 0 runs items 0, 8, 16, ...: within a token, the item offsets that are
+    // multiples of d = gcd(per_t, 8)); KV head g owns offsets [g HB, (g+1) HB).
+    const int64_t d = std::gcd(per_t, (int64_t)qsa::kXcds);
+    int64_t heads = 0;
+    for (int64_t g = 0; g < pr.Hkv; ++g) heads += (g * HB + d - 1) / d * d < (g + 1) * HB;
     const double per_xcd = (double)qsa::kCusPerXcd * qsa::kItemsPerCU / heads;
     if (per_xcd * (double)m.row_stride >= kShareSizeBound * (double)pr.S) return false;
     char *base = (char *)ws + m.share_offset;

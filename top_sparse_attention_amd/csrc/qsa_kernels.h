@@ -241,6 +241,10 @@ struct StreamParams {
     uint32_t *sink;          // [workgroups]
 };
 
+// Sets the calling thread's qsa_last_error() text and returns `status`
+// (defined with the C-ABI layer).
+int set_error(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
 hipError_t launch_compact(const CompactParams &p, hipStream_t stream);
 hipError_t launch_stream_read(const StreamParams &p, int64_t workgroups, hipStream_t stream);
 hipError_t launch_indexer_scores(const IndexerScoreParams &p, hipStream_t stream);
