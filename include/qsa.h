@@ -183,16 +183,16 @@ qsa_status qsa_compact_blocks(const qsa_i32_view *block_idx, int64_t S,
  * by qsa_sparse_attend, the same operation and the same conventions
  * (qsa_check_status(workspace, ..., T, W * block_size, ...) reports invalid
  * entries).  With a workspace of qsa_prefill_blocks_workspace_bytes(T, W,
- * block_size) bytes, blocks of 4 slots or more, W <= 2304, rows of at most
- * 2,730 slots (W * block_size; the aligned row's room, 1.5 times that, must
- * fit 4,096 entries) and the sharing
- * of a long prefill (the layout choice of qsa_sparse_attend takes 8 items
- * per CU without an estimate), the compaction writes aligned lists instead,
- * after the standard layout: each token's part of every span of about 2,048
- * cache slots starts near a fixed place of its row (the gaps masked), so the
- * tokens running at one time reach each part of the cache together.  The
- * result then differs from the plain path's only in the summation order.
- * A workspace of qsa_workspace_bytes(T, W * block_size) runs the plain path.
+ * block_size) bytes, power-of-two blocks of 4 to 64 slots, W <= 2304 blocks
+ * and the sharing of a long prefill (the layout choice of qsa_sparse_attend
+ * takes 8 items per CU without an estimate), the compaction writes aligned
+ * lists instead, after the standard layout: block ids, not slots, where each
+ * token's part of every span of about 2,048 cache slots starts near a fixed
+ * place of its row (the gaps masked), so the tokens running at one time reach
+ * each part of the cache together; the attention expands every block into
+ * its slots.  The result then differs from the plain path's only in the
+ * summation order.  A workspace of qsa_workspace_bytes(T, W * block_size)
+ * runs the plain path.
  */
 size_t qsa_prefill_blocks_workspace_bytes(int64_t T, int64_t W, int32_t block_size);
 

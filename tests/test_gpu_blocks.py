@@ -81,11 +81,12 @@ def _key_bits(n):
 
 
 def aligned_lists_model(block_idx, S, bs):
-    """The aligned lists, written out from their rule: valid blocks grouped by
-    the compaction's 128 slot ranges (stable), super-ranges of at most 2,048
-    slots (unions of those ranges); super-range k starts at
-    max(previous end, min(k * F, room - slots still to place)), F =
-    ceil(1.25 * slots / ranges), room = 1.5 x the row's width in list pads."""
+    """The aligned lists, written out from their rule: valid block ids grouped
+    by the compaction's 128 ranges (stable), super-ranges of at most 2,048
+    slots (unions of those ranges); super-range k starts at list position
+    max(previous end, min(k * F, room - blocks still to place)), F =
+    ceil(1.125 * blocks / ranges), room = 1.5 x the row's width (in blocks)
+    rounded up to list pads.  Entries are block ids; the gaps hold -1."""
     T, W = block_idx.shape
     nb = S // bs
     group_shift = max(_key_bits(nb) - 8, 0)
@@ -94,30 +95,31 @@ def aligned_lists_model(block_idx, S, bs):
         by_size += 1
     shift = max(group_shift, by_size)
     R = -(-nb // (1 << shift))
-    room = -(-((W * bs * 3 + 1) // 2) // 32) * 32
+    room = -(-((W * 3 + 1) // 2) // 32) * 32
     rows = []
     for r in block_idx.astype(np.int64):
         valid = r[(r >= 0) & (r < nb)]
         valid = valid[np.argsort(valid >> group_shift, kind="stable")]
-        slots = len(valid) * bs
-        F = (5 * slots + 4 * R - 1) // (4 * R)
-        end, rem, out = 0, slots, []
+        n = len(valid)
+        F = (9 * n + 8 * R - 1) // (8 * R)
+        end, rem, out = 0, n, []
         for kk in range(R):
             seg = valid[(valid >> shift) == kk]
-            cs = len(seg) * bs
+            cs = len(seg)
             start = max(end, min(kk * F, room - rem)) if cs else end
             out += [-1] * (start - end)
-            out += (seg[:, None] * bs + np.arange(bs)[None, :]).ravel().tolist()
+            out += seg.tolist()
             end, rem = start + cs, rem - cs
         rows.append(np.array(out, dtype=np.int64))
     return rows, room
 
 
 @pytest.mark.parametrize("bs,S,nblocks", [(4, 8192, 200), (8, 16384, 120), (16, 4096, 40),
-                                          (5, 20000, 300), (64, 65536, 40)])
+                                          (32, 65536, 70), (64, 65536, 40), (4, 65536, 2300)])
 def test_aligned_block_lists_follow_their_rule(bs, S, nblocks):
-    """Index work, so bit-exact: the aligned rows the prefill writes into the
-    workspace equal the rule's, and the output meets the gate."""
+    """Index work, so bit-exact: the aligned rows (block ids) the prefill
+    writes into the workspace equal the rule's, and the output meets the
+    gate."""
     case = block_case(1050 + bs, T=19, S=S, Hq=16, Hkv=2, nblocks=nblocks, bs=bs, pad_frac=0.15,
                       interior=True)
     case.slot_idx[3] = -1                                  # an empty row
@@ -129,6 +131,7 @@ def test_aligned_block_lists_follow_their_rule(bs, S, nblocks):
     m = qsa.workspace_layout(case.T, case.W * bs)
     ext = -(-m["total_bytes"] // 256) * 256
     want, room = aligned_lists_model(case.slot_idx, S, bs)
+    assert nbytes == ext + -(-(case.T * room * 4) // 256) * 256
     ws32 = ws.view(torch.int32)
     rows = ws32[ext // 4: ext // 4 + case.T * room].view(case.T, room).cpu().numpy()
     count = ws32[m["count_offset"] // 4: m["count_offset"] // 4 + case.T].cpu().numpy()
@@ -215,19 +218,20 @@ def test_aligned_block_prefill_reports_invalid_blocks():
     print(gate(bf16_tensor_to_f32(out), ref, ~np.any(valid >= 0, axis=1)))
 
 
-def test_wide_block_rows_take_the_plain_lists():
-    """Rows whose aligned room would exceed 4,096 entries (here 200 blocks of 16:
-    3,200 slots) run the plain lists: the aligned area stays as it was, and the
-    output meets the gate."""
-    case = block_case(1080, T=21, S=16384, Hq=16, Hkv=2, nblocks=200, bs=16, pad_frac=0.1,
+@pytest.mark.parametrize("bs,S,nblocks", [(4, 65536, 2400), (5, 20000, 300), (2, 8192, 300)])
+def test_other_block_rows_take_the_plain_lists(bs, S, nblocks):
+    """Rows of more than one sort run (2,304 blocks), block sizes that are not
+    powers of two, and blocks of fewer than 4 slots run the plain lists: the
+    aligned area stays as it was, and the output meets the gate."""
+    case = block_case(1080 + bs, T=21, S=S, Hq=16, Hkv=2, nblocks=nblocks, bs=bs, pad_frac=0.1,
                       interior=True)
     q, k, v, sl = upload(case, DEV)
-    nbytes = qsa.prefill_blocks_workspace_bytes(case.T, case.W, 16)
+    nbytes = qsa.prefill_blocks_workspace_bytes(case.T, case.W, bs)
     ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV)
-    out = qsa.sparse_prefill_blocks(q, k, v, sl, 16, scale=case.scale, workspace=ws)
+    out = qsa.sparse_prefill_blocks(q, k, v, sl, bs, scale=case.scale, workspace=ws)
     torch.cuda.synchronize()
-    m = qsa.workspace_layout(case.T, case.W * 16)
+    m = qsa.workspace_layout(case.T, case.W * bs)
     ext = -(-m["total_bytes"] // 256) * 256
     assert torch.all(ws[ext:] == 0x7F)
-    ref = oracle.prefill_blocks(case.q, case.k_cache, case.v_cache, case.slot_idx, 16, 1.0 / 16.0)
+    ref = oracle.prefill_blocks(case.q, case.k_cache, case.v_cache, case.slot_idx, bs, 1.0 / 16.0)
     print(gate(bf16_tensor_to_f32(out), ref, empty_blocks(case)))

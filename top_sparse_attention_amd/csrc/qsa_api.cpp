@@ -272,6 +272,8 @@ int32_t sort_key_bits(int64_t n) {
 // number and the row room, or shift -1 for the plain list.
 struct AlignSpec {
     int32_t shift = -1, ranges = 0, cap = 0;
+    int32_t block_shift = 0;   // log2 of the block size
+    int32_t block_ids = 1;     // list entries are block ids (else each block's slots)
     int64_t list_offset = 0;   // of the aligned rows in the workspace
 };
 
@@ -295,6 +297,7 @@ qsa_status enqueue_compact(const qsa_i32_view *sl, int64_t T, int64_t W, int64_t
         p.align_shift = align->shift;
         p.align_ranges = align->ranges;
         p.align_cap = align->cap;
+        p.block_ids = align->block_ids;
         p.list = (int32_t *)((char *)ws + align->list_offset);
         p.row_stride = align->cap;
     }
@@ -376,6 +379,7 @@ qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
         p.list = (const int32_t *)((const char *)ws + align->list_offset);
         p.list_stride = align->cap;
         p.masked = 1;
+        p.block_shift = align->block_ids ? align->block_shift : 0;
         p.S_rows = pr.S;
         hipError_t e = qsa::launch_attend(p, kv.type, pr.T, stream, nullptr);
         return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
@@ -386,36 +390,44 @@ qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
     return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
 }
 
-// Room (slots) of an aligned row for a selection of Ws slots.
-int64_t align_room(int64_t Ws) {
-    return round_up((Ws * qsa::kAlignRoomNum + qsa::kAlignRoomDen - 1) / qsa::kAlignRoomDen,
+// Aligned rows hold block ids (the attention expands them) rather than each
+// block's slots.
+constexpr bool kAlignBlockIds = true;
+
+// Room (list entries) of an aligned row for a selection of W blocks.
+int64_t align_room(int64_t W, int32_t block_size) {
+    const int64_t unit = kAlignBlockIds ? 1 : block_size;
+    return round_up((W * unit * qsa::kAlignRoomNum + qsa::kAlignRoomDen - 1) / qsa::kAlignRoomDen,
                     qsa::kListPad);
 }
 
-// The standard layout for Ws slots, then the aligned rows (at *ext_offset).
-bool blocks_layout(int64_t T, int64_t Ws, qsa_workspace_map *m, int64_t *ext_offset,
-                   int64_t *total) {
-    if (!layout_of(T, Ws, m)) return false;
+// The standard layout for W * block_size slots, then the aligned rows (at
+// *ext_offset).
+bool blocks_layout(int64_t T, int64_t W, int32_t block_size, qsa_workspace_map *m,
+                   int64_t *ext_offset, int64_t *total) {
+    if (!layout_of(T, W * block_size, m)) return false;
     *ext_offset = round_up(m->total_bytes, kAlign);
-    *total = *ext_offset + round_up(T * align_room(Ws) * 4, kAlign);
+    *total = *ext_offset + round_up(T * align_room(W, block_size) * 4, kAlign);
     return true;
 }
 
 // Whether a micro-block prefill takes the aligned lists, and their spec:
-// blocks of kAlignMinBlock slots or more, rows of one sort run whose room fits
-// kAlignRoomMax, room in the workspace, and enough sharing that the general
-// layout runs without an estimate (the lists only help tokens that share the
-// L2).
+// power-of-two blocks of kAlignMinBlock to kAlignMaxBlock slots, rows of one
+// sort run whose room fits kAlignRoomMax, room in the workspace, and enough
+// sharing that the general layout runs without an estimate (the lists only
+// help tokens that share the L2).
 AlignSpec align_of(const Problem &pr, int64_t W, int32_t block_size, void *ws,
                    size_t ws_bytes, const qsa_workspace_map &m) {
     AlignSpec al;
-    const int64_t Ws = W * block_size, nb = pr.S / block_size;
-    if (block_size < qsa::kAlignMinBlock || W > qsa::kSortChunk || Ws <= 0 || nb <= 0 ||
+    const int64_t nb = pr.S / block_size;
+    if (block_size < qsa::kAlignMinBlock || block_size > qsa::kAlignMaxBlock ||
+        (block_size & (block_size - 1)) || W > qsa::kSortChunk || W <= 0 || nb <= 0 ||
         pr.Hkv <= 0)
         return al;
     qsa_workspace_map mb;
     int64_t ext = 0, total = 0;
-    if (!blocks_layout(pr.T, Ws, &mb, &ext, &total) || (int64_t)ws_bytes < total) return al;
+    if (!blocks_layout(pr.T, W, block_size, &mb, &ext, &total) || (int64_t)ws_bytes < total)
+        return al;
     qsa::SharingParams sp{};
     const int32_t HB = (pr.Hq / pr.Hkv + 15) / 16;
     if (sharing_of(pr, HB, ws, m, &sp)) return al;
@@ -424,11 +436,13 @@ AlignSpec align_of(const Problem &pr, int64_t W, int32_t block_size, void *ws,
     while (((int64_t)block_size << (by_size + 1)) <= qsa::kAlignSlots) ++by_size;
     shift = std::max(shift, by_size);
     const int64_t ranges = (nb + ((int64_t)1 << shift) - 1) >> shift;
-    if (ranges > qsa::kAlignMaxRanges || align_room(Ws) > qsa::kAlignRoomMax) return al;
+    if (ranges > qsa::kAlignMaxRanges || align_room(W, block_size) > qsa::kAlignRoomMax) return al;
     al.shift = shift;
     al.ranges = (int32_t)ranges;
-    al.cap = (int32_t)align_room(Ws);
+    al.cap = (int32_t)align_room(W, block_size);
+    al.block_ids = kAlignBlockIds;
     al.list_offset = ext;
+    while ((1 << al.block_shift) < block_size) ++al.block_shift;
     return al;
 }
 
@@ -655,7 +669,7 @@ size_t qsa_prefill_blocks_workspace_bytes(int64_t T, int64_t W, int32_t block_si
     if (T < 0 || W < 0 || block_size < 1 || block_size > 64 || W * block_size > kMax32) return 0;
     qsa_workspace_map m;
     int64_t ext = 0, total = 0;
-    if (!blocks_layout(T, W * block_size, &m, &ext, &total)) return 0;
+    if (!blocks_layout(T, W, block_size, &m, &ext, &total)) return 0;
     return (size_t)total;
 }
 

@@ -272,12 +272,25 @@ __device__ __forceinline__ int stand_in(int entry) {
 }
 
 // Masked rows (raw selection rows of decode shares, or aligned block lists):
-// entry of tile row (lane & 15), -1 past the row's W entries, 0 for a tile
-// past the row (a prefetch never used).
-__device__ __forceinline__ int tile_entry_masked(const int32_t *row, int tile, int ntiles, int W,
-                                                 int lane) {
+// the entry of tile row (lane & 15), -1 past the row's n entries, 0 for a tile
+// past the row (a prefetch never used).  Each entry names a block of 2^shift
+// slots (shift 0: a slot): tile row i reads entry i >> shift.  The loaded
+// entry is returned as it is: nothing may compute on it here, or the wave
+// would wait for the load (and, loads completing in order, for every gather
+// issued before it) at once; block_slot expands it a tile later.
+__device__ __forceinline__ int tile_entry_masked(const int32_t *row, int tile, int ntiles, int n,
+                                                 int shift, int lane) {
     const int i = tile * kTileSlots + (lane & 15);
-    return tile < ntiles ? (i < W ? row[i] : -1) : 0;
+    const int e = i >> shift;
+    return tile < ntiles ? (e < n ? row[e] : -1) : 0;
+}
+
+// The slot tile row (lane & 15) of tile `tile` gathers for entry b of a
+// masked list of 2^shift-slot blocks: (b << shift) + the row's offset in its
+// block; -1 and other negative entries stay as they are.
+__device__ __forceinline__ int block_slot(int b, int tile, int shift, int lane) {
+    const int i = tile * kTileSlots + (lane & 15);
+    return b >= 0 ? (b << shift) | (i & ((1 << shift) - 1)) : b;
 }
 
 // stand_in for masked rows: valid entries (in [0, S)) keep their slot; the
@@ -347,15 +360,18 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     // the selection width, -1 and invalid entries included.  Lists compacted
     // for more cache slots than the views hold are refused: the item reads
     // nothing (a zero row, or an empty share) and flags the workspace.
-    int n;
+    // Masked lists count entries of 2^shift slots each (micro-blocks).
+    const int shift = kMasked && !kRawRows ? p.block_shift : 0;
+    int n_entries;
     if constexpr (kRawRows) {
-        n = p.W_raw;
+        n_entries = p.W_raw;
     } else {
         const int cnt = p.count[t];
         const bool fits = (int64_t)p.extent[0] <= p.S_rows;
-        n = fits ? cnt : 0;
+        n_entries = fits ? cnt : 0;
         if (!fits && lane == 0) p.extent[1] = 1;
     }
+    const int n = n_entries << shift;   // slots of the row, gaps included
 
     const int ntiles = (n + kTileSlots - 1) / kTileSlots;
     // Raw rows: the share of (g = 0, head block 0) reports the invalid entries.
@@ -388,14 +404,19 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     const int32_t *list = kRawRows ? p.raw + t * p.raw_stride : p.list + t * p.list_stride;
     // The next list entries of this lane's tile row (compacted list or raw row).
     auto entry_at = [&](int tl) {
-        return kMasked ? tile_entry_masked(list, tl, ntiles, n, lane) : tile_slot(list, tl, ntiles, lane);
+        return kMasked ? tile_entry_masked(list, tl, ntiles, n_entries, shift, lane)
+                       : tile_slot(list, tl, ntiles, lane);
     };
     // Masked rows: the valid-row mask and invalid count of the tile being
     // computed (cur) and of the tile whose gathers were issued last (next).
     uint32_t valid_cur = 0xffffu, valid_next = 0xffffu;
     int bad_next = 0, bad_total = 0;
-    auto resolve = [&](int entry) {
-        if constexpr (kMasked) return stand_in_masked(entry, p.S_rows, &valid_next, &bad_next);
+    // The slot a tile row gathers, from its list entry (loaded a tile
+    // earlier) and the tile's index.
+    auto resolve = [&](int entry, int tl) {
+        if constexpr (kMasked)
+            return stand_in_masked(block_slot(entry, tl, shift, lane), p.S_rows, &valid_next,
+                                   &bad_next);
         else return stand_in(entry);
     };
     const char *kb = (const char *)p.k + (int64_t)g * p.k_sh * Gth::kElemBytes;
@@ -437,7 +458,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     int slot_next = entry_at(tile);
 #pragma unroll
     for (int b = 0; b < kAhead; ++b) {
-        const int slot = resolve(slot_next);
+        const int slot = resolve(slot_next, tile + b * step);
         gather_k<KV>(rkb[b], slot, kb, k_ss, lane);
         slot_next = entry_at(tile + (b + 1) * step);
         gather_v<KV, kScalarVAddr>(rvb[b], slot, vb, v_ss, lane);
@@ -495,7 +516,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
             bad_total += bad_next;
         }
         int slot_g = 0;
-        if constexpr (KV == KvType::kFp8) slot_g = resolve(slot_next);
+        if constexpr (KV == KvType::kFp8) slot_g = resolve(slot_next, tile + kAhead * step);
         __builtin_amdgcn_sched_barrier(0);   // K(i) is consumed before K(i+1) lands
         if constexpr (KV == KvType::kFp8) {
 #pragma unroll
@@ -548,7 +569,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         wave_lds_fence();   // the previous tile's transpose reads are done
         stage_v<KV, Lay::kVPitch>(rv, vs_lds, lane);
         __builtin_amdgcn_sched_barrier(0);   // V(i) is consumed before V(i+1) lands
-        if constexpr (KV == KvType::kBf16) slot_g = resolve(slot_next);
+        if constexpr (KV == KvType::kBf16) slot_g = resolve(slot_next, tile + kAhead * step);
         slot_next = entry_at(tile + (kAhead + 1) * step);
         gather_v<KV, kScalarVAddr>(rv, slot_g, vb, v_ss, lane);
         wave_lds_fence();   // other lanes of this wave wrote the rows read below

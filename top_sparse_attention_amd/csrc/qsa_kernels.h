@@ -54,17 +54,23 @@ constexpr int kSortChunk = kSortThreads * kSortItemsPerThread;   // 2304
 constexpr int kSortKeyBits = 8;
 // Aligned block lists: super-ranges of about kAlignSlots cache slots (half the
 // rows of one head an XCD's 4 MB L2 holds), at most kAlignMaxRanges of them
-// (the sort's 128 groups), and the room a row may take: kAlignRoomNum /
-// kAlignRoomDen of its slots.
+// (the sort's 128 groups); the room a row may take, kAlignRoomNum /
+// kAlignRoomDen of its blocks; and the slack of the fixed start positions:
+// super-range k starts near k F, F = kAlignSlackNum / kAlignSlackDen times
+// the row's mean blocks per super-range.
 constexpr int kAlignSlots = 2048;
 constexpr int kAlignMaxRanges = 1 << (kSortKeyBits - 1);
 constexpr int kAlignRoomNum = 3, kAlignRoomDen = 2;
+constexpr int kAlignSlackNum = 9, kAlignSlackDen = 8;
 // Largest room of an aligned row (entries): the compaction builds the row in
 // LDS before storing it.
 constexpr int kAlignRoomMax = 4096;
-// Smallest block size that takes the aligned lists (2-slot blocks measured
-// within 2%, single slots 4% slower with them).
+// Block sizes that take the aligned lists: powers of two from kAlignMinBlock
+// (2-slot blocks measured within 2%, single slots 4% slower with them) to
+// kAlignMaxBlock (the attention expands list entry e of a tile row as
+// slot e << log2(block) + the row's offset in the block).
 constexpr int kAlignMinBlock = 4;
+constexpr int kAlignMaxBlock = 64;
 
 struct CompactParams {
     const int32_t *slot_idx;
@@ -75,14 +81,16 @@ struct CompactParams {
                          // (S, lo, hi counted in entries of this size)
     int32_t key_bits;    // radix-sort key width: hi - lo - 1 < 2^(key_bits-1), plus one bit for padding
     // Aligned lists (align_shift >= 0; rows of at most kSortChunk entries):
-    // the entries of super-range k (entry key >> align_shift, k < align_ranges
-    // <= kAlignMaxRanges, a union of the sort's slot ranges) start at slot
-    // position max(end of the previous ones, min(k F, align_cap - slots
-    // still to place)), F = ceil(1.25 * row slots / align_ranges); the gaps
-    // hold -1 and count[t] is the end of the last.  align_cap <= row_stride.
+    // block ids, not slots.  The entries of super-range k (entry key >>
+    // align_shift, k < align_ranges <= kAlignMaxRanges, a union of the sort's
+    // slot ranges) start at list position max(end of the previous ones,
+    // min(k F, align_cap - entries still to place)), F = ceil(slack * row
+    // entries / align_ranges); the gaps hold -1 and count[t] is the end of
+    // the last.  align_cap <= row_stride.
     int32_t align_shift;
     int32_t align_ranges;
     int32_t align_cap;
+    int32_t block_ids;   // aligned lists hold block ids (1) or each block's slots (0)
     int32_t *list;
     int64_t row_stride;
     int32_t *count;
@@ -132,7 +140,9 @@ struct AttendParams {
     int64_t units;
     // Unsplit items over a compacted list with -1 gaps (the aligned block
     // lists; masked = 1, BF16, S_rows = S): entries are masked per tile row.
+    // Each entry is a block of 2^block_shift slots; count[t] counts entries.
     int32_t masked;
+    int32_t block_shift;
     // Split mode over raw selection rows (raw_rows = 1; BF16 only): each share
     // reads slot_idx row t itself (W_raw entries, -1 and invalid entries
     // included; valid means in [0, S_rows)) instead of a compacted list, and
