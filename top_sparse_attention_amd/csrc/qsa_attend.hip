@@ -335,7 +335,6 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
                                             char *smem) {
     using Gth = KvGather<KV>;
     using Lay = AttendLayout<kQRows, kItems>;
-    static_assert(!kMasked || Lay::kAhead == 1, "masked rows: one tile ahead");
     constexpr bool kRawRows = kMasked && kSplit;
 
     int lane = threadIdx.x;
@@ -407,16 +406,26 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         return kMasked ? tile_entry_masked(list, tl, ntiles, n_entries, shift, lane)
                        : tile_slot(list, tl, ntiles, lane);
     };
+    // Tiles of gathers in flight per wave (the layout's; two measured slower
+    // for the decode step's split shares too: 25.4 against 24.6 us).
+    constexpr int kAhead = Lay::kAhead;
     // Masked rows: the valid-row mask and invalid count of the tile being
-    // computed (cur) and of the tile whose gathers were issued last (next).
-    uint32_t valid_cur = 0xffffu, valid_next = 0xffffu;
-    int bad_next = 0, bad_total = 0;
+    // computed (cur) and of the tiles whose gathers are in flight, one per
+    // register buffer (q).
+    uint32_t valid_cur = 0xffffu, valid_q[kAhead];
+    int bad_q[kAhead], bad_total = 0;
+#pragma unroll
+    for (int b = 0; b < kAhead; ++b) {
+        valid_q[b] = 0xffffu;
+        bad_q[b] = 0;
+    }
     // The slot a tile row gathers, from its list entry (loaded a tile
-    // earlier) and the tile's index.
-    auto resolve = [&](int entry, int tl) {
+    // earlier) and the tile's index; masked rows record the tile's mask in
+    // register buffer b.
+    auto resolve = [&](int entry, int tl, int b) {
         if constexpr (kMasked)
-            return stand_in_masked(block_slot(entry, tl, shift, lane), p.S_rows, &valid_next,
-                                   &bad_next);
+            return stand_in_masked(block_slot(entry, tl, shift, lane), p.S_rows, &valid_q[b],
+                                   &bad_q[b]);
         else return stand_in(entry);
     };
     const char *kb = (const char *)p.k + (int64_t)g * p.k_sh * Gth::kElemBytes;
@@ -445,7 +454,6 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     // vector is loaded before the V gathers of the tile ahead of it, so
     // waiting for it never waits for those.  (Two tiles ahead measured no
     // faster.)
-    constexpr int kAhead = Lay::kAhead;
     // V row addresses in scalar registers for BF16 at 8 items per CU (the
     // vector form measured 4% slower there: its 64-bit multiplies take vector
     // issue slots); in vector registers for the FP8 layout (12 items per CU,
@@ -458,7 +466,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     int slot_next = entry_at(tile);
 #pragma unroll
     for (int b = 0; b < kAhead; ++b) {
-        const int slot = resolve(slot_next, tile + b * step);
+        const int slot = resolve(slot_next, tile + b * step, b);
         gather_k<KV>(rkb[b], slot, kb, k_ss, lane);
         slot_next = entry_at(tile + (b + 1) * step);
         gather_v<KV, kScalarVAddr>(rvb[b], slot, vb, v_ss, lane);
@@ -484,7 +492,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     // One tile: consumes K(tile) and V(tile) from rk and rv and issues the
     // gathers of tile + kAhead * step into the same registers.
     auto tile_body = [&](const int tile, u32x4_t (&rk)[Gth::kKLoads],
-                         u32x4_t (&rv)[Gth::kVLoads]) {
+                         u32x4_t (&rv)[Gth::kVLoads], const int b) {
         // S^T for the tile: s[i] = score of tile slot 4j+i against head c.
         // The query operands are read from LDS in two halves to bound the
         // registers they hold.
@@ -511,12 +519,12 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         // The next tile's slots: FP8 needs them here; BF16 resolves them after
         // V(i) is staged, where that wait has already covered their load (a
         // resolve here would wait for V(i) before the scores).
-        if constexpr (kMasked) {   // this tile's mask and count, resolved a tile ago
-            valid_cur = valid_next;
-            bad_total += bad_next;
+        if constexpr (kMasked) {   // this tile's mask and count, resolved when its gathers went out
+            valid_cur = valid_q[b];
+            bad_total += bad_q[b];
         }
         int slot_g = 0;
-        if constexpr (KV == KvType::kFp8) slot_g = resolve(slot_next, tile + kAhead * step);
+        if constexpr (KV == KvType::kFp8) slot_g = resolve(slot_next, tile + kAhead * step, b);
         __builtin_amdgcn_sched_barrier(0);   // K(i) is consumed before K(i+1) lands
         if constexpr (KV == KvType::kFp8) {
 #pragma unroll
@@ -569,7 +577,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         wave_lds_fence();   // the previous tile's transpose reads are done
         stage_v<KV, Lay::kVPitch>(rv, vs_lds, lane);
         __builtin_amdgcn_sched_barrier(0);   // V(i) is consumed before V(i+1) lands
-        if constexpr (KV == KvType::kBf16) slot_g = resolve(slot_next, tile + kAhead * step);
+        if constexpr (KV == KvType::kBf16) slot_g = resolve(slot_next, tile + kAhead * step, b);
         slot_next = entry_at(tile + (kAhead + 1) * step);
         gather_v<KV, kScalarVAddr>(rv, slot_g, vb, v_ss, lane);
         wave_lds_fence();   // other lanes of this wave wrote the rows read below
@@ -605,7 +613,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
 #pragma unroll
         for (int b = 0; b < kAhead; ++b) {
             if (b > 0 && tile + b * step >= ntiles) break;
-            tile_body(tile + b * step, rkb[b], rvb[b]);
+            tile_body(tile + b * step, rkb[b], rvb[b], b);
         }
     }
 
@@ -664,8 +672,11 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
 // out[t, h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the parts s,
 // M = max_s m_s; exactly +0.0 when no part saw a slot.  One wave per (t, h)
 // row, 4 dims per lane.  Lane s of each run of 64 parts loads part s's (m, l)
-// and computes its weight; the O rows are then read 8 parts at a time, all 8
-// loads in flight together, each scaled by its part's weight (a readlane).
+// and computes its weight; the O rows are then read kMergeBatch parts at a
+// time, all of a batch's loads in flight together, each scaled by its part's
+// weight (a readlane).  (Batches of 32 measured no faster on the decode step.)
+constexpr int kMergeBatch = 8;
+
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -702,15 +713,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
                 l_part += w * p.part_ml[(s * rows + row) * 2 + 1];
             }
             const int cnt = (int)min<int64_t>(64, n - s0);
-            for (int u = 0; u < cnt; u += 8) {
-                f32x4_t o[8];
+            for (int u = 0; u < cnt; u += kMergeBatch) {
+                f32x4_t o[kMergeBatch];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < kMergeBatch; ++e)
                     o[e] = u + e < cnt ? *(const f32x4_t *)(p.part_o + ((s0 + u + e) * rows + row) *
                                                                        kHeadDim + 4 * lane)
                                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < kMergeBatch; ++e)
                     if (u + e < cnt)   // lane u + e holds that part's weight
                         acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u + e)) *
                                o[e];

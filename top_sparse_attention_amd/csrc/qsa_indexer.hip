@@ -6,9 +6,6 @@
 #include <algorithm>
 #include <stdint.h>
 
-#include <hipcub/block/block_reduce.hpp>
-#include <hipcub/block/block_scan.hpp>
-
 #include "qsa_device.h"
 #include "qsa_kernels.h"
 
@@ -138,6 +135,54 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
     }
 }
 
+// Exclusive prefix sum of x over the 256 threads of a workgroup, in thread
+// order, and the workgroup's total: a 64-lane scan per wave, then the four
+// wave sums through LDS (wave_sums, 4 ints).  Every thread calls it; it
+// returns with the workgroup in step, so wave_sums may be reused at once.
+__device__ __forceinline__ int block_exclusive_sum(int x, int *total, int *wave_sums) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wave_sums[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int c = wave_sums[w];
+        before += w < wave ? c : 0;
+        all += c;
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - x;
+}
+
+// Minimum and maximum of (lo, hi) over the 256 threads of a workgroup, for
+// every thread (wave_lo, wave_hi: 4 floats of LDS each).
+__device__ __forceinline__ void block_min_max(float *lo, float *hi, float *wave_lo,
+                                              float *wave_hi) {
+    float a = *lo, b = *hi;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        a = fminf(a, __shfl_xor(a, off));
+        b = fmaxf(b, __shfl_xor(b, off));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        wave_lo[threadIdx.x >> 6] = a;
+        wave_hi[threadIdx.x >> 6] = b;
+    }
+    __syncthreads();
+    a = fminf(fminf(wave_lo[0], wave_lo[1]), fminf(wave_lo[2], wave_lo[3]));
+    b = fmaxf(fmaxf(wave_hi[0], wave_hi[1]), fmaxf(wave_hi[2], wave_hi[3]));
+    __syncthreads();
+    *lo = a;
+    *hi = b;
+}
+
 // Order-preserving map of FP32 to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t score_key(float x) {
     const uint32_t u = __float_as_uint(x);
@@ -223,18 +268,13 @@ __device__ void radix_select(int n, int need, ScoreAt score_at, InSet in_set, in
 // one or two bins; the linear buckets spread them.
 template <bool kInLds>
 __device__ void select_exact(const IndexerSelectParams &p, int n, const float *row, int32_t *out) {
-    using Scan = hipcub::BlockScan<int, 256>;
-    using Reduce = hipcub::BlockReduce<float, 256>;
     __shared__ float vals[kInLds ? kSelectLdsBlocks : 1];
     __shared__ int hist[256];
     __shared__ int chunk_gt[256], chunk_eq[256];
-    __shared__ union {
-        typename Scan::TempStorage scan;
-        typename Reduce::TempStorage reduce;
-    } tmp;
+    __shared__ int wave_sums[4];
+    __shared__ float wave_lo[4], wave_hi[4];
     __shared__ uint32_t sh_prefix;
     __shared__ int sh_need;
-    __shared__ float sh_lo, sh_hi;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // Row statistics (and the LDS copy): 16-byte loads, four in flight per
@@ -275,16 +315,7 @@ __device__ void select_exact(const IndexerSelectParams &p, int n, const float *r
     uint32_t tau = 0;
     int need = n;   // n <= budget: every key (all > 0) is kept
     if (n > p.budget) {
-        lo = Reduce(tmp.reduce).Reduce(lo, [](float a, float b) { return fminf(a, b); });
-        __syncthreads();
-        hi = Reduce(tmp.reduce).Reduce(hi, [](float a, float b) { return fmaxf(a, b); });
-        if (tid == 0) {
-            sh_lo = lo;
-            sh_hi = hi;
-        }
-        __syncthreads();
-        lo = sh_lo;
-        hi = sh_hi;
+        block_min_max(&lo, &hi, wave_lo, wave_hi);
         const float inv = hi > lo ? 256.0f / (hi - lo) : 0.0f;
         auto bucket = [&](float x) { return min(255, (int)((x - lo) * inv)); };
         // Step 1: the bucket holding the budget-th largest score.
@@ -340,11 +371,9 @@ __device__ void select_exact(const IndexerSelectParams &p, int n, const float *r
         }
         __syncthreads();
         int my_gt = tid < gn ? chunk_gt[tid] : 0, my_eq = tid < gn ? chunk_eq[tid] : 0;
-        int gt_pre, eq_pre, gt_tot, eq_tot;
-        Scan(tmp.scan).ExclusiveSum(my_gt, gt_pre, gt_tot);
-        __syncthreads();
-        Scan(tmp.scan).ExclusiveSum(my_eq, eq_pre, eq_tot);
-        __syncthreads();
+        int gt_tot, eq_tot;
+        const int gt_pre = block_exclusive_sum(my_gt, &gt_tot, wave_sums);
+        const int eq_pre = block_exclusive_sum(my_eq, &eq_tot, wave_sums);
         if (tid < gn) {
             chunk_gt[tid] = gt_pre;
             chunk_eq[tid] = eq_pre;
@@ -454,11 +483,10 @@ __global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel
     // One 16-byte sample load per thread; runs 16 apart or more once n > kCand >= kSelSample.
     static_assert(kSelSample == 4 * 256, "sample runs");
     constexpr int kCandPadded = kCand + kCand / 16;
-    using Scan = hipcub::BlockScan<int, 256>;
     __shared__ float cval[kCandPadded];
     __shared__ int cid[kCandPadded];
     __shared__ int hist[256];
-    __shared__ typename Scan::TempStorage scan;
+    __shared__ int wave_sums[4];
     __shared__ uint32_t sh_prefix;
     __shared__ int sh_need;
 
@@ -542,8 +570,8 @@ __global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel
 #pragma unroll
             for (int e = 0; e < kSelPerThread; ++e)
                 cnt += i0 + e < n && score_key(v[e]) >= tau0;
-            int off, total;
-            Scan(scan).ExclusiveSum(cnt, off, total);
+            int total;
+            const int off = block_exclusive_sum(cnt, &total, wave_sums);
             if (nc + total <= kCand) {
                 int w = nc + off;
 #pragma unroll
@@ -556,7 +584,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel
                 }
             }
             nc += total;
-            __syncthreads();   // the scan storage is reused
+            __syncthreads();   // this slice's candidates are in place
 #pragma unroll
             for (int e = 0; e < kSelPerThread; ++e) {
                 v[e] = v1[e];
@@ -593,10 +621,9 @@ __global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel
                     eq += u == tau;
                 }
             }
-            int gt_pre, eq_pre, total;
-            Scan(scan).ExclusiveSum(gt, gt_pre, total);
-            __syncthreads();
-            Scan(scan).ExclusiveSum(eq, eq_pre, total);
+            int total;
+            int gt_pre = block_exclusive_sum(gt, &total, wave_sums);
+            int eq_pre = block_exclusive_sum(eq, &total, wave_sums);
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
                 const int i = kPer * tid + k;
