@@ -13,7 +13,10 @@
 #include <vector>
 
 #include "qsa.h"
+#include "qsa_errors.h"
+#include "qsa_indexer.h"
 #include "qsa_kernels.h"
+#include "qsa_measure.h"
 
 namespace {
 

@@ -8,6 +8,7 @@
 
 #include "qsa_device.h"
 #include "qsa_kernels.h"
+#include "qsa_indexer.h"
 
 namespace qsa {
 namespace {

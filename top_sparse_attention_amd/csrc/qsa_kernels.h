@@ -212,53 +212,7 @@ struct GatherParams {
     const int32_t *extent;       // the workspace's extent word (see CompactParams)
 };
 
-// QSA indexer: 4 query heads sharing one key head, head dim 128, one key per
-// block of 4 positions.
-constexpr int kIndexHeads = 4;
-constexpr int kIndexDim = 128;
-constexpr int kIndexBlock = 4;
-// Blocks per row that the select kernel keeps in LDS (larger rows are read
-// from global memory on every pass).
-constexpr int kSelectLdsBlocks = 16384;
-
-struct IndexerScoreParams {
-    const uint16_t *iq;       // [T, 4, 128]
-    int64_t q_st, q_sh;
-    const uint16_t *ik;       // [C, 128]
-    int64_t k_st;
-    int64_t T, C;
-    const int32_t *positions; // [T]
-    float *scores;            // [T, C]
-};
-
-struct IndexerSelectParams {
-    const float *scores;      // [T, C]
-    int64_t T, C;
-    const int32_t *positions; // [T]; a row whose position is outside [0, L) is all -1
-    const int32_t *slot_of_pos; // [L]
-    int64_t L;
-    int32_t budget;
-    int32_t *out;             // [T, out_stride], width 4 * budget + 3
-    int64_t out_stride;
-};
-
-// Streaming read (measurement only): `workgroups` workgroups each read
-// chunks_per_wg 16-byte chunks of a footprint of footprint_chunks chunks.
-struct StreamParams {
-    const void *buf;
-    int64_t footprint_chunks;
-    int64_t chunks_per_wg;   // <= footprint_chunks
-    uint32_t *sink;          // [workgroups]
-};
-
-// Sets the calling thread's qsa_last_error() text and returns `status`
-// (defined with the C-ABI layer).
-int set_error(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
-
 hipError_t launch_compact(const CompactParams &p, hipStream_t stream);
-hipError_t launch_stream_read(const StreamParams &p, int64_t workgroups, hipStream_t stream);
-hipError_t launch_indexer_scores(const IndexerScoreParams &p, hipStream_t stream);
-hipError_t launch_indexer_select(const IndexerSelectParams &p, hipStream_t stream);
 // With a non-null `share`, the sharing estimate runs first and picks the
 // layout (general-layout kernels only; others ignore it).
 hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_t stream,

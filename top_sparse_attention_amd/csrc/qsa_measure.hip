@@ -11,6 +11,7 @@
 
 #include "qsa_device.h"
 #include "qsa_kernels.h"
+#include "qsa_measure.h"
 
 namespace qsa {
 namespace {

@@ -16,7 +16,7 @@
 #include <stdint.h>
 
 #include "qsa.h"
-#include "qsa_kernels.h"
+#include "qsa_errors.h"
 
 namespace {
 
