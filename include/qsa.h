@@ -121,8 +121,8 @@ const char *qsa_status_string(qsa_status status);
 /* Message for the last non-OK status returned on the calling thread. */
 const char *qsa_last_error(void);
 
-/* Workspace bytes needed for T tokens of W selection entries (T, W >= 0).
- * Returns 0 for negative sizes. */
+/* Workspace bytes needed for T tokens of W selection entries (0 <= T, W <
+ * 2^31).  Returns 0 for sizes outside that range. */
 size_t qsa_workspace_bytes(int64_t T, int64_t W);
 
 /* The same size under the name of the prefill it serves (qsa_sparse_prefill,

@@ -72,9 +72,14 @@ int32_t *extent_words(const void *ws, const qsa_workspace_map &m) {
     return (int32_t *)((char *)ws + m.share_offset + kExtentOffset);
 }
 
+// Workspace sizes beyond this many list entries are refused (far beyond any
+// device memory; it keeps every byte offset within int64).
+constexpr int64_t kMaxListEntries = (int64_t)1 << 56;
+
 bool layout_of(int64_t T, int64_t W, qsa_workspace_map *m) {
-    if (T < 0 || W < 0) return false;
+    if (T < 0 || W < 0 || T > kMax32 || W > kMax32) return false;
     const int64_t row = round_up(W, qsa::kListPad);
+    if (mul_sat(T, row) > kMaxListEntries) return false;
     m->list_offset = 0;
     m->row_stride = row;
     m->count_offset = round_up(T * row * 4, kAlign);
@@ -137,7 +142,7 @@ qsa_status check_bf16(const qsa_bf16_view *v, const char *name) {
 
 qsa_status check_workspace(const void *ws, size_t bytes, int64_t T, int64_t W,
                            qsa_workspace_map *m) {
-    if (!layout_of(T, W, m)) return fail(QSA_ERR_SHAPE, "negative T or W");
+    if (!layout_of(T, W, m)) return fail(QSA_ERR_SHAPE, "T and W must be in [0, 2^31)");
     if (!ws) return fail(QSA_ERR_WORKSPACE, "workspace is NULL");
     if ((uintptr_t)ws % kAlign) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if ((int64_t)bytes < m->total_bytes)
@@ -409,8 +414,10 @@ int64_t align_room(int64_t W, int32_t block_size) {
 bool blocks_layout(int64_t T, int64_t W, int32_t block_size, qsa_workspace_map *m,
                    int64_t *ext_offset, int64_t *total) {
     if (!layout_of(T, W * block_size, m)) return false;
+    const int64_t entries = mul_sat(T, align_room(W, block_size));
+    if (entries > kMaxListEntries) return false;
     *ext_offset = round_up(m->total_bytes, kAlign);
-    *total = *ext_offset + round_up(T * align_room(W, block_size) * 4, kAlign);
+    *total = *ext_offset + round_up(entries * 4, kAlign);
     return true;
 }
 
@@ -456,7 +463,8 @@ struct PartialsMap {
 
 bool partials_of(int64_t n_parts, int64_t T, int64_t Hq, PartialsMap *pm) {
     if (n_parts < 0 || T < 0 || Hq < 0) return false;
-    const int64_t rows = n_parts * T * Hq;
+    const int64_t rows = mul_sat(mul_sat(n_parts, T), Hq);
+    if (rows > kMaxListEntries / qsa::kHeadDim) return false;
     pm->ml_offset = round_up(rows * qsa::kHeadDim * 4, kAlign);
     pm->total_bytes = pm->ml_offset + round_up(rows * 8, kAlign);
     return true;
@@ -528,10 +536,10 @@ qsa_status enqueue_merge(const void *partials, const PartialsMap &pm, int64_t n_
 int32_t decode_splits(int64_t T, int64_t W, int32_t Hq, int32_t Hkv) {
     if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0) return 1;
     const int64_t G = Hq / Hkv;
-    const int64_t items = T * Hkv * ((G + 15) / 16);
-    const int64_t tiles = (W + qsa::kTileSlots - 1) / qsa::kTileSlots;
+    const int64_t items = mul_sat(mul_sat(T, Hkv), (G + 15) / 16);
+    const int64_t tiles = ceil_div(W, qsa::kTileSlots);
     const int64_t target_blocks = 2048;
-    int64_t s = (target_blocks + items - 1) / items;
+    int64_t s = ceil_div(target_blocks, items);
     s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / qsa::kMinSplitTiles));
     s = std::min<int64_t>(s, 64);
     return (int32_t)std::max<int64_t>(s, 1);
@@ -594,7 +602,7 @@ size_t qsa_sparse_prefill_workspace_bytes(int64_t T, int64_t W) { return qsa_wor
 
 qsa_status qsa_workspace_layout(int64_t T, int64_t W, qsa_workspace_map *map) {
     if (!map) return fail(QSA_ERR_NULL, "map is NULL");
-    if (!layout_of(T, W, map)) return fail(QSA_ERR_SHAPE, "negative T or W");
+    if (!layout_of(T, W, map)) return fail(QSA_ERR_SHAPE, "T and W must be in [0, 2^31)");
     return QSA_OK;
 }
 
@@ -669,7 +677,7 @@ qsa_status qsa_sparse_prefill_blocks(const qsa_bf16_view *q, const qsa_bf16_view
 }
 
 size_t qsa_prefill_blocks_workspace_bytes(int64_t T, int64_t W, int32_t block_size) {
-    if (T < 0 || W < 0 || block_size < 1 || block_size > 64 || W * block_size > kMax32) return 0;
+    if (T < 0 || W < 0 || block_size < 1 || block_size > 64 || W > kMax32 / block_size) return 0;
     qsa_workspace_map m;
     int64_t ext = 0, total = 0;
     if (!blocks_layout(T, W, block_size, &m, &ext, &total)) return 0;
@@ -711,9 +719,10 @@ qsa_status check_scores_grid(int64_t T, int64_t C) {
 qsa_status check_scores(const void *scores, size_t bytes, int64_t T, int64_t C) {
     if (T > 0 && C > 0 && !scores) return fail(QSA_ERR_WORKSPACE, "scores buffer is NULL");
     if ((uintptr_t)scores % 16) return fail(QSA_ERR_WORKSPACE, "scores must be 16-byte aligned");
-    if ((int64_t)bytes < T * C * 4)
+    const int64_t need = mul_sat(mul_sat(T, C), 4);
+    if ((int64_t)bytes < need)
         return fail(QSA_ERR_WORKSPACE, "scores buffer holds %zu bytes, %lld needed", bytes,
-                    (long long)(T * C * 4));
+                    (long long)need);
     return QSA_OK;
 }
 
@@ -1069,7 +1078,8 @@ qsa_status qsa_sparse_prefill_fp8kv(const qsa_bf16_view *q, const qsa_fp8_view *
 }
 
 size_t qsa_indexer_scores_bytes(int64_t T, int64_t C) {
-    return (T < 0 || C < 0) ? 0 : (size_t)(T * C * 4);
+    const int64_t need = mul_sat(mul_sat(T, C), 4);
+    return (T < 0 || C < 0 || need == INT64_MAX) ? 0 : (size_t)need;
 }
 
 qsa_status qsa_indexer_scores(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
