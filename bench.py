@@ -192,6 +192,8 @@ def main():
         iq = to_dev(case.info["iq"].view(np.int16)).view(torch.bfloat16)
         ik = to_dev(case.info["ik"].view(np.int16)).view(torch.bfloat16)
         ipos, isop = to_dev(case.info["positions"]), to_dev(case.info["slot_of_pos"])
+        # The [T, C] FP32 scores the indexer writes and the Top-K reads (the
+        # faster of the two Top-K paths on MI355X).
         iscores = torch.empty((T, ik.shape[0]), dtype=torch.float32, device=dev)
         budget = case.info["budget"]
 

@@ -430,11 +430,29 @@ qsa_status qsa_gather_only_fp8kv(const qsa_fp8_view *k_cache,
  *    2,051-wide rows of the long prefill.
  * Positions outside [0, L) give an all -1 row.  iq is [T, 4, 128], ik
  * [C, 1, 128] (BF16, rows 16-byte aligned); positions, slot_of_pos, scores
- * and slot_idx are device memory.  scores is caller-owned FP32 [T, C]
- * scratch (qsa_indexer_scores_bytes); entries past a query's causal limit are
- * left unspecified.
+ * and slot_idx are device memory.  qsa_indexer_scores writes FP32 [T, C]
+ * scores (entries past a query's causal limit are left unspecified) and
+ * needs qsa_indexer_scores_bytes(T, C) = T * C * 4 bytes;
+ * qsa_indexer_select reads them.  qsa_indexer_topk is the two in one call,
+ * with `scores` as caller-owned scratch of that size.
+ *
+ * qsa_indexer_topk_fused computes the same selection without writing the
+ * full score matrix, in caller-owned scratch of
+ * qsa_indexer_topk_fused_bytes(T, C) bytes (8-byte aligned): a threshold
+ * sampled per token (256 scores of blocks spread over the causal range, the
+ * key about sqrt(budget * 4096) * 256 / n from the top, its top 16 bits),
+ * the scores recomputed and only those at or above it kept as (score,
+ * block) candidates per 1,024-block range, and the exact selection on at
+ * most 4,096 candidates.  Rows where the threshold keeps fewer than
+ * `budget` or more than 4,096 candidates (or more than 512 in one range)
+ * get their full scores and the exact selection, so the result is the same
+ * either way.  It takes budgets up to 512 and C up to 262,144 (else
+ * QSA_ERR_UNSUPPORTED).  On MI355X it is the slower of the two (the
+ * candidate pass is issue-bound, not memory-bound), so qsa_indexer_topk
+ * does not use it.
  */
 size_t qsa_indexer_scores_bytes(int64_t T, int64_t C);
+size_t qsa_indexer_topk_fused_bytes(int64_t T, int64_t C);
 
 qsa_status qsa_indexer_scores(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
                               const int32_t *positions, float *scores,
@@ -452,6 +470,14 @@ qsa_status qsa_indexer_topk(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
                             const int32_t *slot_of_pos, int64_t L,
                             int32_t budget, float *scores, size_t scores_bytes,
                             qsa_i32_view *slot_idx, void *stream);
+
+/* The same selection by the fused path (scratch: `scratch_bytes` >=
+ * qsa_indexer_topk_fused_bytes(T, C)). */
+qsa_status qsa_indexer_topk_fused(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
+                                  const int32_t *positions,
+                                  const int32_t *slot_of_pos, int64_t L,
+                                  int32_t budget, void *scratch, size_t scratch_bytes,
+                                  qsa_i32_view *slot_idx, void *stream);
 
 #ifdef __cplusplus
 }

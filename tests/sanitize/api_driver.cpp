@@ -250,14 +250,41 @@ void indexer() {
     const int32_t budget = 512;
     qsa_bf16_view iq = view3(1, T, 4, 128), ik = view3(2, C, 1, 128);
     qsa_i32_view out = view2(3, T, 4 * budget + 3);
-    const size_t sb = qsa_indexer_scores_bytes(T, C);
+    const size_t sb = qsa_indexer_scores_bytes(T, C), fb = qsa_indexer_topk_fused_bytes(T, C);
+    CHECK(sb == (size_t)(T * C * 4) && fb > sb);
     stub::calls.clear();
-    CHECK(qsa_indexer_topk(&iq, &ik, (const int32_t *)addr(4), (const int32_t *)addr(5), L, budget,
-                           (float *)addr(6), sb, &out, nullptr) == QSA_OK);
-    CHECK(stub::calls.scores.size() == 1 && stub::calls.select.size() == 1);
+    CHECK(qsa_indexer_topk_fused(&iq, &ik, (const int32_t *)addr(4), (const int32_t *)addr(5), L,
+                                 budget, addr(6), fb, &out, nullptr) == QSA_OK);
+    // the fused path: estimate, candidates, selection
+    CHECK(stub::calls.estimate.size() == 1 && stub::calls.scores.size() == 1 &&
+          stub::calls.select.size() == 1);
+    if (stub::calls.scores.size() == 1)
+        CHECK(stub::calls.scores[0].tau != nullptr && stub::calls.scores[0].R == 1 &&
+              stub::calls.scores[0].pair_pitch == C + (C & 1) &&
+              stub::calls.select[0].counts != nullptr &&
+              stub::calls.select[0].pair_pitch == stub::calls.scores[0].pair_pitch);
+    stub::calls.clear();
+    CHECK(qsa_indexer_topk_fused(&iq, &ik, (const int32_t *)addr(4), (const int32_t *)addr(5), L,
+                                 budget, addr(6), fb - 1, &out, nullptr) == QSA_ERR_WORKSPACE);
+    CHECK(stub::calls.estimate.empty() && stub::calls.scores.empty() && stub::calls.select.empty());
+    // qsa_indexer_topk, whatever its scratch: scores, then the selection
+    for (size_t bytes : {sb, fb}) {
+        stub::calls.clear();
+        CHECK(qsa_indexer_topk(&iq, &ik, (const int32_t *)addr(4), (const int32_t *)addr(5), L,
+                               budget, (float *)addr(6), bytes, &out, nullptr) == QSA_OK);
+        CHECK(stub::calls.estimate.empty() && stub::calls.scores.size() == 1 &&
+              stub::calls.scores[0].tau == nullptr && stub::calls.select.size() == 1);
+    }
+    qsa_i32_view out600 = view2(3, T, 4 * 600 + 3);
+    stub::calls.clear();
+    CHECK(qsa_indexer_topk(&iq, &ik, (const int32_t *)addr(4), (const int32_t *)addr(5), L, 600,
+                           (float *)addr(6), sb, &out600, nullptr) == QSA_OK);
+    CHECK(stub::calls.estimate.empty() && stub::calls.select.size() == 1);
+    CHECK(qsa_indexer_topk_fused(&iq, &ik, (const int32_t *)addr(4), (const int32_t *)addr(5), L,
+                                 600, addr(6), fb, &out600, nullptr) == QSA_ERR_UNSUPPORTED);
     CHECK(qsa_indexer_topk(&iq, &ik, (const int32_t *)addr(4), (const int32_t *)addr(5), 100, budget,
                            (float *)addr(6), sb, &out, nullptr) == QSA_ERR_SHAPE);
-    CHECK(qsa_indexer_select((const float *)addr(6), sb - 4, T, C, (const int32_t *)addr(4),
+    CHECK(qsa_indexer_select((const float *)addr(6), (size_t)(T * C * 4) - 4, T, C, (const int32_t *)addr(4),
                              (const int32_t *)addr(5), L, budget, &out, nullptr) == QSA_ERR_WORKSPACE);
 }
 
@@ -274,6 +301,7 @@ void sizes() {
             (void)qsa_decode_workspace_bytes(T, W, 24, 2);
             (void)qsa_decode_splits(T, W, 24, 2);
             (void)qsa_indexer_scores_bytes(T, W);
+            (void)qsa_indexer_topk_fused_bytes(T, W);
             for (int bs : {1, 4, 64}) (void)qsa_prefill_blocks_workspace_bytes(T, W, bs);
         }
     for (int s = -1; s <= 10; ++s) CHECK(qsa_status_string((qsa_status)s) != nullptr);

@@ -53,6 +53,14 @@ hipError_t launch_indexer_select(const IndexerSelectParams &p, hipStream_t) {
     return hipSuccess;
 }
 
+hipError_t launch_indexer_topk_fused(const IndexerEstimateParams &e, const IndexerScoreParams &s,
+                                     const IndexerSelectParams &p, hipStream_t) {
+    stub::calls.estimate.push_back(e);
+    stub::calls.scores.push_back(s);
+    stub::calls.select.push_back(p);
+    return hipSuccess;
+}
+
 hipError_t launch_stream_read(const StreamParams &p, int64_t workgroups, hipStream_t) {
     stub::calls.stream.push_back(p);
     stub::calls.stream_wgs.push_back(workgroups);

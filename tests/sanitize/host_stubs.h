@@ -18,6 +18,7 @@ struct Calls {
     std::vector<qsa::SharingParams> share;
     std::vector<qsa::MergeParams> merge;
     std::vector<qsa::GatherParams> gather;
+    std::vector<qsa::IndexerEstimateParams> estimate;
     std::vector<qsa::IndexerScoreParams> scores;
     std::vector<qsa::IndexerSelectParams> select;
     std::vector<qsa::StreamParams> stream;

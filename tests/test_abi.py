@@ -244,6 +244,26 @@ def test_indexer_entry_points_reject_bad_arguments():
     assert topk(out_=ivew((8, 22), (22, 1), FAKE + (2 << 24))) == "QSA_ERR_SHAPE"
     assert topk(sc_bytes=8 * 16 * 4 - 1) == "QSA_ERR_WORKSPACE"
     assert qsa.indexer_scores.__doc__ and lib.qsa_indexer_scores_bytes(8, 16) == 512
+    # fused path: T rows of C floats (C rounded up to even), then the
+    # per-range counts and thresholds
+    assert lib.qsa_indexer_topk_fused_bytes(8, 16) == 512 + 256 + 256
+    up = lambda x: -(-x // 256) * 256
+    assert lib.qsa_indexer_topk_fused_bytes(7810, 16384) == \
+        up(7810 * 16384 * 4) + up(7810 * 16 * 4) + up(7810 * 4)
+    assert lib.qsa_indexer_topk_fused_bytes(9, 1025) == \
+        up(9 * 1026 * 4) + up(9 * 2 * 4) + up(9 * 4)
+
+    def fused(budget=5, sc_=sc, sc_bytes=big, ik_=ik, L=64):
+        o = ivew((8, 4 * budget + 3), (4 * budget + 3, 1), FAKE + (2 << 24))
+        return qsa.STATUS_NAMES[lib.qsa_indexer_topk_fused(r(iq), r(ik_), pos, sop, L, budget,
+                                                           sc_, sc_bytes, r(o), None)]
+
+    assert fused(budget=0) == "QSA_ERR_SHAPE"
+    assert fused(budget=513) == "QSA_ERR_UNSUPPORTED"         # above the fused path's budget
+    assert fused(sc_bytes=lib.qsa_indexer_topk_fused_bytes(8, 16) - 1) == "QSA_ERR_WORKSPACE"
+    assert fused(sc_=sc + 4) == "QSA_ERR_WORKSPACE"           # pairs need 8-byte alignment
+    many = view((262145, 1, 128), (128, 128, 1), FAKE + (1 << 40))
+    assert fused(ik_=many, L=4 * 262145) == "QSA_ERR_UNSUPPORTED"   # more than 256 key ranges
 
 
 def far_views(T, Hq, S, Hkv, W):

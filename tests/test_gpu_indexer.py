@@ -228,3 +228,54 @@ def test_deferred_rows_do_not_disturb_the_others():
     got = select_on(scores, positions, slot_of_pos, budget)
     want = oracle.indexer_select(scores, positions, slot_of_pos, budget)
     np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------- fused Top-K
+
+def fused_topk(case, budget):
+    iq, ik, pos, sop = dev_inputs(case)
+    sel = qsa.indexer_topk_fused(iq, ik, pos, sop, budget)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy()
+
+
+@pytest.mark.parametrize("L,T,budget", [(65536, 300, 512), (20000, 200, 300), (8192, 100, 64),
+                                        (4099, 37, 300), (777, 50, 8), (262144, 40, 512)])
+def test_fused_topk_is_exact_on_integer_scores(L, T, budget):
+    """The fused path (sampled threshold, candidates, exact selection, full
+    rows where the threshold missed) selects exactly what the oracle selects,
+    ties included, with queries at the end of the request and spread over it."""
+    case = qi.indexed_case(1160 + L % 991, L=L, T=T, Hq=8, Hkv=1, budget=budget,
+                           integer_keys=True)
+    rng = np.random.Generator(np.random.PCG64(1161 + L))
+    spread = np.sort(rng.choice(L, size=T // 2, replace=False)).astype(np.int32)
+    case.info["positions"][: T // 2] = spread
+    sel = fused_topk(case, budget)
+    want = oracle.indexer_select(oracle.indexer_scores(case.info["iq"], case.info["ik"]),
+                                 case.info["positions"], case.info["slot_of_pos"], budget)
+    np.testing.assert_array_equal(sel, want)
+
+
+@pytest.mark.parametrize("rising", [True, False])
+def test_fused_topk_rows_the_estimate_misses(rising):
+    """One estimate group of 16 queries with rows of 3,001 and 16,384
+    eligible blocks: the sample covers the shorter row's blocks only.  Scores
+    that rise with the block index leave the long row far too many
+    candidates, scores that fall leave it too few; either way that row takes
+    the full scores and the exact selection, and the result equals the
+    oracle's, ties to the lower block included."""
+    L, T, budget = 65536, 16, 512
+    case = qi.indexed_case(1170, L=L, T=T, Hq=8, Hkv=1, budget=budget, integer_keys=True)
+    C = case.info["ik"].shape[0]
+    level = 1 + (np.arange(C) if rising else (C - 1 - np.arange(C))) // 128   # <= 129: exact in BF16
+    ik = np.repeat(level.astype(np.float32)[:, None, None], 128, axis=2)
+    case.info["ik"] = qi.bf16_bits(ik)
+    case.info["iq"] = qi.bf16_bits(np.ones((T, 4, 128), dtype=np.float32))
+    pos = np.full(T, L - 1, dtype=np.int32)
+    pos[0] = 4 * 3000 + 3
+    pos[5] = 4 * 9000 + 1
+    case.info["positions"] = pos
+    sel = fused_topk(case, budget)
+    want = oracle.indexer_select(oracle.indexer_scores(case.info["iq"], case.info["ik"]),
+                                 pos, case.info["slot_of_pos"], budget)
+    np.testing.assert_array_equal(sel, want)

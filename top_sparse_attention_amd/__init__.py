@@ -28,7 +28,7 @@ __all__ = [
     "merge_partials", "decode_splits", "decode_workspace_bytes", "sparse_decode",
     "sparse_attend_fp8kv", "sparse_prefill_fp8kv", "gather_only_fp8kv",
     "compact_blocks", "sparse_prefill_blocks", "indexer_scores", "indexer_select",
-    "indexer_topk", "stream_read", "sparse_prefill_noalloc", "noalloc_scratch_bytes",
+    "indexer_topk", "indexer_topk_fused", "indexer_topk_fused_bytes", "indexer_scores_bytes", "stream_read", "sparse_prefill_noalloc", "noalloc_scratch_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -149,6 +149,11 @@ def load_library():
     lib.qsa_indexer_topk.restype = ctypes.c_int
     lib.qsa_indexer_topk.argtypes = [P(BF16View), P(BF16View), vp, vp, i64, ctypes.c_int32, vp,
                                      sz, P(I32View), vp]
+    lib.qsa_indexer_topk_fused_bytes.restype = sz
+    lib.qsa_indexer_topk_fused_bytes.argtypes = [i64, i64]
+    lib.qsa_indexer_topk_fused.restype = ctypes.c_int
+    lib.qsa_indexer_topk_fused.argtypes = [P(BF16View), P(BF16View), vp, vp, i64, ctypes.c_int32,
+                                           vp, sz, P(I32View), vp]
     lib.qsa_noalloc_scratch_bytes.restype = sz
     lib.qsa_noalloc_scratch_bytes.argtypes = []
     lib.qsa_sparse_prefill_noalloc.restype = ctypes.c_int
@@ -569,19 +574,51 @@ def indexer_select(scores: torch.Tensor, positions: torch.Tensor, slot_of_pos: t
     return out
 
 
+def indexer_scores_bytes(T: int, C: int) -> int:
+    """Bytes of the [T, C] float32 scores (the scratch of indexer_topk)."""
+    return int(load_library().qsa_indexer_scores_bytes(T, C))
+
+
+def indexer_topk_fused_bytes(T: int, C: int) -> int:
+    """Scratch bytes of indexer_topk_fused."""
+    return int(load_library().qsa_indexer_topk_fused_bytes(T, C))
+
+
+def _topk_call(fn, iq, ik, positions, slot_of_pos, budget, scratch, out):
+    _check_i32_1d(positions, "positions")
+    _check_i32_1d(slot_of_pos, "slot_of_pos")
+    if out is None:
+        out = torch.empty((iq.shape[0], 4 * budget + 3), dtype=torch.int32, device=iq.device)
+    ov = _i32_view(out, "slot_idx")
+    _raise_on(fn(
+        ctypes.byref(_bf16_any(iq, "iq")), ctypes.byref(_bf16_any(ik, "ik")),
+        positions.data_ptr(), slot_of_pos.data_ptr(), slot_of_pos.numel(), budget,
+        scratch.data_ptr(), scratch.numel() * scratch.element_size(), ctypes.byref(ov),
+        _stream(iq.device)))
+    return out
+
+
 def indexer_topk(iq: torch.Tensor, ik: torch.Tensor, positions: torch.Tensor,
                  slot_of_pos: torch.Tensor, budget: int, scores: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    _check_i32_1d(positions, "positions")
-    _check_i32_1d(slot_of_pos, "slot_of_pos")
-    T, C = iq.shape[0], ik.shape[0]
+    """Indexer scores and Top-K selection in one call.  ``scores`` is the
+    [T, C] float32 scratch (allocated when None); it holds the scores
+    afterwards."""
     if scores is None:
-        scores = torch.empty((T, C), dtype=torch.float32, device=iq.device)
-    if out is None:
-        out = torch.empty((T, 4 * budget + 3), dtype=torch.int32, device=iq.device)
-    ov = _i32_view(out, "slot_idx")
-    _raise_on(load_library().qsa_indexer_topk(
-        ctypes.byref(_bf16_any(iq, "iq")), ctypes.byref(_bf16_any(ik, "ik")),
-        positions.data_ptr(), slot_of_pos.data_ptr(), slot_of_pos.numel(), budget,
-        scores.data_ptr(), scores.numel() * 4, ctypes.byref(ov), _stream(iq.device)))
-    return out
+        scores = torch.empty((iq.shape[0], ik.shape[0]), dtype=torch.float32, device=iq.device)
+    return _topk_call(load_library().qsa_indexer_topk, iq, ik, positions, slot_of_pos, budget,
+                      scores, out)
+
+
+def indexer_topk_fused(iq: torch.Tensor, ik: torch.Tensor, positions: torch.Tensor,
+                       slot_of_pos: torch.Tensor, budget: int,
+                       scratch: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The same selection without the full score matrix (sampled threshold,
+    candidates, exact selection; budgets up to 512).  ``scratch`` is device
+    memory of indexer_topk_fused_bytes(T, C) bytes (allocated when None)."""
+    if scratch is None:
+        scratch = torch.empty(max(indexer_topk_fused_bytes(iq.shape[0], ik.shape[0]), 1),
+                              dtype=torch.uint8, device=iq.device)
+    return _topk_call(load_library().qsa_indexer_topk_fused, iq, ik, positions, slot_of_pos,
+                      budget, scratch, out)

@@ -759,6 +759,76 @@ qsa_status enqueue_indexer_select(const float *scores, int64_t T, int64_t C,
     return e == hipSuccess ? QSA_OK : hip_fail(e, "indexer select launch");
 }
 
+// Scratch of qsa_indexer_topk: T rows of `pitch` FP32 words (C rounded up
+// to even: every score, or, on the fused path, each key range's candidate
+// pairs, 8-byte aligned), then the fused path's per-range candidate counts
+// [T, R] and thresholds [T], at 256-byte boundaries.
+struct TopkScratch {
+    int64_t R, pitch, counts_offset, tau_offset, total;
+};
+
+bool topk_scratch_of(int64_t T, int64_t C, TopkScratch *ts) {
+    if (T < 0 || C < 0 || T > kMax32 || C > kMax32) return false;
+    ts->pitch = C + (C & 1);
+    const int64_t cells = mul_sat(T, ts->pitch);
+    if (cells > kMaxListEntries) return false;
+    ts->R = ceil_div(C, qsa::kScoreSplit);
+    ts->counts_offset = round_up(cells * 4, kAlign);
+    ts->tau_offset = ts->counts_offset + round_up(T * ts->R * 4, kAlign);
+    ts->total = ts->tau_offset + round_up(T * 4, kAlign);
+    return true;
+}
+
+qsa_status enqueue_indexer_topk_fused(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
+                                      const int32_t *positions, const int32_t *slot_of_pos,
+                                      int64_t L, int32_t budget, float *scratch,
+                                      const TopkScratch &ts, const qsa_i32_view *out,
+                                      hipStream_t stream) {
+    int32_t *counts = (int32_t *)((char *)scratch + ts.counts_offset);
+    uint32_t *tau = (uint32_t *)((char *)scratch + ts.tau_offset);
+    qsa::IndexerEstimateParams e{};
+    e.iq = (const uint16_t *)iq->data;
+    e.q_st = iq->stride[0];
+    e.q_sh = iq->stride[1];
+    e.ik = (const uint16_t *)ik->data;
+    e.k_st = ik->stride[0];
+    e.T = iq->size[0];
+    e.C = ik->size[0];
+    e.L = L;
+    e.positions = positions;
+    e.budget = budget;
+    e.tau = tau;
+    qsa::IndexerScoreParams sp{};
+    sp.iq = e.iq;
+    sp.q_st = e.q_st;
+    sp.q_sh = e.q_sh;
+    sp.ik = e.ik;
+    sp.k_st = e.k_st;
+    sp.T = e.T;
+    sp.C = e.C;
+    sp.positions = positions;
+    sp.scores = scratch;
+    sp.tau = tau;
+    sp.counts = counts;
+    sp.R = ts.R;
+    sp.pair_pitch = ts.pitch;
+    qsa::IndexerSelectParams p{};
+    p.scores = scratch;
+    p.T = e.T;
+    p.C = e.C;
+    p.positions = positions;
+    p.slot_of_pos = slot_of_pos;
+    p.L = L;
+    p.budget = budget;
+    p.out = (int32_t *)out->data;
+    p.out_stride = out->stride[0];
+    p.counts = counts;
+    p.R = ts.R;
+    p.pair_pitch = ts.pitch;
+    hipError_t err = qsa::launch_indexer_topk_fused(e, sp, p, stream);
+    return err == hipSuccess ? QSA_OK : hip_fail(err, "indexer top-k launch");
+}
+
 qsa_status check_select_args(int64_t T, int64_t C, const int32_t *positions,
                              const int32_t *slot_of_pos, int64_t L, int32_t budget,
                              const qsa_i32_view *out) {
@@ -1082,6 +1152,11 @@ size_t qsa_indexer_scores_bytes(int64_t T, int64_t C) {
     return (T < 0 || C < 0 || need == INT64_MAX) ? 0 : (size_t)need;
 }
 
+size_t qsa_indexer_topk_fused_bytes(int64_t T, int64_t C) {
+    TopkScratch ts;
+    return topk_scratch_of(T, C, &ts) ? (size_t)ts.total : 0;
+}
+
 qsa_status qsa_indexer_scores(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
                               const int32_t *positions, float *scores, size_t scores_bytes,
                               void *stream) {
@@ -1123,6 +1198,38 @@ qsa_status qsa_indexer_topk(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
     hipStream_t st = (hipStream_t)stream;
     if (C > 0 && (s = enqueue_indexer_scores(iq, ik, positions, scores, st))) return s;
     return enqueue_indexer_select(scores, T, C, positions, slot_of_pos, L, budget, slot_idx, st);
+}
+
+qsa_status qsa_indexer_topk_fused(const qsa_bf16_view *iq, const qsa_bf16_view *ik,
+                                  const int32_t *positions, const int32_t *slot_of_pos, int64_t L,
+                                  int32_t budget, void *scratch, size_t scratch_bytes,
+                                  qsa_i32_view *slot_idx, void *stream) {
+    qsa_status s;
+    if ((s = check_index_view(iq, "iq", qsa::kIndexHeads)) || (s = check_index_view(ik, "ik", 1)))
+        return s;
+    const int64_t T = iq->size[0], C = ik->size[0];
+    if ((s = check_select_args(T, C, positions, slot_of_pos, L, budget, slot_idx))) return s;
+    TopkScratch ts;
+    if (!topk_scratch_of(T, C, &ts))
+        return fail(QSA_ERR_UNSUPPORTED, "indexer top-k: T %lld x C %lld is too large",
+                         (long long)T, (long long)C);
+    if (budget > qsa::kFusedBudgetMax || ts.R > qsa::kFusedMaxRanges)
+        return fail(QSA_ERR_UNSUPPORTED,
+                         "fused top-k takes budgets up to %d and C up to %lld (budget %d, C %lld)",
+                         qsa::kFusedBudgetMax, (long long)qsa::kFusedMaxRanges * qsa::kScoreSplit,
+                         (int)budget, (long long)C);
+    if (T > 0 && C > 0 && (scratch == nullptr || (int64_t)scratch_bytes < ts.total))
+        return fail(QSA_ERR_WORKSPACE, "fused top-k scratch: %zu bytes, needs %lld",
+                         scratch_bytes, (long long)ts.total);
+    if ((uintptr_t)scratch % 8 != 0)
+        return fail(QSA_ERR_WORKSPACE, "fused top-k scratch must be 8-byte aligned");
+    if ((s = check_scores_grid(T, C)) || (s = check_grid(T, 256, "indexer select"))) return s;
+    if (T == 0) return QSA_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (C == 0) return enqueue_indexer_select((const float *)scratch, T, C, positions,
+                                              slot_of_pos, L, budget, slot_idx, st);
+    return enqueue_indexer_topk_fused(iq, ik, positions, slot_of_pos, L, budget, (float *)scratch,
+                                      ts, slot_idx, st);
 }
 
 }  // extern "C"

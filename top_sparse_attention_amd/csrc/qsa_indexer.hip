@@ -25,9 +25,24 @@ namespace {
 constexpr int kScoreTokens = 128;
 constexpr int kScoreRowTiles = kScoreTokens / 4 / 4;   // per wave
 constexpr int kScoreTile = 64;
-constexpr int kScoreSplit = 1024;
 constexpr int kIndexRowBytes = kIndexDim * 2;   // 256 B
 constexpr int kScoreOutPitch = kScoreTile + 4;  // floats per staged row (16-byte aligned)
+
+// Order-preserving map of FP32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t score_key(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Marks, in the first output word, a row that a fast selection left to the
+// exact selection on the full row (no output word holds a value below -1).
+constexpr int32_t kSelDeferred = INT32_MIN;
+
+// What indexer_scores_kernel writes: every score of the tokens' eligible
+// blocks, or only the candidates at or above each token's estimated
+// threshold (the fused Top-K), or every score but only where a token's row
+// was deferred by the fused selection.
+enum ScoreMode { kAllScores, kCandidates, kDeferredRows };
 
 // LDS byte offset of 16-byte chunk `chunk` of index-key tile row `r`.  The
 // chunk index is XOR-swizzled by a bijection of r & 7 so that the 8 rows read
@@ -37,27 +52,63 @@ __device__ __forceinline__ int idx_off(int r, int chunk) {
     return r * kIndexRowBytes + ((chunk ^ swz(r)) << 4);
 }
 
+//
+// Candidate mode (the fused Top-K): each token keeps, of its eligible blocks
+// (4c + 3 <= p), the scores whose key reaches its estimated threshold tau[t],
+// as (score, block id) pairs in block order in its row's part for this key
+// range: the 16 threads that store a staged row's 64 scores scan their pass
+// counts and append at the row's running count.  The count goes to
+// counts[t * R + range] at the end (it may exceed the part's room; the
+// selection then takes the full row instead).
+template <int kMode>
 __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreParams p) {
     // One key tile: the barrier after each tile's scores also orders its reads
     // before the next tile is written.
     __shared__ __attribute__((aligned(16))) char tile[kScoreTile * kIndexRowBytes];
     __shared__ __attribute__((aligned(16))) float out_tile[kScoreTokens * kScoreOutPitch];
-    __shared__ int c_end_shared;
+    __shared__ int c_end_shared, any_deferred;
+    // Candidate mode: per token of the workgroup its eligible blocks, its
+    // threshold key and its running candidate count in this range (in LDS:
+    // the MFMA operands already hold most of the registers).
+    __shared__ int tok_lim[kMode == kCandidates ? kScoreTokens : 1];
+    __shared__ uint32_t tok_tau[kMode == kCandidates ? kScoreTokens : 1];
+    __shared__ int seg_cnt[kMode == kCandidates ? kScoreTokens : 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int c = lane & 15, j = lane >> 4;
     const int64_t t0 = (int64_t)blockIdx.x * kScoreTokens;
     const int c_begin = blockIdx.y * kScoreSplit;
 
-    if (tid == 0) c_end_shared = 0;
-    __syncthreads();
-    if (tid < kScoreTokens && t0 + tid < p.T) {
-        const int64_t lim = ((int64_t)p.positions[t0 + tid] + 1) / kIndexBlock;
-        atomicMax(&c_end_shared, (int)min<int64_t>(lim, p.C));
+    if (tid == 0) {
+        c_end_shared = 0;
+        any_deferred = 0;
     }
     __syncthreads();
+    if (tid < kScoreTokens && t0 + tid < p.T) {
+        const int64_t lim = min<int64_t>(max<int64_t>(((int64_t)p.positions[t0 + tid] + 1) /
+                                                          kIndexBlock, 0), p.C);
+        atomicMax(&c_end_shared, (int)lim);
+        if constexpr (kMode == kCandidates) {
+            tok_lim[tid] = (int)lim;
+            tok_tau[tid] = p.tau[t0 + tid];
+            seg_cnt[tid] = 0;
+        }
+        if constexpr (kMode == kDeferredRows)
+            if (p.deferred[(t0 + tid) * p.deferred_stride] == kSelDeferred) any_deferred = 1;
+    }
+    if (kMode == kCandidates && tid < kScoreTokens && t0 + tid >= p.T) {
+        tok_lim[tid] = 0;
+        tok_tau[tid] = 0;
+        seg_cnt[tid] = 0;
+    }
+    __syncthreads();
+    if (kMode == kDeferredRows && !any_deferred) return;
     const int c_end = min(c_end_shared, c_begin + kScoreSplit);
-    if (c_begin >= c_end) return;
+    if (c_begin >= c_end) {
+        if constexpr (kMode == kCandidates)
+            if (tid < kScoreTokens && t0 + tid < p.T) p.counts[(t0 + tid) * p.R + blockIdx.y] = 0;
+        return;
+    }
 
     // A operands: row tile rt of this wave is tokens t0 + 32 wave + 4 rt ..+3;
     // row r of a tile = (token r/4, head r%4), dims 32 ks + 8 j.
@@ -98,12 +149,13 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
         store_tile(tile, stage);
         __syncthreads();   // the key tile is staged; the previous scores are stored
         if (c0 + kScoreTile < c_end) load_tile(c0 + kScoreTile, stage);
+        const char *kt = tile;
 #pragma unroll
         for (int ct = 0; ct < kScoreTile / 16; ++ct) {
             bf16x8_t kb[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                kb[ks] = *LDS_PTR(bf16x8_t, tile + idx_off(16 * ct + c, 4 * ks + j));
+                kb[ks] = *LDS_PTR(bf16x8_t, kt + idx_off(16 * ct + c, 4 * ks + j));
 #pragma unroll
             for (int rt = 0; rt < kScoreRowTiles; ++rt) {
                 f32x4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -123,7 +175,37 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
             const int r = idx >> 4, k4 = 4 * (idx & 15);
             const int64_t t_out = t0 + r;
             const int64_t blk = c0 + k4;
-            if (t_out < p.T && blk < c_end) {
+            if constexpr (kMode == kCandidates) {
+                // The 16 lanes idx & 15 of row r (one 16-lane row of a wave)
+                // append their passing scores in block order: an inclusive
+                // scan of the pass counts across the row (DPP row shifts),
+                // then the row's total from its last lane (DPP row share).
+                const f32x4_t v = *(const f32x4_t *)(out_tile + r * kScoreOutPitch + k4);
+                const int lim = min(tok_lim[r], c_end);
+                const uint32_t tau = tok_tau[r];
+                int pass = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pass |= (blk + e < lim && score_key(v[e]) >= tau) ? (1 << e) : 0;
+                const int cnt = __popc(pass);
+                int incl = cnt;
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xf, 0xf, true);   // row_shr:1
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xf, 0xf, true);   // row_shr:2
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xf, 0xf, true);   // row_shr:4
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xf, 0xf, true);   // row_shr:8
+                const int total = __builtin_amdgcn_update_dpp(0, incl, 0x15f, 0xf, 0xf, false);   // row_share:15
+                const int base = seg_cnt[r];
+                int at = base + incl - cnt;
+                if ((lane & 15) == 15) seg_cnt[r] = base + total;
+                const int room = min(kScoreSplit, (int)(p.C - c_begin)) / 2;
+                f32x2_t *seg = (f32x2_t *)(p.scores + t_out * p.pair_pitch + c_begin);
+                // One 8-byte store per passing score, lowest block first.
+                for (int bits = pass; bits; bits &= bits - 1, ++at) {
+                    const int e = __builtin_ctz(bits);
+                    const float x = e == 0 ? v[0] : e == 1 ? v[1] : e == 2 ? v[2] : v[3];
+                    if (at < room) seg[at] = f32x2_t{x, __int_as_float((int)blk + e)};
+                }
+            } else if (t_out < p.T && blk < c_end) {
                 const f32x4_t v = *(const f32x4_t *)(out_tile + r * kScoreOutPitch + k4);
                 float *dst = p.scores + t_out * p.C + blk;
                 if (vec_out && blk + 3 < c_end) {
@@ -133,6 +215,136 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
                 }
             }
         }
+    }
+    if constexpr (kMode == kCandidates) {
+        __syncthreads();   // every row's count is final
+        if (tid < kScoreTokens && t0 + tid < p.T)
+            p.counts[(t0 + tid) * p.R + blockIdx.y] = seg_cnt[tid];
+    }
+}
+
+// The threshold estimate of the fused Top-K.  A workgroup takes kEstTokens
+// consecutive query tokens and samples kEstRuns runs of 16 consecutive blocks
+// spread evenly over [0, n_min), n_min the smallest eligible count among its
+// tokens that need an estimate (rows of more than kSelCandSmall eligible
+// blocks), so every sample is eligible for every token (the tokens of a
+// prefill chunk have nearly the same count).  The sampled scores come from
+// bf16 MFMA exactly as in indexer_scores_kernel (rows = (token, head)); each
+// wave then finds, for each of its 4 tokens, the top 16 bits of the key
+// ranked about target * samples / n from the top (two 8-bit radix passes over
+// a per-wave LDS histogram), target = sqrt(budget * kFusedCand) candidates:
+// the middle, on a log scale, of the counts the selection takes (budget to
+// kFusedCand), so the sampling error (about 1 / sqrt(16) of the count at
+// the page's budget) rarely leaves that range.  Taking only the top bits
+// rounds the estimate down, which only adds candidates.  tau = 0 (every
+// eligible block passes) for rows of at most kSelCandSmall eligible blocks.
+constexpr int kEstTokens = 16;                 // 4 MFMA row tiles, one per wave
+constexpr int kEstRuns = 16;
+constexpr int kEstSamples = kEstRuns * 16;     // 256: one 16-key column tile per run
+constexpr int kSelCandSmall = 2048;
+constexpr int kFusedCand = 4096;               // candidate room of a fused-path row
+
+__global__ __launch_bounds__(256) void indexer_estimate_kernel(const IndexerEstimateParams p) {
+    __shared__ float samp[kEstTokens][kEstSamples];
+    __shared__ int hist[4][256];
+    __shared__ int sh_nmin;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int c = lane & 15, j = lane >> 4;
+    const int64_t t0 = (int64_t)blockIdx.x * kEstTokens;
+
+    auto eligible = [&](int64_t t) -> int {
+        if (t >= p.T) return 0;
+        const int64_t pos = p.positions[t];
+        if (pos < 0 || pos >= p.L) return 0;
+        return (int)min<int64_t>((pos + 1) / kIndexBlock, p.C);
+    };
+    if (tid == 0) sh_nmin = INT32_MAX;
+    __syncthreads();
+    if (tid < kEstTokens) {
+        const int n = eligible(t0 + tid);
+        if (n > kSelCandSmall) atomicMin(&sh_nmin, n);
+    }
+    __syncthreads();
+    const int n_min = sh_nmin;
+    if (n_min == INT32_MAX) {   // no row needs an estimate
+        if (tid < kEstTokens && t0 + tid < p.T) p.tau[t0 + tid] = 0;
+        return;
+    }
+
+    // Wave w: tokens t0 + 4w .. +3; lane (c, j) holds rows (token c/4, head c%4)
+    // of the A operand and, in the output, token j against column c.
+    bf16x8_t qa[4];
+    {
+        const int64_t ta = t0 + 4 * wave + (c >> 2);
+        const uint16_t *qrow = ta < p.T ? p.iq + ta * p.q_st + (int64_t)(c & 3) * p.q_sh : kZeroRow;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qa[ks] = ldg16<bf16x8_t>(qrow + 32 * ks + 8 * j);
+    }
+#pragma unroll 4
+    for (int run = 0; run < kEstRuns; ++run) {
+        // n_min > kSelCandSmall keeps the runs distinct and inside [0, n_min).
+        const int start = (int)((int64_t)run * (n_min - 16) / (kEstRuns - 1)) & ~15;
+        const uint16_t *krow = p.ik + (int64_t)(start + c) * p.k_st;
+        bf16x8_t kb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[ks] = ldg16<bf16x8_t>(krow + 32 * ks + 8 * j);
+        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb[ks], d, 0, 0, 0);
+        samp[4 * wave + j][16 * run + c] =
+            fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) + fmaxf(d[3], 0.f);
+    }
+    wave_lds_fence();   // the wave reads back only its own tokens' samples
+
+    int *h = hist[wave];
+    for (int tk = 0; tk < 4; ++tk) {
+        const int64_t t = t0 + 4 * wave + tk;
+        if (t >= p.T) break;
+        const int n = eligible(t);
+        if (n <= kSelCandSmall) {
+            if (lane == 0) p.tau[t] = 0;
+            continue;
+        }
+        const float target = sqrtf((float)p.budget * (float)kFusedCand);
+        const int kth = min(kEstSamples, max(1, (int)ceilf(target * kEstSamples / (float)n)));
+        uint32_t key[kEstSamples / 64];
+#pragma unroll
+        for (int i = 0; i < kEstSamples / 64; ++i) key[i] = score_key(samp[4 * wave + tk][lane + 64 * i]);
+        uint32_t prefix = 0;
+        int need = kth;
+        for (int pass = 0; pass < 2; ++pass) {
+            const int shift = 24 - 8 * pass;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[4 * lane + i] = 0;
+            wave_lds_fence();
+#pragma unroll
+            for (int i = 0; i < kEstSamples / 64; ++i)
+                if (pass == 0 || (key[i] >> 24) == (prefix >> 24))
+                    atomicAdd(&h[(key[i] >> shift) & 255], 1);
+            wave_lds_fence();
+            // lane l owns digits 4l .. 4l + 3; counts of the digits above.
+            const int cnt = h[4 * lane] + h[4 * lane + 1] + h[4 * lane + 2] + h[4 * lane + 3];
+            int incl = cnt;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int v = __shfl_down(incl, off);
+                if (lane + off < 64) incl += v;
+            }
+            const int above = incl - cnt;
+            const bool mine = above < need && need <= incl;
+            int d = 4 * lane + 3, cum = above;
+            if (mine)
+                while (cum + h[d] < need) cum += h[d--];
+            const uint64_t who = __ballot(mine);
+            const int src = who ? __builtin_ctzll(who) : 0;
+            const int digit = __builtin_amdgcn_readlane(d, src);
+            need -= __builtin_amdgcn_readlane(cum, src);
+            prefix |= (uint32_t)digit << shift;
+            wave_lds_fence();   // the histogram is rewritten by the next pass
+        }
+        if (lane == 0) p.tau[t] = prefix;
     }
 }
 
@@ -184,11 +396,6 @@ __device__ __forceinline__ void block_min_max(float *lo, float *hi, float *wave_
     *hi = b;
 }
 
-// Order-preserving map of FP32 to uint32 (larger float -> larger key).
-__device__ __forceinline__ uint32_t score_key(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Find, among the keys of `n` scores that pass `in_set`, the `need`-th largest
 // key tau and how many keys equal to tau must be kept (written to sh_prefix /
@@ -430,9 +637,29 @@ __device__ void expand_row(const IndexerSelectParams &p, int64_t pos, int kept, 
         out[tail0 + i] = i < r ? p.slot_of_pos[pos - r + 1 + i] : -1;
 }
 
-// Marks, in the first output word, a row that indexer_select_fast_kernel
-// left to the exact selection (no output word holds a value below -1).
-constexpr int32_t kSelDeferred = INT32_MIN;
+
+// expand_row for block ids kept in LDS (kept[e], e < n_kept): each thread
+// turns its blocks into slots with one 16-byte slot-table load and one
+// 16-byte store where aligned.
+__device__ void expand_kept(const IndexerSelectParams &p, int64_t pos, int n_kept, const int *kept,
+                            int32_t *out, int width) {
+    const int tid = threadIdx.x;
+    __syncthreads();   // kept[] is complete
+    const bool vec_ok = ((uintptr_t)p.slot_of_pos % 16) == 0 && ((uintptr_t)out % 16) == 0;
+    for (int e = tid; e < n_kept; e += 256) {
+        const int32_t *src = p.slot_of_pos + (int64_t)kIndexBlock * kept[e];
+        if (vec_ok) {
+            *(u32x4_t *)(out + kIndexBlock * e) = *(const u32x4_t *)src;
+        } else {
+#pragma unroll
+            for (int q = 0; q < kIndexBlock; ++q) out[kIndexBlock * e + q] = src[q];
+        }
+    }
+    const int r = (int)((pos + 1) % kIndexBlock);
+    const int tail0 = kIndexBlock * n_kept;
+    for (int i = tid; i < width - tail0; i += 256)
+        out[tail0 + i] = i < r ? p.slot_of_pos[pos - r + 1 + i] : -1;
+}
 
 // kDeferredOnly: a second launch after indexer_select_fast_kernel that
 // selects only the rows it deferred (the others return at once).
@@ -471,11 +698,55 @@ __global__ __launch_bounds__(256) void indexer_select_kernel(const IndexerSelect
 // (Held to 64 registers for 8 per CU the small kernel ran twice as slowly.)
 constexpr int kSelSample = 1024;
 constexpr int kSelCand = 3840;        // multiples of 256
-constexpr int kSelCandSmall = 2048;
 constexpr int kSelPerThread = 16;   // scores per thread per pass over the row
 // Candidate i is stored at i + i / 16: the output pass, where thread t reads
 // candidates kPer t .. kPer t + kPer - 1, then reads different banks.
 __device__ __forceinline__ int cand_at(int i) { return i + (i >> 4); }
+
+// The exact selection among nc candidates (scores cval and block ids cid, in
+// block order, candidate i stored at cand_at(i)): the budget-th largest key
+// tau and how many keys equal to tau to keep, then the kept block ids in
+// block order at kept[e] (LDS, e < budget).  Thread t owns candidates
+// [kPer t, kPer (t + 1)); a kept candidate's position is the number of keys
+// > tau before it plus the number of kept ties (the first `need` in block
+// order) before it.
+template <int kCand>
+__device__ void select_candidates(int nc, int budget, const float *cval, const int *cid, int *hist,
+                                  uint32_t *sh_prefix, int *sh_need, int *wave_sums, int *kept) {
+    const int tid = threadIdx.x;
+    radix_select(nc, budget, [&](int i) { return cval[cand_at(i)]; }, [](float) { return true; },
+                 hist, sh_prefix, sh_need);
+    const uint32_t tau = *sh_prefix;
+    const int need = *sh_need;
+    constexpr int kPer = kCand / 256;
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = kPer * tid + k;
+        if (i < nc) {
+            const uint32_t u = score_key(cval[cand_at(i)]);
+            gt += u > tau;
+            eq += u == tau;
+        }
+    }
+    int total;
+    int gt_pre = block_exclusive_sum(gt, &total, wave_sums);
+    int eq_pre = block_exclusive_sum(eq, &total, wave_sums);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = kPer * tid + k;
+        if (i < nc) {
+            const uint32_t u = score_key(cval[cand_at(i)]);
+            if (u > tau) {
+                kept[gt_pre + min(eq_pre, need)] = cid[cand_at(i)];
+                ++gt_pre;
+            } else if (u == tau) {
+                if (eq_pre < need) kept[gt_pre + eq_pre] = cid[cand_at(i)];
+                ++eq_pre;
+            }
+        }
+    }
+}
 
 template <int kCand, int kWavesPerSimd, bool kDefer>
 __global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel(
@@ -486,6 +757,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel
     constexpr int kCandPadded = kCand + kCand / 16;
     __shared__ float cval[kCandPadded];
     __shared__ int cid[kCandPadded];
+    __shared__ int kept[kCand / 4];   // budget <= kCand / 4
     __shared__ int hist[256];
     __shared__ int wave_sums[4];
     __shared__ uint32_t sh_prefix;
@@ -525,7 +797,7 @@ __global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel
     };
 
     if (n <= p.budget) {
-        for (int e = tid; e < n; e += 256) out[kIndexBlock * e] = e;
+        for (int e = tid; e < n; e += 256) kept[e] = e;
     } else {
         // The first two slices are in flight while the threshold is estimated.
         float v[kSelPerThread], v1[kSelPerThread];
@@ -599,51 +871,103 @@ __global__ __launch_bounds__(256, kWavesPerSimd) void indexer_select_fast_kernel
                 return;
             } else {
                 select_exact<false>(p, n, row, out);
+                expand_row(p, pos, min(n, p.budget), out, width);
+                return;
             }
-        } else {
-            // 3. Exact threshold key tau among the candidates and how many
-            // keys equal to tau to keep.
-            radix_select(nc, p.budget, [&](int i) { return cval[cand_at(i)]; }, all, hist,
-                         &sh_prefix, &sh_need);
-            const uint32_t tau = sh_prefix;
-            const int need = sh_need;
-            // 4. Output in block order.  Thread t owns candidates
-            // [kPer t, kPer (t + 1)); a kept candidate's position is the
-            // number of keys > tau before it plus the number of kept ties
-            // (the first `need` in block order) before it.
-            constexpr int kPer = kCand / 256;
-            int gt = 0, eq = 0;
+        }
+        select_candidates<kCand>(nc, p.budget, cval, cid, hist, &sh_prefix, &sh_need,
+                                 wave_sums, kept);
+    }
+    expand_kept(p, pos, min(n, p.budget), kept, out, width);
+}
+
+// The selection of the fused Top-K, from the candidates indexer_scores_kernel
+// kept (mode kCandidates).  One 256-thread workgroup per token: the counts of
+// the token's key ranges are scanned into offsets, every range's (score,
+// block id) pairs are copied in range order (so the list is in block order)
+// into LDS, and the exact selection runs on them.  A row whose candidates do
+// not fit their range's room, fall below the budget (the estimate was too
+// high) or exceed kFusedCand is marked with kSelDeferred in its first
+// output word; the full scores and the exact selection then take it
+// (indexer_scores_kernel<kDeferredRows>, indexer_select_kernel<false, true>).
+__global__ __launch_bounds__(256, 4) void indexer_select_cand_kernel(const IndexerSelectParams p) {
+    constexpr int kCand = kFusedCand;
+    constexpr int kCandPadded = kCand + kCand / 16;
+    __shared__ float cval[kCandPadded];
+    __shared__ int cid[kCandPadded];
+    __shared__ int kept[kFusedBudgetMax];
+    __shared__ int hist[256];
+    __shared__ int wave_sums[4];
+    __shared__ int r_off[kFusedMaxRanges + 1];
+    __shared__ uint32_t sh_prefix;
+    __shared__ int sh_need, sh_over;
+
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    // Every range's count is written (0 past the token's eligible blocks), so
+    // it is read together with the position.
+    const int cnt_r = tid < p.R ? p.counts[t * p.R + tid] : 0;
+    const int64_t pos = p.positions[t];
+    int32_t *out = p.out + t * p.out_stride;
+    const int width = kIndexBlock * p.budget + 3;
+    if (pos < 0 || pos >= p.L) {
+        for (int i = tid; i < width; i += 256) out[i] = -1;
+        return;
+    }
+    const int n = (int)min<int64_t>((pos + 1) / kIndexBlock, p.C);
+    if (n <= p.budget) {
+        for (int e = tid; e < n; e += 256) kept[e] = e;
+    } else {
+        const int ranges = (n + kScoreSplit - 1) / kScoreSplit;   // <= kFusedMaxRanges
+        if (tid == 0) sh_over = 0;
+        __syncthreads();
+        int cnt = 0;
+        if (tid < ranges) {
+            cnt = cnt_r;
+            const int room = (int)min<int64_t>(kScoreSplit, p.C - (int64_t)tid * kScoreSplit) / 2;
+            if (cnt > room) sh_over = 1;
+        }
+        int total;
+        const int off = block_exclusive_sum(cnt, &total, wave_sums);
+        if (sh_over || total < p.budget || total > kCand) {
+            if (tid == 0) out[0] = kSelDeferred;
+            return;
+        }
+        if (tid < ranges) r_off[tid] = off;
+        if (tid == 0) r_off[ranges] = total;
+        __syncthreads();
+        // Candidate i comes from the range r with r_off[r] <= i < r_off[r + 1]
+        // (a binary search); all of a thread's loads are in flight together.
+        const f32x2_t *row = (const f32x2_t *)(p.scores + t * p.pair_pitch);
+        constexpr int kBatch = 8;
+        for (int i0 = 0; i0 < total; i0 += 256 * kBatch) {
+            f32x2_t pr[kBatch];
 #pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                const int i = kPer * tid + k;
-                if (i < nc) {
-                    const uint32_t u = score_key(cval[cand_at(i)]);
-                    gt += u > tau;
-                    eq += u == tau;
+            for (int k = 0; k < kBatch; ++k) {
+                const int i = i0 + 256 * k + tid;
+                int lo = 0, hi = ranges;   // r_off[lo] <= i < r_off[hi]
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (r_off[mid] <= i) lo = mid;
+                    else hi = mid;
                 }
+                if (i < total) pr[k] = row[lo * (kScoreSplit / 2) + (i - r_off[lo])];
             }
-            int total;
-            int gt_pre = block_exclusive_sum(gt, &total, wave_sums);
-            int eq_pre = block_exclusive_sum(eq, &total, wave_sums);
 #pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                const int i = kPer * tid + k;
-                if (i < nc) {
-                    const uint32_t u = score_key(cval[cand_at(i)]);
-                    if (u > tau) {
-                        out[kIndexBlock * (gt_pre + min(eq_pre, need))] = cid[cand_at(i)];
-                        ++gt_pre;
-                    } else if (u == tau) {
-                        if (eq_pre < need) out[kIndexBlock * (gt_pre + eq_pre)] = cid[cand_at(i)];
-                        ++eq_pre;
-                    }
+            for (int k = 0; k < kBatch; ++k) {
+                const int i = i0 + 256 * k + tid;
+                if (i < total) {
+                    cval[cand_at(i)] = pr[k][0];
+                    cid[cand_at(i)] = __float_as_int(pr[k][1]);
                 }
             }
         }
+        __syncthreads();
+        select_candidates<kCand>(total, p.budget, cval, cid, hist, &sh_prefix, &sh_need,
+                                 wave_sums, kept);
     }
-    expand_row(p, pos, min(n, p.budget), out, width);
+    expand_kept(p, pos, min(n, p.budget), kept, out, width);
 }
-
 
 }  // namespace
 
@@ -651,8 +975,34 @@ hipError_t launch_indexer_scores(const IndexerScoreParams &p, hipStream_t stream
     if (p.T == 0 || p.C == 0) return hipSuccess;
     const int64_t blocks = (p.T + kScoreTokens - 1) / kScoreTokens;
     const int64_t splits = (p.C + kScoreSplit - 1) / kScoreSplit;
-    hipLaunchKernelGGL(indexer_scores_kernel, dim3((unsigned)blocks, (unsigned)splits), dim3(256),
-                       0, stream, p);
+    hipLaunchKernelGGL(indexer_scores_kernel<kAllScores>, dim3((unsigned)blocks, (unsigned)splits),
+                       dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_indexer_topk_fused(const IndexerEstimateParams &e, const IndexerScoreParams &s,
+                                     const IndexerSelectParams &p, hipStream_t stream) {
+    if (p.T == 0) return hipSuccess;
+    if (p.budget > kFusedBudgetMax || s.R > kFusedMaxRanges || s.R < 1 || s.tau == nullptr ||
+        s.deferred != nullptr || s.counts == nullptr || p.counts == nullptr)
+        return hipErrorInvalidValue;
+    const int64_t token_blocks = (p.T + kScoreTokens - 1) / kScoreTokens;
+    hipLaunchKernelGGL(indexer_estimate_kernel, dim3((unsigned)((p.T + kEstTokens - 1) / kEstTokens)),
+                       dim3(256), 0, stream, e);
+    hipLaunchKernelGGL(indexer_scores_kernel<kCandidates>,
+                       dim3((unsigned)token_blocks, (unsigned)s.R), dim3(256), 0, stream, s);
+    hipLaunchKernelGGL(indexer_select_cand_kernel, dim3((unsigned)p.T), dim3(256), 0, stream, p);
+    // Rows the estimate missed: their full scores (only workgroups holding
+    // one), then the exact selection on them (the others return at once).
+    IndexerScoreParams full = s;
+    full.tau = nullptr;
+    full.counts = nullptr;
+    full.deferred = p.out;
+    full.deferred_stride = p.out_stride;
+    hipLaunchKernelGGL(indexer_scores_kernel<kDeferredRows>,
+                       dim3((unsigned)token_blocks, (unsigned)s.R), dim3(256), 0, stream, full);
+    hipLaunchKernelGGL((indexer_select_kernel<false, true>), dim3((unsigned)p.T), dim3(256), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
