@@ -13,6 +13,8 @@
 namespace qsa {
 namespace {
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 // score[t, c] = sum_h max(0, iq[t,h] . ik[c]) with bf16 MFMA.  A workgroup
 // takes 128 tokens (32 per wave, as 8 MFMA row tiles of 4 tokens x 4 heads;
 // 64 measured 2% slower, each key tile then read from LDS by twice as many
