@@ -312,7 +312,7 @@ def test_launches_beyond_the_work_item_limit_are_refused():
     part = 7 << 40
     assert name(lib.qsa_sparse_attend_partial(r(q), r(k), r(v), 1, 0.0625, ws, huge, 4096, 0,
                                               4096, part, huge, None)) == "QSA_ERR_UNSUPPORTED"
-    # the merge: one wave per (token, head), 4 per workgroup of 256
+    # the merge: one workgroup of 256 per (token, head)
     mo = view((1 << 24, 16, 256), (16 * 256, 256, 1), 4 << 40)
     assert name(lib.qsa_merge_partials(part, huge, 2, 1 << 24, 16, r(mo), None)) == \
         "QSA_ERR_UNSUPPORTED"

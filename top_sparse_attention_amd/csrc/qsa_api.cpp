@@ -265,7 +265,7 @@ qsa_status check_attend_grid(int64_t T, int64_t Hq, int64_t Hkv, int64_t splits)
 
 // One wave per (token, head) row, four rows per workgroup.
 qsa_status check_merge_grid(int64_t T, int64_t Hq) {
-    return check_grid(ceil_div(mul_sat(T, Hq), 4), 256, "merge");
+    return check_grid(mul_sat(T, Hq), 256, "merge");   // one workgroup per (token, head)
 }
 
 // Width of the compaction's sort key for entries in [0, n): the bits of

@@ -670,23 +670,34 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
 // ---------------------------------------------------------------- merge
 
 // out[t, h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the parts s,
-// M = max_s m_s; exactly +0.0 when no part saw a slot.  One wave per (t, h)
-// row, 4 dims per lane.  Lane s of each run of 64 parts loads part s's (m, l)
-// and computes its weight; the O rows are then read kMergeBatch parts at a
-// time, all of a batch's loads in flight together, each scaled by its part's
-// weight (a readlane).  (Batches of 32 measured no faster on the decode step.)
+// M = max_s m_s; exactly +0.0 when no part saw a slot.  One 256-thread
+// workgroup per (t, h) row, 4 dims per lane: wave w takes the parts
+// s = w + 4 j.  A wave issues the O loads of its first kMergeBatch parts
+// together with the (m, l) loads (they do not depend on M), so a decode's
+// 32 parts arrive in one memory round trip; the four waves then exchange
+// their maxima and their weighted sums through LDS, added in wave order.
+// (One wave per row, its parts read 8 at a time, took 6.4 us on the decode
+// step: four dependent round trips.)
+constexpr int kMergeWaves = 4;
 constexpr int kMergeBatch = 8;
 
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ float wave_m[kMergeWaves], wave_l[kMergeWaves];
+    __shared__ f32x4_t wave_acc[kMergeWaves][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = blockIdx.x;   // < T * Hq (the grid)
     const int64_t rows = p.T * p.Hq;
-    if (row >= rows) return;
     const int64_t t = row / p.Hq;
     const int h = (int)(row - t * p.Hq);
     const int64_t n = p.n_parts;
-    if (p.clear_flag != nullptr && row == 0 && lane == 0) *p.clear_flag = 0;
-    if (p.bad_part != nullptr && h == 0) {
+    // This wave's parts: s(j) = wave + kMergeWaves j, j < J.
+    const int64_t J = n > wave ? (n - wave + kMergeWaves - 1) / kMergeWaves : 0;
+    auto o_row = [&](int64_t j) {
+        return (const f32x4_t *)(p.part_o + ((wave + kMergeWaves * j) * rows + row) * kHeadDim +
+                                 4 * lane);
+    };
+    if (p.clear_flag != nullptr && row == 0 && threadIdx.x == 0) *p.clear_flag = 0;
+    if (p.bad_part != nullptr && h == 0 && wave == 0) {
         // The invalid entries of token t's row, reported by its raw-row shares.
         int bad = 0;
         for (int64_t s = lane; s < n; s += 64) bad += p.bad_part[s * p.T + t];
@@ -694,47 +705,73 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
         for (int off = 32; off >= 1; off >>= 1) bad += __shfl_xor(bad, off);
         if (lane == 0) p.n_bad[t] = bad;
     }
-    float mmax = kNegInf;
-    for (int64_t s0 = 0; s0 < n; s0 += 64) {
-        const int64_t s = s0 + lane;
-        if (s < n) mmax = fmaxf(mmax, p.part_ml[(s * rows + row) * 2]);
-    }
+    // The first batch of O rows, in flight with the (m, l) loads below.
+    f32x4_t o0[kMergeBatch];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
-    bf16x4_t ob = {(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
-    if (mmax != kNegInf) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        float l_part = 0.0f;
-        for (int64_t s0 = 0; s0 < n; s0 += 64) {
-            const int64_t s = s0 + lane;
+    for (int e = 0; e < kMergeBatch; ++e)
+        o0[e] = e < J ? *o_row(e) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_loc = kNegInf;
+    for (int64_t j = lane; j < J; j += 64)
+        m_loc = fmaxf(m_loc, p.part_ml[((wave + kMergeWaves * j) * rows + row) * 2]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m_loc = fmaxf(m_loc, __shfl_xor(m_loc, off));
+    if (lane == 0) wave_m[wave] = m_loc;
+    __syncthreads();
+    float mmax = wave_m[0];
+#pragma unroll
+    for (int w = 1; w < kMergeWaves; ++w) mmax = fmaxf(mmax, wave_m[w]);
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float l_part = 0.0f;
+    if (mmax != kNegInf) {   // the same for every wave
+        for (int64_t j0 = 0; j0 < J; j0 += 64) {
+            // Lane j - j0 holds part j's weight.
             float w = 0.0f;
-            if (s < n) {
-                w = __builtin_amdgcn_exp2f(p.part_ml[(s * rows + row) * 2] - mmax);
-                l_part += w * p.part_ml[(s * rows + row) * 2 + 1];
+            if (j0 + lane < J) {
+                const float *ml = p.part_ml + ((wave + kMergeWaves * (j0 + lane)) * rows + row) * 2;
+                w = __builtin_amdgcn_exp2f(ml[0] - mmax);
+                l_part += w * ml[1];
             }
-            const int cnt = (int)min<int64_t>(64, n - s0);
+            const int cnt = (int)min<int64_t>(64, J - j0);
             for (int u = 0; u < cnt; u += kMergeBatch) {
                 f32x4_t o[kMergeBatch];
+                if (j0 == 0 && u == 0) {
+#pragma unroll
+                    for (int e = 0; e < kMergeBatch; ++e) o[e] = o0[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < kMergeBatch; ++e)
+                        o[e] = u + e < cnt ? *o_row(j0 + u + e) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
 #pragma unroll
                 for (int e = 0; e < kMergeBatch; ++e)
-                    o[e] = u + e < cnt ? *(const f32x4_t *)(p.part_o + ((s0 + u + e) * rows + row) *
-                                                                       kHeadDim + 4 * lane)
-                                       : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int e = 0; e < kMergeBatch; ++e)
-                    if (u + e < cnt)   // lane u + e holds that part's weight
+                    if (u + e < cnt)
                         acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u + e)) *
                                o[e];
             }
         }
-        float l_tot = l_part;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) l_tot += __shfl_xor(l_tot, off);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ob[i] = (__bf16)(acc[i] / l_tot);
     }
-    *(u32x2_t *)(p.out + t * p.o_st + (int64_t)h * p.o_sh + 4 * lane) =
-        __builtin_bit_cast(u32x2_t, ob);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l_part += __shfl_xor(l_part, off);
+    wave_acc[wave][lane] = acc;
+    if (lane == 0) wave_l[wave] = l_part;
+    __syncthreads();
+    if (wave == 0) {
+        bf16x4_t ob = {(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+        if (mmax != kNegInf) {
+            f32x4_t sum = wave_acc[0][lane];
+            float l_tot = wave_l[0];
+#pragma unroll
+            for (int w = 1; w < kMergeWaves; ++w) {
+                sum += wave_acc[w][lane];
+                l_tot += wave_l[w];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ob[i] = (__bf16)(sum[i] / l_tot);
+        }
+        *(u32x2_t *)(p.out + t * p.o_st + (int64_t)h * p.o_sh + 4 * lane) =
+            __builtin_bit_cast(u32x2_t, ob);
+    }
 }
 
 // ---------------------------------------------------------------- sharing estimate
@@ -1023,7 +1060,7 @@ hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream) {
     const int64_t rows = p.T * p.Hq;
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
