@@ -297,6 +297,15 @@ def main():
     attn_avg = float(np.mean(attn_ms))
     select_ms = float(np.mean([s0[i].elapsed_time(s1[i]) for i in range(K)])) \
         if indexed else None
+    # The compaction pass (a1) alone, where it is a pass of its own; its
+    # workspace traffic is implementation traffic, reported apart from the
+    # algorithmic bytes: the selection rows read, the lists, counts and
+    # invalid counts written.
+    compacts = not split and bs == 1
+    compact_ms = float(np.mean([s1[i].elapsed_time(a0[i]) for i in range(K)])) \
+        if compacts else None
+    compact_bytes = (T * W * 4 + T * qsa.workspace_layout(T, W)["row_stride"] * 4 + 8 * T) \
+        if compacts else None
 
     # Gather only: the same rows, loads and launch shape with no arithmetic,
     # the loads issued back to back.
@@ -461,6 +470,7 @@ def main():
                             "sample": f"{one_rows.size} token rows, {one_pairs} pairs in "
                                       f"{one_dt:.2f} s"},
                "full_config_s_extrapolated": pairs / (cpu_pairs / c_dt),
+               "gpu_over_cpu": (pairs / (ms_step * 1e-3)) / (cpu_pairs / c_dt),
                "full_config_s_one_core_extrapolated": pairs / (one_pairs / one_dt)}
 
     record = {
@@ -492,6 +502,8 @@ def main():
         "read_ceilings": ceilings,
         "cpu_baseline": cpu,
         "attend_kernel_ms": attn_avg,
+        "compact_ms": compact_ms,
+        "compact_bytes": compact_bytes,
         "indexer_topk_ms": select_ms,
         "attend_kernel_ms_min": float(np.min(attn_ms)),
         "attend_kernel_ms_median": float(np.median(attn_ms)),
