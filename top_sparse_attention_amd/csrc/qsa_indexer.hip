@@ -36,6 +36,13 @@ __device__ __forceinline__ uint32_t score_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// max(x, 0) for the finite dot products here, as one integer max on the bits
+// (negative floats, -0.0 included, are negative integers).  fmaxf costs a
+// second instruction per value to quiet a NaN first.
+__device__ __forceinline__ float relu(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Marks, in the first output word, a row that a fast selection left to the
 // exact selection on the full row (no output word holds a value below -1).
 constexpr int32_t kSelDeferred = INT32_MIN;
@@ -62,8 +69,16 @@ __device__ __forceinline__ int idx_off(int r, int chunk) {
 // counts and append at the row's running count.  The count goes to
 // counts[t * R + range] at the end (it may exceed the part's room; the
 // selection then takes the full row instead).
-template <int kMode>
+// kRowStores (every score, rows of a multiple of 4 scores, 16-byte aligned,
+// fewer than 2^31 bytes per workgroup's rows): the 16-byte stores are buffer
+// stores issued unconditionally, those outside the rows or past the walk
+// sent to an offset past the buffer's end, which the hardware drops.  With a
+// branch around each store the compiler cannot count the stores issued
+// after the next key tile's loads, so its wait for those loads also waited
+// for the previous tile's stores.
+template <int kMode, bool kRowStores = false>
 __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreParams p) {
+    static_assert(!kRowStores || kMode == kAllScores, "row stores write every score");
     // One key tile: the barrier after each tile's scores also orders its reads
     // before the next tile is written.
     __shared__ __attribute__((aligned(16))) char tile[kScoreTile * kIndexRowBytes];
@@ -144,13 +159,22 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
     };
     // The staged scores go out as 16-byte stores where the rows allow it.
     const bool vec_out = (p.C % 4) == 0 && ((uintptr_t)p.scores % 16) == 0;
+    // (Unused, and removed, unless kRowStores.)
+    const __amdgpu_buffer_rsrc_t rows_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        p.scores + t0 * p.C, (short)0,
+        kRowStores ? (int)(min<int64_t>(kScoreTokens, p.T - t0) * p.C * 4) : 0, 0x00020000);
 
+    // The next key tile is loaded during this tile's scores and written to
+    // LDS after this tile's scores are stored: its wait then follows those
+    // stores in the same iteration (the memory counter retires in issue
+    // order, so a wait for loads issued before the stores counts them).
     u32x4_t stage[4];
     load_tile(c_begin, stage);
+    store_tile(tile, stage);
+    __syncthreads();   // the first key tile is staged
     for (int c0 = c_begin; c0 < c_end; c0 += kScoreTile) {
-        store_tile(tile, stage);
-        __syncthreads();   // the key tile is staged; the previous scores are stored
-        if (c0 + kScoreTile < c_end) load_tile(c0 + kScoreTile, stage);
+        const bool more = c0 + kScoreTile < c_end;
+        if (more) load_tile(c0 + kScoreTile, stage);
         const char *kt = tile;
 #pragma unroll
         for (int ct = 0; ct < kScoreTile / 16; ++ct) {
@@ -158,18 +182,32 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 kb[ks] = *LDS_PTR(bf16x8_t, kt + idx_off(16 * ct + c, 4 * ks + j));
+            // Several row tiles. MFMA chains at a time, interleaved (k-step
+            // outer), so consecutive MFMAs never wait for each other's
+            // results; four (two beside the candidate state) keep the registers
+            // within two waves per SIMD.
+            constexpr int kChains = kMode == kCandidates ? 2 : 4;
 #pragma unroll
-            for (int rt = 0; rt < kScoreRowTiles; ++rt) {
-                f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+            for (int rt0 = 0; rt0 < kScoreRowTiles; rt0 += kChains) {
+                f32x4_t d[kChains];
+#pragma unroll
+                for (int i = 0; i < kChains; ++i) d[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], kb[ks], d, 0, 0, 0);
-                const float score = fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) +
-                                    fmaxf(d[3], 0.f);
-                out_tile[((kScoreTokens / 4) * wave + 4 * rt + j) * kScoreOutPitch + 16 * ct + c] = score;
+#pragma unroll
+                    for (int i = 0; i < kChains; ++i)
+                        d[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt0 + i][ks], kb[ks],
+                                                                       d[i], 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < kChains; ++i) {
+                    const float score = relu(d[i][0]) + relu(d[i][1]) + relu(d[i][2]) +
+                                        relu(d[i][3]);
+                    out_tile[((kScoreTokens / 4) * wave + 4 * (rt0 + i) + j) * kScoreOutPitch +
+                             16 * ct + c] = score;
+                }
             }
         }
-        __syncthreads();   // the tile's scores are complete
+        __syncthreads();   // the tile's scores are complete, its keys read
         // kScoreTokens rows of 64 scores: 16 chunks of 4 per row.
 #pragma unroll
         for (int u = 0; u < kScoreTokens * (kScoreTile / 4) / 256; ++u) {
@@ -207,6 +245,13 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
                     const float x = e == 0 ? v[0] : e == 1 ? v[1] : e == 2 ? v[2] : v[3];
                     if (at < room) seg[at] = f32x2_t{x, __int_as_float((int)blk + e)};
                 }
+            } else if constexpr (kRowStores) {
+                const f32x4_t v = *(const f32x4_t *)(out_tile + r * kScoreOutPitch + k4);
+                const uint32_t off = t_out < p.T && blk < c_end
+                                         ? (uint32_t)(((int64_t)r * p.C + blk) * 4)
+                                         : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rows_rsrc,
+                                                       (int)off, 0, 0);
             } else if (t_out < p.T && blk < c_end) {
                 const f32x4_t v = *(const f32x4_t *)(out_tile + r * kScoreOutPitch + k4);
                 float *dst = p.scores + t_out * p.C + blk;
@@ -217,9 +262,10 @@ __global__ __launch_bounds__(256) void indexer_scores_kernel(const IndexerScoreP
                 }
             }
         }
+        if (more) store_tile(tile, stage);
+        __syncthreads();   // the next key tile is staged; the scores are read
     }
     if constexpr (kMode == kCandidates) {
-        __syncthreads();   // every row's count is final
         if (tid < kScoreTokens && t0 + tid < p.T)
             p.counts[(t0 + tid) * p.R + blockIdx.y] = seg_cnt[tid];
     }
@@ -977,8 +1023,13 @@ hipError_t launch_indexer_scores(const IndexerScoreParams &p, hipStream_t stream
     if (p.T == 0 || p.C == 0) return hipSuccess;
     const int64_t blocks = (p.T + kScoreTokens - 1) / kScoreTokens;
     const int64_t splits = (p.C + kScoreSplit - 1) / kScoreSplit;
-    hipLaunchKernelGGL(indexer_scores_kernel<kAllScores>, dim3((unsigned)blocks, (unsigned)splits),
-                       dim3(256), 0, stream, p);
+    if (p.C % 4 == 0 && (uintptr_t)p.scores % 16 == 0 &&
+        (int64_t)kScoreTokens * p.C * 4 < ((int64_t)1 << 31))
+        hipLaunchKernelGGL((indexer_scores_kernel<kAllScores, true>),
+                           dim3((unsigned)blocks, (unsigned)splits), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(indexer_scores_kernel<kAllScores>,
+                           dim3((unsigned)blocks, (unsigned)splits), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
