@@ -777,9 +777,11 @@ __device__ void select_candidates(int nc, int budget, const float *cval, const i
             eq += u == tau;
         }
     }
+    // One scan of both counts, packed (each at most kCand < 2^16).
+    static_assert(kCand < (1 << 16), "packed counts");
     int total;
-    int gt_pre = block_exclusive_sum(gt, &total, wave_sums);
-    int eq_pre = block_exclusive_sum(eq, &total, wave_sums);
+    const int both = block_exclusive_sum(gt | (eq << 16), &total, wave_sums);
+    int gt_pre = both & 0xffff, eq_pre = both >> 16;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int i = kPer * tid + k;
