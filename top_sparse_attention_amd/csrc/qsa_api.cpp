@@ -156,6 +156,16 @@ struct Problem {
     int32_t Hq, Hkv;
 };
 
+// The kernels form a cache row's address as base + slot * (slot stride in
+// bytes) with one unsigned 32 x 32 -> 64-bit multiply-add, so the slot
+// stride of the cache views must stay under 4 GiB.
+qsa_status check_slot_strides(const qsa_bf16_view *k, const qsa_bf16_view *v, int kv_bytes) {
+    const int64_t lim = (int64_t)UINT32_MAX;
+    if (k->stride[0] > lim / kv_bytes || v->stride[0] > lim / kv_bytes)
+        return fail(QSA_ERR_UNSUPPORTED, "k_cache/v_cache: slot strides of 4 GiB or more");
+    return QSA_OK;
+}
+
 // Checks of q, k_cache, v_cache, W and scale shared by every attention entry point.
 qsa_status check_inputs(const qsa_bf16_view *q, const qsa_bf16_view *k, const qsa_bf16_view *v,
                         int64_t W, float scale, Problem *pr, int kv_bytes = 2) {
@@ -165,6 +175,7 @@ qsa_status check_inputs(const qsa_bf16_view *q, const qsa_bf16_view *k, const qs
         return s;
     for (int i = 0; i < 3; ++i)
         if (v->size[i] != k->size[i]) return fail(QSA_ERR_SHAPE, "v_cache must have k_cache's shape");
+    if ((s = check_slot_strides(k, v, kv_bytes))) return s;
     pr->T = q->size[0];
     pr->S = k->size[0];
     pr->W = W;
@@ -1044,6 +1055,7 @@ qsa_status gather_only_any(const qsa_bf16_view *k_cache, const qsa_bf16_view *v_
     for (int i = 0; i < 3; ++i)
         if (v_cache->size[i] != k_cache->size[i])
             return fail(QSA_ERR_SHAPE, "v_cache must have k_cache's shape");
+    if ((s = check_slot_strides(k_cache, v_cache, kv_bytes))) return s;
     if (T < 0 || W < 0) return fail(QSA_ERR_SHAPE, "negative T or W");
     if (T > kMax32 || k_cache->size[1] > kMax32)
         return fail(QSA_ERR_UNSUPPORTED, "sizes beyond int32");

@@ -122,8 +122,10 @@ struct AttendLayout {
 // ---------------------------------------------------------------- gathers
 
 // Start of the cache row of `slot` (a valid slot: see stand_in).
-__device__ __forceinline__ const char *row_ptr(const char *base, int64_t ss, int slot) {
-    return base + (int64_t)slot * ss;
+// The slot is at least 0 and the slot stride (bytes) under 2^32 (the host
+// checks it), so one unsigned 32 x 32 -> 64-bit multiply-add forms it.
+__device__ __forceinline__ const char *row_ptr(const char *base, uint32_t ss, int slot) {
+    return base + (uint64_t)(uint32_t)slot * ss;
 }
 
 // K rows go straight from memory into the A operand of the score MFMA.  The
@@ -138,7 +140,7 @@ __device__ __forceinline__ const char *row_ptr(const char *base, int64_t ss, int
 // row (lane & 15), from stand_in.
 template <KvType KV>
 __device__ __forceinline__ void gather_k1(u32x4_t &r, int q, int slot, const char *kb,
-                                          int64_t k_ss, int lane) {
+                                          uint32_t k_ss, int lane) {
     const int j = lane >> 4;
     const char *row = row_ptr(kb, k_ss, slot);
     if constexpr (KV == KvType::kBf16)
@@ -149,7 +151,7 @@ __device__ __forceinline__ void gather_k1(u32x4_t &r, int q, int slot, const cha
 
 template <KvType KV>
 __device__ __forceinline__ void gather_k(u32x4_t (&rk)[KvGather<KV>::kKLoads], int slot,
-                                         const char *kb, int64_t k_ss, int lane) {
+                                         const char *kb, uint32_t k_ss, int lane) {
 #pragma unroll
     for (int q = 0; q < KvGather<KV>::kKLoads; ++q) gather_k1<KV>(rk[q], q, slot, kb, k_ss, lane);
 }
@@ -193,7 +195,7 @@ __device__ __forceinline__ bf16x8_t k_operand(const u32x4_t (&rk)[KvGather<KV>::
 // requests and lets the waves of the chip fall out of step).
 template <KvType KV, bool kScalarAddr>
 __device__ __forceinline__ void gather_v(u32x4_t (&rv)[KvGather<KV>::kVLoads], int slot,
-                                         const char *vb, int64_t v_ss, int lane) {
+                                         const char *vb, uint32_t v_ss, int lane) {
     using G = KvGather<KV>;
     const int byte_in_row = (lane % G::kLanesPerRow) * 16;
     const int sub = lane / G::kLanesPerRow;   // which row of the load this lane reads
@@ -430,7 +432,8 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     };
     const char *kb = (const char *)p.k + (int64_t)g * p.k_sh * Gth::kElemBytes;
     const char *vb = (const char *)p.v + (int64_t)g * p.v_sh * Gth::kElemBytes;
-    const int64_t k_ss = p.k_ss * Gth::kElemBytes, v_ss = p.v_ss * Gth::kElemBytes;
+    const uint32_t k_ss = (uint32_t)(p.k_ss * Gth::kElemBytes);
+    const uint32_t v_ss = (uint32_t)(p.v_ss * Gth::kElemBytes);
     char *vs_lds = smem;
     char *q_lds = smem + Lay::kTileBytes;
 
@@ -929,7 +932,8 @@ __global__ __launch_bounds__(64, kAttendWavesPerSimd) void gather_only_kernel(co
     const int32_t *list = p.list + t * p.list_stride;
     const char *kb = (const char *)p.k + (int64_t)g * p.k_sh * Gth::kElemBytes;
     const char *vb = (const char *)p.v + (int64_t)g * p.v_sh * Gth::kElemBytes;
-    const int64_t k_ss = p.k_ss * Gth::kElemBytes, v_ss = p.v_ss * Gth::kElemBytes;
+    const uint32_t k_ss = (uint32_t)(p.k_ss * Gth::kElemBytes);
+    const uint32_t v_ss = (uint32_t)(p.v_ss * Gth::kElemBytes);
 
     u32x4_t acc = {0, 0, 0, 0};
     u32x4_t rk[Gth::kKLoads], rv[Gth::kVLoads];
