@@ -65,7 +65,9 @@ typedef enum qsa_status {
 } qsa_status;
 
 /* A strided 3-D BF16 tensor: q and out are [T, Hq, D]; k_cache and v_cache
- * are [S, Hkv, D].  `data` points at element [0][0][0]. */
+ * are [S, Hkv, D].  `data` points at element [0][0][0].  The slot stride of
+ * k_cache and v_cache (stride[0], in bytes) must be under 4 GiB; larger ones
+ * are refused with QSA_ERR_UNSUPPORTED. */
 typedef struct qsa_bf16_view {
     void *data;
     int64_t size[3];

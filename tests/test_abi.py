@@ -121,6 +121,9 @@ BAD_CASES = {
     "negative size": (lambda q, k, v, o, s: k.size.__setitem__(0, -1), "QSA_ERR_SHAPE"),
     "out aliases q": (lambda q, k, v, o, s: setattr(o, "data", q.data), "QSA_ERR_ALIAS"),
     "out overlaps v": (lambda q, k, v, o, s: setattr(o, "data", v.data + 64), "QSA_ERR_ALIAS"),
+    # row addresses are formed with a 32-bit slot stride in bytes
+    "k slot stride 4 GiB": (lambda q, k, v, o, s: k.stride.__setitem__(0, 1 << 31),
+                            "QSA_ERR_UNSUPPORTED"),
 }
 
 
