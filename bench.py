@@ -145,7 +145,7 @@ def read_ceilings(qsa, torch, dev, reps=10):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
