@@ -46,7 +46,10 @@ def limits(case):
     return np.minimum((case.info["positions"].astype(np.int64) + 1) // 4, C)
 
 
-@pytest.mark.parametrize("L,T,budget", [(8192, 100, 64), (4099, 37, 300), (777, 50, 8)])
+# (20000, 300, 100): rows of a multiple of 4 scores over several key ranges and
+# token blocks, the last block partial (the scores pass's unconditional row stores)
+@pytest.mark.parametrize("L,T,budget", [(8192, 100, 64), (4099, 37, 300), (777, 50, 8),
+                                        (20000, 300, 100)])
 def test_integer_scores_and_selection_are_exact(L, T, budget):
     case = qi.indexed_case(1100 + L, L=L, T=T, Hq=8, Hkv=1, budget=budget, integer_keys=True)
     # spread the queries over the whole request, including the first positions
