@@ -233,6 +233,21 @@ __device__ __forceinline__ void gather_v(u32x4_t (&rv)[KvGather<KV>::kVLoads], i
     }
 }
 
+// Where tile row r of V sits in the wave's LDS tile, in rows of kVPitch.
+// The transposed reads of P.V take rows 4j..4j+3 for lane groups j = 0, 1
+// together (then j = 2, 3), 32 bytes of each row: those 8 rows must start
+// in 8 different 8-bank windows.  The 544-byte pitch (8 banks per row) does
+// that in order.  The 528-byte pitch of the 8-query-row layout (4 banks per
+// row, which its LDS budget requires) would put rows 0..7 in overlapping
+// windows, two lanes per bank; rows 0..7 therefore take the even places and
+// rows 8..15 the odd ones, 8 banks apart.  (Counters on the FP8 long prefill
+// before this: 48% of the LDS's active cycles stalled on bank conflicts.)
+template <int kVPitch>
+__device__ __forceinline__ constexpr int v_row(int r) {
+    static_assert(kVPitch == kRowBytes + 32 || kVPitch == kRowBytes + 16, "V pitch");
+    return kVPitch == kRowBytes + 32 ? r : (((r & 7) << 1) | (r >> 3));
+}
+
 // Write a gathered V tile into the wave's LDS tile as BF16 rows.
 template <KvType KV, int kVPitch>
 __device__ __forceinline__ void stage_v(const u32x4_t (&rv)[KvGather<KV>::kVLoads], char *vs,
@@ -242,7 +257,7 @@ __device__ __forceinline__ void stage_v(const u32x4_t (&rv)[KvGather<KV>::kVLoad
     const int sub = lane / G::kLanesPerRow;
 #pragma unroll
     for (int q = 0; q < G::kVLoads; ++q) {
-        const int r = G::kRowsPerLoad * q + sub;
+        const int r = v_row<kVPitch>(G::kRowsPerLoad * q + sub);
         if constexpr (KV == KvType::kBf16) {
             *LDS_PTR(u32x4_t, vs + r * kVPitch + 16 * chunk) = rv[q];
         } else {
@@ -489,7 +504,8 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
 #pragma unroll
     for (int db = 0; db < kDimBlocks; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int tr_row = 4 * j + (c >> 2);    // V row this lane addresses in a transpose load
+    // V row this lane addresses in a transpose load (its place in the tile)
+    const int tr_row = v_row<Lay::kVPitch>(4 * j + (c >> 2));
     const int tr_sub = c & 3;               // which 4 of the 16 dims of a block
 
     // One tile: consumes K(tile) and V(tile) from rk and rv and issues the
