@@ -248,6 +248,16 @@ __device__ __forceinline__ constexpr int v_row(int r) {
     return kVPitch == kRowBytes + 32 ? r : (((r & 7) << 1) | (r >> 3));
 }
 
+// FP8 V rows in LDS (as BF16): a lane converts 16 consecutive dims, 32
+// bytes, and writes them as two 16-byte halves.  Written side by side, the 16
+// lanes of a row would hit each bank twice (32-byte stride); instead the
+// first halves of the row's 16 chunks go to bytes [0, 256) and the second
+// halves to [kFp8VHalf, kFp8VHalf + 256), each write contiguous.  Dim d then
+// sits at byte ((d % 16) / 8) * kFp8VHalf + 16 (d / 16) + 2 (d % 8); the
+// 16-byte gap keeps the transposed reads of the two halves 4 banks apart.
+constexpr int kFp8VHalf = 272;
+static_assert(kFp8VHalf + 256 <= kRowBytes + 16, "FP8 V row within its pitch");
+
 // Write a gathered V tile into the wave's LDS tile as BF16 rows.
 template <KvType KV, int kVPitch>
 __device__ __forceinline__ void stage_v(const u32x4_t (&rv)[KvGather<KV>::kVLoads], char *vs,
@@ -261,8 +271,8 @@ __device__ __forceinline__ void stage_v(const u32x4_t (&rv)[KvGather<KV>::kVLoad
         if constexpr (KV == KvType::kBf16) {
             *LDS_PTR(u32x4_t, vs + r * kVPitch + 16 * chunk) = rv[q];
         } else {
-            *LDS_PTR(bf16x8_t, vs + r * kVPitch + 32 * chunk) = fp8x8_to_bf16(rv[q][0], rv[q][1]);
-            *LDS_PTR(bf16x8_t, vs + r * kVPitch + 32 * chunk + 16) =
+            *LDS_PTR(bf16x8_t, vs + r * kVPitch + 16 * chunk) = fp8x8_to_bf16(rv[q][0], rv[q][1]);
+            *LDS_PTR(bf16x8_t, vs + r * kVPitch + kFp8VHalf + 16 * chunk) =
                 fp8x8_to_bf16(rv[q][2], rv[q][3]);
         }
     }
@@ -507,6 +517,11 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     // V row this lane addresses in a transpose load (its place in the tile)
     const int tr_row = v_row<Lay::kVPitch>(4 * j + (c >> 2));
     const int tr_sub = c & 3;               // which 4 of the 16 dims of a block
+    // Byte offset of those 4 dims within dim block 0 of a row (FP8 rows: the
+    // split layout of stage_v; dim block db adds 16 db there, 32 db for BF16).
+    const int tr_off = KV == KvType::kFp8 ? (tr_sub >> 1) * kFp8VHalf + 8 * (tr_sub & 1)
+                                          : 8 * tr_sub;
+    constexpr int kTrBlock = KV == KvType::kFp8 ? 16 : 32;
 
     // One tile: consumes K(tile) and V(tile) from rk and rv and issues the
     // gathers of tile + kAhead * step into the same registers.
@@ -613,7 +628,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
                 const int db = half * (kDimBlocks / 2) + u;
                 va[u] = __builtin_bit_cast(
                     bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(
-                                  i16x4_t, vs_lds + tr_row * Lay::kVPitch + 32 * db + 8 * tr_sub)));
+                                  i16x4_t, vs_lds + tr_row * Lay::kVPitch + kTrBlock * db + tr_off)));
             }
 #pragma unroll
             for (int u = 0; u < kDimBlocks / 2; ++u) {
