@@ -174,6 +174,20 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// The maximum of x over the four lane groups of a column (lanes c, c + 16,
+// c + 32, c + 48), with the row-swap instructions of gfx950 (vector ALU, no
+// trip through the LDS as a lane shuffle takes).  Swapping a value with
+// itself leaves every lane holding its own value and its partner's, in an
+// order that depends on the lane; fmaxf takes both.
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // A operand of k-step ks from the K registers.
 template <KvType KV>
 __device__ __forceinline__ bf16x8_t k_operand(const u32x4_t (&rk)[KvGather<KV>::kKLoads], int ks) {
@@ -577,8 +591,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
             x[i] = keep ? s[i] * p.scale_log2e : kNegInf;
         }
         float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = max_over_lane_groups(mt);
         if constexpr (KV == KvType::kFp8) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
