@@ -5,7 +5,8 @@ index validation/compaction (qsa_compact_slots) followed by the gather
 attention (qsa_sparse_attend), both through the C ABI on torch's current
 stream.  Other workloads: `decode_batch` runs qsa_sparse_decode (split
 attention over the raw selection rows, then the merge), `long_prefill_fp8kv` the
-FP8 E4M3 KV-cache variant (qsa_sparse_attend_fp8kv) and `long_prefill_block4`
+FP8 E4M3 KV-cache variant (qsa_sparse_attend_fp8kv), `decode_batch_fp8kv` the
+decode step over that cache (qsa_sparse_decode_fp8kv) and `long_prefill_block4`
 micro-block selections (qsa_sparse_prefill_blocks: compaction into aligned
 block lists, then the attention);
 `indexed_long_prefill` makes the selection inside the step with the QSA
@@ -55,7 +56,7 @@ def parse():
     ap.add_argument("--workload", default="long_prefill",
                     choices=["tiny", "edge_mix", "long_prefill", "two_request",
                              "max_cache_6_1", "max_cache_3_1", "decode_batch",
-                             "long_prefill_fp8kv", "long_prefill_block4",
+                             "long_prefill_fp8kv", "decode_batch_fp8kv", "long_prefill_block4",
                              "indexed_long_prefill"])
     ap.add_argument("--cpu-rows", type=int, default=2048,
                     help="token rows of the workload the CPU oracle is timed on")
@@ -203,7 +204,7 @@ def main():
 
     # Few-token workloads run qsa_sparse_decode: split attention over the raw
     # selection rows into FP32 partials, then the merge (no compaction pass).
-    split = args.workload == "decode_batch"
+    split = args.workload in ("decode_batch", "decode_batch_fp8kv")
     splits = qsa.decode_splits(T, W, Hq, Hkv) if split else 1
     dws = (torch.empty(qsa.decode_workspace_bytes(T, W, Hq, Hkv), dtype=torch.uint8, device=dev)
            if split else None)
@@ -220,7 +221,10 @@ def main():
         qsa.compact_slots(sl, S, ws)
 
     def attend():
-        if split:
+        if split and fp8:
+            qsa.sparse_decode_fp8kv(q, k, v, k_scale, v_scale, sl, scale=scale, out=out,
+                                    workspace=dws)
+        elif split:
             qsa.sparse_decode(q, k, v, sl, scale=scale, out=out, workspace=dws)
         elif bs > 1:
             qsa.sparse_prefill_blocks(q, k, v, sl, bs, scale=scale, out=out, workspace=bws)

@@ -405,6 +405,25 @@ qsa_status qsa_sparse_prefill_fp8kv(const qsa_bf16_view *q,
                                     void *workspace, size_t workspace_bytes,
                                     void *stream);
 
+/*
+ * qsa_sparse_decode over an FP8 E4M3 KV cache: the split attention over the
+ * raw selection rows and the merge of qsa_sparse_decode, with the cache
+ * reading of qsa_sparse_attend_fp8kv (one scale per tensor, element =
+ * decode(code) * scale; the page's section "Where this sits in the Qwen4Exp
+ * serving build-out" reports decode measured with an fp8_e4m3 KV cache).
+ * Arguments as qsa_sparse_prefill_fp8kv; the workspace must hold
+ * qsa_decode_workspace_bytes(T, W, Hq, Hkv) bytes, 256-byte aligned, and
+ * qsa_check_status(workspace, ..., T, W, ...) reports the invalid entries.
+ * k_scale and v_scale must be finite (QSA_ERR_SCALE otherwise).
+ */
+qsa_status qsa_sparse_decode_fp8kv(const qsa_bf16_view *q,
+                                   const qsa_fp8_view *k_cache,
+                                   const qsa_fp8_view *v_cache, float k_scale,
+                                   float v_scale, const qsa_i32_view *slot_idx,
+                                   float scale, qsa_bf16_view *out,
+                                   void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
 /* qsa_gather_only for an FP8 KV cache (same tiles, waves and loads as
  * qsa_sparse_attend_fp8kv; XOR of the 32-bit words of every read row). */
 qsa_status qsa_gather_only_fp8kv(const qsa_fp8_view *k_cache,

@@ -287,6 +287,7 @@ def with_fp8_kv(case: Case) -> Case:
         out[name] = (codes, v8, scale)
     case.info.update(k8=out["k"][1], v8=out["v"][1], k_scale=out["k"][2],
                      v_scale=out["v"][2], k8_base=out["k"][0], v8_base=out["v"][0])
+    case.name += "_fp8kv"
     return case
 
 
@@ -381,6 +382,7 @@ WORKLOADS = {
     "max_cache_3_1": lambda seed=105: max_cache(seed, (3, 1)),
     "decode_batch": decode_batch,
     "long_prefill_fp8kv": lambda seed=103: with_fp8_kv(long_prefill(seed)),
+    "decode_batch_fp8kv": lambda seed=106: with_fp8_kv(decode_batch(seed)),
     "long_prefill_block4": long_prefill_blocks,
     "indexed_long_prefill": indexed_long_prefill,
 }

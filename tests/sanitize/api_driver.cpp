@@ -118,6 +118,28 @@ void decode_and_split() {
         CHECK(stub::calls.merge[0].n_parts == 32 && stub::calls.merge[0].clear_flag != nullptr);
     CHECK(qsa_sparse_decode(&q, &k, &v, &sl, 0.0625f, &o, addr(6), bytes - 1, nullptr) ==
           QSA_ERR_WORKSPACE);
+    // the FP8 cache: the same shares, K's scale folded into the softmax scale
+    {
+        qsa_fp8_view k8{}, v8{};
+        k8.data = k.data;
+        v8.data = v.data;
+        for (int i = 0; i < 3; ++i) {
+            k8.size[i] = v8.size[i] = k.size[i];
+            k8.stride[i] = v8.stride[i] = k.stride[i];
+        }
+        stub::calls.clear();
+        CHECK(qsa_sparse_decode_fp8kv(&q, &k8, &v8, 0.5f, 2.0f, &sl, 0.0625f, &o, addr(6), bytes,
+                                      nullptr) == QSA_OK);
+        CHECK(stub::calls.partial.size() == 1 && stub::calls.merge.size() == 1 &&
+              stub::calls.attend_kv.size() == 1 && stub::calls.attend_kv[0] == qsa::KvType::kFp8);
+        if (stub::calls.partial.size() == 1) {
+            const qsa::AttendParams &a = stub::calls.partial[0];
+            CHECK(a.raw_rows == 1 && a.splits == 32 && a.v_scale == 2.0f);
+            CHECK(std::fabs(a.scale_log2e - 0.03125f * 1.4426950408889634f) < 1e-6f);
+        }
+        CHECK(qsa_sparse_decode_fp8kv(&q, &k8, &v8, NAN, 2.0f, &sl, 0.0625f, &o, addr(6), bytes,
+                                      nullptr) == QSA_ERR_SCALE);
+    }
     // an empty cache takes the compaction route
     qsa_bf16_view k0 = view3(2, 0, Hkv), v0 = view3(3, 0, Hkv);
     stub::calls.clear();

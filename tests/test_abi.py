@@ -227,6 +227,31 @@ def test_split_entry_points_reject_bad_arguments():
 
 
 @host_only
+def test_fp8_decode_rejects_bad_arguments():
+    lib = _lib()
+    r = ctypes.byref
+    q, _, _, o, s = good()
+    k8 = view((64, 2, 256), (512, 256, 1), FAKE + (1 << 24))
+    v8 = view((64, 2, 256), (512, 256, 1), FAKE + (2 << 24))
+    ws, big = FAKE + (5 << 24), 1 << 30
+
+    def decode(k_scale=0.5, v_scale=0.25, slot=s, ws=ws, ws_bytes=big, k=k8):
+        return qsa.STATUS_NAMES[lib.qsa_sparse_decode_fp8kv(
+            r(q), r(k), r(v8), k_scale, v_scale, None if slot is None else r(slot), 0.0625,
+            r(o), ws, ws_bytes, None)]
+
+    assert decode(k_scale=float("nan")) == "QSA_ERR_SCALE"
+    assert decode(v_scale=float("inf")) == "QSA_ERR_SCALE"
+    assert decode(slot=None) == "QSA_ERR_NULL"
+    assert decode(ws_bytes=qsa.decode_workspace_bytes(4, 8, 4, 2) - 1) == "QSA_ERR_WORKSPACE"
+    assert decode(ws=FAKE + 16) == "QSA_ERR_WORKSPACE"
+    assert decode(k=view((64, 2, 256), (512, 256, 1), FAKE + (1 << 24) + 8)) == "QSA_ERR_STRIDE"
+    # a BF16-sized token stride over FP8 rows is fine; a 4 GiB one is not
+    assert decode(k=view((64, 2, 256), (1 << 32, 256, 1), FAKE + (1 << 24))) == \
+        "QSA_ERR_UNSUPPORTED"
+
+
+@host_only
 def test_indexer_entry_points_reject_bad_arguments():
     lib = _lib()
     r = ctypes.byref

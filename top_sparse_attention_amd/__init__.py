@@ -26,7 +26,7 @@ __all__ = [
     "sparse_attend", "sparse_prefill", "check_status", "gather_only",
     "compact_slot_range", "partials_bytes", "new_partials", "sparse_attend_partial",
     "merge_partials", "decode_splits", "decode_workspace_bytes", "sparse_decode",
-    "sparse_attend_fp8kv", "sparse_prefill_fp8kv", "gather_only_fp8kv",
+    "sparse_attend_fp8kv", "sparse_prefill_fp8kv", "sparse_decode_fp8kv", "gather_only_fp8kv",
     "compact_blocks", "sparse_prefill_blocks", "indexer_scores", "indexer_select",
     "indexer_topk", "indexer_topk_fused", "indexer_topk_fused_bytes", "indexer_scores_bytes", "stream_read", "sparse_prefill_noalloc", "noalloc_scratch_bytes",
 ]
@@ -132,6 +132,9 @@ def load_library():
     lib.qsa_sparse_prefill_fp8kv.restype = ctypes.c_int
     lib.qsa_sparse_prefill_fp8kv.argtypes = [P(BF16View), P(BF16View), P(BF16View), f32, f32,
                                              P(I32View), f32, P(BF16View), vp, sz, vp]
+    lib.qsa_sparse_decode_fp8kv.restype = ctypes.c_int
+    lib.qsa_sparse_decode_fp8kv.argtypes = [P(BF16View), P(BF16View), P(BF16View), f32, f32,
+                                            P(I32View), f32, P(BF16View), vp, sz, vp]
     lib.qsa_prefill_blocks_workspace_bytes.restype = sz
     lib.qsa_prefill_blocks_workspace_bytes.argtypes = [i64, i64, ctypes.c_int32]
     lib.qsa_compact_blocks.restype = ctypes.c_int
@@ -470,6 +473,27 @@ def sparse_prefill_fp8kv(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, k_
                       _bf16_view(out, "out"))
     sv = _i32_view(slot_idx, "slot_idx")
     _raise_on(load_library().qsa_sparse_prefill_fp8kv(
+        ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), float(k_scale), float(v_scale),
+        ctypes.byref(sv), _default_scale(scale, q.shape[-1]), ctypes.byref(ov),
+        workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+    return out
+
+
+def sparse_decode_fp8kv(q: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, k_scale: float,
+                        v_scale: float, slot_idx: torch.Tensor, scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sparse_decode over an FP8 E4M3 KV cache (element = decode(code) * scale)."""
+    T, W = slot_idx.shape
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if workspace is None:
+        nbytes = decode_workspace_bytes(T, W, q.shape[1], k8.shape[1])
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    qv, kv, vv, ov = (_bf16_view(q, "q"), _fp8_view(k8, "k_cache"), _fp8_view(v8, "v_cache"),
+                      _bf16_view(out, "out"))
+    sv = _i32_view(slot_idx, "slot_idx")
+    _raise_on(load_library().qsa_sparse_decode_fp8kv(
         ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), float(k_scale), float(v_scale),
         ctypes.byref(sv), _default_scale(scale, q.shape[-1]), ctypes.byref(ov),
         workspace.data_ptr(), workspace.numel(), _stream(q.device)))

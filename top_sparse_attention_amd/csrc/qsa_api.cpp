@@ -498,10 +498,11 @@ qsa_status enqueue_partial(const qsa_bf16_view *q, const qsa_bf16_view *k,
                            const qsa_bf16_view *v, const Problem &pr, float scale, const void *ws,
                            const qsa_workspace_map &m, int32_t splits, int64_t part_base,
                            void *partials, const PartialsMap &pm, hipStream_t stream,
-                           const qsa_i32_view *raw = nullptr, int32_t *bad_part = nullptr) {
+                           const qsa_i32_view *raw = nullptr, int32_t *bad_part = nullptr,
+                           KvKind kv = KvKind()) {
     if (pr.T == 0 || pr.Hq == 0) return QSA_OK;
     qsa::AttendParams p{};
-    fill_attend(p, q, k, v, pr, scale, ws, m);
+    fill_attend(p, q, k, v, pr, scale * kv.k_scale, ws, m);
     if (raw != nullptr) {
         p.raw_rows = 1;
         p.raw = raw->data;
@@ -510,14 +511,14 @@ qsa_status enqueue_partial(const qsa_bf16_view *q, const qsa_bf16_view *k,
         p.S_rows = pr.S;
         p.bad_part = bad_part;
     }
-    p.v_scale = 1.0f;
+    p.v_scale = kv.v_scale;
     p.splits = splits;
     p.part_base = part_base;
     p.T = pr.T;
     p.Hq = pr.Hq;
     p.part_o = (float *)partials;
     p.part_ml = (float *)((char *)partials + pm.ml_offset);
-    hipError_t e = qsa::launch_attend_partial(p, qsa::KvType::kBf16, pr.T, stream);
+    hipError_t e = qsa::launch_attend_partial(p, kv.type, pr.T, stream);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "partial attention launch");
 }
 
@@ -578,6 +579,60 @@ void fill_attend(qsa::AttendParams &p, const qsa_bf16_view *q, const qsa_bf16_vi
     p.HB = (p.G + 15) / 16;
     p.scale_log2e = (float)((double)scale * 1.4426950408889634);
     p.splits = 1;
+}
+
+// qsa_sparse_decode for a BF16 (kv_bytes 2) or FP8 (kv_bytes 1) cache.
+qsa_status decode_any(const qsa_bf16_view *q, const qsa_bf16_view *k_cache,
+                      const qsa_bf16_view *v_cache, const qsa_i32_view *slot_idx, float scale,
+                      qsa_bf16_view *out, void *workspace, size_t workspace_bytes, void *stream,
+                      int kv_bytes, KvKind kv) {
+    if (!slot_idx) return fail(QSA_ERR_NULL, "slot_idx: view pointer is NULL");
+    Problem pr;
+    qsa_status s = check_attend(q, k_cache, v_cache, out, slot_idx->size[1], scale, &pr,
+                                kv_bytes);
+    if (s) return s;
+    if (kv.type == qsa::KvType::kFp8 && (s = check_fp8_scales(kv.k_scale, kv.v_scale))) return s;
+    int64_t W = 0;
+    if ((s = check_slots(slot_idx, pr.T, &W))) return s;
+    const size_t need = qsa_decode_workspace_bytes(pr.T, W, pr.Hq, pr.Hkv);
+    if (!workspace) return fail(QSA_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)workspace % kAlign) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(QSA_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+    if ((s = check_compact_grid(pr.T)) ||
+        (s = check_attend_grid(pr.T, pr.Hq, pr.Hkv, decode_splits(pr.T, W, pr.Hq, pr.Hkv))) ||
+        (s = check_merge_grid(pr.T, pr.Hq)))
+        return s;
+    if (pr.T == 0) return QSA_OK;
+    qsa_workspace_map m;
+    layout_of(pr.T, W, &m);
+    const int32_t splits = decode_splits(pr.T, W, pr.Hq, pr.Hkv);
+    void *partials = (char *)workspace + round_up(m.total_bytes, kAlign);
+    PartialsMap pm;
+    partials_of(splits, pr.T, pr.Hq, &pm);
+    hipStream_t st = (hipStream_t)stream;
+    if (pr.S == 0) {
+        // An empty cache: no entry is valid and there is no row for a stand-in
+        // slot to read, so the compacted (empty) lists serve instead.
+        if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, 0, pr.S, workspace, m, st))) return s;
+        if ((s = enqueue_partial(q, k_cache, v_cache, pr, scale, workspace, m, splits, 0, partials,
+                                 pm, st, nullptr, nullptr, kv)))
+            return s;
+        return enqueue_merge(partials, pm, splits, pr.T, pr.Hq, out, st);
+    }
+    // No compaction pass: the shares read the selection rows themselves (for
+    // a few tokens the grouping by slot range buys nothing) and count their
+    // invalid entries in the list area of the workspace; the merge adds them
+    // up into n_bad, where qsa_check_status reads them.
+    if ((int64_t)splits * pr.T * 4 > m.bad_offset - m.list_offset)
+        return fail(QSA_ERR_WORKSPACE, "decode workspace too small for the per-share counts");
+    int32_t *bad_part = (int32_t *)((char *)workspace + m.list_offset);
+    if ((s = enqueue_partial(q, k_cache, v_cache, pr, scale, workspace, m, splits, 0, partials, pm,
+                             st, slot_idx, bad_part, kv)))
+        return s;
+    return enqueue_merge(partials, pm, splits, pr.T, pr.Hq, out, st, bad_part,
+                         (int32_t *)((char *)workspace + m.bad_offset),
+                         extent_words(workspace, m) + 1);
 }
 
 }  // namespace
@@ -964,51 +1019,17 @@ qsa_status qsa_sparse_decode(const qsa_bf16_view *q, const qsa_bf16_view *k_cach
                              const qsa_bf16_view *v_cache, const qsa_i32_view *slot_idx,
                              float scale, qsa_bf16_view *out, void *workspace,
                              size_t workspace_bytes, void *stream) {
-    if (!slot_idx) return fail(QSA_ERR_NULL, "slot_idx: view pointer is NULL");
-    Problem pr;
-    qsa_status s = check_attend(q, k_cache, v_cache, out, slot_idx->size[1], scale, &pr);
-    if (s) return s;
-    int64_t W = 0;
-    if ((s = check_slots(slot_idx, pr.T, &W))) return s;
-    const size_t need = qsa_decode_workspace_bytes(pr.T, W, pr.Hq, pr.Hkv);
-    if (!workspace) return fail(QSA_ERR_WORKSPACE, "workspace is NULL");
-    if ((uintptr_t)workspace % kAlign) return fail(QSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (workspace_bytes < need)
-        return fail(QSA_ERR_WORKSPACE, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
-    if ((s = check_compact_grid(pr.T)) ||
-        (s = check_attend_grid(pr.T, pr.Hq, pr.Hkv, decode_splits(pr.T, W, pr.Hq, pr.Hkv))) ||
-        (s = check_merge_grid(pr.T, pr.Hq)))
-        return s;
-    if (pr.T == 0) return QSA_OK;
-    qsa_workspace_map m;
-    layout_of(pr.T, W, &m);
-    const int32_t splits = decode_splits(pr.T, W, pr.Hq, pr.Hkv);
-    void *partials = (char *)workspace + round_up(m.total_bytes, kAlign);
-    PartialsMap pm;
-    partials_of(splits, pr.T, pr.Hq, &pm);
-    hipStream_t st = (hipStream_t)stream;
-    if (pr.S == 0) {
-        // An empty cache: no entry is valid and there is no row for a stand-in
-        // slot to read, so the compacted (empty) lists serve instead.
-        if ((s = enqueue_compact(slot_idx, pr.T, W, pr.S, 0, pr.S, workspace, m, st))) return s;
-        if ((s = enqueue_partial(q, k_cache, v_cache, pr, scale, workspace, m, splits, 0, partials,
-                                 pm, st)))
-            return s;
-        return enqueue_merge(partials, pm, splits, pr.T, pr.Hq, out, st);
-    }
-    // No compaction pass: the shares read the selection rows themselves (for
-    // a few tokens the grouping by slot range buys nothing) and count their
-    // invalid entries in the list area of the workspace; the merge adds them
-    // up into n_bad, where qsa_check_status reads them.
-    if ((int64_t)splits * pr.T * 4 > m.bad_offset - m.list_offset)
-        return fail(QSA_ERR_WORKSPACE, "decode workspace too small for the per-share counts");
-    int32_t *bad_part = (int32_t *)((char *)workspace + m.list_offset);
-    if ((s = enqueue_partial(q, k_cache, v_cache, pr, scale, workspace, m, splits, 0, partials, pm,
-                             st, slot_idx, bad_part)))
-        return s;
-    return enqueue_merge(partials, pm, splits, pr.T, pr.Hq, out, st, bad_part,
-                         (int32_t *)((char *)workspace + m.bad_offset),
-                         extent_words(workspace, m) + 1);
+    return decode_any(q, k_cache, v_cache, slot_idx, scale, out, workspace, workspace_bytes,
+                      stream, 2, KvKind());
+}
+
+qsa_status qsa_sparse_decode_fp8kv(const qsa_bf16_view *q, const qsa_fp8_view *k8,
+                                   const qsa_fp8_view *v8, float k_scale, float v_scale,
+                                   const qsa_i32_view *slot_idx, float scale,
+                                   qsa_bf16_view *out, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    return decode_any(q, as_view(k8), as_view(v8), slot_idx, scale, out, workspace,
+                      workspace_bytes, stream, 1, KvKind{qsa::KvType::kFp8, k_scale, v_scale});
 }
 
 qsa_status qsa_check_status(const void *workspace, size_t workspace_bytes, int64_t T,

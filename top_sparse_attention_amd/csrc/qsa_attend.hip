@@ -1096,9 +1096,14 @@ hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
                                  hipStream_t stream) {
     const int64_t blocks = T * (int64_t)p.Hkv * p.HB * p.splits;
     if (blocks == 0) return hipSuccess;
-    if (p.raw_rows) {
-        if (kv != KvType::kBf16 || (p.raw == nullptr && p.W_raw > 0)) return hipErrorInvalidValue;
-        launch_attend_kernel<true, KvType::kBf16, 16, kItemsPerCU, true>(p, blocks, stream);
+    if (p.raw_rows) {   // raw selection rows, masked per tile; the layouts of launch_attend_any
+        if (p.raw == nullptr && p.W_raw > 0) return hipErrorInvalidValue;
+        if (kv == KvType::kFp8 && p.G <= 8)
+            launch_attend_kernel<true, KvType::kFp8, 8, kItemsPerCU, true>(p, blocks, stream);
+        else if (kv == KvType::kFp8)
+            launch_attend_kernel<true, KvType::kFp8, 16, kItemsPerCU, true>(p, blocks, stream);
+        else
+            launch_attend_kernel<true, KvType::kBf16, 16, kItemsPerCU, true>(p, blocks, stream);
         return hipGetLastError();
     }
     launch_attend_any<true>(p, kv, blocks, stream);
