@@ -329,6 +329,10 @@ def test_launches_beyond_the_work_item_limit_are_refused():
     q, k, v, o, s, ws = far_views(1 << 25, 16, 64, 2, 1)
     assert name(lib.qsa_sparse_attend(r(q), r(k), r(v), 1, 0.0625, ws, huge, r(o),
                                       None)) == "QSA_ERR_UNSUPPORTED"
+    k8 = view((64, 2, 256), (512, 256, 1), k.data)
+    v8 = view((64, 2, 256), (512, 256, 1), v.data)
+    assert name(lib.qsa_sparse_attend_fp8kv(r(q), r(k8), r(v8), 1.0, 1.0, 1, 0.0625, ws, huge,
+                                            r(o), None)) == "QSA_ERR_UNSUPPORTED"
     # one fewer token fits: the call gets as far as the launch, which fails
     # on a host without a GPU
     q, k, v, o, s, ws = far_views((1 << 25) - 1, 16, 64, 2, 1)

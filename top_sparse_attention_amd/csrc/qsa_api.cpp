@@ -1152,6 +1152,7 @@ qsa_status qsa_sparse_attend_fp8kv(const qsa_bf16_view *q, const qsa_fp8_view *k
     if ((s = check_fp8_scales(k_scale, v_scale))) return s;
     qsa_workspace_map m;
     if ((s = check_workspace(workspace, workspace_bytes, pr.T, W, &m))) return s;
+    if ((s = check_attend_grid(pr.T, pr.Hq, pr.Hkv, 1))) return s;
     KvKind kv{qsa::KvType::kFp8, k_scale, v_scale};
     return enqueue_attend(q, as_view(k8), as_view(v8), out, pr, scale, workspace, m,
                           (hipStream_t)stream, kv);
