@@ -149,6 +149,16 @@ def test_fp8_decode_small_batches(T, Hq, Hkv, W, pad):
     print(f"{case.name} fp8 decode: {m}", flush=True)
 
 
+def test_fp8_decode_edge_mix_strided_views():
+    """Stride-2 query tokens, K and V interleaved per slot, interior and tail
+    padding, fully masked rows."""
+    case = qi.with_fp8_kv(qi.edge_mix())
+    assert case.info["k8"].strides[0] == 512
+    o = run_decode_fp8(case)
+    m = gate(bf16_tensor_to_f32(o), oracle_fp8(case), empty_row_mask(case.slot_idx, case.S))
+    print(f"{case.name} fp8 decode: {m}", flush=True)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 1), (32, 2)])
 def test_fp8_decode_drops_and_counts_invalid_entries(Hq, Hkv):
     """Entries neither -1 nor in [0, S) are dropped (the result is the

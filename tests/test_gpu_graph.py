@@ -1,5 +1,5 @@
-"""The prefill, FP8 prefill, micro-block prefill, decode and indexer paths
-captured in a HIP graph.
+"""The prefill, FP8 prefill, micro-block prefill, decode, FP8 decode and
+indexer paths captured in a HIP graph.
 
 These paths record no memset and make no synchronous call, so a captured
 step replays exactly: every replay is compared bit for bit with the eager
@@ -93,6 +93,18 @@ def test_decode_graph_replays_exactly():
     nbytes = qsa.decode_workspace_bytes(case.T, case.W, case.Hq, case.Hkv)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     replay_matches_eager(lambda: qsa.sparse_decode(q, k, v, sl, out=out, workspace=ws), out)
+
+
+def test_fp8_decode_graph_replays_exactly():
+    case = qi.with_fp8_kv(qi.random_case(1208, T=6, S=30000, Hq=16, Hkv=2, W=1500,
+                                         pad_frac=0.1, interior=True))
+    q, _, _, sl = upload(case, DEV)
+    k8, v8, ks, vs = upload_fp8(case, DEV)
+    out = torch.empty_like(q)
+    ws = torch.empty(qsa.decode_workspace_bytes(case.T, case.W, case.Hq, case.Hkv),
+                     dtype=torch.uint8, device=DEV)
+    replay_matches_eager(
+        lambda: qsa.sparse_decode_fp8kv(q, k8, v8, ks, vs, sl, out=out, workspace=ws), out)
 
 
 def test_indexer_topk_graph_replays_exactly():

@@ -132,6 +132,43 @@ def test_cache_sharded_by_slot_ranges(bounds):
     gate(bf16_tensor_to_f32(out), bf16_tensor_to_f32(whole), np.zeros(case.T, dtype=bool))
 
 
+def _partials_views(parts, n, T, Hq):
+    """The O [n, T, Hq, 256] and (m, l) [n, T, Hq, 2] float32 views of a
+    partials buffer (the (m, l) block starts at the next 256-byte boundary)."""
+    o_bytes = n * T * Hq * 256 * 4
+    ml_off = (o_bytes + 255) // 256 * 256
+    o = parts[:o_bytes].view(torch.float32).view(n, T, Hq, 256)
+    ml = parts[ml_off:ml_off + n * T * Hq * 8].view(torch.float32).view(n, T, Hq, 2)
+    return o, ml
+
+
+@pytest.mark.parametrize("splits", [1, 3, 70, 260])
+def test_merge_kernels_agree_bit_for_bit(splits):
+    """Merges of 4,096 rows or more run one wave per row; smaller ones a
+    four-wave workgroup per row.  Both add the same terms in the same order:
+    the 4,096-row merge equals, bit for bit, the merges of its 64-token
+    slices (1,024 rows each).  260 parts take more than one round of 64
+    weights per part sequence; empty shares (max -inf) occur at every count."""
+    case = qi.random_case(870 + splits, T=256, S=8000, Hq=16, Hkv=2, W=1200, pad_frac=0.3,
+                          interior=True)
+    T, Hq = case.T, case.Hq
+    q, k, v, sl = upload(case, DEV)
+    ws = qsa.compact_slots(sl, case.S)
+    parts = qsa.new_partials(splits, T, Hq, DEV)
+    qsa.sparse_attend_partial(q, k, v, ws, case.W, splits, 0, splits, parts, scale=case.scale)
+    full = qsa.merge_partials(parts, splits, T, Hq)
+    po, pml = _partials_views(parts, splits, T, Hq)
+    for t0 in range(0, T, 64):
+        cp = qsa.new_partials(splits, 64, Hq, DEV)
+        co, cml = _partials_views(cp, splits, 64, Hq)
+        co.copy_(po[:, t0:t0 + 64])
+        cml.copy_(pml[:, t0:t0 + 64])
+        sliced = qsa.merge_partials(cp, splits, 64, Hq)
+        torch.cuda.synchronize()
+        assert torch.equal(sliced.view(torch.int16), full[t0:t0 + 64].view(torch.int16)), t0
+    check(case, full)
+
+
 def test_shard_compaction_keeps_local_numbering():
     case = qi.random_case(850, T=20, S=3000, Hq=2, Hkv=1, W=200, pad_frac=0.1, interior=True)
     case.slot_idx[3, 5] = 3000          # invalid everywhere

@@ -821,6 +821,111 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
     }
 }
 
+// Many rows: one wave per row, kMergeRowsPerWg rows per workgroup, no LDS and
+// no barrier.  The wave runs merge_kernel's four part sequences s = w + 4 j
+// one after the other with the same operations in the same order (weights in
+// the lanes of their sequence, weighted O rows added in sequence order,
+// denominators reduced across lanes per sequence, the four sums added in
+// sequence order), so both kernels give the same bits and the choice between
+// them is one of speed only.  merge_kernel spends a workgroup and two barriers
+// on each row: on 124,960 rows of one part (the long prefill's rows) it took
+// 0.38 ms, about 60 generations of short-lived workgroups.
+constexpr int kMergeRowsPerWg = 4;
+constexpr int kMergeRowsAhead = 2;   // O rows per sequence loaded with the maxima
+constexpr int kMergeRowsBatch = 4;   // O rows per sequence loaded together after that
+static_assert(kMergeRowsAhead <= kMergeRowsBatch, "the rows loaded ahead serve the first batch");
+// merge_kernel below this many rows (the parts of a row spread over four waves
+// keep a decode step's few rows in one memory round trip), this kernel from it.
+constexpr int64_t kMergeRowsMin = 4096;
+
+__global__ __launch_bounds__(256) void merge_rows_kernel(const MergeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t rows = p.T * p.Hq;
+    const int64_t row = (int64_t)blockIdx.x * kMergeRowsPerWg + (threadIdx.x >> 6);
+    if (row >= rows) return;   // (whole waves; nothing below waits on other waves)
+    const int64_t t = row / p.Hq;
+    const int h = (int)(row - t * p.Hq);
+    const int64_t n = p.n_parts;
+    auto o_row = [&](int64_t s) {
+        return (const f32x4_t *)(p.part_o + (s * rows + row) * kHeadDim + 4 * lane);
+    };
+    if (p.clear_flag != nullptr && row == 0 && lane == 0) *p.clear_flag = 0;
+    if (p.bad_part != nullptr && h == 0) {
+        int bad = 0;
+        for (int64_t s = lane; s < n; s += 64) bad += p.bad_part[s * p.T + t];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) bad += __shfl_xor(bad, off);
+        if (lane == 0) p.n_bad[t] = bad;
+    }
+    // The first O rows of every sequence, in flight with the maxima.
+    f32x4_t o0[kMergeWaves][kMergeRowsAhead];
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w)
+#pragma unroll
+        for (int e = 0; e < kMergeRowsAhead; ++e) {
+            const int64_t s = w + (int64_t)kMergeWaves * e;
+            o0[w][e] = s < n ? *o_row(s) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    float mmax = kNegInf;
+    for (int64_t s = lane; s < n; s += 64) mmax = fmaxf(mmax, p.part_ml[(s * rows + row) * 2]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
+
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+    float l_tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+        const int64_t J = n > w ? (n - w + kMergeWaves - 1) / kMergeWaves : 0;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float l_part = 0.0f;
+        if (mmax != kNegInf) {
+            for (int64_t j0 = 0; j0 < J; j0 += 64) {
+                // Lane j - j0 holds part w + 4 j's weight.
+                float wt = 0.0f;
+                if (j0 + lane < J) {
+                    const float *ml = p.part_ml + ((w + kMergeWaves * (j0 + lane)) * rows + row) * 2;
+                    wt = __builtin_amdgcn_exp2f(ml[0] - mmax);
+                    l_part += wt * ml[1];
+                }
+                const int cnt = (int)min<int64_t>(64, J - j0);
+                for (int u = 0; u < cnt; u += kMergeRowsBatch) {
+                    f32x4_t o[kMergeRowsBatch];
+                    const bool first = j0 == 0 && u == 0;
+#pragma unroll
+                    for (int e = 0; e < kMergeRowsBatch; ++e) {
+                        if (e < kMergeRowsAhead && first)
+                            o[e] = o0[w][e < kMergeRowsAhead ? e : 0];
+                        else
+                            o[e] = u + e < cnt ? *o_row(w + kMergeWaves * (j0 + u + e))
+                                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    }
+#pragma unroll
+                    for (int e = 0; e < kMergeRowsBatch; ++e)
+                        if (u + e < cnt)
+                            acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt),
+                                                                             u + e)) * o[e];
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) l_part += __shfl_xor(l_part, off);
+        if (w == 0) {
+            sum = acc;
+            l_tot = l_part;
+        } else {
+            sum += acc;
+            l_tot += l_part;
+        }
+    }
+    bf16x4_t ob = {(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+    if (mmax != kNegInf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ob[i] = (__bf16)(sum[i] / l_tot);
+    }
+    *(u32x2_t *)(p.out + t * p.o_st + (int64_t)h * p.o_sh + 4 * lane) =
+        __builtin_bit_cast(u32x2_t, ob);
+}
+
 // ---------------------------------------------------------------- sharing estimate
 
 // One workgroup per sampled token pair (a, b): a's list (at most kShareKeys
@@ -1113,7 +1218,12 @@ hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream) {
     const int64_t rows = p.T * p.Hq;
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(256), 0, stream, p);
+    if (rows >= kMergeRowsMin)
+        hipLaunchKernelGGL(merge_rows_kernel,
+                           dim3((unsigned)((rows + kMergeRowsPerWg - 1) / kMergeRowsPerWg)),
+                           dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(merge_kernel, dim3((unsigned)rows), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
