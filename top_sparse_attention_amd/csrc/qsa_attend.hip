@@ -829,10 +829,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 // sequence order), so both kernels give the same bits and the choice between
 // them is one of speed only.  merge_kernel spends a workgroup and two barriers
 // on each row: on 124,960 rows of one part (the long prefill's rows) it took
-// 0.38 ms, about 60 generations of short-lived workgroups.
+// 0.38 ms, about 60 generations of short-lived workgroups; this kernel takes
+// 56 us.  Its few loads ahead keep it at 60 VGPRs, 8 waves per SIMD: two rows
+// ahead per sequence and batches of four (94 VGPRs) took 77 us.
 constexpr int kMergeRowsPerWg = 4;
-constexpr int kMergeRowsAhead = 2;   // O rows per sequence loaded with the maxima
-constexpr int kMergeRowsBatch = 4;   // O rows per sequence loaded together after that
+constexpr int kMergeRowsAhead = 1;   // O rows per sequence loaded with the maxima
+constexpr int kMergeRowsBatch = 2;   // O rows per sequence loaded together after that
 static_assert(kMergeRowsAhead <= kMergeRowsBatch, "the rows loaded ahead serve the first batch");
 // merge_kernel below this many rows (the parts of a row spread over four waves
 // keep a decode step's few rows in one memory round trip), this kernel from it.
