@@ -196,6 +196,43 @@ def test_single_slot_rows_return_the_value_row_bit_exactly():
             np.testing.assert_array_equal(got[t, h], case.v_cache[s, h // 6])
 
 
+def test_identical_value_rows_return_that_row_bit_exactly():
+    """Every cache slot holds the same V row (per KV head): the weights sum
+    out, out = that row.  The two FP32 sums (the weighted rows and the
+    weights) differ by far less than half a BF16 step, so the BF16 output is
+    the row bit for bit."""
+    case = qi.random_case(710, T=25, S=3000, Hq=16, Hkv=2, W=700, pad_frac=0.2, interior=True)
+    case.v_cache[:] = case.v_cache[0]
+    case.slot_idx[3] = -1
+    o, _ = run_case(case)
+    got = bf16_tensor_bits(o)
+    G = case.Hq // case.Hkv
+    for t in range(case.T):
+        if t == 3:
+            assert np.all(got[t] == 0)
+            continue
+        for h in range(case.Hq):
+            np.testing.assert_array_equal(got[t, h], case.v_cache[0, h // G])
+
+
+def test_zero_queries_give_the_mean_of_the_selected_values():
+    """All-zero query rows score every selected slot 0: equal weights, so the
+    output is the plain mean of the selected V rows (FP64 closed form)."""
+    case = qi.random_case(711, T=19, S=2500, Hq=12, Hkv=2, W=300, pad_frac=0.25,
+                          interior=True)
+    case.q[:] = 0
+    o, _ = run_case(case)
+    v = qi.bf16_to_f32(case.v_cache).astype(np.float64)
+    G = case.Hq // case.Hkv
+    want = np.zeros((case.T, case.Hq, 256))
+    for t in range(case.T):
+        sel = case.slot_idx[t][case.slot_idx[t] != -1]
+        for h in range(case.Hq):
+            want[t, h] = v[sel, h // G].mean(axis=0)
+    m = gate(bf16_tensor_to_f32(o), want.astype(np.float32), empty_row_mask(case.slot_idx, case.S))
+    print(f"zero queries: {m}", flush=True)
+
+
 def test_padding_position_is_bitwise_irrelevant():
     case = qi.random_case(701, T=30, S=3000, Hq=16, Hkv=2, W=400, pad_frac=0.3)
     a, _ = run_case(case)
