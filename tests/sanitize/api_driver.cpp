@@ -79,8 +79,12 @@ void prefill_shapes() {
             const qsa::AttendParams &a = stub::calls.attend[0];
             CHECK(a.G == s.Hq / s.Hkv && a.HB == (a.G + 15) / 16 && a.S_rows == s.S);
             CHECK(std::fabs(a.scale_log2e - 0.0625f * 1.4426950408889634f) < 1e-6f);
+            // The long prefill's sizes bound its sharing at 8.1: the general
+            // layout without an estimate and with its keys direct.
+            if (s.T == 7810) CHECK(!stub::calls.attend_shared[0] && a.keys_lds == 0);
             if (stub::calls.attend_shared[0]) {
                 const qsa::SharingParams &sp = stub::calls.share[0];
+                CHECK(sp.lds_threshold == qsa::kShareKeysLds && a.keys_lds == 0);
                 for (int i = 0; i < sp.pairs; ++i)
                     CHECK(sp.pair_a[i] >= 0 && sp.pair_a[i] < s.T && sp.pair_b[i] >= 0 &&
                           sp.pair_b[i] < s.T && sp.pair_a[i] != sp.pair_b[i]);
@@ -98,6 +102,23 @@ void prefill_shapes() {
         CHECK(qsa_sparse_prefill_fp8kv(&q, &k8, &v8, 0.5f, 2.0f, &sl, 0.0625f, &o, addr(6), ws_bytes,
                                        nullptr) == QSA_OK);
         CHECK(stub::calls.attend.size() == 1 && stub::calls.attend_kv[0] == qsa::KvType::kFp8);
+        if (stub::calls.attend.size() == 1) {
+            // FP8 caches have no keys-through-LDS form
+            CHECK(stub::calls.attend[0].keys_lds == 0);
+            if (stub::calls.attend_shared[0]) CHECK(stub::calls.share[0].lds_threshold == 0.0f);
+        }
+    }
+    // Sizes that bound the sharing at 32: keys through LDS, no estimate.
+    {
+        const Shape s{4096, 16384, 2048, 16, 2};
+        qsa_bf16_view q = view3(1, s.T, s.Hq), k = view3(2, s.S, s.Hkv), v = view3(3, s.S, s.Hkv),
+                      o = view3(4, s.T, s.Hq);
+        qsa_i32_view sl = view2(5, s.T, s.W);
+        stub::calls.clear();
+        CHECK(qsa_sparse_prefill(&q, &k, &v, &sl, 0.0625f, &o, addr(6), qsa_workspace_bytes(s.T, s.W),
+                                 nullptr) == QSA_OK);
+        CHECK(stub::calls.attend.size() == 1 && !stub::calls.attend_shared[0] &&
+              stub::calls.attend[0].keys_lds == 1);
     }
 }
 

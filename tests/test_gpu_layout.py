@@ -1,10 +1,12 @@
-"""The attention's layout choice (8 or 4 items per CU) and its sharing estimate.
+"""The attention's layout choice and its sharing estimate.
 
 Where the sizes leave the cache large against the selection width, a small
 kernel samples pairs of neighbouring tokens, counts their common slots and
-picks 4 items per CU if the tokens running together share few cache rows.
+picks 4 items per CU if the tokens running together share few cache rows,
+8 with the keys taken through LDS (BF16) if they share many, else 8 as they
+are.  Where the sizes alone bound the sharing high, no estimate runs.
 These tests check the choice the estimate writes into the workspace on
-selections of known sharing, that both layouts give the oracle's result
+selections of known sharing, that every layout gives the oracle's result
 within the gate, and that they give the same bits.
 """
 import numpy as np
@@ -76,10 +78,26 @@ def test_two_kv_heads_at_sharing_four_take_four_per_cu():
     print(check_rows(out, case.q, case.k_cache, case.v_cache, case.slot_idx, case.S, rows))
 
 
-def test_large_cache_with_a_small_referenced_part_keeps_eight_per_cu():
-    # The tokens select among 40,000 slots scattered over a 262,144-slot cache:
-    # the sizes suggest little sharing, the lists show about 13 readers per row.
-    base = qi.random_case(1303, T=4096, S=40000, Hq=3, Hkv=1, W=2048)
+def direct_keys_reference(q, k, v, sl, S):
+    """The same attention through the split kernel with one share (keys
+    gathered straight into the score operands) and the merge: one share's
+    O / l, the same bits as the unsplit kernel's."""
+    T, W = sl.shape
+    ws = qsa.compact_slots(sl, S)
+    parts = qsa.new_partials(1, T, q.shape[1], DEV)
+    qsa.sparse_attend_partial(q, k, v, ws, W, 1, 0, 1, parts)
+    out = qsa.merge_partials(parts, 1, T, q.shape[1])
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("referenced,want_choice", [(40000, 2), (75000, 0)])
+def test_large_cache_with_a_small_referenced_part(referenced, want_choice):
+    # The tokens select among `referenced` slots scattered over a 262,144-slot
+    # cache: the sizes suggest little sharing, the lists show about
+    # 256 * 2048 / referenced readers per row: 13 (keys through LDS) or 7
+    # (the general layout as it is).
+    base = qi.random_case(1303, T=4096, S=referenced, Hq=3, Hkv=1, W=2048)
     q, kb, vb, slb = upload(base, DEV)
     S = 262144
     new_of_old = torch.from_numpy(
@@ -91,10 +109,27 @@ def test_large_cache_with_a_small_referenced_part_keeps_eight_per_cu():
     v[new_of_old] = vb
     sl = new_of_old[slb.long()].to(torch.int32)
     out, choice = prefill_with_choice(q, k, v, sl)
-    assert choice == 0
+    assert choice == want_choice
     rows = qi.sample_rows(base.T, 16, seed=33)
     # Relocated rows: the oracle of the original cache gives the same result.
     print(check_rows(out, base.q, base.k_cache, base.v_cache, base.slot_idx, base.S, rows))
+    ref = direct_keys_reference(q, k, v, sl, S)
+    assert np.array_equal(bf16_tensor_bits(out), bf16_tensor_bits(ref))
+
+
+def test_sizes_alone_take_keys_through_lds_with_the_same_bits():
+    # 2,048 of 16,384 slots per token, (16,2): the sizes bound the sharing at
+    # 256 * 2048 / 16384 = 32, so the keys-through-LDS form runs without an
+    # estimate (the choice word is not written).
+    case = qi.random_case(1309, T=4096, S=16384, Hq=16, Hkv=2, W=2048, pad_frac=0.05,
+                          interior=True)
+    q, k, v, sl = upload(case, DEV)
+    out, choice = prefill_with_choice(q, k, v, sl)
+    assert choice == -7
+    rows = qi.sample_rows(case.T, 16, seed=37)
+    print(check_rows(out, case.q, case.k_cache, case.v_cache, case.slot_idx, case.S, rows))
+    ref = direct_keys_reference(q, k, v, sl, case.S)
+    assert np.array_equal(bf16_tensor_bits(out), bf16_tensor_bits(ref))
 
 
 def test_fp8_cache_with_more_than_eight_heads_per_kv_head_takes_four_per_cu():
@@ -156,7 +191,7 @@ def test_mostly_empty_rows_with_the_estimate():
     case.slot_idx[empty] = -1
     q, k, v, sl = upload(case, DEV)
     out, choice = prefill_with_choice(q, k, v, sl)
-    assert choice in (0, 1)
+    assert choice in (0, 1, 2)
     rows = np.unique(np.concatenate([qi.sample_rows(case.T, 10, seed=36), [3, 13, 4093]]))
     print(check_rows(out, case.q, case.k_cache, case.v_cache, case.slot_idx, case.S, rows))
     assert torch.count_nonzero(out[torch.as_tensor(np.flatnonzero(empty), device=DEV)]) == 0

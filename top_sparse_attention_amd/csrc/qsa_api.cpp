@@ -345,9 +345,12 @@ constexpr double kShareSizeBound = 6.0;
 // Parameters of the sharing estimate for an attention launch, or false where
 // the kItemsPerCU layout is taken without one: the sizes already bound the
 // sharing above kShareSizeBound, or there are fewer than two chip-fulls of
-// items for the layout to matter.
+// items for the layout to matter.  Without an estimate, *keys_lds says
+// whether the sizes alone bound the sharing at or above kShareKeysLds (BF16:
+// the general layout then takes its keys through LDS).
 bool sharing_of(const Problem &pr, int32_t HB, void *ws, const qsa_workspace_map &m,
-                qsa::SharingParams *sp) {
+                qsa::SharingParams *sp, bool bf16, bool *keys_lds) {
+    *keys_lds = false;
     const int64_t per_t = (int64_t)pr.Hkv * HB;
     const int64_t chip = (int64_t)qsa::kXcds * qsa::kCusPerXcd * qsa::kItemsPerCU;
     if (pr.T < 2 || pr.T > kMax32 || per_t <= 0 || pr.T * per_t < 2 * chip || pr.S <= 0)
@@ -359,7 +362,11 @@ bool sharing_of(const Problem &pr, int32_t HB, void *ws, const qsa_workspace_map
     int64_t heads = 0;
     for (int64_t g = 0; g < pr.Hkv; ++g) heads += (g * HB + d - 1) / d * d < (g + 1) * HB;
     const double per_xcd = (double)qsa::kCusPerXcd * qsa::kItemsPerCU / heads;
-    if (per_xcd * (double)m.row_stride >= kShareSizeBound * (double)pr.S) return false;
+    const double bound = per_xcd * (double)m.row_stride;   // over S
+    if (bound >= kShareSizeBound * (double)pr.S) {
+        *keys_lds = bf16 && bound >= (double)qsa::kShareKeysLds * (double)pr.S;
+        return false;
+    }
     char *base = (char *)ws + m.share_offset;
     sp->list = (const int32_t *)((const char *)ws + m.list_offset);
     sp->row_stride = m.row_stride;
@@ -376,6 +383,7 @@ bool sharing_of(const Problem &pr, int32_t HB, void *ws, const qsa_workspace_map
     sp->lambda_scale = (float)per_xcd;
     sp->threshold = m.row_stride >= qsa::kShareLongList ? qsa::kShareThreshold
                                                         : qsa::kShareThresholdShort;
+    sp->lds_threshold = bf16 ? qsa::kShareKeysLds : 0.0f;
     sp->est = (float *)base;
     sp->choice = (int32_t *)(base + qsa::kSharePairs * 8);
     return true;
@@ -404,7 +412,9 @@ qsa_status enqueue_attend(const qsa_bf16_view *q, const qsa_bf16_view *k,
         return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
     }
     qsa::SharingParams sp{};
-    const bool share = sharing_of(pr, p.HB, ws, m, &sp);
+    bool keys_lds = false;
+    const bool share = sharing_of(pr, p.HB, ws, m, &sp, kv.type == qsa::KvType::kBf16, &keys_lds);
+    p.keys_lds = keys_lds ? 1 : 0;
     hipError_t e = qsa::launch_attend(p, kv.type, pr.T, stream, share ? &sp : nullptr);
     return e == hipSuccess ? QSA_OK : hip_fail(e, "attention launch");
 }
@@ -451,7 +461,8 @@ AlignSpec align_of(const Problem &pr, int64_t W, int32_t block_size, void *ws,
         return al;
     qsa::SharingParams sp{};
     const int32_t HB = (pr.Hq / pr.Hkv + 15) / 16;
-    if (sharing_of(pr, HB, ws, m, &sp)) return al;
+    bool keys_lds = false;   // (aligned lists run the masked form, keys direct)
+    if (sharing_of(pr, HB, ws, m, &sp, true, &keys_lds)) return al;
     int32_t shift = std::max(sort_key_bits(nb) - qsa::kSortKeyBits, 0);
     int32_t by_size = 0;   // largest with 2^by_size blocks <= kAlignSlots slots
     while (((int64_t)block_size << (by_size + 1)) <= qsa::kAlignSlots) ++by_size;

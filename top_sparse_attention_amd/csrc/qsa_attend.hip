@@ -371,12 +371,22 @@ __device__ __forceinline__ int stand_in_masked(int entry, int64_t S, uint32_t *v
 // it; each tile masks them with a ballot of its rows.  Split shares then read
 // the raw selection rows (W_raw entries each); unsplit items read a
 // compacted list with -1 gaps (count[t] entries, the aligned block lists).
-template <bool kSplit, KvType KV, int kQRows, int kItems, bool kMasked>
+//
+// kKeysLds (BF16, general layout, compacted lists): the keys are gathered
+// like the values, as whole rows, two per load instruction, a whole tile
+// ahead: at the start of each tile K(i) goes from its registers into the
+// wave's LDS tile, the gathers of K(i+1) are issued into those registers at
+// once, and the score MFMAs read their K operands back from LDS with the
+// same dims per lane as the direct form, so both give the same bits.  The
+// values then overwrite the tile as usual.
+template <bool kSplit, KvType KV, int kQRows, int kItems, bool kMasked, bool kKeysLds>
 __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t unit,
                                             char *smem) {
     using Gth = KvGather<KV>;
     using Lay = AttendLayout<kQRows, kItems>;
     constexpr bool kRawRows = kMasked && kSplit;
+    static_assert(!kKeysLds || (KV == KvType::kBf16 && kQRows == 16 && !kMasked),
+                  "keys through LDS: BF16 general layout over compacted lists");
 
     int lane = threadIdx.x;
     // In the unit loop of a persistent layout, the lane index is made opaque,
@@ -509,7 +519,8 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
 #pragma unroll
     for (int b = 0; b < kAhead; ++b) {
         const int slot = resolve(slot_next, tile + b * step, b);
-        gather_k<KV>(rkb[b], slot, kb, k_ss, lane);
+        if constexpr (kKeysLds) gather_v<KV, kScalarVAddr>(rkb[b], slot, kb, k_ss, lane);
+        else gather_k<KV>(rkb[b], slot, kb, k_ss, lane);
         slot_next = entry_at(tile + (b + 1) * step);
         gather_v<KV, kScalarVAddr>(rvb[b], slot, vb, v_ss, lane);
     }
@@ -545,6 +556,20 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         // The query operands are read from LDS in two halves to bound the
         // registers they hold.
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+        int slot_g = 0;   // slots of the tile whose gathers go out next
+        bf16x8_t ka[kKeysLds ? kKSteps : 1];
+        if constexpr (kKeysLds) {
+            wave_lds_fence();   // the previous tile's transpose reads are done
+            stage_v<KV, Lay::kVPitch>(rk, vs_lds, lane);   // K(i) rows into the tile
+            __builtin_amdgcn_sched_barrier(0);
+            slot_g = resolve(slot_next, tile + kAhead * step, b);
+            gather_v<KV, kScalarVAddr>(rk, slot_g, kb, k_ss, lane);   // K(i+1)
+            wave_lds_fence();
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks)
+                ka[ks] = *LDS_PTR(bf16x8_t, vs_lds + v_row<Lay::kVPitch>(c) * Lay::kVPitch +
+                                                16 * q_chunk(ks, j));
+        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             bf16x8_t qb[kKSteps / 2];
@@ -554,9 +579,13 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
                                  q_lds + (c % kQRows) * kQPitch +
                                      16 * q_chunk(half * kKSteps / 2 + u, j));
 #pragma unroll
-            for (int u = 0; u < kKSteps / 2; ++u)
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    k_operand<KV>(rk, half * kKSteps / 2 + u), qb[u], s, 0, 0, 0);
+            for (int u = 0; u < kKSteps / 2; ++u) {
+                const int ks = half * kKSteps / 2 + u;
+                bf16x8_t kop;
+                if constexpr (kKeysLds) kop = ka[ks];
+                else kop = k_operand<KV>(rk, ks);
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qb[u], s, 0, 0, 0);
+            }
         }
         // Where the loads of the next tile's K go: FP8 tiles are short and
         // latency-bound, so they are issued early, half before the softmax
@@ -571,7 +600,6 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
             valid_cur = valid_q[b];
             bad_total += bad_q[b];
         }
-        int slot_g = 0;
         if constexpr (KV == KvType::kFp8) slot_g = resolve(slot_next, tile + kAhead * step, b);
         __builtin_amdgcn_sched_barrier(0);   // K(i) is consumed before K(i+1) lands
         if constexpr (KV == KvType::kFp8) {
@@ -624,7 +652,8 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         wave_lds_fence();   // the previous tile's transpose reads are done
         stage_v<KV, Lay::kVPitch>(rv, vs_lds, lane);
         __builtin_amdgcn_sched_barrier(0);   // V(i) is consumed before V(i+1) lands
-        if constexpr (KV == KvType::kBf16) slot_g = resolve(slot_next, tile + kAhead * step, b);
+        if constexpr (KV == KvType::kBf16 && !kKeysLds)
+            slot_g = resolve(slot_next, tile + kAhead * step, b);
         slot_next = entry_at(tile + (kAhead + 1) * step);
         gather_v<KV, kScalarVAddr>(rv, slot_g, vb, v_ss, lane);
         wave_lds_fence();   // other lanes of this wave wrote the rows read below
@@ -648,7 +677,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
                 const int db = half * (kDimBlocks / 2) + u;
                 o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[u], pb, o[db], 0, 0, 0);
                 constexpr int kEvery = kDimBlocks / Gth::kKLoads;
-                if (KV == KvType::kBf16 && db % kEvery == kEvery - 1) {
+                if (KV == KvType::kBf16 && !kKeysLds && db % kEvery == kEvery - 1) {
                     __builtin_amdgcn_sched_barrier(0);
                     gather_k1<KV>(rk[db / kEvery], db / kEvery, slot_g, kb, k_ss, lane);
                     __builtin_amdgcn_sched_barrier(0);
@@ -698,19 +727,20 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
 // u % 8).  Persistent workgroups measured 1.5-2% faster at 4 items per CU
 // and 2.5-4% slower at 8 and 12, where the hardware's refill of finished
 // workgroups keeps the running tokens closer together.
-template <bool kSplit, KvType KV, int kQRows, int kItems = kItemsPerCU, bool kMasked = false>
+template <bool kSplit, KvType KV, int kQRows, int kItems = kItemsPerCU, bool kMasked = false,
+          bool kKeysLds = false>
 __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) void attend_kernel(
     const AttendParams p) {
     using Lay = AttendLayout<kQRows, kItems>;
     __shared__ __attribute__((aligned(16))) char smem[Lay::kLds];
-    if (p.choice != nullptr && ((*p.choice == 1) != (p.choice_value == 1))) return;
+    if (p.choice != nullptr && *p.choice != p.choice_value) return;
     if constexpr (Lay::kPersistent) {
         for (int64_t unit = blockIdx.x; unit < p.units; unit += gridDim.x) {
             wave_lds_fence();   // the previous unit's LDS reads are done
-            attend_unit<kSplit, KV, kQRows, kItems, kMasked>(p, unit, smem);
+            attend_unit<kSplit, KV, kQRows, kItems, kMasked, kKeysLds>(p, unit, smem);
         }
     } else {
-        attend_unit<kSplit, KV, kQRows, kItems, kMasked>(p, blockIdx.x, smem);
+        attend_unit<kSplit, KV, kQRows, kItems, kMasked, kKeysLds>(p, blockIdx.x, smem);
     }
 }
 
@@ -1051,8 +1081,13 @@ __global__ __launch_bounds__(64) void sharing_choice_kernel(const SharingParams 
         common += __shfl_xor(common, off);
         len += __shfl_xor(len, off);
     }
-    if (lane == 0)
-        *p.choice = (len > 0.0f && p.lambda_scale * common < p.threshold * len) ? 1 : 0;
+    if (lane == 0) {
+        const float shared = p.lambda_scale * common;
+        int choice = 0;
+        if (len > 0.0f && shared < p.threshold * len) choice = 1;
+        else if (len > 0.0f && p.lds_threshold > 0.0f && shared >= p.lds_threshold * len) choice = 2;
+        *p.choice = choice;
+    }
 }
 
 // ---------------------------------------------------------------- gather only
@@ -1141,7 +1176,8 @@ int device_cus() {
 
 // attend_kernel over `units` work units: one workgroup each, or at most one
 // chip-full (a multiple of the XCDs) for a persistent layout.
-template <bool kSplit, KvType KV, int kQRows, int kItems = kItemsPerCU, bool kMasked = false>
+template <bool kSplit, KvType KV, int kQRows, int kItems = kItemsPerCU, bool kMasked = false,
+          bool kKeysLds = false>
 void launch_attend_kernel(AttendParams p, int64_t units, hipStream_t stream) {
     using Lay = AttendLayout<kQRows, kItems>;
     p.units = units;
@@ -1151,8 +1187,8 @@ void launch_attend_kernel(AttendParams p, int64_t units, hipStream_t stream) {
             kXcds, (int64_t)Lay::kItems * device_cus() / kXcds * kXcds);
         grid = std::min(units, full);
     }
-    hipLaunchKernelGGL((attend_kernel<kSplit, KV, kQRows, kItems, kMasked>), dim3((unsigned)grid),
-                       dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((attend_kernel<kSplit, KV, kQRows, kItems, kMasked, kKeysLds>),
+                       dim3((unsigned)grid), dim3(64), 0, stream, p);
 }
 
 // FP8 caches with at most 8 query heads per KV head take the 8-query-row
@@ -1176,12 +1212,17 @@ hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_
         launch_attend_kernel<false, KvType::kBf16, 16, kItemsPerCU, true>(p, items, stream);
         return hipGetLastError();
     }
+    if (share == nullptr && p.keys_lds && kv == KvType::kBf16) {
+        launch_attend_kernel<false, KvType::kBf16, 16, kItemsPerCU, false, true>(p, items, stream);
+        return hipGetLastError();
+    }
     if (share == nullptr || (kv == KvType::kFp8 && p.G <= 8)) {
         launch_attend_any<false>(p, kv, items, stream);
         return hipGetLastError();
     }
-    // The estimate picks one of two launches of the general layout; the other
-    // returns at once.  Both compute the same bits.
+    // The estimate picks one of the gated launches of the general layout (8
+    // items per CU; 4; BF16: 8 with keys through LDS); the others return at
+    // once.  All compute the same bits.
     hipLaunchKernelGGL(sharing_kernel, dim3((unsigned)share->pairs), dim3(256), 0, stream, *share);
     hipLaunchKernelGGL(sharing_choice_kernel, dim3(1), dim3(64), 0, stream, *share);
     AttendParams g = p;
@@ -1196,6 +1237,10 @@ hipError_t launch_attend(const AttendParams &p, KvType kv, int64_t T, hipStream_
         launch_attend_kernel<false, KvType::kFp8, 16, kLowShareItemsPerCU>(g, items, stream);
     else
         launch_attend_kernel<false, KvType::kBf16, 16, kLowShareItemsPerCU>(g, items, stream);
+    if (kv == KvType::kBf16 && share->lds_threshold > 0.0f) {
+        g.choice_value = 2;
+        launch_attend_kernel<false, KvType::kBf16, 16, kItemsPerCU, false, true>(g, items, stream);
+    }
     return hipGetLastError();
 }
 

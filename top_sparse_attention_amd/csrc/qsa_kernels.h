@@ -43,6 +43,16 @@ constexpr int kSharePairs = 32;
 constexpr float kShareThreshold = 5.0f;
 constexpr float kShareThresholdShort = 3.0f;
 constexpr int kShareLongList = 1024;
+// The sharing at or above which BF16 items of the general layout take their
+// keys through LDS (choice 2), from the estimate or from the sizes alone.
+// Keys gathered as whole rows, two per load instruction like the values, touch
+// 8 cache rows per instruction instead of 16; the L1 side of each CU, which
+// the gathers wait on, then serves more of them.  They pass through the wave's
+// LDS tile to reach the score MFMA, a round trip on each tile's path that
+// costs more than it saves where most gathers miss the L2 (measured crossover
+// near 8.5 on the long prefill's shape: 4% slower at 8.0, 14% faster at 10.7,
+// 16-17% faster at 13 and above).
+constexpr float kShareKeysLds = 9.0f;
 // Fewest tiles a split of the decode path takes.
 constexpr int kMinSplitTiles = 4;
 // Entries of a selection row sorted together by the compaction pass.
@@ -131,10 +141,13 @@ struct AttendParams {
     float *part_o;       // [n_parts][T][Hq][256], O not yet divided by l
     float *part_ml;      // [n_parts][T][Hq][2]: running max (log2 units) and sum
     // Gated launch (non-null choice): the kernel does its work only if
-    // (*choice == 1) == (choice_value == 1), so of two launches with values 0
-    // and 1 exactly one works, whatever the word holds.
+    // *choice == choice_value; the sharing estimate writes the word (0, 1 or
+    // 2) before the gated launches, so exactly one of them works.
     const int32_t *choice;
     int32_t choice_value;
+    // Ungated BF16 launch of the general layout: keys_lds = 1 takes its
+    // keys-through-LDS form (see SharingParams), which computes the same bits.
+    int32_t keys_lds;
     // Work units of the launch (items, times splits in split mode); set by
     // the launcher, which sizes the grid.
     int64_t units;
@@ -143,7 +156,7 @@ struct AttendParams {
     // Each entry is a block of 2^block_shift slots; count[t] counts entries.
     int32_t masked;
     int32_t block_shift;
-    // Split mode over raw selection rows (raw_rows = 1; BF16 only): each share
+    // Split mode over raw selection rows (raw_rows = 1): each share
     // reads slot_idx row t itself (W_raw entries, -1 and invalid entries
     // included; valid means in [0, S_rows)) instead of a compacted list, and
     // the share with g = 0 and head block 0 writes its count of invalid
@@ -170,7 +183,9 @@ struct AttendParams {
 // for tokens a, b that run together.  The estimate takes `pairs` token
 // pairs (pair_a[i], pair_b[i]), counts each pair's common slots, and writes
 // choice = 1 (take the kLowShareItemsPerCU layout) if
-// lambda_scale * sum|L_a & L_b| < threshold * sum|L_b|, else 0.
+// lambda_scale * sum|L_a & L_b| < threshold * sum|L_b|; else choice = 2 (the
+// general layout with keys through LDS) if lds_threshold > 0 and
+// lambda_scale * sum|L_a & L_b| >= lds_threshold * sum|L_b|; else 0.
 struct SharingParams {
     const int32_t *list;
     int64_t row_stride;
@@ -179,6 +194,7 @@ struct SharingParams {
     int32_t pair_a[kSharePairs], pair_b[kSharePairs];   // token rows, a != b
     float lambda_scale;   // concurrent items of one KV head per XCD
     float threshold;
+    float lds_threshold;  // 0: no keys-through-LDS form (FP8 caches)
     float *est;           // [pairs][2]: common slots (scaled), |L_b|
     int32_t *choice;
 };
