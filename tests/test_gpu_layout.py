@@ -132,6 +132,41 @@ def test_sizes_alone_take_keys_through_lds_with_the_same_bits():
     assert np.array_equal(bf16_tensor_bits(out), bf16_tensor_bits(ref))
 
 
+# Sizes bounding the sharing at 9 or more for other head shapes, widths and
+# padding: (Hq, Hkv, T, S, W, pad).  G = 20 runs two head blocks per KV head;
+# W = 33 leaves a one-slot last tile.
+@pytest.mark.parametrize("Hq,Hkv,T,S,W,pad", [(40, 2, 1100, 20000, 1000, 0.1),
+                                              (3, 1, 4096, 16000, 777, 0.3),
+                                              (16, 2, 4096, 1024, 33, 0.0)])
+def test_keys_through_lds_across_shapes(Hq, Hkv, T, S, W, pad):
+    case = qi.random_case(1310 + Hq, T=T, S=S, Hq=Hq, Hkv=Hkv, W=W, pad_frac=pad, interior=True)
+    q, k, v, sl = upload(case, DEV)
+    out, choice = prefill_with_choice(q, k, v, sl)
+    assert choice == -7      # no estimate: the sizes decide
+    rows = qi.sample_rows(case.T, 12, seed=38)
+    print(check_rows(out, case.q, case.k_cache, case.v_cache, case.slot_idx, case.S, rows))
+    ref = direct_keys_reference(q, k, v, sl, case.S)
+    assert np.array_equal(bf16_tensor_bits(out), bf16_tensor_bits(ref))
+
+
+def test_keys_through_lds_over_interleaved_cache_views():
+    """K and V as views of one [S, 2, Hkv, 256] buffer (slot stride 2 rows)."""
+    case = qi.random_case(1320, T=4096, S=12000, Hq=16, Hkv=2, W=1500, pad_frac=0.1,
+                          interior=True)
+    q, k0, v0, sl = upload(case, DEV)
+    kv = torch.empty((case.S, 2, case.Hkv, 256), dtype=torch.bfloat16, device=DEV)
+    kv[:, 0] = k0
+    kv[:, 1] = v0
+    k, v = kv[:, 0], kv[:, 1]
+    assert k.stride(0) == 2 * case.Hkv * 256
+    out, choice = prefill_with_choice(q, k, v, sl)
+    assert choice == -7
+    rows = qi.sample_rows(case.T, 12, seed=39)
+    print(check_rows(out, case.q, case.k_cache, case.v_cache, case.slot_idx, case.S, rows))
+    ref = direct_keys_reference(q, k, v, sl, case.S)
+    assert np.array_equal(bf16_tensor_bits(out), bf16_tensor_bits(ref))
+
+
 def test_fp8_cache_with_more_than_eight_heads_per_kv_head_takes_four_per_cu():
     # FP8 caches with G > 8 run the general layout, so the estimate applies.
     case = qi.with_fp8_kv(qi.random_case(1305, T=4096, S=131072, Hq=12, Hkv=1, W=1024))
