@@ -1,5 +1,5 @@
-"""The prefill, FP8 prefill, micro-block prefill, decode, FP8 decode and
-indexer paths captured in a HIP graph.
+"""The prefill (every attention layout), FP8 prefill, micro-block prefill,
+decode, FP8 decode and indexer paths captured in a HIP graph.
 
 These paths record no memset and make no synchronous call, so a captured
 step replays exactly: every replay is compared bit for bit with the eager
@@ -127,3 +127,24 @@ def test_prefill_with_sharing_estimate_graph_replays_exactly():
     out = torch.empty_like(q)
     ws = qsa.new_workspace(case.T, case.W, DEV)
     replay_matches_eager(lambda: qsa.sparse_prefill(q, k, v, sl, out=out, workspace=ws), out)
+
+
+def test_prefill_with_keys_through_lds_graph_replays_exactly():
+    # High sharing hidden in a large cache: the estimate picks the gated
+    # keys-through-LDS launch (choice 2) on every replay.
+    base = qi.random_case(1209, T=4096, S=30000, Hq=3, Hkv=1, W=2048)
+    q, kb, vb, slb = upload(base, DEV)
+    S = 262144
+    new_of_old = torch.from_numpy(
+        np.random.Generator(np.random.PCG64(1210)).permutation(S)[:base.S].astype(np.int64)
+    ).to(DEV)
+    k = torch.zeros((S, 1, 256), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros_like(k)
+    k[new_of_old] = kb
+    v[new_of_old] = vb
+    sl = new_of_old[slb.long()].to(torch.int32)
+    out = torch.empty_like(q)
+    ws = qsa.new_workspace(base.T, base.W, DEV)
+    replay_matches_eager(lambda: qsa.sparse_prefill(q, k, v, sl, out=out, workspace=ws), out)
+    off = qsa.workspace_layout(base.T, base.W)["share_offset"] + 32 * 8
+    assert int(ws[off:off + 4].view(torch.int32).item()) == 2
