@@ -487,10 +487,25 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     char *q_lds = smem + Lay::kTileBytes;
 
     // The item's query rows (16 heads; absent heads are zero) go to LDS; their
-    // loads are issued before the first gathers and written after them.
+    // loads are issued before the first gathers and written after them.  With
+    // the keys through LDS, each lane instead keeps its own query operands of
+    // all k-steps in registers (32 more VGPRs; the tiles then read only K and
+    // V from LDS: 3.8% faster on the two-request prefill, no change for the
+    // direct form, slightly slower at 4 items per CU).
+    constexpr bool kQRegs = kKeysLds;
+    bf16x8_t qk[kQRegs ? kKSteps : 1];
+    if constexpr (kQRegs) {
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+            const uint16_t *src = c < nh ? p.q + t * p.q_st + (int64_t)(h0 + c) * p.q_sh +
+                                               8 * q_chunk(ks, j)
+                                         : kZeroRow + 8 * q_chunk(ks, j);
+            qk[ks] = ldg16<bf16x8_t>(src);
+        }
+    }
     u32x4_t qr[Lay::kQChunksPerLane];
 #pragma unroll
-    for (int u = 0; u < Lay::kQChunksPerLane; ++u) {
+    for (int u = 0; u < (kQRegs ? 0 : Lay::kQChunksPerLane); ++u) {
         const int idx = lane + 64 * u;
         const int r = idx / kChunksPerRow, ch = idx % kChunksPerRow;
         const uint16_t *src =
@@ -526,7 +541,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     }
 
 #pragma unroll
-    for (int u = 0; u < Lay::kQChunksPerLane; ++u) {
+    for (int u = 0; u < (kQRegs ? 0 : Lay::kQChunksPerLane); ++u) {
         const int idx = lane + 64 * u;
         *LDS_PTR(u32x4_t, q_lds + (idx / kChunksPerRow) * kQPitch + 16 * (idx % kChunksPerRow)) =
             qr[u];
@@ -574,10 +589,12 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         for (int half = 0; half < 2; ++half) {
             bf16x8_t qb[kKSteps / 2];
 #pragma unroll
-            for (int u = 0; u < kKSteps / 2; ++u)
-                qb[u] = *LDS_PTR(bf16x8_t,
-                                 q_lds + (c % kQRows) * kQPitch +
-                                     16 * q_chunk(half * kKSteps / 2 + u, j));
+            for (int u = 0; u < kKSteps / 2; ++u) {
+                if constexpr (kQRegs) qb[u] = qk[(half * kKSteps / 2 + u) % (kQRegs ? kKSteps : 1)];
+                else qb[u] = *LDS_PTR(bf16x8_t,
+                                      q_lds + (c % kQRows) * kQPitch +
+                                          16 * q_chunk(half * kKSteps / 2 + u, j));
+            }
 #pragma unroll
             for (int u = 0; u < kKSteps / 2; ++u) {
                 const int ks = half * kKSteps / 2 + u;
