@@ -221,7 +221,10 @@ qsa_status qsa_sparse_prefill_blocks(const qsa_bf16_view *q,
  * the tokens running together share cache rows in L2.  Where the sizes allow
  * little sharing (a cache large against W), a small estimate first samples
  * pairs of neighbouring tokens' lists and counts their common slots; if the
- * tokens share few rows, 4 items per CU are run instead.  Both layouts give
+ * tokens share few rows, 4 items per CU are run instead, and if they share
+ * many (BF16 caches), the 8 items take their keys through LDS as whole rows
+ * (fewer cache rows per load instruction).  Sizes that alone bound the
+ * sharing high enough take that form without an estimate.  All layouts give
  * the same bits.  The estimate writes the workspace's share words (the rest
  * of the workspace is only read), so calls on one workspace must not
  * overlap.
