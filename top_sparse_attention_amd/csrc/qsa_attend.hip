@@ -27,8 +27,11 @@
 //     use; computes the 16x16 score tile with bf16 MFMA (K rows x query
 //     heads, the query rows read from LDS), runs an online softmax in FP32
 //     and accumulates P.V with bf16 MFMA fed by LDS transpose loads, then
-//     writes the row in BF16.  Its split form writes FP32 (O, m, l) partials
-//     of a share of the tiles instead, which merge_kernel combines.
+//     writes the row in BF16.  Where the running tokens share many rows
+//     (BF16), the keys come as whole rows through the LDS tile instead
+//     (kKeysLds).  Its split form writes FP32 (O, m, l) partials of a share
+//     of the tiles instead, which merge_kernel (or merge_rows_kernel)
+//     combines.
 // This file holds the attention kernels, their merge, the sharing estimate
 // and gather_only_kernel (the attention's loads alone, a measurement aid);
 // qsa_compact.hip holds the compaction pass and qsa_indexer.hip the QSA
@@ -569,7 +572,8 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
                          u32x4_t (&rv)[Gth::kVLoads], const int b) {
         // S^T for the tile: s[i] = score of tile slot 4j+i against head c.
         // The query operands are read from LDS in two halves to bound the
-        // registers they hold.
+        // registers they hold (with the keys through LDS they stay in
+        // registers, and the K operands come from the tile instead).
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
         int slot_g = 0;   // slots of the tile whose gathers go out next
         bf16x8_t ka[kKeysLds ? kKSteps : 1];
@@ -609,10 +613,12 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         // and half after its row maximum; BF16 loads are spread over the P.V
         // MFMAs below, one per two MFMAs (measured fastest of the placements
         // tried: all at once after the scores, spread over the softmax, or
-        // alternating with the V loads).
+        // alternating with the V loads).  With the keys through LDS they went
+        // out as one burst at the start of the tile, above.
         // The next tile's slots: FP8 needs them here; BF16 resolves them after
         // V(i) is staged, where that wait has already covered their load (a
-        // resolve here would wait for V(i) before the scores).
+        // resolve here would wait for V(i) before the scores), or, with the
+        // keys through LDS, at the start of the tile.
         if constexpr (kMasked) {   // this tile's mask and count, resolved when its gathers went out
             valid_cur = valid_q[b];
             bad_total += bad_q[b];
