@@ -174,6 +174,11 @@ def main():
     bs = int(case.info.get("block_size", 1))
     Wl = W * bs
     ws = qsa.new_workspace(T, Wl, dev)
+    # The attention's layout choice word (share area, after the 32 sampled
+    # pairs' floats): a value the sharing estimate never writes, so that it
+    # stays where no estimate runs.
+    choice_off = qsa.workspace_layout(T, Wl)["share_offset"] + 32 * 8
+    ws[choice_off:choice_off + 4].view(torch.int32).fill_(-1)
     scale = case.scale if case.scale is not None else 1.0 / np.sqrt(case.D)
     torch.cuda.synchronize()
 
@@ -417,6 +422,14 @@ def main():
             hierarchy["beyond_l2_frac_of_hbm_ceiling"] = \
                 hierarchy["beyond_l2_GBps"] / ceilings["hbm"]["GBps"]
 
+    # The sharing estimate's choice for the prefill attention (0: 8 items per
+    # CU, 1: 4 per CU, 2: 8 with the keys through LDS), None where no
+    # estimate ran (the sizes decided) or the step has no such attention.
+    layout_choice = None
+    if not split and bs == 1:
+        c_ = int(ws[choice_off:choice_off + 4].view(torch.int32).item())
+        layout_choice = c_ if c_ >= 0 else None
+
     # Parity of this very output on a sample of rows, checked against the oracle.
     import oracle
 
@@ -494,7 +507,8 @@ def main():
         "config": {"workload": case.name, "T": T, "S": S, "W": W, "Hq": Hq, "Hkv": Hkv,
                    "D": case.D, "scale": scale, "seed": case.info.get("seed"),
                    "splits": splits, "block_size": bs, "parallelism": "none (1 GPU)",
-                   "launch": "hip_graph" if args.graph else "eager"},
+                   "launch": "hip_graph" if args.graph else "eager",
+                   "sharing_estimate_choice": layout_choice},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS if achieved else None,
                      "traffic": traffic,
