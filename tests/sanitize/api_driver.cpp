@@ -127,16 +127,16 @@ void decode_and_split() {
     qsa_bf16_view q = view3(1, T, Hq), k = view3(2, S, Hkv), v = view3(3, S, Hkv), o = view3(4, T, Hq);
     qsa_i32_view sl = view2(5, T, W);
     const size_t bytes = qsa_decode_workspace_bytes(T, W, (int32_t)Hq, (int32_t)Hkv);
-    CHECK(qsa_decode_splits(T, W, (int32_t)Hq, (int32_t)Hkv) == 32);
+    CHECK(qsa_decode_splits(T, W, (int32_t)Hq, (int32_t)Hkv) == 16);
     stub::calls.clear();
     CHECK(qsa_sparse_decode(&q, &k, &v, &sl, 0.0625f, &o, addr(6), bytes, nullptr) == QSA_OK);
     CHECK(stub::calls.compact.empty() && stub::calls.partial.size() == 1 && stub::calls.merge.size() == 1);
     if (stub::calls.partial.size() == 1) {
         const qsa::AttendParams &a = stub::calls.partial[0];
-        CHECK(a.raw_rows == 1 && a.splits == 32 && a.W_raw == W && a.bad_part != nullptr);
+        CHECK(a.raw_rows == 1 && a.splits == 16 && a.W_raw == W && a.bad_part != nullptr);
     }
     if (stub::calls.merge.size() == 1)
-        CHECK(stub::calls.merge[0].n_parts == 32 && stub::calls.merge[0].clear_flag != nullptr);
+        CHECK(stub::calls.merge[0].n_parts == 16 && stub::calls.merge[0].clear_flag != nullptr);
     CHECK(qsa_sparse_decode(&q, &k, &v, &sl, 0.0625f, &o, addr(6), bytes - 1, nullptr) ==
           QSA_ERR_WORKSPACE);
     // the FP8 cache: the same shares, K's scale folded into the softmax scale
@@ -155,7 +155,7 @@ void decode_and_split() {
               stub::calls.attend_kv.size() == 1 && stub::calls.attend_kv[0] == qsa::KvType::kFp8);
         if (stub::calls.partial.size() == 1) {
             const qsa::AttendParams &a = stub::calls.partial[0];
-            CHECK(a.raw_rows == 1 && a.splits == 32 && a.v_scale == 2.0f);
+            CHECK(a.raw_rows == 1 && a.splits == 16 && a.v_scale == 2.0f);
             CHECK(std::fabs(a.scale_log2e - 0.03125f * 1.4426950408889634f) < 1e-6f);
         }
         CHECK(qsa_sparse_decode_fp8kv(&q, &k8, &v8, NAN, 2.0f, &sl, 0.0625f, &o, addr(6), bytes,

@@ -179,8 +179,13 @@ def test_partials_and_decode_sizes():
     o_bytes = (rows * 256 * 4 + 255) // 256 * 256
     assert qsa.partials_bytes(3, 5, 7) == o_bytes + (rows * 8 + 255) // 256 * 256
     assert qsa.partials_bytes(-1, 5, 7) == 0
-    # enough workgroups to cover the GPU, >= 4 tiles per split, <= 64 splits
-    assert qsa.decode_splits(16, 2048, 24, 2) == 32
+    # about 1,024 workgroups; >= 8 tiles per split unless that leaves fewer
+    # than 512 workgroups; >= 4 tiles per split; <= 64 splits
+    assert qsa.decode_splits(16, 2048, 24, 2) == 16
+    assert qsa.decode_splits(8, 2048, 24, 2) == 32
+    assert qsa.decode_splits(32, 2048, 24, 2) == 16
+    assert qsa.decode_splits(64, 2048, 24, 2) == 8
+    assert qsa.decode_splits(256, 2048, 24, 2) == 2
     assert qsa.decode_splits(1, 2048, 16, 2) == 32
     assert qsa.decode_splits(1, 100000, 16, 2) == 64
     assert qsa.decode_splits(7810, 2051, 16, 2) == 1
@@ -188,7 +193,7 @@ def test_partials_and_decode_sizes():
     assert qsa.decode_splits(0, 64, 8, 1) == 1
     ws = qsa.workspace_bytes(16, 2048)
     assert qsa.decode_workspace_bytes(16, 2048, 24, 2) == \
-        (ws + 255) // 256 * 256 + qsa.partials_bytes(32, 16, 24)
+        (ws + 255) // 256 * 256 + qsa.partials_bytes(16, 16, 24)
 
 
 @host_only

@@ -34,7 +34,7 @@ def check(case, got, rows=None):
 def test_decode_batch_workload():
     case = qi.decode_batch()
     q, k, v, sl = upload(case, DEV)
-    assert qsa.decode_splits(case.T, case.W, case.Hq, case.Hkv) == 32
+    assert qsa.decode_splits(case.T, case.W, case.Hq, case.Hkv) == 16
     out = qsa.sparse_decode(q, k, v, sl)
     torch.cuda.synchronize()
     check(case, out)

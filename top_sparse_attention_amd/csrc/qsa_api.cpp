@@ -553,17 +553,19 @@ qsa_status enqueue_merge(const void *partials, const PartialsMap &pm, int64_t n_
     return e == hipSuccess ? QSA_OK : hip_fail(e, "merge launch");
 }
 
-// Splits per item for qsa_sparse_decode: enough workgroups to cover every
-// CU a few times over, at least kMinSplitTiles tiles per split, at most 64.
-// A pure function of the sizes, so results are reproducible.
+// Splits per item for qsa_sparse_decode: about kDecodeUnits workgroups;
+// at least kDecodeShareTiles tiles per split unless that leaves fewer than
+// kDecodeMinUnits workgroups; at least kMinSplitTiles tiles; at most 64.  A
+// pure function of the sizes, so results are reproducible.
 int32_t decode_splits(int64_t T, int64_t W, int32_t Hq, int32_t Hkv) {
     if (T <= 0 || W <= 0 || Hq <= 0 || Hkv <= 0) return 1;
     const int64_t G = Hq / Hkv;
     const int64_t items = mul_sat(mul_sat(T, Hkv), (G + 15) / 16);
     const int64_t tiles = ceil_div(W, qsa::kTileSlots);
-    const int64_t target_blocks = 2048;
-    int64_t s = ceil_div(target_blocks, items);
-    s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / qsa::kMinSplitTiles));
+    int64_t s = ceil_div(qsa::kDecodeUnits, items);
+    s = std::min<int64_t>(
+        s, std::max<int64_t>(tiles / qsa::kDecodeShareTiles, ceil_div(qsa::kDecodeMinUnits, items)));
+    s = std::min<int64_t>(s, tiles / qsa::kMinSplitTiles);
     s = std::min<int64_t>(s, 64);
     return (int32_t)std::max<int64_t>(s, 1);
 }

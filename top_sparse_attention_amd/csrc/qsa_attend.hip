@@ -461,7 +461,8 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
                        : tile_slot(list, tl, ntiles, lane);
     };
     // Tiles of gathers in flight per wave (the layout's; two measured slower
-    // for the decode step's split shares too: 25.4 against 24.6 us).
+    // for the decode step's split shares too: 25.4 against 24.6 us at 8
+    // items per CU, 23.2 against 22.5 at 4).
     constexpr int kAhead = Lay::kAhead;
     // Masked rows: the valid-row mask and invalid count of the tile being
     // computed (cur) and of the tiles whose gathers are in flight, one per
@@ -773,8 +774,8 @@ __global__ __launch_bounds__(64, (AttendLayout<kQRows, kItems>::kWavesPerSimd)) 
 // M = max_s m_s; exactly +0.0 when no part saw a slot.  One 256-thread
 // workgroup per (t, h) row, 4 dims per lane: wave w takes the parts
 // s = w + 4 j.  A wave issues the O loads of its first kMergeBatch parts
-// together with the (m, l) loads (they do not depend on M), so a decode's
-// 32 parts arrive in one memory round trip; the four waves then exchange
+// together with the (m, l) loads (they do not depend on M), so up to 32
+// parts arrive in one memory round trip; the four waves then exchange
 // their maxima and their weighted sums through LDS, added in wave order.
 // (One wave per row, its parts read 8 at a time, took 6.4 us on the decode
 // step: four dependent round trips.)
@@ -1271,12 +1272,21 @@ hipError_t launch_attend_partial(const AttendParams &p, KvType kv, int64_t T,
                                  hipStream_t stream) {
     const int64_t blocks = T * (int64_t)p.Hkv * p.HB * p.splits;
     if (blocks == 0) return hipSuccess;
-    if (p.raw_rows) {   // raw selection rows, masked per tile; the layouts of launch_attend_any
+    if (p.raw_rows) {   // raw selection rows, masked per tile
         if (p.raw == nullptr && p.W_raw > 0) return hipErrorInvalidValue;
+        // The layouts of launch_attend_any, except that BF16 shares take the
+        // 4-items-per-CU layout from kDecodeMinUnits units up (decode step of
+        // 16 tokens at 16 shares: 21.0 against 22.7 us; 64 tokens at 8 shares:
+        // 53.2 against 53.4) and the 8-items one below (1 to 4 tokens at 32
+        // shares: 0.2-0.3 us faster).  FP8 caches: the 8-items layouts
+        // measured faster (17.1 against 18.1 us on the 16-token step).
         if (kv == KvType::kFp8 && p.G <= 8)
             launch_attend_kernel<true, KvType::kFp8, 8, kItemsPerCU, true>(p, blocks, stream);
         else if (kv == KvType::kFp8)
             launch_attend_kernel<true, KvType::kFp8, 16, kItemsPerCU, true>(p, blocks, stream);
+        else if (blocks >= kDecodeMinUnits)
+            launch_attend_kernel<true, KvType::kBf16, 16, kLowShareItemsPerCU, true>(p, blocks,
+                                                                                      stream);
         else
             launch_attend_kernel<true, KvType::kBf16, 16, kItemsPerCU, true>(p, blocks, stream);
         return hipGetLastError();

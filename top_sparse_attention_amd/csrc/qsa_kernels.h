@@ -53,8 +53,19 @@ constexpr int kShareLongList = 1024;
 // near 8.5 on the long prefill's shape: 4% slower at 8.0, 14% faster at 10.7,
 // 16-17% faster at 13 and above).
 constexpr float kShareKeysLds = 9.0f;
-// Fewest tiles a split of the decode path takes.
+// Splits of the decode path (decode_splits): about kDecodeUnits work units
+// (one share of one item each), a wave slot each of the 4-items-per-CU
+// layout; shares of at least kDecodeShareTiles tiles unless that leaves
+// fewer than kDecodeMinUnits units, and never under kMinSplitTiles.  Fewer
+// shares write and merge fewer partial rows (at 32 shares of a 2,048-entry
+// row, the partials of 24 query heads are 38% of the K and V bytes the
+// shares gather); more units keep more gathers in flight where few tokens
+// run.  From kDecodeMinUnits units up, BF16 shares take the 4-items-per-CU
+// layout.
 constexpr int kMinSplitTiles = 4;
+constexpr int kDecodeShareTiles = 8;
+constexpr int kDecodeUnits = 1024;
+constexpr int kDecodeMinUnits = 512;
 // Entries of a selection row sorted together by the compaction pass.
 constexpr int kSortThreads = 256;
 constexpr int kSortItemsPerThread = 9;
