@@ -288,8 +288,9 @@ qsa_status qsa_merge_partials(const void *partials, size_t partials_bytes,
                               qsa_bf16_view *out, void *stream);
 
 /* Splits per item that qsa_sparse_decode uses for these sizes (a pure
- * function of the sizes: enough workgroups to cover the GPU, at least four
- * 16-slot tiles per split, at most 64). */
+ * function of the sizes: about 1,024 workgroups; at least eight 16-slot tiles
+ * per split unless that leaves fewer than 512 workgroups; at least four; at
+ * most 64 splits). */
 int32_t qsa_decode_splits(int64_t T, int64_t W, int32_t Hq, int32_t Hkv);
 
 /* Workspace bytes for qsa_sparse_decode: the area of qsa_workspace_bytes(T, W)
