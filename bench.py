@@ -343,20 +343,28 @@ def main():
     if not args.no_cold:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         steps_ms, attend_ms_cold = [], []
+        # The step with no events inside it (as in the warm loop; an event
+        # between two launches adds a few microseconds to a short step), then
+        # separate steps with events around the attention alone.
         for _ in range(min(K, 10)):
             flush.fill_(1)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             ev[0].record()
+            step()
+            ev[1].record()
+            torch.cuda.synchronize()
+            steps_ms.append(ev[0].elapsed_time(ev[1]))
+        for _ in range(min(K, 10)):
+            flush.fill_(1)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             select()
             compact()
-            ev[1].record()
+            ev[0].record()
             attend()
-            ev[2].record()
+            ev[1].record()
             finish()
-            ev[3].record()
             torch.cuda.synchronize()
-            steps_ms.append(ev[0].elapsed_time(ev[3]))
-            attend_ms_cold.append(ev[1].elapsed_time(ev[2]))
+            attend_ms_cold.append(ev[0].elapsed_time(ev[1]))
         cold = {"ms_per_step_median": float(np.median(steps_ms)),
                 "attend_kernel_ms_median": float(np.median(attend_ms_cold)),
                 "steps": len(steps_ms), "flush_bytes": 1 << 30}
