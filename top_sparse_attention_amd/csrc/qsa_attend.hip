@@ -531,6 +531,17 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
     // whose waves share the scalar unit of the CU) and at 4 items per CU,
     // where the vector form measured 2-5% faster.
     constexpr bool kScalarVAddr = KV == KvType::kBf16 && Lay::kItems == 8;
+    // Wave priority (BF16 keys straight into the MFMA operands): the wave
+    // computing its scores, softmax and P.V, with the next tile's K gathers
+    // spread over the P.V, takes issue priority over the waves of its SIMD
+    // that stage V and issue the next tile's whole-row V gathers.  The V
+    // gathers of the waves then reach the memory system at the pace of the
+    // others' arithmetic rather than in bursts: long prefill 2.36 against
+    // 2.43 ms per step.  The whole-row K gathers of the keys-through-LDS form
+    // and the FP8 tiles measured slower this way (two requests 2.12 against
+    // 1.98 ms with the priority held over those K gathers), and a priority
+    // raised over the V gathers instead made the long prefill 17% slower.
+    constexpr bool kPrio = KV == KvType::kBf16 && !kKeysLds;
     const int step = splits;
     u32x4_t rkb[kAhead][Gth::kKLoads], rvb[kAhead][Gth::kVLoads];
     int tile = split;
@@ -575,6 +586,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         // The query operands are read from LDS in two halves to bound the
         // registers they hold (with the keys through LDS they stay in
         // registers, and the K operands come from the tile instead).
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
         int slot_g = 0;   // slots of the tile whose gathers go out next
         bf16x8_t ka[kKeysLds ? kKSteps : 1];
@@ -673,6 +685,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
             lsum += (float)pr;
         }
 
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
         wave_lds_fence();   // the previous tile's transpose reads are done
         stage_v<KV, Lay::kVPitch>(rv, vs_lds, lane);
         __builtin_amdgcn_sched_barrier(0);   // V(i) is consumed before V(i+1) lands
@@ -682,6 +695,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         gather_v<KV, kScalarVAddr>(rv, slot_g, vb, v_ss, lane);
         wave_lds_fence();   // other lanes of this wave wrote the rows read below
 
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
         // O^T += V^T . P^T over the tile's 16 slots.  The k index of lane
         // group j is slots 4j..4j+3, matching pb.  ds_read_b64_tr_b16: lane i
         // of a 16-lane group addresses row 4j + i/4, dims 16 db + 4 (i%4);
@@ -714,6 +728,7 @@ __device__ __forceinline__ void attend_unit(const AttendParams &p, const int64_t
         for (int b = 0; b < kAhead; ++b) {
             if (b > 0 && tile + b * step >= ntiles) break;
             tile_body(tile + b * step, rkb[b], rvb[b], b);
+            if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
         }
     }
 
