@@ -101,7 +101,7 @@ def aligned_lists_model(block_idx, S, bs):
         valid = r[(r >= 0) & (r < nb)]
         valid = valid[np.argsort(valid >> group_shift, kind="stable")]
         n = len(valid)
-        F = (9 * n + 8 * R - 1) // (8 * R)
+        F = (33 * n + 32 * R - 1) // (32 * R)
         end, rem, out = 0, n, []
         for kk in range(R):
             seg = valid[(valid >> shift) == kk]

@@ -78,11 +78,14 @@ constexpr int kSortKeyBits = 8;
 // (the sort's 128 groups); the room a row may take, kAlignRoomNum /
 // kAlignRoomDen of its blocks; and the slack of the fixed start positions:
 // super-range k starts near k F, F = kAlignSlackNum / kAlignSlackDen times
-// the row's mean blocks per super-range.
+// the row's mean blocks per super-range (33/32: with the attention's wave
+// priority the waves keep in step on their own, and 33/32 measured 2.42-2.43
+// ms on the block4 long prefill against 2.43-2.44 at 17/16, 2.47-2.48 at 9/8
+// and 2.58-2.59 at 5/4).
 constexpr int kAlignSlots = 2048;
 constexpr int kAlignMaxRanges = 1 << (kSortKeyBits - 1);
 constexpr int kAlignRoomNum = 3, kAlignRoomDen = 2;
-constexpr int kAlignSlackNum = 9, kAlignSlackDen = 8;
+constexpr int kAlignSlackNum = 33, kAlignSlackDen = 32;
 // Largest room of an aligned row (entries): the compaction builds the row in
 // LDS before storing it.
 constexpr int kAlignRoomMax = 4096;
